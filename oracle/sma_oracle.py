@@ -1,0 +1,206 @@
+"""CPU oracle for the sparse-MLA prefill path: indexer -> top-k -> sparse MLA.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package entry's smoke check
+and the bench's CPU-baseline leg may import this module.  The GPU library
+never calls it and shares no code with it.
+
+It is the method written out plainly, one query at a time, in float64
+(the pages fix no precision; float64 is at least as accurate as the fp32
+accumulation the GPU kernels use).  Library primitives (a matrix product,
+``np.partition``, ``np.exp``) serve as steps; there is no blocking, fusion
+or reordering beyond what each definition states.
+
+Sources, by page and section:
+
+* GLM-5.3 part 2 (PCP, DCP and Hybrid HiSparse on 16 H200), section
+  "Pourquoi pas TP ou DP ?": the indexer scores every earlier token of the
+  prompt and keeps the 2,048 that sparse MLA then reads.
+* same page, section "PCP : répartir les tokens, pas les têtes": sparse MLA
+  runs with every latent KV row serving all 64 heads; the prompt is cut into
+  16 chunks and each of 8 GPUs takes one early and one late chunk.
+* same page, section "Essayez-le": with the MQA mode forced, prompts that fit
+  inside top-k still run sparse MLA (so sparse equals dense causal there).
+* same page, footnote 1: QK runs over 576 dims, PV over 512; indices are
+  4 bytes; q and o are bf16.
+* same page, footnote 3: an FP8 key is 128 values plus a 4-byte scale.
+* DeepSeek multi-node deployment page (Perplexity), sections
+  "Parallélisme de tenseurs" and "Travaux futurs": the latent is shared by
+  all heads; kv_b_proj maps it to each head; decode absorbs the projection.
+
+Readings where the pages are silent (each also listed in the design notes):
+
+* indexer score I[i,s] = sum_h w[i,h] * ReLU(q_I[i,h,:] . k_I[s,:]) for
+  0 <= s <= p_i (the query's own token included), no bias, no scaling;
+* top-k keeps the min(K, p_i+1) largest scores; ties at the threshold go to
+  the lowest positions; the list is ascending by position, padded with -1;
+  -0.0 and +0.0 are the same value;
+* attention scale tau = 1/sqrt(192); value = the first 512 latent dims;
+  LSE is the natural-log log-sum-exp of the scaled logits;
+* FP8 is OCP e4m3fn (bias 7, max 448, no infinities) times a per-token fp32
+  scale; the oracle dequantises first, then runs the same steps.
+
+Pins: tests/test_oracle_*.py check each function against what the pages and
+the mathematics fix (integer brute force, library routines for the dense and
+non-absorbed special cases, invariants, the FP8 library cast, the pages'
+printed byte and FLOP figures).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+D_QK = 576
+D_V = 512
+
+
+# ---------------------------------------------------------------- storage --
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 is the upper half of an fp32: widen the 16 bits and reinterpret."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_value(code: int) -> float:
+    """Value of one OCP FP8 E4M3FN code: 1 sign, 4 exponent (bias 7),
+    3 mantissa bits; exponent 0 is subnormal; S.1111.111 is NaN; no inf."""
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** (1 - 7)
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e4m3fn_table() -> np.ndarray:
+    return np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+_E4M3 = e4m3fn_table()
+
+
+def fp8_rows_to_f64(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Dequantise per-token FP8 rows: x[s, :] = e4m3(code[s, :]) * scale[s]
+    (GLM-5.3 part 2, footnote 3: 128 FP8 values plus a 4-byte scale)."""
+    return _E4M3[np.asarray(codes, dtype=np.uint8)] * np.asarray(scale, dtype=np.float64)[:, None]
+
+
+def keys_f64(k, fp8: bool) -> np.ndarray:
+    return fp8_rows_to_f64(*k) if fp8 else bf16_bits_to_f64(k)
+
+
+# ----------------------------------------------------------------- a1 -----
+
+def index_scores(q_idx: np.ndarray, w: np.ndarray, k_idx: np.ndarray, q_pos: np.ndarray) -> list:
+    """Indexer scores of each query over its causal prefix.
+
+    q_idx [n_q, H_I, d_I] float64, w [n_q, H_I] float64, k_idx [n_k, d_I]
+    float64, q_pos [n_q] int.  Returns a list: entry i is the float64 vector
+    I[i, 0..p_i] with I[i,s] = sum_h w[i,h] * max(0, q_idx[i,h,:] . k_idx[s,:]).
+    "Scores every earlier token" (GLM-5.3 part 2, "Pourquoi pas TP ou DP ?");
+    the query's own position is included.
+    """
+    out = []
+    for i in range(q_idx.shape[0]):
+        p = int(q_pos[i])
+        dots = q_idx[i] @ k_idx[: p + 1].T          # [H_I, p+1]
+        out.append(w[i] @ np.maximum(dots, 0.0))    # [p+1]
+    return out
+
+
+# ----------------------------------------------------------------- a2 -----
+
+def topk_row(scores: np.ndarray, top_k: int) -> np.ndarray:
+    """Top-k of one causal row (positions 0..len-1), ascending, -1 padded.
+
+    Keeps m = min(top_k, len) positions: every position whose score is above
+    the m-th largest value T, then the lowest positions whose score equals T
+    until m are kept.
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.size
+    m = min(top_k, n)
+    out = np.full(top_k, -1, dtype=np.int32)
+    if m == 0:
+        return out
+    t = np.partition(s, n - m)[n - m]               # m-th largest value
+    above = np.flatnonzero(s > t)
+    ties = np.flatnonzero(s == t)[: m - above.size]
+    sel = np.sort(np.concatenate([above, ties]))
+    out[:m] = sel
+    return out
+
+
+def topk_select(score_rows: list, top_k: int) -> np.ndarray:
+    return np.stack([topk_row(r, top_k) for r in score_rows]) if score_rows else \
+        np.zeros((0, top_k), dtype=np.int32)
+
+
+def topk_threshold(scores: np.ndarray, top_k: int) -> float:
+    """The m-th largest score of a row (the value the selection is cut at)."""
+    s = np.asarray(scores, dtype=np.float64)
+    m = min(top_k, s.size)
+    return float(np.partition(s, s.size - m)[s.size - m])
+
+
+# ----------------------------------------------------------------- a4 -----
+
+def sparse_mla(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, sm_scale: float):
+    """Absorbed (MQA-mode) sparse MLA over each query's selected latent rows.
+
+    q [n_q, H, 576] float64, kv [n_k, 576] float64, idx [n_q, K] int
+    (negative entries are padding).  For each query i and head h over the
+    selected set S_i: z_s = tau * q[i,h,:] . kv[s,:576];
+    o[i,h,:] = sum_s softmax(z)_s * kv[s,:512]; lse[i,h] = log sum_s exp(z_s).
+    One latent row serves all heads (GLM-5.3 part 2, "PCP : répartir les
+    tokens, pas les têtes"); QK over 576, PV over 512 (footnote 1).
+    An empty set gives o = 0 and lse = -inf.
+    """
+    n_q, n_h, _ = q.shape
+    out = np.zeros((n_q, n_h, D_V), dtype=np.float64)
+    lse = np.full((n_q, n_h), -np.inf, dtype=np.float64)
+    for i in range(n_q):
+        sel = idx[i][idx[i] >= 0]
+        if sel.size == 0:
+            continue
+        rows = kv[sel]                               # [m, 576]
+        z = sm_scale * (q[i] @ rows.T)               # [H, m]
+        mx = z.max(axis=1, keepdims=True)
+        e = np.exp(z - mx)
+        den = e.sum(axis=1, keepdims=True)
+        out[i] = (e @ rows[:, :D_V]) / den
+        lse[i] = mx[:, 0] + np.log(den[:, 0])
+    return out, lse
+
+
+# --------------------------------------------------------------- compose --
+
+def prefill(q_idx, w, k_idx, q, kv, q_pos, top_k: int, sm_scale: float):
+    """indexer -> top-k -> sparse MLA for the given query rows (float64 in)."""
+    scores = index_scores(q_idx, w, k_idx, q_pos)
+    idx = topk_select(scores, top_k)
+    out, lse = sparse_mla(q, kv, idx, sm_scale)
+    return scores, idx, out, lse
+
+
+def pcp_positions(rank: int, pcp_size: int, L_total: int) -> np.ndarray:
+    """Query positions of one PCP rank: the prompt is cut into 2*pcp_size
+    equal chunks and rank r takes chunk r and chunk 2*pcp_size-1-r, in that
+    order (GLM-5.3 part 2, "PCP : répartir les tokens, pas les têtes"; the
+    page's figure text naming the pair is lost, the pair (r, 15-r) for 8
+    ranks is the plain reading of 'one early and one late chunk')."""
+    nchunk = 2 * pcp_size
+    if not (0 <= rank < pcp_size) or L_total % nchunk:
+        raise ValueError("rank out of range or L_total not divisible by 2*pcp_size")
+    c = L_total // nchunk
+    return np.concatenate([np.arange(rank * c, (rank + 1) * c),
+                           np.arange((nchunk - 1 - rank) * c, (nchunk - rank) * c)]).astype(np.int32)
+
+
+def pcp_rank_share(rank: int, pcp_size: int, q_idx_full, w_full, k_idx, q_full, kv,
+                   top_k: int, sm_scale: float):
+    """One rank's share: rows of the full prompt at pcp_positions(rank),
+    run through the same three steps against the whole causal context."""
+    pos = pcp_positions(rank, pcp_size, k_idx.shape[0])
+    return prefill(q_idx_full[pos], w_full[pos], k_idx, q_full[pos], kv, pos, top_k, sm_scale)
