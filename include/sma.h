@@ -1,0 +1,203 @@
+/*
+ * sma.h — C ABI of the MI355X (gfx950) sparse-MLA prefill path:
+ *   indexer scores -> per-query top-k -> sparse MLA over the selected
+ *   latent rows, plus one PCP rank's load-balanced share.
+ *
+ * The operations follow the GLM-5.3 part 2 article (PCP, DCP and Hybrid
+ * HiSparse on 16 H200):
+ *   - section "Pourquoi pas TP ou DP ?": an indexer scores every earlier
+ *     token of the prompt and keeps the 2,048 that sparse MLA consults;
+ *   - section "PCP : répartir les tokens, pas les têtes": one latent KV row
+ *     serves all 64 heads; a prompt is cut into 16 chunks and each of 8
+ *     ranks computes one early and one late chunk;
+ *   - footnote 1: QK over 576 dims, PV over 512, a 4-byte index per
+ *     selected row, bf16 query and output;
+ *   - footnote 3: an FP8 key row carries a 4-byte scale.
+ * The indexer's form (ReLU of per-head dot products, weighted by a per-head
+ * weight and summed over heads, causal with the query's own token
+ * included), the lowest-position tie-break and "value = first 512 dims"
+ * are the readings this library implements where the pages are silent.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is DEVICE memory owned by the caller, row-major,
+ *    contiguous except where a stride argument is given.  The library never
+ *    allocates, frees or keeps a pointer after returning.  Scratch memory is
+ *    the caller's workspace (sma_workspace_bytes).
+ *  - bf16 tensors are passed as uint16_t bit patterns.  FP8 tensors are OCP
+ *    e4m3fn codes (uint8_t) with one fp32 scale per row (value = code*scale,
+ *    scale >= 0).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *    enqueued on it in order; no call synchronises the host.
+ *  - Arguments are validated on the host before anything is launched.  A bad
+ *    call returns a negative sma_status, launches nothing, and leaves a
+ *    message for sma_last_error() (thread-local).  A failed launch returns
+ *    SMA_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *    synchronisation.
+ *  - Device-resident values the host cannot see are made safe in the
+ *    kernels: a query position p is clamped to [-1, n_k-1] (p = -1 means an
+ *    empty causal prefix); an index outside [0, n_k) in an index list is
+ *    skipped like the -1 padding.
+ *  - Results are deterministic: the same inputs give bit-identical outputs,
+ *    whatever the launch split (a PCP share equals the matching rows of the
+ *    unsharded call).
+ *  - Only gfx950 devices are supported (SMA_ERR_UNSUPPORTED otherwise).
+ */
+#ifndef SMA_H
+#define SMA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SMA_OK = 0,
+  SMA_ERR_INVALID_ARG = -1,
+  SMA_ERR_UNSUPPORTED = -2,
+  SMA_ERR_WORKSPACE = -3,
+  SMA_ERR_HIP = -4
+} sma_status;
+
+typedef enum { SMA_DT_BF16 = 0, SMA_DT_FP8_E4M3 = 1, SMA_DT_FP32 = 2 } sma_dtype;
+
+typedef enum {
+  SMA_OP_INDEX_SCORES = 0,
+  SMA_OP_TOPK = 1,
+  SMA_OP_SPARSE_MLA = 2,
+  SMA_OP_PREFILL = 3,
+  SMA_OP_PCP_SHARE = 4
+} sma_op;
+
+/* Fixed MLA geometry: 64 heads share one 576-wide latent row (512 latent +
+ * 64 rope); the value is the first 512 dims. */
+#define SMA_HEADS 64
+#define SMA_D_QK 576
+#define SMA_D_V 512
+#define SMA_MAX_TOPK 2048
+
+/*
+ * sma_index_scores — indexer scores over each query's causal prefix
+ * (GLM-5.3 part 2, "Pourquoi pas TP ou DP ?").
+ *
+ *   scores[i*ld + s] = sum_h w[i*w_stride + h] * max(0, q_idx[i,h,:] . k_idx[s,:])
+ *   for 0 <= s <= p_i, p_i = clamp(q_pos[i], -1, n_k-1);
+ *   with FP8 keys the key row is code*k_scale[s].
+ *
+ *  q_idx    [n_q, h_idx, d_idx] bf16
+ *  w        fp32, element (i,h) at w[i*w_stride + h]; w_stride = 0 shares
+ *           one [h_idx] vector across queries
+ *  k_idx    [n_k, d_idx] bf16, or e4m3fn codes when k_dtype = SMA_DT_FP8_E4M3
+ *  k_scale  [n_k] fp32 when FP8, else must be NULL
+ *  q_pos    [n_q] int32 global positions
+ *  scores   [n_q, ld_scores] fp32; only s <= p_i is written, the rest of the
+ *           row is left untouched
+ *  Supported: h_idx in {8,16,32,64}, d_idx in {64,128}, ld_scores >= n_k,
+ *  n_k < 2^31.  n_q = 0 is a no-op.  Products are bf16 x bf16 with fp32
+ *  accumulation; the ReLU, head weights and head sum are fp32.
+ */
+sma_status sma_index_scores(const uint16_t* q_idx, const float* w, int64_t w_stride,
+                            const void* k_idx, const float* k_scale, int32_t k_dtype,
+                            const int32_t* q_pos, int32_t n_q, int64_t n_k,
+                            int32_t h_idx, int32_t d_idx,
+                            float* scores, int64_t ld_scores, void* stream);
+
+/*
+ * sma_topk_select — per-query top-k of the causal scores (same article,
+ * "Pourquoi pas TP ou DP ?"; 4-byte indices, footnote 1).
+ *
+ *  Row i holds n_i = clamp(q_pos[i], -1, n_k-1) + 1 scores at
+ *  scores[i*ld_scores + 0 .. n_i-1].  idx[i*top_k + 0 .. m_i-1] receives the
+ *  m_i = min(top_k, n_i) positions with the largest scores, in ascending
+ *  position order; slots m_i .. top_k-1 receive -1.  Ties at the threshold
+ *  go to the lowest positions; -0.0 and +0.0 are one value; a NaN ranks
+ *  above every number.
+ *  Supported: 1 <= top_k <= 2048, ld_scores >= n_k, n_k < 2^31.
+ *  ws/ws_bytes: workspace (sma_workspace_bytes(SMA_OP_TOPK, ...), may be 0).
+ */
+sma_status sma_topk_select(const float* scores, int64_t ld_scores, const int32_t* q_pos,
+                           int32_t n_q, int64_t n_k, int32_t top_k, int32_t* idx,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sma_sparse_mla_prefill — absorbed ("MQA" mode) sparse MLA: all 64 heads
+ * of query i attend over the latent rows idx[i, :] (same article, "PCP :
+ * répartir les tokens, pas les têtes", "Essayez-le", footnote 1).
+ *
+ *   z_s      = sm_scale * q[i,h,:] . kv[s, 0:576]          for s in S_i
+ *   out[i,h] = sum_s softmax(z)_s * kv[s, 0:512]
+ *   lse[i,h] = log(sum_s exp(z_s))                          (natural log)
+ *
+ *  q        [n_q, 64, 576] bf16
+ *  kv       [n_k, 576] bf16, or e4m3fn codes with kv_scale [n_k] fp32
+ *  idx      [n_q, top_k] int32; entries < 0 or >= n_k are skipped
+ *  out      [n_q, 64, 512], out_dtype SMA_DT_BF16 or SMA_DT_FP32
+ *  lse      [n_q, 64] fp32, or NULL.  A query with no valid index gets
+ *           out = 0 and lse = -inf.
+ *  Softmax and accumulation are fp32; QK and PV run on bf16 MFMA (an FP8
+ *  row is widened to bf16 exactly; its scale multiplies the logit and the
+ *  softmax weight).
+ *  Supported: 1 <= top_k <= 2048.  ws may be NULL (ws_bytes 0).
+ */
+sma_status sma_sparse_mla_prefill(const uint16_t* q, const void* kv, const float* kv_scale,
+                                  int32_t kv_dtype, int64_t n_k, const int32_t* idx,
+                                  int32_t n_q, int32_t top_k, float sm_scale,
+                                  void* out, int32_t out_dtype, float* lse,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sma_prefill — indexer -> top-k -> sparse MLA for n_q query rows at
+ * positions q_pos against the n_k-row context.  Arguments as above.
+ *  idx_out  [n_q, top_k] int32 or NULL (then kept in the workspace).
+ *  The scores are produced block by block in the workspace; a larger
+ *  workspace allows larger query blocks (fewer launches), never different
+ *  results.  Minimum size: sma_workspace_bytes(SMA_OP_PREFILL, ...).
+ */
+sma_status sma_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride,
+                       const void* k_idx, const float* k_scale, int32_t k_dtype,
+                       const uint16_t* q, const void* kv, const float* kv_scale, int32_t kv_dtype,
+                       const int32_t* q_pos, int32_t n_q, int64_t n_k,
+                       int32_t h_idx, int32_t d_idx, int32_t top_k, float sm_scale,
+                       void* out, int32_t out_dtype, float* lse, int32_t* idx_out,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sma_pcp_rank_share — one PCP rank's share of a prompt of L_total tokens
+ * cut into 2*pcp_size equal chunks of C = L_total/(2*pcp_size) tokens
+ * (same article, "PCP : répartir les tokens, pas les têtes": one early and
+ * one late chunk per rank; the pair is (rank, 2*pcp_size-1-rank)).
+ *
+ *  The share's 2C query rows are chunk `rank` (positions rank*C ..) followed
+ *  by chunk 2*pcp_size-1-rank; q_idx_share, w_share, q_share, out_share,
+ *  lse_share and idx_share are indexed by these 2C rows.  k_idx and kv hold
+ *  the whole gathered context (L_total rows).  The positions are built on
+ *  the device in the workspace; the rest is sma_prefill.
+ *  Requires 0 <= rank < pcp_size and L_total % (2*pcp_size) == 0.
+ */
+sma_status sma_pcp_rank_share(int32_t rank, int32_t pcp_size, int64_t L_total,
+                              const uint16_t* q_idx_share, const float* w_share, int64_t w_stride,
+                              const void* k_idx, const float* k_scale, int32_t k_dtype,
+                              const uint16_t* q_share, const void* kv, const float* kv_scale,
+                              int32_t kv_dtype, int32_t h_idx, int32_t d_idx, int32_t top_k,
+                              float sm_scale, void* out_share, int32_t out_dtype, float* lse_share,
+                              int32_t* idx_share, void* ws, size_t ws_bytes, void* stream);
+
+/* Minimum workspace in bytes for `op` (an sma_op) at these sizes.  For
+ * SMA_OP_PREFILL / SMA_OP_PCP_SHARE, n_q is the number of query rows and the
+ * figure assumes idx_out == NULL (the index list lives in the workspace). */
+size_t sma_workspace_bytes(int32_t op, int32_t n_q, int64_t n_k, int32_t top_k,
+                           int32_t h_idx, int32_t d_idx);
+
+/* Message of the calling thread's last failed call ("" if none).  The
+ * pointer stays valid until the thread's next call into the library. */
+const char* sma_last_error(void);
+
+/* ABI version: (major << 16) | minor. */
+int32_t sma_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SMA_H */

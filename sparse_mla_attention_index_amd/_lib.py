@@ -1,0 +1,216 @@
+"""ctypes binding of libsma.so (the HIP kernels behind include/sma.h).
+
+Argument marshalling only: every step of the path runs in the library's
+kernels.  Tensors are torch tensors on one ROCm device; bf16 data may be
+passed as torch.bfloat16 or as 16-bit integer bit patterns, FP8 data as
+torch.float8_e4m3fn or uint8 codes.  Work is enqueued on torch's current
+stream of the tensors' device.  Any failure raises SmaError carrying the
+library's message; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsma.so")
+
+SMA_DT_BF16, SMA_DT_FP8_E4M3, SMA_DT_FP32 = 0, 1, 2
+SMA_OP_INDEX_SCORES, SMA_OP_TOPK, SMA_OP_SPARSE_MLA, SMA_OP_PREFILL, SMA_OP_PCP_SHARE = 0, 1, 2, 3, 4
+HEADS, D_QK, D_V = 64, 576, 512
+
+# (name, restype, argtypes) of every entry point declared in include/sma.h
+_P, _I32, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+SIGNATURES = {
+    "sma_index_scores": (_I32, [_P, _P, _I64, _P, _P, _I32, _P, _I32, _I64, _I32, _I32, _P, _I64, _P]),
+    "sma_topk_select": (_I32, [_P, _I64, _P, _I32, _I64, _I32, _P, _P, _SZ, _P]),
+    "sma_sparse_mla_prefill": (_I32, [_P, _P, _P, _I32, _I64, _P, _I32, _I32, _F, _P, _I32, _P, _P, _SZ, _P]),
+    "sma_prefill": (_I32, [_P, _P, _I64, _P, _P, _I32, _P, _P, _P, _I32, _P, _I32, _I64, _I32, _I32, _I32, _F,
+                           _P, _I32, _P, _P, _P, _SZ, _P]),
+    "sma_pcp_rank_share": (_I32, [_I32, _I32, _I64, _P, _P, _I64, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
+                                  _I32, _F, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "sma_workspace_bytes": (_SZ, [_I32, _I32, _I64, _I32, _I32, _I32]),
+    "sma_last_error": (ctypes.c_char_p, []),
+    "sma_version": (_I32, []),
+}
+
+_lib = None
+
+
+class SmaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"sma status {status}: {msg}")
+        self.status = status
+
+
+def lib():
+    """Load libsma.so (raises if it was not built: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with "
+                              "`python -m sparse_mla_attention_index_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().sma_last_error().decode()
+
+
+def version() -> int:
+    return int(lib().sma_version())
+
+
+def workspace_bytes(op: int, n_q: int, n_k: int, top_k: int, h_idx: int = 64, d_idx: int = 128) -> int:
+    return int(lib().sma_workspace_bytes(op, n_q, n_k, top_k, h_idx, d_idx))
+
+
+def _check(status: int):
+    if status != 0:
+        raise SmaError(status, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _bf16(t, name):
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name}: expected bf16 data (bfloat16 or 16-bit bit patterns), got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _keys(t, scale, name):
+    """-> dtype code for a key/KV tensor (bf16 or FP8 codes + per-row scale)."""
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        if scale is None or scale.dtype != torch.float32 or not scale.is_contiguous():
+            raise ValueError(f"{name}: FP8 data needs a contiguous fp32 per-row scale")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return SMA_DT_FP8_E4M3
+    _bf16(t, name)
+    if scale is not None:
+        raise ValueError(f"{name}: a scale is only taken with FP8 data")
+    return SMA_DT_BF16
+
+
+def _w_stride(w, n_q, h):
+    if w.dtype != torch.float32 or w.dim() != 2 or w.shape[1] != h or w.stride(1) != 1:
+        raise ValueError("w must be fp32 [n_q, h_idx] with unit stride along heads")
+    return int(w.stride(0)) if n_q > 1 or w.stride(0) == 0 else h
+
+
+def index_scores(q_idx, w, k_idx, q_pos, *, k_scale=None, scores=None):
+    """Indexer scores [n_q, n_k] fp32; only s <= q_pos[i] is written."""
+    n_q, h, d = q_idx.shape
+    n_k = k_idx.shape[0]
+    _bf16(q_idx, "q_idx")
+    kdt = _keys(k_idx, k_scale, "k_idx")
+    if q_pos.dtype != torch.int32 or not q_pos.is_contiguous():
+        raise ValueError("q_pos must be contiguous int32")
+    if scores is None:
+        scores = torch.empty((n_q, n_k), dtype=torch.float32, device=q_idx.device)
+    if scores.dtype != torch.float32 or scores.stride(1) != 1:
+        raise ValueError("scores must be fp32 with unit column stride")
+    _check(lib().sma_index_scores(_ptr(q_idx), _ptr(w), _w_stride(w, n_q, h), _ptr(k_idx), _ptr(k_scale), kdt,
+                                  _ptr(q_pos), n_q, n_k, h, d, _ptr(scores), scores.stride(0),
+                                  _stream(q_idx.device)))
+    return scores
+
+
+def topk_select(scores, q_pos, top_k: int, *, n_k: int | None = None, idx=None):
+    """Top-k positions per row, ascending, -1 padded: int32 [n_q, top_k]."""
+    n_q = scores.shape[0]
+    n_k = scores.shape[1] if n_k is None else n_k
+    if scores.dtype != torch.float32 or scores.stride(1) != 1:
+        raise ValueError("scores must be fp32 with unit column stride")
+    if q_pos.dtype != torch.int32 or not q_pos.is_contiguous():
+        raise ValueError("q_pos must be contiguous int32")
+    if idx is None:
+        idx = torch.empty((n_q, top_k), dtype=torch.int32, device=scores.device)
+    _check(lib().sma_topk_select(_ptr(scores), scores.stride(0), _ptr(q_pos), n_q, n_k, top_k, _ptr(idx),
+                                 None, 0, _stream(scores.device)))
+    return idx
+
+
+def sparse_mla_prefill(q, kv, idx, sm_scale: float, *, kv_scale=None, out=None, out_dtype=torch.bfloat16,
+                       lse=None, want_lse: bool = False):
+    """Sparse MLA over idx: returns (out [n_q, 64, 512], lse [n_q, 64] or None)."""
+    n_q = q.shape[0]
+    _bf16(q, "q")
+    kdt = _keys(kv, kv_scale, "kv")
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32")
+    if out is None:
+        out = torch.empty((n_q, HEADS, D_V), dtype=out_dtype, device=q.device)
+    odt = SMA_DT_FP32 if out.dtype == torch.float32 else SMA_DT_BF16
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, HEADS), dtype=torch.float32, device=q.device)
+    _check(lib().sma_sparse_mla_prefill(_ptr(q), _ptr(kv), _ptr(kv_scale), kdt, kv.shape[0], _ptr(idx), n_q,
+                                        idx.shape[1], float(sm_scale), _ptr(out), odt, _ptr(lse), None, 0,
+                                        _stream(q.device)))
+    return out, lse
+
+
+def prefill(q_idx, w, k_idx, q, kv, q_pos, top_k: int, sm_scale: float, *, k_scale=None, kv_scale=None,
+            out=None, out_dtype=torch.bfloat16, want_lse=False, idx_out=None, workspace=None):
+    """indexer -> top-k -> sparse MLA; returns (out, lse or None, idx or None)."""
+    n_q, h, d = q_idx.shape
+    n_k = k_idx.shape[0]
+    kdt = _keys(k_idx, k_scale, "k_idx")
+    vdt = _keys(kv, kv_scale, "kv")
+    _bf16(q_idx, "q_idx")
+    _bf16(q, "q")
+    dev = q.device
+    if out is None:
+        out = torch.empty((n_q, HEADS, D_V), dtype=out_dtype, device=dev)
+    odt = SMA_DT_FP32 if out.dtype == torch.float32 else SMA_DT_BF16
+    lse = torch.empty((n_q, HEADS), dtype=torch.float32, device=dev) if want_lse else None
+    if workspace is None:
+        nbytes = workspace_bytes(SMA_OP_PREFILL, n_q, n_k, top_k, h, d)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().sma_prefill(_ptr(q_idx), _ptr(w), _w_stride(w, n_q, h), _ptr(k_idx), _ptr(k_scale), kdt,
+                             _ptr(q), _ptr(kv), _ptr(kv_scale), vdt, _ptr(q_pos), n_q, n_k, h, d, top_k,
+                             float(sm_scale), _ptr(out), odt, _ptr(lse), _ptr(idx_out), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, lse, idx_out
+
+
+def pcp_rank_share(rank: int, pcp_size: int, q_idx_share, w_share, k_idx, q_share, kv, top_k: int,
+                   sm_scale: float, *, k_scale=None, kv_scale=None, out=None, out_dtype=torch.bfloat16,
+                   want_lse=False, idx_share=None, workspace=None):
+    """One PCP rank's share (chunks rank and 2*pcp_size-1-rank of a prompt of
+    k_idx.shape[0] tokens); returns (out, lse or None, idx or None)."""
+    n_q, h, d = q_idx_share.shape
+    L = k_idx.shape[0]
+    kdt = _keys(k_idx, k_scale, "k_idx")
+    vdt = _keys(kv, kv_scale, "kv")
+    _bf16(q_idx_share, "q_idx_share")
+    _bf16(q_share, "q_share")
+    dev = q_share.device
+    if out is None:
+        out = torch.empty((n_q, HEADS, D_V), dtype=out_dtype, device=dev)
+    odt = SMA_DT_FP32 if out.dtype == torch.float32 else SMA_DT_BF16
+    lse = torch.empty((n_q, HEADS), dtype=torch.float32, device=dev) if want_lse else None
+    if workspace is None:
+        nbytes = workspace_bytes(SMA_OP_PCP_SHARE, n_q, L, top_k, h, d)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().sma_pcp_rank_share(rank, pcp_size, L, _ptr(q_idx_share), _ptr(w_share),
+                                    _w_stride(w_share, n_q, h), _ptr(k_idx), _ptr(k_scale), kdt, _ptr(q_share),
+                                    _ptr(kv), _ptr(kv_scale), vdt, h, d, top_k, float(sm_scale), _ptr(out), odt,
+                                    _ptr(lse), _ptr(idx_share), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, lse, idx_share

@@ -1,0 +1,337 @@
+// C ABI of the sparse-MLA prefill library: argument validation, workspace
+// carving and kernel dispatch on the caller's stream.  Declarations and the
+// contract of every entry point are in include/sma.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/sma.h"
+#include "sma_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sma_status fail(sma_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sma_status fail(sma_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+sma_status hip_fail(hipError_t e, const char* what) {
+  return fail(SMA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxDevices = 64;
+int g_dev_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other (benign race: idempotent)
+
+sma_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SMA_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  if (g_dev_ok[dev] != 1) return fail(SMA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return SMA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int64_t kMaxKeys = 0x7FFFFFFFLL;
+constexpr int32_t kMinScoreBlock = 64;   // query rows of scores the prefill workspace must hold
+
+#define SMA_CHECK(cond, ...) \
+  do {                       \
+    if (!(cond)) return fail(SMA_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+
+sma_status validate_indexer(const uint16_t* q_idx, const float* w, int64_t w_stride, const void* k_idx,
+                            const float* k_scale, int32_t k_dtype, const int32_t* q_pos, int32_t n_q,
+                            int64_t n_k, int32_t h_idx, int32_t d_idx, bool pos_from_caller = true) {
+  SMA_CHECK(n_q >= 0, "n_q = %d < 0", n_q);
+  SMA_CHECK(n_k >= 1 && n_k <= kMaxKeys, "n_k = %lld out of [1, 2^31)", (long long)n_k);
+  if (!(h_idx == 8 || h_idx == 16 || h_idx == 32 || h_idx == 64))
+    return fail(SMA_ERR_UNSUPPORTED, "h_idx = %d (supported: 8, 16, 32, 64)", h_idx);
+  if (!(d_idx == 64 || d_idx == 128))
+    return fail(SMA_ERR_UNSUPPORTED, "d_idx = %d (supported: 64, 128)", d_idx);
+  SMA_CHECK(k_dtype == SMA_DT_BF16 || k_dtype == SMA_DT_FP8_E4M3, "k_dtype = %d", k_dtype);
+  SMA_CHECK(k_idx != nullptr, "k_idx is NULL");
+  SMA_CHECK((k_dtype == SMA_DT_FP8_E4M3) == (k_scale != nullptr),
+            "k_scale must be given exactly when the keys are FP8");
+  SMA_CHECK(aligned(k_idx, 16), "k_idx not 16-byte aligned");
+  SMA_CHECK(w_stride == 0 || w_stride >= h_idx, "w_stride = %lld (0 or >= h_idx)", (long long)w_stride);
+  if (n_q > 0) {
+    SMA_CHECK(q_idx && w && (q_pos || !pos_from_caller), "q_idx, w and q_pos must be non-NULL");
+    SMA_CHECK(aligned(q_idx, 16), "q_idx not 16-byte aligned");
+  }
+  return SMA_OK;
+}
+
+sma_status validate_topk(int32_t n_q, int64_t n_k, int32_t top_k) {
+  SMA_CHECK(n_q >= 0, "n_q = %d < 0", n_q);
+  SMA_CHECK(n_k >= 1 && n_k <= kMaxKeys, "n_k = %lld out of [1, 2^31)", (long long)n_k);
+  SMA_CHECK(top_k >= 1 && top_k <= SMA_MAX_TOPK, "top_k = %d out of [1, %d]", top_k, SMA_MAX_TOPK);
+  return SMA_OK;
+}
+
+sma_status validate_mla(const uint16_t* q, const void* kv, const float* kv_scale, int32_t kv_dtype,
+                        int64_t n_k, const int32_t* idx, int32_t n_q, int32_t top_k, float sm_scale,
+                        void* out, int32_t out_dtype, bool idx_may_be_null) {
+  SMA_CHECK(n_q >= 0, "n_q = %d < 0", n_q);
+  SMA_CHECK(n_k >= 1 && n_k <= kMaxKeys, "n_k = %lld out of [1, 2^31)", (long long)n_k);
+  SMA_CHECK(top_k >= 1 && top_k <= SMA_MAX_TOPK, "top_k = %d out of [1, %d]", top_k, SMA_MAX_TOPK);
+  SMA_CHECK(kv_dtype == SMA_DT_BF16 || kv_dtype == SMA_DT_FP8_E4M3, "kv_dtype = %d", kv_dtype);
+  SMA_CHECK(out_dtype == SMA_DT_BF16 || out_dtype == SMA_DT_FP32, "out_dtype = %d", out_dtype);
+  SMA_CHECK(kv != nullptr, "kv is NULL");
+  SMA_CHECK((kv_dtype == SMA_DT_FP8_E4M3) == (kv_scale != nullptr),
+            "kv_scale must be given exactly when the KV is FP8");
+  SMA_CHECK(aligned(kv, 16), "kv not 16-byte aligned");
+  SMA_CHECK(std::isfinite(sm_scale), "sm_scale not finite");
+  if (n_q > 0) {
+    SMA_CHECK(q && out && (idx || idx_may_be_null), "q, idx and out must be non-NULL");
+    SMA_CHECK(aligned(q, 16), "q not 16-byte aligned");
+    SMA_CHECK(aligned(out, out_dtype == SMA_DT_FP32 ? 16 : 8), "out not aligned");
+  }
+  return SMA_OK;
+}
+
+sma::IdxArgs idx_args(const uint16_t* q_idx, const float* w, int64_t w_stride, const void* k_idx,
+                      const float* k_scale, int32_t k_dtype, const int32_t* q_pos, int32_t n_q,
+                      int64_t n_k, int32_t h_idx, int32_t d_idx, float* scores, int64_t ld) {
+  sma::IdxArgs a;
+  a.q_idx = q_idx; a.w = w; a.w_stride = w_stride; a.k_idx = k_idx; a.k_scale = k_scale;
+  a.fp8 = k_dtype == SMA_DT_FP8_E4M3; a.q_pos = q_pos; a.n_q = n_q; a.n_k = n_k;
+  a.h_idx = h_idx; a.d_idx = d_idx; a.scores = scores; a.ld = ld;
+  return a;
+}
+
+size_t prefill_fixed_bytes(int32_t n_q, int32_t top_k, bool need_idx, bool need_pos) {
+  size_t b = 0;
+  if (need_pos) b += align_up((size_t)n_q * 4, 256);
+  if (need_idx) b += align_up((size_t)n_q * top_k * 4, 256);
+  return b;
+}
+
+// The composed path shared by sma_prefill and sma_pcp_rank_share.  `pos` is
+// a device array of n_q positions; `ws` past `fixed` holds score blocks.
+sma_status run_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride, const void* k_idx,
+                       const float* k_scale, int32_t k_dtype, const uint16_t* q, const void* kv,
+                       const float* kv_scale, int32_t kv_dtype, const int32_t* pos, int32_t n_q,
+                       int64_t n_k, int32_t h_idx, int32_t d_idx, int32_t top_k, float sm_scale,
+                       void* out, int32_t out_dtype, float* lse, int32_t* idx, uint8_t* score_ws,
+                       size_t score_ws_bytes, hipStream_t st) {
+  const size_t row_bytes = (size_t)n_k * 4;
+  int64_t qb = (int64_t)(score_ws_bytes / row_bytes);
+  if (qb >= n_q) qb = n_q;
+  else qb = qb / 16 * 16;
+  if (qb < 1) return fail(SMA_ERR_WORKSPACE, "workspace holds no score block");
+  float* scores = reinterpret_cast<float*>(score_ws);
+  for (int64_t q0 = 0; q0 < n_q; q0 += qb) {
+    const int32_t nb = (int32_t)((n_q - q0) < qb ? (n_q - q0) : qb);
+    sma::IdxArgs ia = idx_args(q_idx + q0 * h_idx * d_idx, w + q0 * w_stride, w_stride, k_idx, k_scale,
+                               k_dtype, pos + q0, nb, n_k, h_idx, d_idx, scores, n_k);
+    hipError_t e = sma::launch_index_scores(ia, st);
+    if (e != hipSuccess) return hip_fail(e, "index_scores launch");
+    sma::TopkArgs ta{scores, n_k, pos + q0, nb, n_k, top_k, idx + q0 * top_k};
+    e = sma::launch_topk(ta, st);
+    if (e != hipSuccess) return hip_fail(e, "topk launch");
+  }
+  sma::MlaArgs ma{q, kv, kv_scale, kv_dtype == SMA_DT_FP8_E4M3, n_k, idx, n_q, top_k, sm_scale,
+                  out, out_dtype == SMA_DT_FP32, lse};
+  hipError_t e = sma::launch_sparse_mla(ma, st);
+  if (e != hipSuccess) return hip_fail(e, "sparse_mla launch");
+  return SMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sma_status sma_index_scores(const uint16_t* q_idx, const float* w, int64_t w_stride, const void* k_idx,
+                            const float* k_scale, int32_t k_dtype, const int32_t* q_pos, int32_t n_q,
+                            int64_t n_k, int32_t h_idx, int32_t d_idx, float* scores, int64_t ld_scores,
+                            void* stream) {
+  g_err.clear();
+  sma_status s = validate_indexer(q_idx, w, w_stride, k_idx, k_scale, k_dtype, q_pos, n_q, n_k, h_idx, d_idx);
+  if (s != SMA_OK) return s;
+  SMA_CHECK(ld_scores >= n_k, "ld_scores = %lld < n_k = %lld", (long long)ld_scores, (long long)n_k);
+  if (n_q > 0) SMA_CHECK(scores != nullptr, "scores is NULL");
+  if (n_q == 0) return SMA_OK;
+  if ((s = check_device()) != SMA_OK) return s;
+  hipError_t e = sma::launch_index_scores(
+      idx_args(q_idx, w, w_stride, k_idx, k_scale, k_dtype, q_pos, n_q, n_k, h_idx, d_idx, scores, ld_scores),
+      (hipStream_t)stream);
+  return e == hipSuccess ? SMA_OK : hip_fail(e, "index_scores launch");
+}
+
+sma_status sma_topk_select(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t n_q,
+                           int64_t n_k, int32_t top_k, int32_t* idx, void* ws, size_t ws_bytes,
+                           void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  g_err.clear();
+  sma_status s = validate_topk(n_q, n_k, top_k);
+  if (s != SMA_OK) return s;
+  SMA_CHECK(ld_scores >= n_k, "ld_scores = %lld < n_k = %lld", (long long)ld_scores, (long long)n_k);
+  if (n_q > 0) SMA_CHECK(scores && q_pos && idx, "scores, q_pos and idx must be non-NULL");
+  if (n_q == 0) return SMA_OK;
+  if ((s = check_device()) != SMA_OK) return s;
+  sma::TopkArgs a{scores, ld_scores, q_pos, n_q, n_k, top_k, idx};
+  hipError_t e = sma::launch_topk(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMA_OK : hip_fail(e, "topk launch");
+}
+
+sma_status sma_sparse_mla_prefill(const uint16_t* q, const void* kv, const float* kv_scale,
+                                  int32_t kv_dtype, int64_t n_k, const int32_t* idx, int32_t n_q,
+                                  int32_t top_k, float sm_scale, void* out, int32_t out_dtype,
+                                  float* lse, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  g_err.clear();
+  sma_status s = validate_mla(q, kv, kv_scale, kv_dtype, n_k, idx, n_q, top_k, sm_scale, out,
+                              out_dtype, false);
+  if (s != SMA_OK) return s;
+  if (n_q == 0) return SMA_OK;
+  if ((s = check_device()) != SMA_OK) return s;
+  sma::MlaArgs a{q, kv, kv_scale, kv_dtype == SMA_DT_FP8_E4M3, n_k, idx, n_q, top_k, sm_scale,
+                 out, out_dtype == SMA_DT_FP32, lse};
+  hipError_t e = sma::launch_sparse_mla(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMA_OK : hip_fail(e, "sparse_mla launch");
+}
+
+size_t sma_workspace_bytes(int32_t op, int32_t n_q, int64_t n_k, int32_t top_k, int32_t h_idx,
+                           int32_t d_idx) {
+  (void)h_idx;
+  (void)d_idx;
+  if (n_q < 0 || n_k < 1 || top_k < 1) return 0;
+  switch (op) {
+    case SMA_OP_INDEX_SCORES:
+    case SMA_OP_TOPK:
+    case SMA_OP_SPARSE_MLA:
+      return 0;
+    case SMA_OP_PREFILL:
+    case SMA_OP_PCP_SHARE: {
+      const int32_t blk = n_q < kMinScoreBlock ? n_q : kMinScoreBlock;
+      return prefill_fixed_bytes(n_q, top_k, true, op == SMA_OP_PCP_SHARE) +
+             align_up((size_t)blk * (size_t)n_k * 4, 256);
+    }
+    default:
+      return 0;
+  }
+}
+
+sma_status sma_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride, const void* k_idx,
+                       const float* k_scale, int32_t k_dtype, const uint16_t* q, const void* kv,
+                       const float* kv_scale, int32_t kv_dtype, const int32_t* q_pos, int32_t n_q,
+                       int64_t n_k, int32_t h_idx, int32_t d_idx, int32_t top_k, float sm_scale,
+                       void* out, int32_t out_dtype, float* lse, int32_t* idx_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  g_err.clear();
+  sma_status s = validate_indexer(q_idx, w, w_stride, k_idx, k_scale, k_dtype, q_pos, n_q, n_k, h_idx, d_idx);
+  if (s != SMA_OK) return s;
+  if ((s = validate_mla(q, kv, kv_scale, kv_dtype, n_k, idx_out, n_q, top_k, sm_scale, out, out_dtype,
+                        true)) != SMA_OK)
+    return s;
+  if (n_q == 0) return SMA_OK;
+  const size_t fixed = prefill_fixed_bytes(n_q, top_k, idx_out == nullptr, false);
+  const int32_t blk = n_q < kMinScoreBlock ? n_q : kMinScoreBlock;
+  const size_t need = fixed + align_up((size_t)blk * (size_t)n_k * 4, 256);
+  if (ws_bytes < need || (ws == nullptr && need > 0))
+    return fail(SMA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
+  if ((s = check_device()) != SMA_OK) return s;
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  int32_t* idx = idx_out;
+  if (!idx) {
+    idx = reinterpret_cast<int32_t*>(p);
+    p += align_up((size_t)n_q * top_k * 4, 256);
+  }
+  return run_prefill(q_idx, w, w_stride, k_idx, k_scale, k_dtype, q, kv, kv_scale, kv_dtype, q_pos, n_q,
+                     n_k, h_idx, d_idx, top_k, sm_scale, out, out_dtype, lse, idx, p,
+                     ws_bytes - (size_t)(p - static_cast<uint8_t*>(ws)), (hipStream_t)stream);
+}
+
+sma_status sma_pcp_rank_share(int32_t rank, int32_t pcp_size, int64_t L_total, const uint16_t* q_idx_share,
+                              const float* w_share, int64_t w_stride, const void* k_idx,
+                              const float* k_scale, int32_t k_dtype, const uint16_t* q_share,
+                              const void* kv, const float* kv_scale, int32_t kv_dtype, int32_t h_idx,
+                              int32_t d_idx, int32_t top_k, float sm_scale, void* out_share,
+                              int32_t out_dtype, float* lse_share, int32_t* idx_share, void* ws,
+                              size_t ws_bytes, void* stream) {
+  g_err.clear();
+  SMA_CHECK(pcp_size >= 1, "pcp_size = %d < 1", pcp_size);
+  SMA_CHECK(rank >= 0 && rank < pcp_size, "rank = %d not in [0, %d)", rank, pcp_size);
+  SMA_CHECK(L_total >= 2 * pcp_size && L_total % (2 * pcp_size) == 0,
+            "L_total = %lld is not a positive multiple of 2*pcp_size = %d", (long long)L_total, 2 * pcp_size);
+  SMA_CHECK(L_total <= kMaxKeys, "L_total too large");
+  const int64_t n_q64 = L_total / pcp_size;   // two chunks of L_total / (2 pcp_size)
+  SMA_CHECK(n_q64 <= 0x7FFFFFFF, "share too large");
+  const int32_t n_q = (int32_t)n_q64;
+  sma_status s = validate_indexer(q_idx_share, w_share, w_stride, k_idx, k_scale, k_dtype,
+                                  nullptr, n_q, L_total, h_idx, d_idx, false);
+  if (s != SMA_OK) return s;
+  if ((s = validate_mla(q_share, kv, kv_scale, kv_dtype, L_total, idx_share, n_q, top_k, sm_scale,
+                        out_share, out_dtype, true)) != SMA_OK)
+    return s;
+  const size_t fixed = prefill_fixed_bytes(n_q, top_k, idx_share == nullptr, true);
+  const int32_t blk = n_q < kMinScoreBlock ? n_q : kMinScoreBlock;
+  const size_t need = fixed + align_up((size_t)blk * (size_t)L_total * 4, 256);
+  if (ws_bytes < need || ws == nullptr)
+    return fail(SMA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
+  if ((s = check_device()) != SMA_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  int32_t* pos = reinterpret_cast<int32_t*>(p);
+  p += align_up((size_t)n_q * 4, 256);
+  int32_t* idx = idx_share;
+  if (!idx) {
+    idx = reinterpret_cast<int32_t*>(p);
+    p += align_up((size_t)n_q * top_k * 4, 256);
+  }
+  hipError_t e = sma::launch_pcp_positions(pos, rank, pcp_size, L_total, st);
+  if (e != hipSuccess) return hip_fail(e, "pcp positions launch");
+  return run_prefill(q_idx_share, w_share, w_stride, k_idx, k_scale, k_dtype, q_share, kv, kv_scale,
+                     kv_dtype, pos, n_q, L_total, h_idx, d_idx, top_k, sm_scale, out_share, out_dtype,
+                     lse_share, idx, p, ws_bytes - (size_t)(p - static_cast<uint8_t*>(ws)), st);
+}
+
+const char* sma_last_error(void) { return g_err.c_str(); }
+
+int32_t sma_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"
+
+namespace sma {
+
+__global__ void pcp_positions_kernel(int32_t* pos, int32_t rank, int32_t nchunk, int32_t c) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= 2 * c) return;
+  pos[j] = j < c ? rank * c + j : (nchunk - 1 - rank) * c + (j - c);
+}
+
+hipError_t launch_pcp_positions(int32_t* pos, int32_t rank, int32_t pcp_size, int64_t L_total,
+                                hipStream_t st) {
+  const int32_t nchunk = 2 * pcp_size;
+  const int32_t c = (int32_t)(L_total / nchunk);
+  const int n = 2 * c;
+  hipLaunchKernelGGL(pcp_positions_kernel, dim3((n + 255) / 256), dim3(256), 0, st, pos, rank, nchunk, c);
+  return hipGetLastError();
+}
+
+}  // namespace sma

@@ -1,0 +1,72 @@
+// Device-side helpers shared by the sparse-MLA kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sma {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kHeads = 64;
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round two floats to bf16 (nearest-even, the hardware convert) and pack.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// One OCP e4m3fn code -> bf16 bits, exactly.  Normal codes (exponent field
+// e >= 1) re-bias the exponent from 7 to 127 and widen the 3-bit mantissa;
+// subnormal codes m * 2^-9 (m = 1..7) are built through fp32, where they are
+// normal numbers.  The NaN code maps to a bf16 NaN.
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 8;
+  const uint32_t mag = c & 0x7Fu;
+  uint32_t r;
+  if (mag >= 8u) {
+    r = (mag << 4) + (120u << 7);              // (e + 120) << 7 | m << 4
+    if (mag == 0x7Fu) r = 0x7FC0u;             // NaN
+  } else {
+    r = __float_as_uint((float)mag * 0.001953125f) >> 16;   // m * 2^-9, exact in bf16
+  }
+  return sign | r;
+}
+
+// Four e4m3 codes packed in a dword -> four bf16 in two dwords (low first).
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  u32x2 r;
+  r[0] = e4m3_to_bf16_bits(w & 0xFFu) | (e4m3_to_bf16_bits((w >> 8) & 0xFFu) << 16);
+  r[1] = e4m3_to_bf16_bits((w >> 16) & 0xFFu) | (e4m3_to_bf16_bits(w >> 24) << 16);
+  return r;
+}
+
+// Order-preserving map of an fp32 score onto uint32 (larger score -> larger
+// key); -0.0 is folded onto +0.0 so the two zeros are one key.  The result
+// is never 0 (the one NaN pattern that would map there is moved up by one),
+// which leaves 0 free as a "no element" marker.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  if (b == 0x80000000u) b = 0u;
+  const uint32_t k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return k ? k : 1u;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace sma

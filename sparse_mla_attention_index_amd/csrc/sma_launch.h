@@ -1,0 +1,55 @@
+// Internal launch interface between the C ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define SMA_MAX_TOPK_DEV 2048
+
+namespace sma {
+
+struct IdxArgs {
+  const uint16_t* q_idx;
+  const float* w;
+  int64_t w_stride;
+  const void* k_idx;
+  const float* k_scale;
+  bool fp8;
+  const int32_t* q_pos;
+  int32_t n_q;
+  int64_t n_k;
+  int32_t h_idx, d_idx;
+  float* scores;
+  int64_t ld;
+};
+
+struct TopkArgs {
+  const float* scores;
+  int64_t ld;
+  const int32_t* q_pos;
+  int32_t n_q;
+  int64_t n_k;
+  int32_t top_k;
+  int32_t* idx;
+};
+
+struct MlaArgs {
+  const uint16_t* q;
+  const void* kv;
+  const float* kv_scale;
+  bool fp8;
+  int64_t n_k;
+  const int32_t* idx;
+  int32_t n_q, top_k;
+  float sm_scale;
+  void* out;
+  bool out_f32;
+  float* lse;
+};
+
+hipError_t launch_index_scores(const IdxArgs& a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t s);
+hipError_t launch_pcp_positions(int32_t* pos, int32_t rank, int32_t pcp_size, int64_t L_total,
+                                hipStream_t s);
+
+}  // namespace sma

@@ -1,0 +1,291 @@
+// Per-query top-k selection over causal indexer scores (gfx950).
+//
+// Keeps the min(K, n) largest of a row's n scores, ties at the threshold to
+// the lowest positions, written in ascending position order (the selection
+// of 2,048 tokens per query in the GLM-5.3 part 2 article, "Pourquoi pas TP
+// ou DP ?", with the tie-break reading).
+//
+// One 1024-thread workgroup per row, no atomics outside LDS, deterministic:
+//  1. scores become order-preserving uint32 keys (-0.0 folded onto +0.0);
+//  2. the key range [lo, hi] of the row is found (min/max reduce);
+//  3. radix refinement: the range is cut into <= 2048 equal-width bins,
+//     an LDS histogram locates the bin holding the K-th largest key, and the
+//     range shrinks to that bin, until it is a single key T (at most three
+//     11-bit rounds for 32-bit keys).  Because the bins span the row's
+//     actual range rather than fixed bit fields, the first histogram is
+//     spread over the scores' distribution and LDS atomics rarely collide;
+//  4. an ordered compaction writes every position with key > T plus the
+//     first (K - #greater) positions with key == T, each to the slot given by
+//     a block-wide prefix count, so the output is ascending by position.
+// Rows up to 1024*V scores are read once into registers (blocked: thread t
+// owns positions [t*V, t*V+V)); longer rows are streamed from memory in
+// every pass.
+#include "sma_device.h"
+#include "sma_launch.h"
+
+namespace sma {
+
+constexpr int kBins = 2048;
+constexpr int kStreamV = 16;   // elements per thread per streamed chunk
+
+template <int THREADS>
+struct TopkShared {
+  static constexpr int WAVES = THREADS / 64;
+  uint32_t hist[kBins];
+  uint32_t red[WAVES * 2];
+  uint32_t bcast[4];
+};
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive block-wide prefix of two counters at once (packed as 2 x 32 bit
+// in a 64-bit lane value would overflow for long rows, so they are scanned
+// separately through the same LDS slots).
+template <int THREADS>
+__device__ __forceinline__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_t& ea, uint32_t& eb,
+                                                 uint32_t& ta, uint32_t& tb, TopkShared<THREADS>& sh) {
+  constexpr int kTopkWaves = THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t ia = wave_incl_scan(a, lane), ib = wave_incl_scan(b, lane);
+  if (lane == 63) {
+    sh.red[wave] = ia;
+    sh.red[kTopkWaves + wave] = ib;
+  }
+  __syncthreads();
+  uint32_t pa = 0, pb = 0, sa = 0, sb = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t xa = sh.red[w], xb = sh.red[kTopkWaves + w];
+    if (w < wave) { pa += xa; pb += xb; }
+    sa += xa;
+    sb += xb;
+  }
+  ea = pa + ia - a;
+  eb = pb + ib - b;
+  ta = sa;
+  tb = sb;
+  __syncthreads();
+}
+
+template <int V>
+struct RowSource {
+  // V > 0: keys in registers; V == 0: streamed from `row`.
+  uint32_t key[V > 0 ? V : 1];
+};
+
+template <int THREADS, int V>
+__global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restrict__ scores,
+                                                               int64_t ld,
+                                                               const int32_t* __restrict__ q_pos,
+                                                               int n_k, int K,
+                                                               int32_t* __restrict__ idx) {
+  constexpr int kTopkThreads = THREADS, kTopkWaves = THREADS / 64;
+  static_assert(kBins % THREADS == 0, "whole histogram bins per thread");
+  __shared__ TopkShared<THREADS> sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  int p = q_pos[row];
+  p = p < -1 ? -1 : (p > n_k - 1 ? n_k - 1 : p);
+  const int n = p + 1;
+  int32_t* out = idx + (int64_t)row * K;
+  const float* src = scores + (int64_t)row * ld;
+
+  if (n <= K) {
+    for (int e = tid; e < K; e += kTopkThreads) out[e] = e < n ? e : -1;
+    return;
+  }
+
+  // Positions past the row end carry key 0, below every real key (score_key
+  // never returns 0), so no pass needs a per-position bound check.
+  RowSource<V> rs;
+  if constexpr (V > 0) {
+    const int base = tid * V;
+#pragma unroll
+    for (int v = 0; v < V; v += 4) {
+      const int p0 = base + v;
+      f32x4 x;
+      if (p0 + 3 < n) {
+        x = *reinterpret_cast<const f32x4*>(src + p0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = p0 + e < n ? src[p0 + e] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rs.key[v + e] = p0 + e < n ? score_key(x[e]) : 0u;
+    }
+  }
+
+  // Visit every (position, key) of this thread in ascending position; keys
+  // of positions >= n are 0.
+  auto for_each = [&](auto&& fn) {
+    if constexpr (V > 0) {
+      const int base = tid * V;
+#pragma unroll
+      for (int v = 0; v < V; ++v) fn(base + v, rs.key[v]);
+    } else {
+      for (int c0 = 0; c0 < n; c0 += kTopkThreads * kStreamV) {
+        const int base = c0 + tid * kStreamV;
+#pragma unroll
+        for (int v = 0; v < kStreamV; ++v) fn(base + v, base + v < n ? score_key(src[base + v]) : 0u);
+      }
+    }
+  };
+
+  // ---- 2. key range ----
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for_each([&](int, uint32_t k) {
+    kmin = min(kmin, k ? k : 0xFFFFFFFFu);
+    kmax = max(kmax, k);
+  });
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  if (lane == 0) {
+    sh.red[wave] = kmin;
+    sh.red[kTopkWaves + wave] = kmax;
+  }
+  __syncthreads();
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    lo = min(lo, sh.red[w]);
+    hi = max(hi, sh.red[kTopkWaves + w]);
+  }
+  __syncthreads();
+
+  // ---- 3. radix refinement of [lo, hi] down to the threshold key ----
+  uint32_t remaining = (uint32_t)K;   // still to take from keys inside [lo, hi]
+  // Each round shrinks the range by 11 bits: three rounds reach a single key;
+  // the bound keeps the loop finite whatever the data.
+  for (int round = 0; round < 4 && hi != lo; ++round) {
+    const uint32_t width = hi - lo;
+    const int bits = 32 - __clz(width);
+    const int shift = bits > 11 ? bits - 11 : 0;
+    const int nbins = (int)(width >> shift) + 1;
+    for (int b = tid; b < nbins; b += kTopkThreads) sh.hist[b] = 0u;
+    if (tid == 0) {
+      sh.bcast[0] = 0u;
+      sh.bcast[1] = 0u;
+    }
+    __syncthreads();
+    for_each([&](int, uint32_t k) {
+      if (k >= lo && k <= hi) atomicAdd(&sh.hist[(k - lo) >> shift], 1u);
+    });
+    __syncthreads();
+    // thread t owns bins [BPT*t, BPT*t + BPT); keys above a bin = total minus
+    // the inclusive prefix up to and including it
+    constexpr int BPT = kBins / THREADS;
+    uint32_t hb[BPT], hsum = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      const int b = BPT * tid + e;
+      hb[e] = b < nbins ? sh.hist[b] : 0u;
+      hsum += hb[e];
+    }
+    uint32_t ex, dummy_e, tot, dummy_t;
+    block_excl_scan2<THREADS>(hsum, 0u, ex, dummy_e, tot, dummy_t, sh);
+    uint32_t above = tot - (ex + hsum);   // keys in bins past this thread's last bin
+#pragma unroll
+    for (int e = BPT - 1; e >= 0; --e) {
+      const int b = BPT * tid + e;
+      if (b < nbins && above < remaining && remaining <= above + hb[e]) {
+        sh.bcast[0] = (uint32_t)b;
+        sh.bcast[1] = above;
+      }
+      above += hb[e];
+    }
+    __syncthreads();
+    const uint32_t bsel = sh.bcast[0], above_sel = sh.bcast[1];
+    __syncthreads();
+    remaining -= above_sel;
+    const uint64_t nlo = (uint64_t)lo + ((uint64_t)bsel << shift);
+    const uint64_t nhi = nlo + ((uint64_t)1 << shift) - 1;
+    lo = (uint32_t)nlo;
+    hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+  }
+  const uint32_t T = lo;
+  const uint32_t need_ties = remaining;   // >= 1 keys equal to T are taken
+
+  // ---- 4. ordered compaction ----
+  if constexpr (V > 0) {
+    uint32_t cg = 0, ce = 0;
+    for_each([&](int, uint32_t k) {
+      cg += k > T;
+      ce += k == T;
+    });
+    uint32_t g_before, e_before, tg, te;
+    block_excl_scan2<THREADS>(cg, ce, g_before, e_before, tg, te, sh);
+    for_each([&](int pos, uint32_t k) {
+      if (k > T) {
+        const uint32_t slot = g_before + min(e_before, need_ties);
+        if (slot < (uint32_t)K) out[slot] = pos;
+        ++g_before;
+      } else if (k == T) {
+        if (e_before < need_ties && g_before + e_before < (uint32_t)K) out[g_before + e_before] = pos;
+        ++e_before;
+      }
+    });
+  } else {
+    uint32_t g_run = 0, e_run = 0;   // totals of earlier chunks
+    for (int c0 = 0; c0 < n; c0 += kTopkThreads * kStreamV) {
+      const int base = c0 + tid * kStreamV;
+      uint32_t kk[kStreamV];
+      uint32_t cg = 0, ce = 0;
+#pragma unroll
+      for (int v = 0; v < kStreamV; ++v) {
+        kk[v] = base + v < n ? score_key(src[base + v]) : 0u;
+        cg += kk[v] > T;
+        ce += kk[v] == T;
+      }
+      uint32_t g_before, e_before, tg, te;
+      block_excl_scan2<THREADS>(cg, ce, g_before, e_before, tg, te, sh);
+      g_before += g_run;
+      e_before += e_run;
+#pragma unroll
+      for (int v = 0; v < kStreamV; ++v) {
+        const uint32_t k = kk[v];
+        if (k > T) {
+          const uint32_t slot = g_before + min(e_before, need_ties);
+          if (slot < (uint32_t)K) out[slot] = base + v;
+          ++g_before;
+        } else if (k == T) {
+          if (e_before < need_ties && g_before + e_before < (uint32_t)K) out[g_before + e_before] = base + v;
+          ++e_before;
+        }
+      }
+      g_run += tg;
+      e_run += te;
+    }
+  }
+}
+
+hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
+  if (A.n_q <= 0) return hipSuccess;
+  const dim3 grid((unsigned)A.n_q);
+  // Rows that fit are held in registers (1024 x 16 or 1024 x 32 keys, read
+  // with 16-byte loads, so rows must start 16-byte aligned); longer or
+  // unaligned rows are streamed from memory in every pass.
+  const bool rows_aligned = (reinterpret_cast<uintptr_t>(A.scores) % 16 == 0) && (A.ld % 4 == 0);
+  if (rows_aligned && A.n_k <= 1024 * 16) {
+    hipLaunchKernelGGL((topk_kernel<1024, 16>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
+                       (int)A.n_k, A.top_k, A.idx);
+  } else if (rows_aligned && A.n_k <= 1024 * 32) {
+    hipLaunchKernelGGL((topk_kernel<1024, 32>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
+                       (int)A.n_k, A.top_k, A.idx);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<1024, 0>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
+                       (int)A.n_k, A.top_k, A.idx);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sma

@@ -1,0 +1,96 @@
+"""The C-ABI library loads, exports every symbol include/sma.h declares, and
+rejects bad arguments on the host before touching a device (no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mla_attention_index_amd as sma
+from sparse_mla_attention_index_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "sma.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(sma_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_symbol():
+    L = sma.lib()
+    for name in _declared():
+        assert getattr(L, name) is not None
+    assert sma.version() >> 16 == 1
+
+
+def test_workspace_sizes():
+    # prefill: idx list + one 64-row score block (256-byte aligned pieces)
+    assert sma.workspace_bytes(_lib.SMA_OP_PREFILL, 65536, 65536, 2048) == 65536 * 2048 * 4 + 64 * 65536 * 4
+    assert sma.workspace_bytes(_lib.SMA_OP_PCP_SHARE, 16384, 131072, 2048) == \
+        16384 * 4 + 16384 * 2048 * 4 + 64 * 131072 * 4
+    assert sma.workspace_bytes(_lib.SMA_OP_TOPK, 10, 10, 5) == 0
+    assert sma.workspace_bytes(_lib.SMA_OP_PREFILL, 10, 100, 5) == 256 + 4096   # 200 B and 4000 B, 256-aligned
+    assert sma.workspace_bytes(99, 10, 10, 5) == 0
+
+
+P = ctypes.c_void_p
+FAKE = P(4096)   # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,code,msg", [
+    (dict(h=7), -2, "h_idx"),
+    (dict(d=96), -2, "d_idx"),
+    (dict(k=None), -1, "k_idx is NULL"),
+    (dict(kdt=1), -1, "k_scale"),
+    (dict(ld=5), -1, "ld_scores"),
+    (dict(nq=-1), -1, "n_q"),
+    (dict(nk=0), -1, "n_k"),
+    (dict(wstride=3), -1, "w_stride"),
+])
+def test_index_scores_validation(args, code, msg):
+    a = dict(h=64, d=128, k=FAKE, kdt=0, ld=10, nq=1, nk=10, wstride=64)
+    a.update(args)
+    r = sma.lib().sma_index_scores(FAKE, FAKE, a["wstride"], a["k"], None, a["kdt"], FAKE, a["nq"], a["nk"],
+                                   a["h"], a["d"], FAKE, a["ld"], None)
+    assert r == code and msg in sma.last_error()
+
+
+@pytest.mark.parametrize("topk,ld,code", [(0, 10, -1), (2049, 10, -1), (5, 9, -1)])
+def test_topk_validation(topk, ld, code):
+    assert sma.lib().sma_topk_select(FAKE, ld, FAKE, 1, 10, topk, FAKE, None, 0, None) == code
+
+
+@pytest.mark.parametrize("kvdt,scale,odt,topk,msg", [
+    (1, None, 0, 8, "kv_scale"), (0, FAKE, 0, 8, "kv_scale"), (0, None, 1, 8, "out_dtype"),
+    (0, None, 0, 0, "top_k"), (5, None, 0, 8, "kv_dtype")])
+def test_mla_validation(kvdt, scale, odt, topk, msg):
+    r = sma.lib().sma_sparse_mla_prefill(FAKE, FAKE, scale, kvdt, 100, FAKE, 1, topk, 0.1, FAKE, odt, None,
+                                         None, 0, None)
+    assert r == -1 and msg in sma.last_error()
+
+
+def test_prefill_workspace_check():
+    r = sma.lib().sma_prefill(FAKE, FAKE, 64, FAKE, None, 0, FAKE, FAKE, None, 0, FAKE, 16, 1000, 64, 128, 64,
+                              0.1, FAKE, 0, None, None, FAKE, 100, None)
+    assert r == -3 and "workspace" in sma.last_error()
+
+
+@pytest.mark.parametrize("rank,P_,L,msg", [(8, 8, 1024, "rank"), (-1, 8, 1024, "rank"), (0, 8, 1000, "L_total"),
+                                           (0, 0, 1024, "pcp_size")])
+def test_pcp_validation(rank, P_, L, msg):
+    r = sma.lib().sma_pcp_rank_share(rank, P_, L, FAKE, FAKE, 64, FAKE, None, 0, FAKE, FAKE, None, 0, 64, 128,
+                                     2048, 0.1, FAKE, 0, None, None, FAKE, 1 << 40, None)
+    assert r == -1 and msg in sma.last_error()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libsma.so"))
+    with pytest.raises(ImportError):
+        _lib.lib()

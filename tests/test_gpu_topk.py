@@ -1,0 +1,57 @@
+"""GPU parity of sma_topk_select: bit-exact index lists against the oracle
+on the same fp32 scores (the selection is unique given the scores)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mla_attention_index_amd as sma
+from sparse_mla_attention_index_amd import synth
+from _gpuhelp import dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _positions(n_rows, n_k, top_k, seed):
+    rng = np.random.default_rng(seed)
+    pos = rng.integers(0, n_k, size=n_rows)
+    fixed = [0, 1, top_k - 2, top_k - 1, top_k, top_k + 1, n_k - 1, n_k // 2]
+    pos[: len(fixed)] = np.clip(fixed, 0, n_k - 1)
+    return pos.astype(np.int32)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ints", "ties", "signed_zero"])
+@pytest.mark.parametrize("n_k,top_k", [(300, 128), (5000, 2048), (20000, 2048), (40000, 1), (70000, 2048),
+                                       (140000, 2048)])
+def test_topk_exact(kind, n_k, top_k):
+    n_rows = 24
+    sc = synth.random_scores(n_k % 1000 + len(kind), n_rows, n_k, kind)
+    pos = _positions(n_rows, n_k, top_k, n_k)
+    idx = sma.topk_select(dev(sc), dev(pos), top_k)
+    got = host(idx)
+    for r in range(n_rows):
+        ref = oracle.topk_row(sc[r, : pos[r] + 1], top_k)
+        assert np.array_equal(got[r], ref), (kind, n_k, top_k, r, pos[r])
+
+
+@pytest.mark.parametrize("pad", [1, 3, 64])
+def test_topk_row_stride(pad):
+    """Rows with a leading dimension larger than n_k (aligned or not)."""
+    n_k, top_k, n_rows = 9000, 512, 16
+    sc = synth.random_scores(77, n_rows, n_k + pad, "normal")
+    pos = _positions(n_rows, n_k, top_k, pad)
+    t = dev(sc)
+    idx = sma.topk_select(t, dev(pos), top_k, n_k=n_k)
+    got = host(idx)
+    for r in range(n_rows):
+        assert np.array_equal(got[r], oracle.topk_row(sc[r, : pos[r] + 1], top_k)), r
+
+
+def test_topk_clamped_positions():
+    n_k, top_k = 3000, 100
+    sc = synth.random_scores(3, 4, n_k, "ints")
+    pos = np.array([-7, -1, 5000, 50], dtype=np.int32)
+    got = host(sma.topk_select(dev(sc), dev(pos), top_k))
+    assert np.all(got[0] == -1) and np.all(got[1] == -1)
+    assert np.array_equal(got[2], oracle.topk_row(sc[2], top_k))
+    assert np.array_equal(got[3], oracle.topk_row(sc[3, :51], top_k))
