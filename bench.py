@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-MLA prefill path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill64k|pcp|decode]
+
+A step is one pass of the hot path over the workload's batch: indexer
+scores -> per-query top-k -> sparse MLA (sma_prefill), inputs resident in
+HBM before timing starts.  The default workload is a single-layer prefill of
+L = 65,536 tokens (top_k = 2,048, 64-head indexer of dim 128, 64-head MLA
+over a 576-wide bf16 latent), on seeded synthetic data.
+
+Besides the timed steps, each kernel is timed on its own (HIP events on the
+stream it runs on), the dominant kernel is placed against its roofline, the
+CPU oracle is timed on a bounded sample of query rows, and the GPU's outputs
+for those rows are checked against the oracle.  One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="prefill64k", choices=["prefill64k", "prefill16k", "pcp", "decode"])
+    ap.add_argument("--score-block", type=int, default=0,
+                    help="query rows per score block inside sma_prefill (0: all rows at once)")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="query rows in the CPU-oracle sample (0: a per-workload default of ~10-30 s)")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
+                                   "(the PCP rank share is benchmarked on one GPU with --workload pcp)"}))
+        sys.exit(2)
+
+    import torch
+
+    import sparse_mla_attention_index_amd as sma
+    from sparse_mla_attention_index_amd import accounting as acc
+    from sparse_mla_attention_index_amd import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    sma.lib()   # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = {"prefill64k": 3, "prefill16k": 2, "pcp": 4, "decode": 5}[args.workload]
+    w = synth.workload(cfg)
+    # PCP: the step is rank 7's share (chunks 7 and 8); rank 0 (chunks 0 and
+    # 15) is timed beside it for the load-balance ratio.
+    rank = 7 if args.workload == "pcp" else 0
+    pos_np = synth.query_positions(w, rank)
+    n_q, n_k = pos_np.size, w.n_keys
+
+    # ---------------------------------------------------------- inputs --
+    t0 = time.time()
+
+    def upload_rows(tensor, start, stop, rows_per_chunk):
+        first = synth.rows(w, tensor, start, min(stop, start + rows_per_chunk))
+        if isinstance(first, tuple):
+            codes = torch.empty((stop - start,) + first[0].shape[1:], dtype=torch.uint8, device=dev)
+            scale = torch.empty((stop - start,), dtype=torch.float32, device=dev)
+            out = (codes, scale)
+        else:
+            dt = torch.float32 if first.dtype == np.float32 else torch.int16
+            out = torch.empty((stop - start,) + first.shape[1:], dtype=dt, device=dev)
+        a = start
+        while a < stop:
+            b = min(stop, a + rows_per_chunk)
+            x = first if a == start else synth.rows(w, tensor, a, b)
+            if isinstance(x, tuple):
+                out[0][a - start:b - start].copy_(torch.from_numpy(x[0]))
+                out[1][a - start:b - start].copy_(torch.from_numpy(x[1]))
+            else:
+                out[a - start:b - start].copy_(torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x))
+            a = b
+        return out
+
+    def upload_query(tensor, positions, rows_per_chunk):
+        # query-side rows at the given positions (one upload per contiguous run)
+        parts = []
+        cuts = np.flatnonzero(np.diff(positions) != 1) + 1
+        for seg in np.split(positions, cuts):
+            parts.append(upload_rows(tensor, int(seg[0]), int(seg[-1]) + 1, rows_per_chunk))
+        return parts[0] if len(parts) == 1 else torch.cat(parts, 0)
+
+    k_idx = upload_rows("k_idx", 0, n_k, 65536)
+    kv = upload_rows("kv", 0, n_k, 16384)
+    q_idx = upload_query("q_idx", pos_np, 1024)
+    wts = upload_query("w", pos_np, 65536)
+    q = upload_query("q", pos_np, 256)
+    q_pos = torch.from_numpy(pos_np).to(dev)
+    k_scale = kv_scale = None
+    if isinstance(k_idx, tuple):
+        k_idx, k_scale = k_idx
+    if isinstance(kv, tuple):
+        kv, kv_scale = kv
+    if args.workload == "pcp":
+        pos0 = synth.query_positions(w, 0)
+        q_idx0, wts0, q0 = (upload_query("q_idx", pos0, 1024), upload_query("w", pos0, 65536),
+                            upload_query("q", pos0, 256))
+    torch.cuda.synchronize()
+    _log(f"inputs for {w.name} ready in {time.time() - t0:.1f}s (n_q={n_q}, n_k={n_k})")
+
+    out_dtype = torch.float32 if w.out_fp32 else torch.bfloat16
+    out = torch.empty((n_q, 64, 512), dtype=out_dtype, device=dev)
+    idx = torch.empty((n_q, w.top_k), dtype=torch.int32, device=dev)
+    blk = n_q if args.score_block <= 0 else max(64, min(args.score_block, n_q))
+    ws = torch.empty(blk * n_k * 4 + n_q * 4 + 4096, dtype=torch.uint8, device=dev)
+
+    if args.workload == "pcp":
+        def run_share(r, qi_, w_, q_):
+            sma.pcp_rank_share(r, w.pcp_size, qi_, w_, k_idx, q_, kv, w.top_k, w.sm_scale, k_scale=k_scale,
+                               kv_scale=kv_scale, out=out, idx_share=idx, workspace=ws)
+
+        def step():
+            run_share(rank, q_idx, wts, q)
+    else:
+        def step():
+            sma.prefill(q_idx, wts, k_idx, q, kv, q_pos, w.top_k, w.sm_scale, k_scale=k_scale,
+                        kv_scale=kv_scale, out=out, idx_out=idx, workspace=ws)
+
+    # ------------------------------------------------------ timed steps --
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t_start) * 1e3 / max(args.steps, 1)
+    _log(f"step {ms_step:.2f} ms over {args.steps} steps")
+
+    # ------------------------------------------- per-kernel breakdown --
+    scores = ws[: blk * n_k * 4].view(torch.float32).view(blk, n_k)
+    reps = max(2, min(args.steps, 5))
+
+    def timed(fn, reps):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    nb = scores.shape[0]
+    t_idx = timed(lambda: sma.index_scores(q_idx[:nb], wts[:nb], k_idx, q_pos[:nb], k_scale=k_scale,
+                                           scores=scores), reps) * (n_q / nb)
+    t_topk = timed(lambda: sma.topk_select(scores, q_pos[:nb], w.top_k, idx=idx[:nb]), reps) * (n_q / nb)
+    # the full index list for the attention kernel comes from the timed steps
+    step()
+    t_mla = timed(lambda: sma.sparse_mla_prefill(q, kv, idx, w.sm_scale, kv_scale=kv_scale, out=out), reps)
+    _log(f"kernels: index_scores {t_idx:.2f} ms, topk {t_topk:.2f} ms, sparse_mla {t_mla:.2f} ms")
+    pcp = None
+    if args.workload == "pcp":
+        t_r7 = timed(step, reps)
+        t_r0 = timed(lambda: run_share(0, q_idx0, wts0, q0), reps)
+        step()   # leave rank 7's results in out/idx for the parity sample
+        pcp = {"rank7_ms": round(t_r7, 3), "rank0_ms": round(t_r0, 3), "rank0_over_rank7": round(t_r0 / t_r7, 4)}
+        _log(f"pcp: rank0 {t_r0:.2f} ms, rank7 {t_r7:.2f} ms")
+
+    pairs = acc.causal_pairs(pos_np)
+    key_bytes = (w.d_idx + 4) if w.fp8 else 2 * w.d_idx
+    row_bytes = (576 + 4) if w.fp8 else 1152
+    out_bytes = 4 if w.out_fp32 else 2
+    idx_flops = pairs * acc.indexer_flops_per_pair(w.h_idx, w.d_idx)
+    mla_flops = acc.mla_flops(pos_np, w.top_k)
+    topk_b = acc.topk_bytes(pos_np, w.top_k)
+    kern = {
+        "index_scores": {"ms": t_idx, "bound": "mfma", "achieved": idx_flops / (t_idx * 1e-3) / 1e12,
+                         "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "hbm_gbs": acc.indexer_bytes(pos_np, w.h_idx, w.d_idx, key_bytes) / (t_idx * 1e-3) / 1e9},
+        "topk_select": {"ms": t_topk, "bound": "hbm", "achieved": topk_b / (t_topk * 1e-3) / 1e9,
+                        "peak": acc.PEAK_HBM_GBS, "unit": "GB/s"},
+        "sparse_mla": {"ms": t_mla, "bound": "mfma", "achieved": mla_flops / (t_mla * 1e-3) / 1e12,
+                       "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "gather_gbs": acc.mla_bytes(pos_np, w.top_k, row_bytes, out_bytes) / (t_mla * 1e-3) / 1e9},
+    }
+    for v in kern.values():
+        v["frac"] = v["achieved"] / v["peak"]
+    dom = max(kern, key=lambda k: kern[k]["ms"])
+    roof = {"kernel": dom, "bound": kern[dom]["bound"], "achieved": round(kern[dom]["achieved"], 3),
+            "peak": kern[dom]["peak"], "unit": kern[dom]["unit"], "frac": round(kern[dom]["frac"], 4),
+            "traffic": None}
+
+    # ---------------------------------------- CPU oracle on a sample --
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            threads = os.cpu_count()
+        m = min(args.cpu_rows or {"prefill64k": 384, "prefill16k": 512, "pcp": 160, "decode": 6}[args.workload],
+                n_q)
+        sample = np.unique(np.linspace(0, n_q - 1, m).round().astype(np.int64))
+        f = oracle.bf16_bits_to_f64
+        kk = oracle.keys_f64((host(k_idx, np.uint8), host(k_scale)) if w.fp8 else host(k_idx, np.uint16), w.fp8)
+        kvv = oracle.keys_f64((host(kv, np.uint8), host(kv_scale)) if w.fp8 else host(kv, np.uint16), w.fp8)
+        s_idx = torch.from_numpy(sample).to(dev)
+        qi_s = f(host(q_idx[s_idx], np.uint16))
+        w_s = host(wts[s_idx]).astype(np.float64)
+        q_s = f(host(q[s_idx], np.uint16))
+        p_s = pos_np[sample]
+        t_c = time.perf_counter()
+        sc, ref_idx, ref_out, _ = oracle.prefill(qi_s, w_s, kk, q_s, kvv, p_s, w.top_k, w.sm_scale)
+        cpu_s = time.perf_counter() - t_c
+        cpu = {"value": round(sample.size / cpu_s, 3), "unit": "tokens/s", "cores": int(threads),
+               "kind": "oracle",
+               "sample": f"{sample.size} query rows spread evenly over the {n_q} rows of {w.name} "
+                         f"(indexer over each row's causal prefix, top-k, sparse MLA), float64 numpy, "
+                         f"{cpu_s:.1f} s"}
+        _log(f"oracle: {sample.size} rows in {cpu_s:.1f}s")
+        # parity of the GPU's rows against the oracle on the same sample
+        g_idx = host(idx[s_idx])
+        g_out = host(out[s_idx].float()).astype(np.float64)
+        rule = all(_threshold_rule_ok(oracle, g_idx[j], sc[j], w.top_k) for j in range(sample.size))
+        own_ref, _ = oracle.sparse_mla(q_s, kvv, g_idx, w.sm_scale)
+        err = float(np.abs(g_out - own_ref).max() / np.abs(own_ref).max())
+        exact_sets = float(np.mean([np.array_equal(g_idx[j], ref_idx[j]) for j in range(sample.size)]))
+        parity = {"rows": int(sample.size), "topk_threshold_rule": bool(rule), "topk_sets_identical": exact_sets,
+                  "mla_max_err_rel_to_max_ref": err, "tolerance": 3e-2 if w.fp8 else 1e-2,
+                  "ok": bool(rule and err <= (3e-2 if w.fp8 else 1e-2))}
+
+    tokens_s = n_q / (ms_step * 1e-3)
+    res = {
+        "metric": "sparse-MLA prefill tokens/s + indexer keys/s at 64K ctx; % of HBM/MFMA roofline",
+        "value": round(tokens_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, generated per run)",
+        "config": {"workload": w.name, "n_queries": int(n_q), "n_keys": int(n_k), "top_k": w.top_k,
+                   "mla_heads": 64, "d_qk": 576, "d_v": 512, "indexer_heads": w.h_idx, "d_idx": w.d_idx,
+                   "kv": "fp8-e4m3+scale" if w.fp8 else "bf16", "score_block_rows": int(nb)},
+        "causal_pairs": int(pairs), "selected_rows": int(acc.selected_rows(pos_np, w.top_k)),
+        "indexer_keys_per_s": round(pairs / (t_idx * 1e-3), 1),
+        "indexer_plus_topk_keys_per_s": round(pairs / ((t_idx + t_topk) * 1e-3), 1),
+        "sparse_mla_tokens_per_s": round(n_q / (t_mla * 1e-3), 1),
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kern.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    if pcp:
+        res["pcp_load_balance"] = pcp
+    print(json.dumps(res), flush=True)
+
+
+def _threshold_rule_ok(oracle, got, ref_scores, top_k, rel=1e-3):
+    """GPU index list vs the oracle's: same length, ascending, and members
+    may differ only where the oracle score is within rel*|threshold| of it."""
+    n = ref_scores.size
+    m = min(top_k, n)
+    v = np.asarray(got[:m])
+    if np.any(np.asarray(got[m:]) != -1) or np.any(v < 0) or np.any(v >= n) or np.any(np.diff(v) <= 0):
+        return False
+    ref = oracle.topk_row(ref_scores, top_k)[:m]
+    t = oracle.topk_threshold(ref_scores, top_k)
+    diff = np.setxor1d(v, ref)
+    return bool(np.all(np.abs(ref_scores[diff] - t) <= rel * abs(t)))
+
+
+def host(t, view=None):
+    import torch
+    a = t.detach().cpu()
+    if view is np.uint16:
+        return a.view(torch.int16).numpy().view(np.uint16)
+    if view is np.uint8:
+        return a.view(torch.uint8).numpy()
+    return a.numpy()
+
+
+if __name__ == "__main__":
+    main()
