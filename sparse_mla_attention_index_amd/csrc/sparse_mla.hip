@@ -255,19 +255,290 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     lse[(int64_t)qi * kHeads + head] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
+// ---------------------------------------------------------------------------
+// bf16 KV: the same computation with the gather issued as direct
+// global->LDS loads (global_load_lds_dwordx4) into a 4-deep ring of 32-row
+// tiles, so three tiles are in flight while one is consumed and no VGPRs
+// stage the gather.  Tiles are unpadded (1152 B per row) and every wave
+// issues exactly 9 one-KiB loads per tile, which keeps the per-wave vmcnt
+// bookkeeping exact.  Inside a row the 16-byte chunks are XOR-swizzled by
+// the row's low three bits so the K reads (16 rows, same chunk) and the
+// transposed V reads spread over the LDS banks.
+// ---------------------------------------------------------------------------
+constexpr int kDmaStages = 4;
+constexpr int kDmaRowB = kDqk * 2;                      // 1152
+constexpr int kDmaTileB = kMlaRows * kDmaRowB;          // 36864
+constexpr int kDmaLoadsPerWave = kDmaTileB / 1024 / 4;  // 9
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// One 16-byte-per-lane global->LDS load: lane l's 16 bytes land at LDS byte
+// address lds_base + 16*l.  Issued from inline assembly so that the
+// compiler's wait-count insertion does not treat it as aliasing the ring
+// slots being read; completion is tracked by hand with wait_vmcnt<>.
+__device__ __forceinline__ void dma_load16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ int chunk_swz(int row, int c) { return c ^ (row & 7); }
+
+// Place a value in the AGPR file (an empty asm with an AGPR in/out operand).
+// MFMA source operands may come from AGPRs, so the wave's 72 Q registers can
+// live there, leaving the VGPR file to the output accumulators and to K
+// operands prefetched from LDS ahead of their MFMAs.
+__device__ __forceinline__ void pin_agpr(bf16x8& x) { asm volatile("" : "+a"(x)); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int n_k,
+    const int32_t* __restrict__ idx, int n_q, int K, float scale_log2, void* __restrict__ out,
+    float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_kv[kDmaStages][kDmaTileB];
+  __shared__ int s_list[SMA_MAX_TOPK_DEV];
+  __shared__ uint32_t s_cnt[kMlaThreads / 64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qi = blockIdx.x;
+  const int g = lane >> 4, i = lane & 15;
+
+  // ---- compact the valid indices, keeping their order ----
+  constexpr int PER = SMA_MAX_TOPK_DEV / kMlaThreads;
+  int v[PER];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int j = tid * PER + e;
+    int x = j < K ? idx[(int64_t)qi * K + j] : -1;
+    if (x < 0 || x >= n_k) x = -1;
+    v[e] = x;
+    cnt += x >= 0;
+  }
+  uint32_t incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_cnt[tid >> 6] = incl;
+  __syncthreads();
+  uint32_t before = incl - cnt, total = 0;
+#pragma unroll
+  for (int w = 0; w < kMlaThreads / 64; ++w) {
+    if (w < (tid >> 6)) before += s_cnt[w];
+    total += s_cnt[w];
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (v[e] >= 0) s_list[before++] = v[e];
+  __syncthreads();
+  const int n_valid = (int)total;
+
+  const int head = 16 * (tid >> 6) + i;
+  if (n_valid == 0) {
+    for (int mt = 0; mt < kDv / 16; ++mt) {
+      const int64_t o_off = ((int64_t)qi * kHeads + head) * kDv + 16 * mt + 4 * g;
+      if constexpr (OUT_F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o_off) = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o_off) = u32x2{0u, 0u};
+      }
+    }
+    if (lse && g == 0) lse[(int64_t)qi * kHeads + head] = -INFINITY;
+    return;
+  }
+
+  // ---- the wave's Q fragment: head 16w+i, dims 32ks + 8g .. +7 ----
+  bf16x8 qf[kDqk / 32];
+  {
+    const uint16_t* src = q + ((int64_t)qi * kHeads + head) * kDqk + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + 32 * ks);
+  }
+  // Retire the Q loads here: from now on every outstanding vector-memory
+  // operation of the wave is a gather DMA, which wait_vmcnt<> counts.
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int ks = 0; ks < kDqk / 32; ++ks) pin_agpr(qf[ks]);
+
+  // ---- DMA gather of tile t into ring slot b (9 one-KiB loads per wave) ----
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
+  auto issue_tile = [&](int t, int b) {
+    // all source addresses first (one round of LDS reads), then the loads
+    const uint8_t* src[kDmaLoadsPerWave];
+#pragma unroll
+    for (int j = 0; j < kDmaLoadsPerWave; ++j) {
+      const int p = (wave * kDmaLoadsPerWave + j) * 1024 + lane * 16;
+      const int row = p / kDmaRowB;
+      const int c = chunk_swz(row, (p - row * kDmaRowB) >> 4);
+      const int li = t * kMlaRows + row;
+      src[j] = kvb + (int64_t)s_list[li < n_valid ? li : 0] * kDmaRowB + c * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < kDmaLoadsPerWave; ++j) {
+      const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)&s_kv[b][(wave * kDmaLoadsPerWave + j) * 1024];
+      dma_load16(src[j], __builtin_amdgcn_readfirstlane(dst));
+    }
+  };
+
+  f32x4 o[kDv / 16];
+#pragma unroll
+  for (int mt = 0; mt < kDv / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int ntiles = (n_valid + kMlaRows - 1) / kMlaRows;
+#pragma unroll
+  for (int t = 0; t < kDmaStages - 1; ++t)
+    if (t < ntiles) issue_tile(t, t);
+
+  // Per-lane LDS byte offsets inside a tile.  The swizzle XORs the chunk
+  // index c with (row & 7); splitting c into bit fields turns every read
+  // address into one of a few per-lane bases plus a compile-time offset.
+  //  K reads, row 16mt+i, chunk 4ks+g:  (4ks+g)^x = 8(ks>>1) + 4((ks&1)^(x>>2)) + ((g^x)&3)
+  const int xa = i & 7;
+  const int kbase = i * kDmaRowB + (((g ^ xa) & 3) << 4);
+  const int kb_even = kbase + ((xa >> 2) << 6);          // ks even
+  const int kb_odd = kbase + ((1 - (xa >> 2)) << 6);     // ks odd
+  //  V reads, rows rv and rv+16, chunk 2mt+vsub, 8-byte half vhalf:
+  //  (2mt+vsub)^x = 8(mt>>2) + 2((mt&3)^(x>>1)) + (vsub^(x&1))
+  const int rv = 4 * g + (i >> 2);
+  const int xv = rv & 7;
+  const int vsub = (i & 3) >> 1, vhalf = (i & 1) * 8;
+  int vbase[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    vbase[m] = rv * kDmaRowB + vhalf + ((2 * (m ^ (xv >> 1)) + (vsub ^ (xv & 1))) << 4);
+
+  for (int t = 0; t < ntiles; ++t) {
+    // tile t is complete once at most (tiles issued after it) x 9 loads remain
+    const int ahead = min(kDmaStages - 2, ntiles - 1 - t);
+    if (ahead >= 2) wait_vmcnt<2 * kDmaLoadsPerWave>();
+    else if (ahead == 1) wait_vmcnt<kDmaLoadsPerWave>();
+    else wait_vmcnt<0>();
+    block_sync_lds();
+    if (t + kDmaStages - 1 < ntiles) issue_tile(t + kDmaStages - 1, (t + kDmaStages - 1) % kDmaStages);
+    const uint8_t* tile = s_kv[t % kDmaStages];
+
+    // S^T = K . Q^T : rows 16mt + 4g + r, head i.  The K operands are read
+    // kPf k-steps ahead of the MFMAs that consume them.
+    constexpr int kKs = kDqk / 32, kPf = 4;
+    auto kread = [&](int ks, int mt) {
+      return *reinterpret_cast<const bf16x8*>(tile + ((ks & 1) ? kb_odd : kb_even) + (ks >> 1) * 128 +
+                                             mt * 16 * kDmaRowB);
+    };
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    bf16x8 kop[kPf][2];
+#pragma unroll
+    for (int ks = 0; ks < kPf; ++ks) {
+      kop[ks][0] = kread(ks, 0);
+      kop[ks][1] = kread(ks, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the issue order written here
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
+      const bf16x8 a0 = kop[ks % kPf][0], a1 = kop[ks % kPf][1];
+      if (ks + kPf < kKs) {
+        kop[ks % kPf][0] = kread(ks + kPf, 0);
+        kop[ks % kPf][1] = kread(ks + kPf, 1);
+      }
+      sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], sacc[1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    const int valid_rows = n_valid - t * kMlaRows;
+    float s2[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * mt + 4 * g + r;
+        const float x = row < valid_rows ? sacc[mt][r] * scale_log2 : -INFINITY;
+        s2[4 * mt + r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+    bf16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = exp2f(s2[e] - m_new);
+      psum += pe;
+      pb[e] = (__bf16)pe;
+    }
+    l_run = l_run * alpha + psum;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int mt = 0; mt < kDv / 16; ++mt) o[mt] *= alpha;
+    }
+    m_run = m_new;
+
+    // O^T += V^T . P^T ; V^T read transposed from the swizzled row-major tile
+#pragma unroll
+    for (int mt = 0; mt < kDv / 16; ++mt) {
+      const uint8_t* vp = tile + vbase[mt & 3] + (mt >> 2) * 128;
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vp);
+      const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 16 * kDmaRowB));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mt], 0, 0, 0);
+    }
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float inv = 1.f / l_tot;
+#pragma unroll
+  for (int mt = 0; mt < kDv / 16; ++mt) {
+    const int64_t o_off = ((int64_t)qi * kHeads + head) * kDv + 16 * mt + 4 * g;
+    const f32x4 r = o[mt] * inv;
+    if constexpr (OUT_F32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o_off) = r;
+    } else {
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o_off) =
+          u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+    }
+  }
+  if (lse && g == 0)
+    lse[(int64_t)qi * kHeads + head] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+}
+
 hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
   if (A.n_q <= 0) return hipSuccess;
   const float scale_log2 = A.sm_scale * 1.4426950408889634f;
   const dim3 grid((unsigned)A.n_q), block(kMlaThreads);
-#define SMA_MLA(F8, F32)                                                                         \
-  hipLaunchKernelGGL((sparse_mla_kernel<F8, F32>), grid, block, 0, st, A.q, A.kv, A.kv_scale,   \
-                     (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse)
   if (A.fp8) {
-    if (A.out_f32) SMA_MLA(true, true); else SMA_MLA(true, false);
+    if (A.out_f32)
+      hipLaunchKernelGGL((sparse_mla_kernel<true, true>), grid, block, 0, st, A.q, A.kv, A.kv_scale, (int)A.n_k,
+                         A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
+    else
+      hipLaunchKernelGGL((sparse_mla_kernel<true, false>), grid, block, 0, st, A.q, A.kv, A.kv_scale,
+                         (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
   } else {
-    if (A.out_f32) SMA_MLA(false, true); else SMA_MLA(false, false);
+    const uint16_t* kv = static_cast<const uint16_t*>(A.kv);
+    if (A.out_f32)
+      hipLaunchKernelGGL((sparse_mla_bf16_kernel<true>), grid, block, 0, st, A.q, kv, (int)A.n_k, A.idx, A.n_q,
+                         A.top_k, scale_log2, A.out, A.lse);
+    else
+      hipLaunchKernelGGL((sparse_mla_bf16_kernel<false>), grid, block, 0, st, A.q, kv, (int)A.n_k, A.idx,
+                         A.n_q, A.top_k, scale_log2, A.out, A.lse);
   }
-#undef SMA_MLA
   return hipGetLastError();
 }
 
