@@ -266,6 +266,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
 // transposed V reads spread over the LDS banks.
 // ---------------------------------------------------------------------------
 constexpr int kDmaStages = 4;
+constexpr float kRescaleSlack = 8.f;                    // log2 units
 constexpr int kDmaRowB = kDqk * 2;                      // 1152
 constexpr int kDmaTileB = kMlaRows * kDmaRowB;          // 36864
 constexpr int kDmaLoadsPerWave = kDmaTileB / 1024 / 4;  // 9
@@ -473,22 +474,29 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
+    // Lazy rescaling: the exponent reference m_run only moves when a logit
+    // exceeds it by more than kRescaleSlack (log2 units), so weights stay
+    // <= 2^kRescaleSlack and O is rescaled (128 VALU ops) only on those rare
+    // tiles instead of on every change of the running max.
+    if (t == 0) {
+      m_run = mx;
+    } else if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < kDv / 16; ++mt) o[mt] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
     bf16x8 pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = exp2f(s2[e] - m_new);
+      const float pe = __builtin_amdgcn_exp2f(s2[e] - m_run);
       psum += pe;
       pb[e] = (__bf16)pe;
     }
-    l_run = l_run * alpha + psum;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int mt = 0; mt < kDv / 16; ++mt) o[mt] *= alpha;
-    }
-    m_run = m_new;
+    l_run += psum;
 
     // O^T += V^T . P^T ; V^T read transposed from the swizzled row-major tile
 #pragma unroll
