@@ -80,7 +80,7 @@ struct RowSource {
   uint32_t key[V > 0 ? V : 1];
 };
 
-template <int THREADS, int V>
+template <int THREADS, int V, int VL>
 __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restrict__ scores,
                                                                int64_t ld,
                                                                const int32_t* __restrict__ q_pos,
@@ -89,6 +89,9 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
   constexpr int kTopkThreads = THREADS, kTopkWaves = THREADS / 64;
   static_assert(kBins % THREADS == 0, "whole histogram bins per thread");
   __shared__ TopkShared<THREADS> sh;
+  // Keys of positions THREADS*V + tid*VL + j live in LDS at word j*THREADS + tid
+  // (consecutive threads hit consecutive banks).
+  __shared__ uint32_t lds_keys[VL > 0 ? VL * THREADS : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;
   int p = q_pos[row];
@@ -122,13 +125,41 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
     }
   }
 
-  // Visit every (position, key) of this thread in ascending position; keys
-  // of positions >= n are 0.
+  constexpr int kSeg2 = THREADS * V;   // first position held in LDS
+  if constexpr (VL > 0) {
+    const int base = kSeg2 + tid * VL;
+#pragma unroll
+    for (int v = 0; v < VL; v += 4) {
+      const int p0 = base + v;
+      f32x4 x;
+      if (p0 + 3 < n) {
+        x = *reinterpret_cast<const f32x4*>(src + p0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = p0 + e < n ? src[p0 + e] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lds_keys[(v + e) * THREADS + tid] = p0 + e < n ? score_key(x[e]) : 0u;
+    }
+    __syncthreads();
+  }
+
+  // Visit every (position, key) of this thread; within each segment
+  // (registers, then LDS) in ascending position.  Keys of positions >= n are 0.
+  auto for_seg1 = [&](auto&& fn) {
+    const int base = tid * V;
+#pragma unroll
+    for (int v = 0; v < V; ++v) fn(base + v, rs.key[v]);
+  };
+  auto for_seg2 = [&](auto&& fn) {
+    const int base = kSeg2 + tid * VL;
+#pragma unroll 4
+    for (int v = 0; v < VL; ++v) fn(base + v, lds_keys[v * THREADS + tid]);
+  };
   auto for_each = [&](auto&& fn) {
     if constexpr (V > 0) {
-      const int base = tid * V;
-#pragma unroll
-      for (int v = 0; v < V; ++v) fn(base + v, rs.key[v]);
+      for_seg1(fn);
+      if constexpr (VL > 0) for_seg2(fn);
     } else {
       for (int c0 = 0; c0 < n; c0 += kTopkThreads * kStreamV) {
         const int base = c0 + tid * kStreamV;
@@ -217,23 +248,32 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
 
   // ---- 4. ordered compaction ----
   if constexpr (V > 0) {
-    uint32_t cg = 0, ce = 0;
-    for_each([&](int, uint32_t k) {
-      cg += k > T;
-      ce += k == T;
-    });
-    uint32_t g_before, e_before, tg, te;
-    block_excl_scan2<THREADS>(cg, ce, g_before, e_before, tg, te, sh);
-    for_each([&](int pos, uint32_t k) {
-      if (k > T) {
-        const uint32_t slot = g_before + min(e_before, need_ties);
-        if (slot < (uint32_t)K) out[slot] = pos;
-        ++g_before;
-      } else if (k == T) {
-        if (e_before < need_ties && g_before + e_before < (uint32_t)K) out[g_before + e_before] = pos;
-        ++e_before;
-      }
-    });
+    uint32_t g_run = 0, e_run = 0;   // totals of earlier segments
+    auto compact = [&](auto&& seg) {
+      uint32_t cg = 0, ce = 0;
+      seg([&](int, uint32_t k) {
+        cg += k > T;
+        ce += k == T;
+      });
+      uint32_t g_before, e_before, tg, te;
+      block_excl_scan2<THREADS>(cg, ce, g_before, e_before, tg, te, sh);
+      g_before += g_run;
+      e_before += e_run;
+      seg([&](int pos, uint32_t k) {
+        if (k > T) {
+          const uint32_t slot = g_before + min(e_before, need_ties);
+          if (slot < (uint32_t)K) out[slot] = pos;
+          ++g_before;
+        } else if (k == T) {
+          if (e_before < need_ties && g_before + e_before < (uint32_t)K) out[g_before + e_before] = pos;
+          ++e_before;
+        }
+      });
+      g_run += tg;
+      e_run += te;
+    };
+    compact(for_seg1);
+    if constexpr (VL > 0) compact(for_seg2);
   } else {
     uint32_t g_run = 0, e_run = 0;   // totals of earlier chunks
     for (int c0 = 0; c0 < n; c0 += kTopkThreads * kStreamV) {
@@ -271,18 +311,22 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
 hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   if (A.n_q <= 0) return hipSuccess;
   const dim3 grid((unsigned)A.n_q);
-  // Rows that fit are held in registers (1024 x 16 or 1024 x 32 keys, read
+  // Rows that fit are read once and kept on chip: 1024 x 16 or 1024 x 32
+  // keys in registers, or 1024 x 32 in registers plus 1024 x 32 in LDS (read
   // with 16-byte loads, so rows must start 16-byte aligned); longer or
   // unaligned rows are streamed from memory in every pass.
   const bool rows_aligned = (reinterpret_cast<uintptr_t>(A.scores) % 16 == 0) && (A.ld % 4 == 0);
   if (rows_aligned && A.n_k <= 1024 * 16) {
-    hipLaunchKernelGGL((topk_kernel<1024, 16>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
+    hipLaunchKernelGGL((topk_kernel<1024, 16, 0>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
                        (int)A.n_k, A.top_k, A.idx);
   } else if (rows_aligned && A.n_k <= 1024 * 32) {
-    hipLaunchKernelGGL((topk_kernel<1024, 32>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
+    hipLaunchKernelGGL((topk_kernel<1024, 32, 0>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
+                       (int)A.n_k, A.top_k, A.idx);
+  } else if (rows_aligned && A.n_k <= 1024 * 64) {
+    hipLaunchKernelGGL((topk_kernel<1024, 32, 32>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
                        (int)A.n_k, A.top_k, A.idx);
   } else {
-    hipLaunchKernelGGL((topk_kernel<1024, 0>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
+    hipLaunchKernelGGL((topk_kernel<1024, 0, 0>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
                        (int)A.n_k, A.top_k, A.idx);
   }
   return hipGetLastError();
