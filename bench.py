@@ -216,7 +216,7 @@ def main():
             threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         except Exception:
             threads = os.cpu_count()
-        m = min(args.cpu_rows or {"prefill64k": 384, "prefill16k": 512, "pcp": 160, "decode": 6}[args.workload],
+        m = min(args.cpu_rows or {"prefill64k": 4096, "prefill16k": 8192, "pcp": 2048, "decode": 64}[args.workload],
                 n_q)
         sample = np.unique(np.linspace(0, n_q - 1, m).round().astype(np.int64))
         f = oracle.bf16_bits_to_f64
