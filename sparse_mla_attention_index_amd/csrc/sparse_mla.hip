@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
 // transposed V reads spread over the LDS banks.
 // ---------------------------------------------------------------------------
 constexpr int kDmaStages = 4;
-constexpr float kRescaleSlack = 8.f;                    // log2 units
+constexpr float kRefGap = 64.f;                         // log2 units
 constexpr int kDmaRowB = kDqk * 2;                      // 1152
 constexpr int kDmaTileB = kMlaRows * kDmaRowB;          // 36864
 constexpr int kDmaLoadsPerWave = kDmaTileB / 1024 / 4;  // 9
@@ -395,15 +395,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     }
   };
 
-  f32x4 o[kDv / 16];
-#pragma unroll
-  for (int mt = 0; mt < kDv / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
   const int ntiles = (n_valid + kMlaRows - 1) / kMlaRows;
-#pragma unroll
-  for (int t = 0; t < kDmaStages - 1; ++t)
-    if (t < ntiles) issue_tile(t, t);
 
   // Per-lane LDS byte offsets inside a tile.  The swizzle XORs the chunk
   // index c with (row & 7); splitting c into bit fields turns every read
@@ -423,91 +415,113 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   for (int m = 0; m < 4; ++m)
     vbase[m] = rv * kDmaRowB + vhalf + ((2 * (m ^ (xv >> 1)) + (vsub ^ (xv & 1))) << 4);
 
-  for (int t = 0; t < ntiles; ++t) {
-    // tile t is complete once at most (tiles issued after it) x 9 loads remain
-    const int ahead = min(kDmaStages - 2, ntiles - 1 - t);
-    if (ahead >= 2) wait_vmcnt<2 * kDmaLoadsPerWave>();
-    else if (ahead == 1) wait_vmcnt<kDmaLoadsPerWave>();
-    else wait_vmcnt<0>();
-    block_sync_lds();
-    if (t + kDmaStages - 1 < ntiles) issue_tile(t + kDmaStages - 1, (t + kDmaStages - 1) % kDmaStages);
-    const uint8_t* tile = s_kv[t % kDmaStages];
+  // One sweep over the selected rows.  Softmax weights are exp2(z - m_ref)
+  // with a FIXED per-head reference: the first tile's maximum (fast sweep)
+  // or the exact maximum (rerun).  O is therefore never rescaled and is only
+  // ever touched by MFMAs inside the loop.  Weights above 1 are fine up to
+  // 2^kRefGap; the sweep records the true maximum m_max, and reports whether
+  // any logit passed m_ref + kRefGap (then the caller reruns with m_max).
+  f32x4 o[kDv / 16];
+  float l_run = 0.f, m_ref = 0.f, m_max = -INFINITY;
+  auto sweep = [&](bool ref_from_first_tile) -> bool {
+#pragma unroll
+    for (int mt = 0; mt < kDv / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+    bool far = false;
+#pragma unroll
+    for (int t = 0; t < kDmaStages - 1; ++t)
+      if (t < ntiles) issue_tile(t, t);
 
-    // S^T = K . Q^T : rows 16mt + 4g + r, head i.  The K operands are read
-    // kPf k-steps ahead of the MFMAs that consume them.
-    constexpr int kKs = kDqk / 32, kPf = 4;
-    auto kread = [&](int ks, int mt) {
-      return *reinterpret_cast<const bf16x8*>(tile + ((ks & 1) ? kb_odd : kb_even) + (ks >> 1) * 128 +
-                                             mt * 16 * kDmaRowB);
-    };
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    bf16x8 kop[kPf][2];
+    for (int t = 0; t < ntiles; ++t) {
+      // tile t is complete once at most (tiles issued after it) x 9 loads remain
+      const int ahead = min(kDmaStages - 2, ntiles - 1 - t);
+      if (ahead >= 2) wait_vmcnt<2 * kDmaLoadsPerWave>();
+      else if (ahead == 1) wait_vmcnt<kDmaLoadsPerWave>();
+      else wait_vmcnt<0>();
+      block_sync_lds();
+      if (t + kDmaStages - 1 < ntiles) issue_tile(t + kDmaStages - 1, (t + kDmaStages - 1) % kDmaStages);
+      const uint8_t* tile = s_kv[t % kDmaStages];
+
+      // S^T = K . Q^T : rows 16mt + 4g + r, head i.  K operands are read kPf
+      // k-steps ahead of the MFMAs that consume them.
+      constexpr int kKs = kDqk / 32, kPf = 4;
+      auto kread = [&](int ks, int mt) {
+        return *reinterpret_cast<const bf16x8*>(tile + ((ks & 1) ? kb_odd : kb_even) + (ks >> 1) * 128 +
+                                               mt * 16 * kDmaRowB);
+      };
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      bf16x8 kop[kPf][2];
 #pragma unroll
-    for (int ks = 0; ks < kPf; ++ks) {
-      kop[ks][0] = kread(ks, 0);
-      kop[ks][1] = kread(ks, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);   // keep the issue order written here
-#pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
-      const bf16x8 a0 = kop[ks % kPf][0], a1 = kop[ks % kPf][1];
-      if (ks + kPf < kKs) {
-        kop[ks % kPf][0] = kread(ks + kPf, 0);
-        kop[ks % kPf][1] = kread(ks + kPf, 1);
+      for (int ks = 0; ks < kPf; ++ks) {
+        kop[ks][0] = kread(ks, 0);
+        kop[ks][1] = kread(ks, 1);
       }
-      sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], sacc[1], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    const int valid_rows = n_valid - t * kMlaRows;
-    float s2[8];
-    float mx = -INFINITY;
+      __builtin_amdgcn_sched_barrier(0);   // keep the issue order written here
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mt + 4 * g + r;
-        const float x = row < valid_rows ? sacc[mt][r] * scale_log2 : -INFINITY;
-        s2[4 * mt + r] = x;
-        mx = fmaxf(mx, x);
+      for (int ks = 0; ks < kKs; ++ks) {
+        const bf16x8 a0 = kop[ks % kPf][0], a1 = kop[ks % kPf][1];
+        if (ks + kPf < kKs) {
+          kop[ks % kPf][0] = kread(ks + kPf, 0);
+          kop[ks % kPf][1] = kread(ks + kPf, 1);
+        }
+        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], sacc[1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Lazy rescaling: the exponent reference m_run only moves when a logit
-    // exceeds it by more than kRescaleSlack (log2 units), so weights stay
-    // <= 2^kRescaleSlack and O is rescaled (128 VALU ops) only on those rare
-    // tiles instead of on every change of the running max.
-    if (t == 0) {
-      m_run = mx;
-    } else if (__any(mx > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < kDv / 16; ++mt) o[mt] *= alpha;
-      m_run = m_new;
-    }
-    float psum = 0.f;
-    bf16x8 pb;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(s2[e] - m_run);
-      psum += pe;
-      pb[e] = (__bf16)pe;
-    }
-    l_run += psum;
 
-    // O^T += V^T . P^T ; V^T read transposed from the swizzled row-major tile
+      const int valid_rows = n_valid - t * kMlaRows;
+      float s2[8];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < kDv / 16; ++mt) {
-      const uint8_t* vp = tile + vbase[mt & 3] + (mt >> 2) * 128;
-      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vp);
-      const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 16 * kDmaRowB));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mt], 0, 0, 0);
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * mt + 4 * g + r;
+          const float x = row < valid_rows ? sacc[mt][r] * scale_log2 : -INFINITY;
+          s2[4 * mt + r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (ref_from_first_tile && t == 0) m_ref = mx;
+      m_max = fmaxf(m_max, mx);
+      far |= mx > m_ref + kRefGap;
+      float psum = 0.f;
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(fminf(s2[e] - m_ref, kRefGap));
+        psum += pe;
+        pb[e] = (__bf16)pe;
+      }
+      l_run += psum;
+
+      // O^T += V^T . P^T ; V^T read transposed from the swizzled row-major tile
+#pragma unroll
+      for (int mt = 0; mt < kDv / 16; ++mt) {
+        const uint8_t* vp = tile + vbase[mt & 3] + (mt >> 2) * 128;
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vp);
+        const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 16 * kDmaRowB));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mt], 0, 0, 0);
+      }
     }
+    return far;
+  };
+
+  // Fast sweep; a query whose logits rose more than 2^kRefGap above its first
+  // tile's maximum is swept again with the exact maximum as the reference.
+  // The decision is made for the whole workgroup (the gather ring is shared).
+  const bool far = sweep(true);
+  if (lane == 0) s_cnt[tid >> 6] = far ? 1u : 0u;
+  block_sync_lds();
+  const bool redo = (s_cnt[0] | s_cnt[1] | s_cnt[2] | s_cnt[3]) != 0u;
+  if (redo) {
+    m_ref = m_max;
+    block_sync_lds();   // all waves have read the flags before the ring is reused
+    sweep(false);
   }
+  const float m_run = m_ref;
 
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);

@@ -98,3 +98,25 @@ def test_mla_deterministic():
     a, _ = sma.sparse_mla_prefill(dev(q), dev(kv), dev(idx), TAU)
     b, _ = sma.sparse_mla_prefill(dev(q), dev(kv), dev(idx), TAU)
     assert torch.equal(a, b)
+
+
+def test_mla_logits_rising_far_above_first_tile():
+    """Later selected rows whose logits exceed the first tile's maximum by
+    far more than the fixed-reference range (the kernel then sweeps the
+    query again with the exact maximum)."""
+    rng = np.random.default_rng(21)
+    n_q, n_k, top_k = 6, 400, 256
+    q = (rng.standard_normal((n_q, 64, 576)) * 0.1).astype(np.float32)
+    kv = (rng.standard_normal((n_k, 576)) * 0.1).astype(np.float32)
+    q[:, :, :] = np.abs(q) + 0.05               # positive, so large rows give large logits
+    kv[300:] = np.abs(kv[300:]) * 40 + 2.0       # rows 300.. carry logits ~1e2-1e3 above the rest
+    idx = np.stack([np.sort(rng.choice(n_k, top_k, replace=False)) for _ in range(n_q)]).astype(np.int32)
+    idx[:, :40] = np.arange(40)                  # the first tile holds small rows only
+    idx = np.sort(idx, axis=1)
+    qb, kvb = synth.to_bf16_bits(q), synth.to_bf16_bits(kv)
+    out, lse = sma.sparse_mla_prefill(dev(qb), dev(kvb), dev(idx), TAU, out_dtype=torch.float32, want_lse=True)
+    ref, ref_lse = _ref(qb, kvb, idx)
+    got = out_f64(out)
+    assert np.all(np.isfinite(got))
+    assert np.abs(got - ref).max() <= 2e-3 * np.abs(ref).max()
+    assert np.abs(host(lse) - ref_lse).max() <= 1e-3 * np.abs(ref_lse).max()
