@@ -109,7 +109,7 @@ def test_mla_logits_rising_far_above_first_tile():
     q = (rng.standard_normal((n_q, 64, 576)) * 0.1).astype(np.float32)
     kv = (rng.standard_normal((n_k, 576)) * 0.1).astype(np.float32)
     q[:, :, :] = np.abs(q) + 0.05               # positive, so large rows give large logits
-    kv[300:] = np.abs(kv[300:]) * 40 + 2.0       # rows 300.. carry logits ~1e2-1e3 above the rest
+    kv[300:] = np.abs(kv[300:]) * 100 + 5.0      # rows 300.. carry logits ~100 log2 units above the rest
     idx = np.stack([np.sort(rng.choice(n_k, top_k, replace=False)) for _ in range(n_q)]).astype(np.int32)
     idx[:, :40] = np.arange(40)                  # the first tile holds small rows only
     idx = np.sort(idx, axis=1)
