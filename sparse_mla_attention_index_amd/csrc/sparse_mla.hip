@@ -296,11 +296,27 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier that makes this wave's LDS writes visible (waits for
+// its outstanding LDS operations) but leaves vector-memory loads in flight:
+// the gather DMA is waited for explicitly with wait_vmcnt<>.
 __device__ __forceinline__ void block_sync_lds() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+
+// The bf16 kernel splits a query's work over its 4 waves so that each
+// gathered byte is read from LDS by as few waves as possible:
+//   QK   wave w computes S^T for rows 16*(w&1)..+15 of the tile and heads
+//        32*(w>>1)..+31 (one K operand read feeds two 16-head MFMAs; the
+//        wave's Q fragment is 32 heads x 576 dims, 144 AGPRs);
+//   PV   wave w owns output dims 128w..128w+127 for all 64 heads, reading
+//        only its slice of V^T (transposed LDS reads) and the tile's P,
+//        which the QK waves write to LDS as bf16 [head][row].
+// Per 32-row tile the CU's LDS moves 160 KB (36 KB gather, 72 KB K, 32 KB
+// V, 20 KB P) instead of the 308 KB a 16-heads-per-wave split needs.
+constexpr int kPRowB = 80;                              // P^T row: 32 bf16 + 16 B pad
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
@@ -309,12 +325,15 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
     float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_kv[kDmaStages][kDmaTileB];
   __shared__ int s_list[SMA_MAX_TOPK_DEV];
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[kHeads * kPRowB];
+  __shared__ float s_red[4][kHeads];
   __shared__ uint32_t s_cnt[kMlaThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qi = blockIdx.x;
   const int g = lane >> 4, i = lane & 15;
+  const int rh = wave & 1, hh = wave >> 1;   // QK role: row half, head half
 
   // ---- compact the valid indices, keeping their order ----
   constexpr int PER = SMA_MAX_TOPK_DEV / kMlaThreads;
@@ -348,37 +367,42 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
   __syncthreads();
   const int n_valid = (int)total;
 
-  const int head = 16 * (tid >> 6) + i;
+  // output element (head 16n+i, dim 128w + 16m + 4g + r) lives in o[m][n][r]
+  auto out_off = [&](int m, int n) {
+    return ((int64_t)qi * kHeads + 16 * n + i) * kDv + 128 * (tid >> 6) + 16 * m + 4 * g;
+  };
   if (n_valid == 0) {
-    for (int mt = 0; mt < kDv / 16; ++mt) {
-      const int64_t o_off = ((int64_t)qi * kHeads + head) * kDv + 16 * mt + 4 * g;
-      if constexpr (OUT_F32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o_off) = f32x4{0.f, 0.f, 0.f, 0.f};
-      } else {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o_off) = u32x2{0u, 0u};
+    for (int m = 0; m < 8; ++m)
+      for (int n = 0; n < 4; ++n) {
+        if constexpr (OUT_F32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + out_off(m, n)) = f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + out_off(m, n)) = u32x2{0u, 0u};
+        }
       }
-    }
-    if (lse && g == 0) lse[(int64_t)qi * kHeads + head] = -INFINITY;
+    if (lse && tid < kHeads) lse[(int64_t)qi * kHeads + tid] = -INFINITY;
     return;
   }
 
-  // ---- the wave's Q fragment: head 16w+i, dims 32ks + 8g .. +7 ----
-  bf16x8 qf[kDqk / 32];
-  {
-    const uint16_t* src = q + ((int64_t)qi * kHeads + head) * kDqk + 8 * g;
+  // ---- Q fragment: heads 32hh + 16n + i, dims 32ks + 8g .. +7 ----
+  bf16x8 qf[2][kDqk / 32];
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + 32 * ks);
+  for (int n = 0; n < 2; ++n) {
+    const uint16_t* src = q + ((int64_t)qi * kHeads + 32 * hh + 16 * n + i) * kDqk + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) qf[n][ks] = *reinterpret_cast<const bf16x8*>(src + 32 * ks);
   }
   // Retire the Q loads here: from now on every outstanding vector-memory
   // operation of the wave is a gather DMA, which wait_vmcnt<> counts.
   wait_vmcnt<0>();
 #pragma unroll
-  for (int ks = 0; ks < kDqk / 32; ++ks) pin_agpr(qf[ks]);
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) (void)qf[n][ks];
 
   // ---- DMA gather of tile t into ring slot b (9 one-KiB loads per wave) ----
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
   auto issue_tile = [&](int t, int b) {
-    // all source addresses first (one round of LDS reads), then the loads
     const uint8_t* src[kDmaLoadsPerWave];
 #pragma unroll
     for (int j = 0; j < kDmaLoadsPerWave; ++j) {
@@ -394,151 +418,193 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
       dma_load16(src[j], __builtin_amdgcn_readfirstlane(dst));
     }
   };
-
   const int ntiles = (n_valid + kMlaRows - 1) / kMlaRows;
 
-  // Per-lane LDS byte offsets inside a tile.  The swizzle XORs the chunk
-  // index c with (row & 7); splitting c into bit fields turns every read
-  // address into one of a few per-lane bases plus a compile-time offset.
-  //  K reads, row 16mt+i, chunk 4ks+g:  (4ks+g)^x = 8(ks>>1) + 4((ks&1)^(x>>2)) + ((g^x)&3)
+  // ---- per-lane LDS byte offsets (swizzle: chunk ^= row & 7) ----
+  // K operand: row 16rh + i, chunk 4ks + g.
   const int xa = i & 7;
-  const int kbase = i * kDmaRowB + (((g ^ xa) & 3) << 4);
-  const int kb_even = kbase + ((xa >> 2) << 6);          // ks even
-  const int kb_odd = kbase + ((1 - (xa >> 2)) << 6);     // ks odd
-  //  V reads, rows rv and rv+16, chunk 2mt+vsub, 8-byte half vhalf:
-  //  (2mt+vsub)^x = 8(mt>>2) + 2((mt&3)^(x>>1)) + (vsub^(x&1))
-  const int rv = 4 * g + (i >> 2);
-  const int xv = rv & 7;
-  const int vsub = (i & 3) >> 1, vhalf = (i & 1) * 8;
-  int vbase[4];
+  const int kbase = (16 * rh + i) * kDmaRowB + (((g ^ xa) & 3) << 4);
+  const int kb_even = kbase + ((xa >> 2) << 6);
+  const int kb_odd = kbase + ((1 - (xa >> 2)) << 6);
+  // V^T operand of M-tile m: rows 8g + (i>>2) (+4), dims 128w + 16m + 4(i&3),
+  // i.e. chunk 16w + 2m + vsub, 8-byte half i&1; (2(m&3)+vsub) ^ x splits per m&3.
+  const int xr = i >> 2, vsub = (i & 3) >> 1, vhalf = (i & 1) * 8;
+  const int ra = 8 * g + xr;
+  int va_off[4], vb_off[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    vbase[m] = rv * kDmaRowB + vhalf + ((2 * (m ^ (xv >> 1)) + (vsub ^ (xv & 1))) << 4);
+  for (int mm = 0; mm < 4; ++mm) {
+    const int cl = 2 * mm + vsub;
+    va_off[mm] = ra * kDmaRowB + (16 * wave + (cl ^ xr)) * 16 + vhalf;
+    vb_off[mm] = (ra + 4) * kDmaRowB + (16 * wave + (cl ^ xr ^ 4)) * 16 + vhalf;
+  }
+  // P^T operand of N-tile n: head 16n + i, rows 8g..8g+7
+  const int p_rd = i * kPRowB + 16 * g;
+  // P^T written by the QK roles: head 32hh + 16n + i, rows 16rh + 4g .. +3
+  const int p_wr = (32 * hh + i) * kPRowB + (16 * rh + 4 * g) * 2;
 
-  // One sweep over the selected rows.  Softmax weights are exp2(z - m_ref)
-  // with a FIXED per-head reference: the first tile's maximum (fast sweep)
-  // or the exact maximum (rerun).  O is therefore never rescaled and is only
-  // ever touched by MFMAs inside the loop.  Weights above 1 are fine up to
-  // 2^kRefGap; the sweep records the true maximum m_max, and reports whether
-  // any logit passed m_ref + kRefGap (then the caller reruns with m_max).
-  f32x4 o[kDv / 16];
-  float l_run = 0.f, m_ref = 0.f, m_max = -INFINITY;
+  f32x4 o[8][4];
+  float m_ref[2], m_max[2] = {-INFINITY, -INFINITY}, l_part[2];   // per QK head 32hh+16n+i
+
+  // One sweep over the selected rows with a FIXED per-head exponent
+  // reference (the first tile's maximum, or the exact maximum on a rerun):
+  // O is only ever touched by MFMAs in the loop.  Returns whether some logit
+  // passed m_ref + kRefGap (weights above 1 are fine below that).
   auto sweep = [&](bool ref_from_first_tile) -> bool {
 #pragma unroll
-    for (int mt = 0; mt < kDv / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    l_run = 0.f;
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) o[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_part[0] = l_part[1] = 0.f;
     bool far = false;
 #pragma unroll
     for (int t = 0; t < kDmaStages - 1; ++t)
       if (t < ntiles) issue_tile(t, t);
 
     for (int t = 0; t < ntiles; ++t) {
-      // tile t is complete once at most (tiles issued after it) x 9 loads remain
       const int ahead = min(kDmaStages - 2, ntiles - 1 - t);
       if (ahead >= 2) wait_vmcnt<2 * kDmaLoadsPerWave>();
       else if (ahead == 1) wait_vmcnt<kDmaLoadsPerWave>();
       else wait_vmcnt<0>();
-      block_sync_lds();
+      block_sync_lds();   // tile t in LDS; every wave is done with tile t-1 and P
       if (t + kDmaStages - 1 < ntiles) issue_tile(t + kDmaStages - 1, (t + kDmaStages - 1) % kDmaStages);
       const uint8_t* tile = s_kv[t % kDmaStages];
 
-      // S^T = K . Q^T : rows 16mt + 4g + r, head i.  K operands are read kPf
-      // k-steps ahead of the MFMAs that consume them.
-      constexpr int kKs = kDqk / 32, kPf = 4;
-      auto kread = [&](int ks, int mt) {
-        return *reinterpret_cast<const bf16x8*>(tile + ((ks & 1) ? kb_odd : kb_even) + (ks >> 1) * 128 +
-                                               mt * 16 * kDmaRowB);
+      // ---- S^T (16 rows x 32 heads) = K . Q^T ----
+      constexpr int kKs = kDqk / 32, kPf = 6;
+      auto kread = [&](int ks) {
+        return *reinterpret_cast<const bf16x8*>(tile + ((ks & 1) ? kb_odd : kb_even) + (ks >> 1) * 128);
       };
       f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      bf16x8 kop[kPf][2];
+      bf16x8 kop[kPf];
 #pragma unroll
-      for (int ks = 0; ks < kPf; ++ks) {
-        kop[ks][0] = kread(ks, 0);
-        kop[ks][1] = kread(ks, 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);   // keep the issue order written here
+      for (int ks = 0; ks < kPf; ++ks) kop[ks] = kread(ks);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < kKs; ++ks) {
-        const bf16x8 a0 = kop[ks % kPf][0], a1 = kop[ks % kPf][1];
-        if (ks + kPf < kKs) {
-          kop[ks % kPf][0] = kread(ks + kPf, 0);
-          kop[ks % kPf][1] = kread(ks + kPf, 1);
-        }
-        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], sacc[1], 0, 0, 0);
+        const bf16x8 a = kop[ks % kPf];
+        if (ks + kPf < kKs) kop[ks % kPf] = kread(ks + kPf);
+        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][ks], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][ks], sacc[1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
 
+      // ---- softmax weights with the fixed reference ----
       const int valid_rows = n_valid - t * kMlaRows;
-      float s2[8];
-      float mx = -INFINITY;
+      float s2[2][4], mx[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int n = 0; n < 2; ++n) {
+        mx[n] = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = 16 * mt + 4 * g + r;
-          const float x = row < valid_rows ? sacc[mt][r] * scale_log2 : -INFINITY;
-          s2[4 * mt + r] = x;
-          mx = fmaxf(mx, x);
+          const float x = 16 * rh + 4 * g + r < valid_rows ? sacc[n][r] * scale_log2 : -INFINITY;
+          s2[n][r] = x;
+          mx[n] = fmaxf(mx[n], x);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (ref_from_first_tile && t == 0) m_ref = mx;
-      m_max = fmaxf(m_max, mx);
-      far |= mx > m_ref + kRefGap;
-      float psum = 0.f;
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(fminf(s2[e] - m_ref, kRefGap));
-        psum += pe;
-        pb[e] = (__bf16)pe;
       }
-      l_run += psum;
-
-      // O^T += V^T . P^T ; V^T read transposed from the swizzled row-major tile
+      if (ref_from_first_tile && t == 0) {
+        // reference = max over the first tile's 32 rows (both row halves)
 #pragma unroll
-      for (int mt = 0; mt < kDv / 16; ++mt) {
-        const uint8_t* vp = tile + vbase[mt & 3] + (mt >> 2) * 128;
-        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vp);
-        const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 16 * kDmaRowB));
+        for (int n = 0; n < 2; ++n) {
+          float x = fmaxf(mx[n], __shfl_xor(mx[n], 16, 64));
+          x = fmaxf(x, __shfl_xor(x, 32, 64));
+          if (g == 0) s_red[wave][16 * n + i] = x;
+        }
+        block_sync_lds();
+#pragma unroll
+        for (int n = 0; n < 2; ++n) m_ref[n] = fmaxf(s_red[wave][16 * n + i], s_red[wave ^ 1][16 * n + i]);
+      }
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        m_max[n] = fmaxf(m_max[n], mx[n]);
+        far |= mx[n] > m_ref[n] + kRefGap;
+        float ps = 0.f;
+        float pe[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pe[r] = __builtin_amdgcn_exp2f(fminf(s2[n][r] - m_ref[n], kRefGap));
+          ps += pe[r];
+        }
+        l_part[n] += ps;
+        *reinterpret_cast<u32x2*>(s_p + p_wr + 16 * n * kPRowB) =
+            u32x2{pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3])};
+      }
+      block_sync_lds();   // P of tile t complete
+
+      // ---- O^T (128 dims x 64 heads) += V^T . P^T ----
+      bf16x8 pb[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        pb[n] = *reinterpret_cast<const bf16x8*>(s_p + p_rd + 16 * n * kPRowB);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int mo = (m >> 2) * 128;
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + va_off[m & 3] + mo));
+        const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb_off[m & 3] + mo));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mt], 0, 0, 0);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) o[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[n], o[m][n], 0, 0, 0);
       }
     }
     return far;
   };
 
-  // Fast sweep; a query whose logits rose more than 2^kRefGap above its first
-  // tile's maximum is swept again with the exact maximum as the reference.
-  // The decision is made for the whole workgroup (the gather ring is shared).
+  // Combine per-wave partials over the two row halves: per QK head, the
+  // maximum (op = max) or the sum (op = add) of the lanes' values.
+  auto combine_heads = [&](float (&vals)[2], bool is_max) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      float x = vals[n];
+      const float y = __shfl_xor(x, 16, 64);
+      x = is_max ? fmaxf(x, y) : x + y;
+      const float z = __shfl_xor(x, 32, 64);
+      x = is_max ? fmaxf(x, z) : x + z;
+      if (g == 0) s_red[wave][16 * n + i] = x;
+    }
+    block_sync_lds();
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const float a = s_red[wave][16 * n + i], b = s_red[wave ^ 1][16 * n + i];
+      vals[n] = is_max ? fmaxf(a, b) : a + b;
+    }
+    block_sync_lds();
+  };
+
   const bool far = sweep(true);
   if (lane == 0) s_cnt[tid >> 6] = far ? 1u : 0u;
   block_sync_lds();
   const bool redo = (s_cnt[0] | s_cnt[1] | s_cnt[2] | s_cnt[3]) != 0u;
   if (redo) {
-    m_ref = m_max;
-    block_sync_lds();   // all waves have read the flags before the ring is reused
+    combine_heads(m_max, true);
+    m_ref[0] = m_max[0];
+    m_ref[1] = m_max[1];
     sweep(false);
   }
-  const float m_run = m_ref;
+  combine_heads(l_part, false);   // l per QK head (32hh + 16n + i), all rows
 
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  const float inv = 1.f / l_tot;
+  // every wave needs l for all 64 heads: publish by head
+  if (rh == 0 && g == 0) {
+    s_red[2][32 * hh + i] = l_part[0];
+    s_red[2][32 * hh + 16 + i] = l_part[1];
+    s_red[3][32 * hh + i] = m_ref[0];
+    s_red[3][32 * hh + 16 + i] = m_ref[1];
+  }
+  block_sync_lds();
 #pragma unroll
-  for (int mt = 0; mt < kDv / 16; ++mt) {
-    const int64_t o_off = ((int64_t)qi * kHeads + head) * kDv + 16 * mt + 4 * g;
-    const f32x4 r = o[mt] * inv;
-    if constexpr (OUT_F32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o_off) = r;
-    } else {
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o_off) =
-          u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+  for (int n = 0; n < 4; ++n) {
+    const float inv = 1.f / s_red[2][16 * n + i];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const f32x4 r = o[m][n] * inv;
+      if constexpr (OUT_F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + out_off(m, n)) = r;
+      } else {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + out_off(m, n)) =
+            u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+      }
     }
   }
-  if (lse && g == 0)
-    lse[(int64_t)qi * kHeads + head] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+  if (lse && tid < kHeads)
+    lse[(int64_t)qi * kHeads + tid] = (s_red[3][tid] + __log2f(s_red[2][tid])) * 0.69314718055994531f;
 }
 
 hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
