@@ -1,4 +1,4 @@
-// Sparse MLA gather-attention kernel (gfx950), absorbed / "MQA" mode.
+// Sparse MLA gather-attention kernels (gfx950), absorbed / "MQA" mode.
 //
 // All 64 heads of one query attend over the query's selected latent rows:
 // z = tau * q_h . kv_s[0:576], softmax over the selected set, o_h = sum_s
@@ -6,20 +6,19 @@
 // têtes" and footnote 1: one KV row read serves every head; QK over 576, PV
 // over 512).
 //
-// One workgroup (4 waves) per query; wave w owns heads 16w..16w+15.  The
-// selected rows are gathered 32 at a time into a double-buffered, row-major
-// LDS tile that serves both products:
-//   S^T[row][head] = K_tile . Q^T    v_mfma_f32_16x16x32_bf16, A = K rows read
-//                                    with ds_read_b128, B = the wave's Q
-//                                    fragment kept in registers;
-//   O^T[dim][head] += V^T . P^T      A = V^T read straight from the row-major
-//                                    tile with ds_read_b64_tr_b16, B = P taken
-//                                    from the S^T accumulators in registers.
+// Two kernels share that computation:
+//  * sparse_mla_kernel (FP8-e4m3 KV with a per-row scale): one 4-wave
+//    workgroup per query, wave w owns heads
+//    16w..16w+15, rows staged through registers into a padded row-major
+//    LDS tile and dequantised to bf16 on the way; v_mfma_f32_16x16x32_bf16
+//    for S^T = K.Q^T and O^T += V^T.P^T with an online softmax.
+//  * sparse_mla_bf16_kernel (bf16 KV): one 2-wave workgroup per query that
+//    splits both contractions by dims, gathers with direct global->LDS
+//    loads and uses v_mfma_f32_32x32x16_bf16 (twice the rate of the 16x16
+//    form on gfx950); its design is described where it is defined.
 // Writing the products transposed puts one head per lane column in both
-// accumulators, so the online-softmax statistics of a head and the output
-// rows they rescale live in the same lanes, and P never leaves registers.
-// Softmax runs in fp32 in the exp2 domain with a running max; the rescale of
-// O is skipped when no head's max moved.
+// accumulators, so the softmax statistics of a head and the output rows
+// they scale live in the same lanes.
 #include "sma_device.h"
 #include "sma_launch.h"
 
@@ -256,22 +255,15 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// bf16 KV: the same computation with the gather issued as direct
-// global->LDS loads (global_load_lds_dwordx4) into a 4-deep ring of 32-row
-// tiles, so three tiles are in flight while one is consumed and no VGPRs
-// stage the gather.  Tiles are unpadded (1152 B per row) and every wave
-// issues exactly 9 one-KiB loads per tile, which keeps the per-wave vmcnt
-// bookkeeping exact.  Inside a row the 16-byte chunks are XOR-swizzled by
-// the row's low three bits so the K reads (16 rows, same chunk) and the
-// transposed V reads spread over the LDS banks.
+// Helpers of the bf16 kernel below: direct global->LDS loads, hand-kept
+// vmcnt bookkeeping, and MFMAs with VGPR accumulators.
 // ---------------------------------------------------------------------------
-constexpr int kDmaStages = 4;
 constexpr float kRefGap = 64.f;                         // log2 units
 constexpr int kDmaRowB = kDqk * 2;                      // 1152
 constexpr int kDmaTileB = kMlaRows * kDmaRowB;          // 36864
-constexpr int kDmaLoadsPerWave = kDmaTileB / 1024 / 4;  // 9
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef float f32x16v_t __attribute__((ext_vector_type(16)));
 
 // One 16-byte-per-lane global->LDS load: lane l's 16 bytes land at LDS byte
 // address lds_base + 16*l.  Issued from inline assembly so that the
@@ -282,13 +274,24 @@ __device__ __forceinline__ void dma_load16(const void* gaddr, uint32_t lds_base)
                : "memory", "m0");
 }
 
-__device__ __forceinline__ int chunk_swz(int row, int c) { return c ^ (row & 7); }
-
-// Place a value in the AGPR file (an empty asm with an AGPR in/out operand).
-// MFMA source operands may come from AGPRs, so the wave's 72 Q registers can
-// live there, leaving the VGPR file to the output accumulators and to K
-// operands prefetched from LDS ahead of their MFMAs.
-__device__ __forceinline__ void pin_agpr(bf16x8& x) { asm volatile("" : "+a"(x)); }
+// v_mfma_f32_32x32x16_bf16 with its accumulator in VGPRs.  The compiler
+// emits every MFMA builtin of a kernel that also uses AGPRs in the AGPR
+// form; the output accumulators fill the AGPR file, so the QK partial sums
+// are formed through these instead.  Being opaque to the compiler's hazard
+// recognizer, they carry their own wait states: two before each MFMA (a
+// VALU write of an A/B register just before it) and, in drain, 24 after the
+// last one before any VALU or LDS instruction reads the result (an 8-pass
+// XDL op needs 11).  A dependent chain through the same accumulator needs
+// none.
+__device__ __forceinline__ void mfma32_vgpr_first(f32x16v_t& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_vgpr(f32x16v_t& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_vgpr_drain(f32x16v_t& x, f32x16v_t& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -306,305 +309,305 @@ __device__ __forceinline__ void block_sync_lds() {
   asm volatile("" ::: "memory");
 }
 
-// The bf16 kernel splits a query's work over its 4 waves so that each
-// gathered byte is read from LDS by as few waves as possible:
-//   QK   wave w computes S^T for rows 16*(w&1)..+15 of the tile and heads
-//        32*(w>>1)..+31 (one K operand read feeds two 16-head MFMAs; the
-//        wave's Q fragment is 32 heads x 576 dims, 144 AGPRs);
-//   PV   wave w owns output dims 128w..128w+127 for all 64 heads, reading
-//        only its slice of V^T (transposed LDS reads) and the tile's P,
-//        which the QK waves write to LDS as bf16 [head][row].
-// Per 32-row tile the CU's LDS moves 160 KB (36 KB gather, 72 KB K, 32 KB
-// V, 20 KB P) instead of the 308 KB a 16-heads-per-wave split needs.
-constexpr int kPRowB = 80;                              // P^T row: 32 bf16 + 16 B pad
+// bf16 KV kernel.  One 2-wave workgroup per query, two workgroups per CU
+// (one wave per SIMD).  The two waves split every contraction by dims, so
+// each byte of a gathered tile is read from LDS by exactly one wave:
+//   QK: wave d holds Q for all 64 heads over dims 288d..288d+287 (144
+//       VGPRs) and forms a partial S^T[32 rows x 64 heads] with
+//       v_mfma_f32_32x32x16_bf16 (A = K rows, B = Q);  the partner's
+//       half-sum for the heads this wave owns arrives through LDS;
+//   softmax: wave d owns heads 32d..32d+31;  its bf16 P goes to the partner
+//       through LDS;
+//   PV: wave d accumulates O^T[dims 256d..256d+255 x 64 heads] (256 AGPRs)
+//       with A = V^T read by ds_read_b64_tr_b16 and B = P.
+// Softmax weights use a fixed per-head reference (below), so the output
+// registers are only ever written by MFMAs.
+//
+// Tile layout (32 rows x 576 dims, 36 KiB): a 1-KiB block holds 16 rows x
+// 4 chunks of 16 bytes.  Chunk c of row r sits in block 2(c>>2) + (r>>4) at
+// slot 16(c&3) + ((r&15) ^ 4(c&1)).  A direct global->LDS load fills one
+// block, so each load reads 64 contiguous bytes from each of 16 rows (whole
+// 64-byte lines), and lane l of every load fetches one of the two rows
+// ((l&15) ^ 4((l>>4)&1)) + {0, 16}: two indices per lane per tile.  The K
+// operand of a k-step and the transposed V reads of a 16-lane group both hit
+// 16 distinct bank groups, and every read offset is an immediate.  The rope
+// blocks (chunks 64..71, bytes 32768..36863) are dead after QK and carry the
+// S/P exchange of one direction; a 4-KiB buffer carries the other.
+//
+// Entries are used in their given order without compaction: invalid ones
+// (negative, past n_k or past top_k) gather row 0 and are masked out of the
+// softmax by a per-tile row mask.
+constexpr int kPairThreads = 128;
+constexpr int kPairLoads = kDmaTileB / 1024 / 2;   // 18 one-KiB loads per wave per tile
+constexpr int kPairKs = kDqk / 16 / 2;             // 18 k-steps of QK per wave
+constexpr int kPairMt = kDv / 32 / 2;              // 8 M-tiles of PV per wave
+constexpr int kRopeOff = kDv * 2 / 32 * 1024;      // 32768: first byte of the rope blocks
+constexpr int kIdxChunk = 256;                     // entries per staged index chunk (8 tiles)
+
+// One 4-byte-per-lane global->LDS load (lane l's word lands at lds_base + 4l).
+__device__ __forceinline__ void dma_load4(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+typedef f32x16v_t f32x16v;
 
 template <bool OUT_F32>
-__global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_bf16_kernel(
+__global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int n_k,
     const int32_t* __restrict__ idx, int n_q, int K, float scale_log2, void* __restrict__ out,
     float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_kv[kDmaStages][kDmaTileB];
-  __shared__ int s_list[SMA_MAX_TOPK_DEV];
-  __shared__ __attribute__((aligned(16))) uint8_t s_p[kHeads * kPRowB];
-  __shared__ float s_red[4][kHeads];
-  __shared__ uint32_t s_cnt[kMlaThreads / 64];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_kv[2][kDmaTileB];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x[4096];
+  __shared__ __attribute__((aligned(1024))) int s_idx[2][kIdxChunk];
+  __shared__ float s_l[kHeads];
+  __shared__ int s_red[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int d = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qi = blockIdx.x;
-  const int g = lane >> 4, i = lane & 15;
-  const int rh = wave & 1, hh = wave >> 1;   // QK role: row half, head half
+  const int h = lane >> 5, c32 = lane & 31;
+  const int32_t* irow = idx + (int64_t)qi * K;
 
-  // ---- compact the valid indices, keeping their order ----
-  constexpr int PER = SMA_MAX_TOPK_DEV / kMlaThreads;
-  int v[PER];
-  uint32_t cnt = 0;
+  // ---- extent of the selection: entries [0, n_ext) hold every valid index ----
+  int last = -1;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int j = tid * PER + e;
-    int x = j < K ? idx[(int64_t)qi * K + j] : -1;
-    if (x < 0 || x >= n_k) x = -1;
-    v[e] = x;
-    cnt += x >= 0;
+  for (int e = 0; e < SMA_MAX_TOPK_DEV / kPairThreads; ++e) {
+    const int j = e * kPairThreads + tid;
+    if (j < K) {
+      const int x = irow[j];
+      if (x >= 0 && x < n_k) last = j;
+    }
   }
-  uint32_t incl = cnt;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) s_cnt[tid >> 6] = incl;
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  if (lane == 0) s_red[d] = last;
   __syncthreads();
-  uint32_t before = incl - cnt, total = 0;
-#pragma unroll
-  for (int w = 0; w < kMlaThreads / 64; ++w) {
-    if (w < (tid >> 6)) before += s_cnt[w];
-    total += s_cnt[w];
-  }
-#pragma unroll
-  for (int e = 0; e < PER; ++e)
-    if (v[e] >= 0) s_list[before++] = v[e];
-  __syncthreads();
-  const int n_valid = (int)total;
-
-  // output element (head 16n+i, dim 128w + 16m + 4g + r) lives in o[m][n][r]
-  auto out_off = [&](int m, int n) {
-    return ((int64_t)qi * kHeads + 16 * n + i) * kDv + 128 * (tid >> 6) + 16 * m + 4 * g;
-  };
-  if (n_valid == 0) {
-    for (int m = 0; m < 8; ++m)
-      for (int n = 0; n < 4; ++n) {
-        if constexpr (OUT_F32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + out_off(m, n)) = f32x4{0.f, 0.f, 0.f, 0.f};
-        } else {
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + out_off(m, n)) = u32x2{0u, 0u};
-        }
+  const int n_ext = max(s_red[0], s_red[1]) + 1;
+  if (n_ext == 0) {
+    for (int i = tid; i < kHeads * kDv / 4; i += kPairThreads) {
+      if constexpr (OUT_F32) {
+        reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)qi * kHeads * kDv)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (int64_t)qi * kHeads * kDv)[i] = u32x2{0u, 0u};
       }
+    }
     if (lse && tid < kHeads) lse[(int64_t)qi * kHeads + tid] = -INFINITY;
     return;
   }
+  const int ntiles = (n_ext + kMlaRows - 1) / kMlaRows;
 
-  // ---- Q fragment: heads 32hh + 16n + i, dims 32ks + 8g .. +7 ----
-  bf16x8 qf[2][kDqk / 32];
+  // ---- Q: block 0 = own heads 32d+c32, block 1 = partner heads; dims 288d + 16ks + 8h .. +7 ----
+  bf16x8 qf[2][kPairKs];
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const uint16_t* src = q + ((int64_t)qi * kHeads + 32 * hh + 16 * n + i) * kDqk + 8 * g;
+  for (int hb = 0; hb < 2; ++hb) {
+    const uint16_t* src = q + ((int64_t)qi * kHeads + 32 * (d ^ hb) + c32) * kDqk + 16 * kPairKs * d + 8 * h;
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) qf[n][ks] = *reinterpret_cast<const bf16x8*>(src + 32 * ks);
+    for (int ks = 0; ks < kPairKs; ++ks) qf[hb][ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
   }
-  // Retire the Q loads here: from now on every outstanding vector-memory
-  // operation of the wave is a gather DMA, which wait_vmcnt<> counts.
-  wait_vmcnt<0>();
-#pragma unroll
-  for (int n = 0; n < 2; ++n)
-#pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) (void)qf[n][ks];
 
-  // ---- DMA gather of tile t into ring slot b (9 one-KiB loads per wave) ----
-  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
-  auto issue_tile = [&](int t, int b) {
-    const uint8_t* src[kDmaLoadsPerWave];
+  // ---- gather: block B (wave d issues B = 18d..18d+17) lane l fetches row
+  // 16(B&1) + rsel, chunk 4(B>>1) + (l>>4) ----
+  const int rsel = (lane & 15) ^ (4 * ((lane >> 4) & 1));
+  // The entries are staged through LDS in chunks of 8 tiles (one chunk
+  // ahead), so the per-tile index reads are LDS reads and the only
+  // vector-memory operations in flight are the gathers and chunk loads.
+  auto stage_chunk = [&](int c) {
+    const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)&s_idx[c & 1][kIdxChunk / 2 * d];
 #pragma unroll
-    for (int j = 0; j < kDmaLoadsPerWave; ++j) {
-      const int p = (wave * kDmaLoadsPerWave + j) * 1024 + lane * 16;
-      const int row = p / kDmaRowB;
-      const int c = chunk_swz(row, (p - row * kDmaRowB) >> 4);
-      const int li = t * kMlaRows + row;
-      src[j] = kvb + (int64_t)s_list[li < n_valid ? li : 0] * kDmaRowB + c * 16;
-    }
-#pragma unroll
-    for (int j = 0; j < kDmaLoadsPerWave; ++j) {
-      const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)&s_kv[b][(wave * kDmaLoadsPerWave + j) * 1024];
-      dma_load16(src[j], __builtin_amdgcn_readfirstlane(dst));
-    }
+    for (int i = 0; i < kIdxChunk / 2 / 64; ++i)
+      dma_load4(irow + min(c * kIdxChunk + kIdxChunk / 2 * d + 64 * i + lane, K - 1), dst + 256 * i);
   };
-  const int ntiles = (n_valid + kMlaRows - 1) / kMlaRows;
-
-  // ---- per-lane LDS byte offsets (swizzle: chunk ^= row & 7) ----
-  // K operand: row 16rh + i, chunk 4ks + g.
-  const int xa = i & 7;
-  const int kbase = (16 * rh + i) * kDmaRowB + (((g ^ xa) & 3) << 4);
-  const int kb_even = kbase + ((xa >> 2) << 6);
-  const int kb_odd = kbase + ((1 - (xa >> 2)) << 6);
-  // V^T operand of M-tile m: rows 8g + (i>>2) (+4), dims 128w + 16m + 4(i&3),
-  // i.e. chunk 16w + 2m + vsub, 8-byte half i&1; (2(m&3)+vsub) ^ x splits per m&3.
-  const int xr = i >> 2, vsub = (i & 3) >> 1, vhalf = (i & 1) * 8;
-  const int ra = 8 * g + xr;
-  int va_off[4], vb_off[4];
+  auto entry_raw = [&](int t, int half) -> int {
+    const int e = t * kMlaRows + 16 * half + rsel;
+    return s_idx[(e / kIdxChunk) & 1][e % kIdxChunk];
+  };
+  auto entry_ok = [&](int t, int half, int x) -> bool {
+    return t * kMlaRows + 16 * half + rsel < n_ext && x >= 0 && x < n_k;
+  };
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv) + 16 * (lane >> 4) + 64 * (kPairLoads / 2) * d;
+  auto issue_tile = [&](int t, int b) -> uint32_t {   // returns the tile's row mask
+    const int raw_lo = entry_raw(t, 0), raw_hi = entry_raw(t, 1);
+    const bool ok_lo = entry_ok(t, 0, raw_lo), ok_hi = entry_ok(t, 1, raw_hi);
+    const uint8_t* src_lo = kvb + (int64_t)(ok_lo ? raw_lo : 0) * kDmaRowB;
+    const uint8_t* src_hi = kvb + (int64_t)(ok_hi ? raw_hi : 0) * kDmaRowB;
+    const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)&s_kv[b][kPairLoads * 1024 * d];
 #pragma unroll
-  for (int mm = 0; mm < 4; ++mm) {
-    const int cl = 2 * mm + vsub;
-    va_off[mm] = ra * kDmaRowB + (16 * wave + (cl ^ xr)) * 16 + vhalf;
-    vb_off[mm] = (ra + 4) * kDmaRowB + (16 * wave + (cl ^ xr ^ 4)) * 16 + vhalf;
-  }
-  // P^T operand of N-tile n: head 16n + i, rows 8g..8g+7
-  const int p_rd = i * kPRowB + 16 * g;
-  // P^T written by the QK roles: head 32hh + 16n + i, rows 16rh + 4g .. +3
-  const int p_wr = (32 * hh + i) * kPRowB + (16 * rh + 4 * g) * 2;
+    for (int j = 0; j < kPairLoads; ++j) dma_load16((j & 1 ? src_hi : src_lo) + 64 * (j >> 1), dst + 1024 * j);
+    // rows 0..15: lanes 0..15 (rsel = lane) of the lo half; rows 16..31: of the hi half
+    return ((uint32_t)__ballot(ok_lo) & 0xFFFFu) | (((uint32_t)__ballot(ok_hi) & 0xFFFFu) << 16);
+  };
+  // Retire the Q and extent loads: from here on the wave's outstanding
+  // vector-memory operations are gathers and index-chunk loads only.
+  wait_vmcnt<0>();
 
-  f32x4 o[8][4];
-  float m_ref[2], m_max[2] = {-INFINITY, -INFINITY}, l_part[2];   // per QK head 32hh+16n+i
+  // K operand of k-step ks (global 18d+ks): row c32, chunk 36d + 2ks + h.
+  const int kbase = (kPairLoads * 1024) * d + (c32 >> 4) * 1024 + 256 * h + 16 * ((c32 & 15) ^ (4 * h));
+  auto koff = [](int ks) { return (ks >> 1) * 2048 + (ks & 1) * 512; };
+  // V^T operand of M-tile m (dims 256d+32m..), k-step kk, half e: 16-lane group b = lane>>4
+  // reads rows 16kk + 8e + 4h + (L>>2) at dims 32m + 16(b&1) + 4(L&3), L = lane&15.
+  const int L = lane & 15, pL = (L >> 1) & 1;
+  const int vbase = (kPairMt * 2048) * d + 512 * ((lane >> 4) & 1) + 256 * pL + 64 * (h ^ pL) + 16 * (L >> 2) +
+                    8 * (L & 1);
 
-  // One sweep over the selected rows with a FIXED per-head exponent
-  // reference (the first tile's maximum, or the exact maximum on a rerun):
-  // O is only ever touched by MFMAs in the loop.  Returns whether some logit
-  // passed m_ref + kRefGap (weights above 1 are fine below that).
-  auto sweep = [&](bool ref_from_first_tile) -> bool {
+  f32x16v o[kPairMt][2];
+  float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.f;
+
+  // One sweep over the entries with a FIXED per-head exponent reference
+  // (the first tile's maximum, or the exact maximum on a rerun).  Returns
+  // whether some logit passed m_ref + kRefGap.
+  auto sweep = [&]() -> bool {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int n = 0; n < 4; ++n) o[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    l_part[0] = l_part[1] = 0.f;
+    for (int m = 0; m < kPairMt; ++m) o[m][0] = o[m][1] = f32x16v{};
+    l_run = 0.f;
     bool far = false;
-#pragma unroll
-    for (int t = 0; t < kDmaStages - 1; ++t)
-      if (t < ntiles) issue_tile(t, t);
-
+    // Vector-memory operations of iteration t: [index chunk], gather(t+1).
+    stage_chunk(0);
+    wait_vmcnt<0>();
+    block_sync_lds();
+    uint32_t mask = issue_tile(0, 0);
     for (int t = 0; t < ntiles; ++t) {
-      const int ahead = min(kDmaStages - 2, ntiles - 1 - t);
-      if (ahead >= 2) wait_vmcnt<2 * kDmaLoadsPerWave>();
-      else if (ahead == 1) wait_vmcnt<kDmaLoadsPerWave>();
-      else wait_vmcnt<0>();
-      block_sync_lds();   // tile t in LDS; every wave is done with tile t-1 and P
-      if (t + kDmaStages - 1 < ntiles) issue_tile(t + kDmaStages - 1, (t + kDmaStages - 1) % kDmaStages);
-      const uint8_t* tile = s_kv[t % kDmaStages];
+      wait_vmcnt<0>();     // tile t (and any index chunk) has landed
+      block_sync_lds();    // for both waves; tile t-1's slot and the exchange buffers are free
+      if (t % (kIdxChunk / kMlaRows) == 0 && (t / (kIdxChunk / kMlaRows) + 1) * kIdxChunk < n_ext)
+        stage_chunk(t / (kIdxChunk / kMlaRows) + 1);
+      uint32_t mask_next = 0;
+      if (t + 1 < ntiles) mask_next = issue_tile(t + 1, (t + 1) & 1);
+      uint8_t* tile = s_kv[t & 1];
 
-      // ---- S^T (16 rows x 32 heads) = K . Q^T ----
-      constexpr int kKs = kDqk / 32, kPf = 6;
-      auto kread = [&](int ks) {
-        return *reinterpret_cast<const bf16x8*>(tile + ((ks & 1) ? kb_odd : kb_even) + (ks >> 1) * 128);
-      };
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      // ---- partial S^T over this wave's dims, both head blocks ----
+      constexpr int kPf = 3;
+      auto kread = [&](int ks) { return *reinterpret_cast<const bf16x8*>(tile + kbase + koff(ks)); };
+      f32x16v s_own, s_oth;
       bf16x8 kop[kPf];
 #pragma unroll
       for (int ks = 0; ks < kPf; ++ks) kop[ks] = kread(ks);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) {
+      for (int ks = 0; ks < kPairKs; ++ks) {
         const bf16x8 a = kop[ks % kPf];
-        if (ks + kPf < kKs) kop[ks % kPf] = kread(ks + kPf);
-        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][ks], sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][ks], sacc[1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        if (ks + kPf < kPairKs) kop[ks % kPf] = kread(ks + kPf);
+        if (ks == 0) {
+          mfma32_vgpr_first(s_own, a, qf[0][0]);
+          mfma32_vgpr_first(s_oth, a, qf[1][0]);
+        } else {
+          mfma32_vgpr(s_own, a, qf[0][ks]);
+          mfma32_vgpr(s_oth, a, qf[1][ks]);
+        }
+      }
+      mfma32_vgpr_drain(s_own, s_oth);
+
+      // ---- exchange half-sums: wave 1 writes into the (now dead) rope blocks, wave 0 into s_x ----
+      uint8_t* xw = d ? tile + kRopeOff : s_x;   // written by this wave
+      uint8_t* xr = d ? s_x : tile + kRopeOff;   // written by the partner
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        *reinterpret_cast<f32x4*>(xw + 1024 * p + 16 * lane) =
+            f32x4{s_oth[4 * p], s_oth[4 * p + 1], s_oth[4 * p + 2], s_oth[4 * p + 3]};
+      block_sync_lds();
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const f32x4 y = *reinterpret_cast<const f32x4*>(xr + 1024 * p + 16 * lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_own[4 * p + r] += y[r];
       }
 
-      // ---- softmax weights with the fixed reference ----
-      const int valid_rows = n_valid - t * kMlaRows;
-      float s2[2][4], mx[2];
+      // ---- softmax weights of the own heads: element j is row 8(j>>2) + 4h + (j&3) ----
+      const uint32_t mh = mask >> (4 * h);
+      float x[16], mx = -INFINITY;
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        mx[n] = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float x = 16 * rh + 4 * g + r < valid_rows ? sacc[n][r] * scale_log2 : -INFINITY;
-          s2[n][r] = x;
-          mx[n] = fmaxf(mx[n], x);
-        }
+      for (int j = 0; j < 16; ++j) {
+        const bool v = (mh >> (8 * (j >> 2) + (j & 3))) & 1u;
+        x[j] = v ? s_own[j] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[j]);
       }
-      if (ref_from_first_tile && t == 0) {
-        // reference = max over the first tile's 32 rows (both row halves)
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (m_ref == -INFINITY) m_ref = mx;   // first tile holding a valid row
+      m_max = fmaxf(m_max, mx);
+      far |= mx > m_ref + kRefGap;
+      bf16x8 pb[2];
+      float ps = 0.f;
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          float x = fmaxf(mx[n], __shfl_xor(mx[n], 16, 64));
-          x = fmaxf(x, __shfl_xor(x, 32, 64));
-          if (g == 0) s_red[wave][16 * n + i] = x;
-        }
-        block_sync_lds();
-#pragma unroll
-        for (int n = 0; n < 2; ++n) m_ref[n] = fmaxf(s_red[wave][16 * n + i], s_red[wave ^ 1][16 * n + i]);
+      for (int j = 0; j < 16; ++j) {
+        const float pe = x[j] > -INFINITY ? __builtin_amdgcn_exp2f(fminf(x[j] - m_ref, kRefGap)) : 0.f;
+        ps += pe;
+        pb[j >> 3][j & 7] = (__bf16)pe;
       }
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        m_max[n] = fmaxf(m_max[n], mx[n]);
-        far |= mx[n] > m_ref[n] + kRefGap;
-        float ps = 0.f;
-        float pe[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pe[r] = __builtin_amdgcn_exp2f(fminf(s2[n][r] - m_ref[n], kRefGap));
-          ps += pe[r];
-        }
-        l_part[n] += ps;
-        *reinterpret_cast<u32x2*>(s_p + p_wr + 16 * n * kPRowB) =
-            u32x2{pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3])};
-      }
-      block_sync_lds();   // P of tile t complete
+      l_run += ps;
 
-      // ---- O^T (128 dims x 64 heads) += V^T . P^T ----
-      bf16x8 pb[4];
+      // ---- P to the partner (into the buffer just read), P of the partner's heads back ----
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
-        pb[n] = *reinterpret_cast<const bf16x8*>(s_p + p_rd + 16 * n * kPRowB);
+      for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(xr + 1024 * kk + 16 * lane) = pb[kk];
+      block_sync_lds();
+      bf16x8 pq[2];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int mo = (m >> 2) * 128;
-        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + va_off[m & 3] + mo));
-        const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb_off[m & 3] + mo));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int kk = 0; kk < 2; ++kk) pq[kk] = *reinterpret_cast<const bf16x8*>(xw + 1024 * kk + 16 * lane);
+
+      // ---- O^T += V^T . P^T over this wave's dims, both head blocks ----
+      auto vread = [&](int m, int kk) {
+        const uint8_t* vp = tile + vbase + 2048 * m + 1024 * kk;
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vp);
+        const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 128));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vop[2][2];
+      vop[0][0] = vread(0, 0);
+      vop[0][1] = vread(0, 1);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) o[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[n], o[m][n], 0, 0, 0);
+      for (int m = 0; m < kPairMt; ++m) {
+        if (m + 1 < kPairMt) {
+          vop[(m + 1) & 1][0] = vread(m + 1, 0);
+          vop[(m + 1) & 1][1] = vread(m + 1, 1);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          o[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m & 1][kk], pb[kk], o[m][0], 0, 0, 0);
+          o[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m & 1][kk], pq[kk], o[m][1], 0, 0, 0);
+        }
       }
+      mask = mask_next;
     }
     return far;
   };
 
-  // Combine per-wave partials over the two row halves: per QK head, the
-  // maximum (op = max) or the sum (op = add) of the lanes' values.
-  auto combine_heads = [&](float (&vals)[2], bool is_max) {
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      float x = vals[n];
-      const float y = __shfl_xor(x, 16, 64);
-      x = is_max ? fmaxf(x, y) : x + y;
-      const float z = __shfl_xor(x, 32, 64);
-      x = is_max ? fmaxf(x, z) : x + z;
-      if (g == 0) s_red[wave][16 * n + i] = x;
-    }
+  // Fast sweep; a query whose logits rose more than 2^kRefGap above its first
+  // valid tile's maximum is swept again with the exact maximum as the
+  // reference (one copy of the sweep code, run at most twice).
+#pragma nounroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool far = __ballot(sweep()) != 0;
+    block_sync_lds();   // both waves are done with the ring and s_x
+    if (lane == 0) s_red[d] = far ? 1 : 0;
     block_sync_lds();
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const float a = s_red[wave][16 * n + i], b = s_red[wave ^ 1][16 * n + i];
-      vals[n] = is_max ? fmaxf(a, b) : a + b;
-    }
-    block_sync_lds();
-  };
-
-  const bool far = sweep(true);
-  if (lane == 0) s_cnt[tid >> 6] = far ? 1u : 0u;
-  block_sync_lds();
-  const bool redo = (s_cnt[0] | s_cnt[1] | s_cnt[2] | s_cnt[3]) != 0u;
-  if (redo) {
-    combine_heads(m_max, true);
-    m_ref[0] = m_max[0];
-    m_ref[1] = m_max[1];
-    sweep(false);
+    const bool redo = (s_red[0] | s_red[1]) != 0;
+    block_sync_lds();   // flags read before they are rewritten
+    if (!redo) break;
+    m_ref = m_max;      // this lane's head, over every valid row
   }
-  combine_heads(l_part, false);   // l per QK head (32hh + 16n + i), all rows
 
-  // every wave needs l for all 64 heads: publish by head
-  if (rh == 0 && g == 0) {
-    s_red[2][32 * hh + i] = l_part[0];
-    s_red[2][32 * hh + 16 + i] = l_part[1];
-    s_red[3][32 * hh + i] = m_ref[0];
-    s_red[3][32 * hh + 16 + i] = m_ref[1];
-  }
+  // ---- normalise and write: o[m][hb] holds head 32(d^hb)+c32, dims 256d + 32m + 8jj + 4h + r ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (h == 0) s_l[32 * d + c32] = l_tot;
   block_sync_lds();
+  const float inv[2] = {1.f / l_tot, 1.f / s_l[32 * (d ^ 1) + c32]};
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const float inv = 1.f / s_red[2][16 * n + i];
+  for (int hb = 0; hb < 2; ++hb) {
+    const int64_t row_off = ((int64_t)qi * kHeads + 32 * (d ^ hb) + c32) * kDv + 256 * d + 4 * h;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const f32x4 r = o[m][n] * inv;
-      if constexpr (OUT_F32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + out_off(m, n)) = r;
-      } else {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + out_off(m, n)) =
-            u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+    for (int m = 0; m < kPairMt; ++m)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 r = f32x4{o[m][hb][4 * jj], o[m][hb][4 * jj + 1], o[m][hb][4 * jj + 2], o[m][hb][4 * jj + 3]} *
+                        inv[hb];
+        const int64_t off = row_off + 32 * m + 8 * jj;
+        if constexpr (OUT_F32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = r;
+        } else {
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + off) =
+              u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+        }
       }
-    }
   }
-  if (lse && tid < kHeads)
-    lse[(int64_t)qi * kHeads + tid] = (s_red[3][tid] + __log2f(s_red[2][tid])) * 0.69314718055994531f;
+  if (lse && h == 0) lse[(int64_t)qi * kHeads + 32 * d + c32] = (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
 hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
@@ -620,11 +623,12 @@ hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
                          (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
   } else {
     const uint16_t* kv = static_cast<const uint16_t*>(A.kv);
+    const dim3 block2(kPairThreads);
     if (A.out_f32)
-      hipLaunchKernelGGL((sparse_mla_bf16_kernel<true>), grid, block, 0, st, A.q, kv, (int)A.n_k, A.idx, A.n_q,
+      hipLaunchKernelGGL((sparse_mla_bf16_kernel<true>), grid, block2, 0, st, A.q, kv, (int)A.n_k, A.idx, A.n_q,
                          A.top_k, scale_log2, A.out, A.lse);
     else
-      hipLaunchKernelGGL((sparse_mla_bf16_kernel<false>), grid, block, 0, st, A.q, kv, (int)A.n_k, A.idx,
+      hipLaunchKernelGGL((sparse_mla_bf16_kernel<false>), grid, block2, 0, st, A.q, kv, (int)A.n_k, A.idx,
                          A.n_q, A.top_k, scale_log2, A.out, A.lse);
   }
   return hipGetLastError();
