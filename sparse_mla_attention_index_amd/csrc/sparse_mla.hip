@@ -325,12 +325,14 @@ __device__ __forceinline__ void block_sync_lds() {
 //
 // Tile layout (32 rows x 576 dims, 36 KiB): a 1-KiB block holds 16 rows x
 // 4 chunks of 16 bytes.  Chunk c of row r sits in block 2(c>>2) + (r>>4) at
-// slot 16(c&3) + ((r&15) ^ 4(c&1)).  A direct global->LDS load fills one
+// slot 16(c&3) + ((r&15) ^ 4(c&3)).  A direct global->LDS load fills one
 // block, so each load reads 64 contiguous bytes from each of 16 rows (whole
 // 64-byte lines), and lane l of every load fetches one of the two rows
-// ((l&15) ^ 4((l>>4)&1)) + {0, 16}: two indices per lane per tile.  The K
-// operand of a k-step and the transposed V reads of a 16-lane group both hit
-// 16 distinct bank groups, and every read offset is an immediate.  The rope
+// ((l&15) ^ 4(l>>4)) + {0, 16}: two indices per lane per tile.  A 16-byte
+// read serves 16 lanes per cycle and a transposed 8-byte read 32 lanes; the
+// swizzle puts each such group of the K operand reads and of the V^T reads
+// on distinct banks, and the reads need two base registers each plus
+// immediate offsets.  The rope
 // blocks (chunks 64..71, bytes 32768..36863) are dead after QK and carry the
 // S/P exchange of one direction; a 4-KiB buffer carries the other.
 //
@@ -408,7 +410,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
 
   // ---- gather: block B (wave d issues B = 18d..18d+17) lane l fetches row
   // 16(B&1) + rsel, chunk 4(B>>1) + (l>>4) ----
-  const int rsel = (lane & 15) ^ (4 * ((lane >> 4) & 1));
+  const int rsel = (lane & 15) ^ (4 * (lane >> 4));
   // The entries are staged through LDS in chunks of 8 tiles (one chunk
   // ahead), so the per-tile index reads are LDS reads and the only
   // vector-memory operations in flight are the gathers and chunk loads.
@@ -442,13 +444,21 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
   wait_vmcnt<0>();
 
   // K operand of k-step ks (global 18d+ks): row c32, chunk 36d + 2ks + h.
-  const int kbase = (kPairLoads * 1024) * d + (c32 >> 4) * 1024 + 256 * h + 16 * ((c32 & 15) ^ (4 * h));
-  auto koff = [](int ks) { return (ks >> 1) * 2048 + (ks & 1) * 512; };
+  // c&3 = 2(ks&1) + h, so even and odd k-steps use two bases.
+  int kb[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    kb[e] = (kPairLoads * 1024) * d + (c32 >> 4) * 1024 + 256 * (2 * e + h) + 16 * ((c32 & 15) ^ (4 * (2 * e + h)));
   // V^T operand of M-tile m (dims 256d+32m..), k-step kk, half e: 16-lane group b = lane>>4
   // reads rows 16kk + 8e + 4h + (L>>2) at dims 32m + 16(b&1) + 4(L&3), L = lane&15.
   const int L = lane & 15, pL = (L >> 1) & 1;
-  const int vbase = (kPairMt * 2048) * d + 512 * ((lane >> 4) & 1) + 256 * pL + 64 * (h ^ pL) + 16 * (L >> 2) +
-                    8 * (L & 1);
+  // c&3 = 2(b&1) + pL and r&15 = 8e + 4h + (L>>2), so the two row halves e use two bases.
+  int vb[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int b1 = (lane >> 4) & 1;
+    vb[e] = (kPairMt * 2048) * d + 512 * b1 + 256 * pL + 16 * (8 * (e ^ b1) + 4 * (h ^ pL) + (L >> 2)) + 8 * (L & 1);
+  }
 
   f32x16v o[kPairMt][2];
   float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.f;
@@ -477,7 +487,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
 
       // ---- partial S^T over this wave's dims, both head blocks ----
       constexpr int kPf = 3;
-      auto kread = [&](int ks) { return *reinterpret_cast<const bf16x8*>(tile + kbase + koff(ks)); };
+      auto kread = [&](int ks) { return *reinterpret_cast<const bf16x8*>(tile + kb[ks & 1] + (ks >> 1) * 2048); };
       f32x16v s_own, s_oth;
       bf16x8 kop[kPf];
 #pragma unroll
@@ -544,10 +554,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
 
       // ---- O^T += V^T . P^T over this wave's dims, both head blocks ----
       auto vread = [&](int m, int kk) {
-        const uint8_t* vp = tile + vbase + 2048 * m + 1024 * kk;
-        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vp);
-        const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 128));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+        const int off = 2048 * m + 1024 * kk;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb[0] + off));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb[1] + off));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       bf16x8 vop[2][2];
       vop[0][0] = vread(0, 0);
