@@ -211,8 +211,187 @@ static hipError_t launch_idx(const IdxArgs& A, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// bf16 keys, 64 heads x d_I = 128 (the prefill shape): eight waves, one query
+// each, share a ring of key tiles filled by direct global->LDS loads, so a
+// key tile read from L2 serves eight queries and up to kIdxStages - 1 tiles
+// are in flight while one is consumed.  Two waves per SIMD let one wave's
+// ReLU / head-weight epilogue overlap the other's MFMAs.
+//
+// Tile: 64 keys x 256 bytes, dense; 16-byte chunk c of key r sits at slot
+// c ^ (r & 15) of the key's row, so the 16 lanes of a B-operand read (16
+// keys, one chunk) hit 16 distinct bank groups.  A 1-KiB load covers four
+// keys; lane l fetches key 4b + (l >> 4), slot l & 15.
+// ---------------------------------------------------------------------------
+constexpr int kIdxWaves = 8;
+constexpr int kIdxKT = 64;                                  // keys per tile
+constexpr int kIdxStages = 8;                               // ring depth
+constexpr int kIdxTileB = kIdxKT * 256;                     // 16 KiB
+constexpr int kIdxLoadsPerWave = kIdxTileB / 1024 / kIdxWaves;   // 2
+
+typedef __attribute__((address_space(3))) uint8_t idx_lds_u8;
+
+__device__ __forceinline__ void idx_dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void idx_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void idx_sync_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt not waited
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int64_t w_stride,
+    const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos, int n_q, int n_k,
+    float* __restrict__ scores, int64_t ld, int n_qblocks, int n_chunks, int chunk_keys) {
+  constexpr int H = 64, DI = 128, KS = DI / 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_k[kIdxStages][kIdxTileB];
+  __shared__ int s_pos[kIdxWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Later query blocks carry longer causal prefixes: hand them out first.
+  const int qb = n_qblocks - 1 - (int)(blockIdx.x / n_chunks);
+  const int chunk = (int)(blockIdx.x % n_chunks);
+  const int q0 = qb * kIdxWaves;
+
+  if (tid < kIdxWaves) {
+    const int qi = q0 + tid;
+    const int p = qi < n_q ? q_pos[qi] : -1;
+    s_pos[tid] = p < -1 ? -1 : (p > n_k - 1 ? n_k - 1 : p);
+  }
+  __syncthreads();
+  int pmax = -1;
+#pragma unroll
+  for (int t = 0; t < kIdxWaves; ++t) pmax = max(pmax, s_pos[t]);
+  const int k_begin = chunk * chunk_keys;
+  const int k_end = min(k_begin + chunk_keys, pmax + 1);
+  if (k_begin >= k_end) return;   // uniform across the workgroup
+  const int ntiles = (k_end - k_begin + kIdxKT - 1) / kIdxKT;
+  const int mypos = s_pos[wave];
+  const int qi = min(q0 + wave, n_q - 1);
+
+  // ---- A operands: the wave's query, head rows 32t + lrow, dims 16j + 8khalf .. +7 ----
+  const int lrow = lane & 31, khalf = lane >> 5;
+  bf16x8 a[2][KS];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint16_t* src = q_idx + ((int64_t)qi * H + 32 * t + lrow) * DI + khalf * 8;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) a[t][j] = *reinterpret_cast<const bf16x8*>(src + j * 16);
+  }
+  // head weights of this lane's accumulator rows 32t + 8(jj>>2) + 4khalf + (jj&3)
+  float wv[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) wv[t][jj] = w[(int64_t)qi * w_stride + 32 * t + 8 * (jj >> 2) + 4 * khalf + (jj & 3)];
+
+  // ---- gather of tile i (keys k_begin + 64i ..) into slot i % kIdxStages ----
+  const int dkey = kIdxLoadsPerWave * 4 * wave + (lane >> 4);   // key of load 0 within the tile
+  auto issue = [&](int i) {
+    const uint32_t dst = (uint32_t)(uintptr_t)(idx_lds_u8*)&s_k[i % kIdxStages][1024 * kIdxLoadsPerWave * wave];
+#pragma unroll
+    for (int j = 0; j < kIdxLoadsPerWave; ++j) {
+      const int key = min(k_begin + kIdxKT * i + dkey + 4 * j, n_k - 1);
+      const int c = (lane & 15) ^ ((dkey + 4 * j) & 15);
+      idx_dma16(k_idx + (int64_t)key * DI + 8 * c, dst + 1024 * j);
+    }
+  };
+  // Retire the operand loads so that only gathers are outstanding below.
+  idx_wait_vmcnt<0>();
+#pragma unroll
+  for (int i = 0; i < kIdxStages - 1; ++i) issue(i);
+
+  // B operand of N-tile u, k-step j: key 32u + lrow, chunk 2j + khalf at slot (2j + khalf) ^ (lrow & 15).
+  int boff[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) boff[j] = lrow * 256 + 16 * ((2 * j + khalf) ^ (lrow & 15));
+
+  // Software pipeline over 32-key N-tiles: the MFMAs of N-tile n run while
+  // the ReLU / head-weight epilogue of N-tile n-1 is issued, so the VALU work
+  // hides under the matrix core instead of following it.
+  f32x16 acc[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};   // [buffer][M tile]
+  int prev_key = -1;  // first key of the N-tile whose sums wait in the other buffer
+  auto epilogue = [&](const f32x16& c0, const f32x16& c1, int key0) {
+    float part = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      // ReLU as an integer max on the float's bits (negative values and -0
+      // have the sign bit set): one instruction, no NaN canonicalisation
+      part = fmaf(wv[0][jj], __int_as_float(max(__float_as_int(c0[jj]), 0)), part);
+      part = fmaf(wv[1][jj], __int_as_float(max(__float_as_int(c1[jj]), 0)), part);
+    }
+    part += __shfl_xor(part, 32, 64);
+    const int key = key0 + lrow;
+    if (khalf == 0 && key0 >= 0 && q0 + wave < n_q && key <= mypos && key < k_end)
+      scores[(int64_t)(q0 + wave) * ld + key] = part;
+  };
+  for (int i = 0; i < ntiles; ++i) {
+    // tile i has landed once at most the kIdxStages - 2 younger tiles are outstanding
+    idx_wait_vmcnt<(kIdxStages - 2) * kIdxLoadsPerWave>();
+    idx_sync_lds();             // for every wave; slot (i - 1) % kIdxStages is free
+    issue(i + kIdxStages - 1);  // past the range these load clamped keys into a free slot
+    const uint8_t* tile = s_k[i % kIdxStages];
+    const int k0 = k_begin + kIdxKT * i;
+#pragma unroll
+    for (int u = 0; u < kIdxKT / 32; ++u) {
+      const f32x16 p0 = acc[(u + 1) & 1][0], p1 = acc[(u + 1) & 1][1];
+      f32x16 c0 = f32x16{}, c1 = f32x16{};
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(tile + 8192 * u + boff[j]);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][j], b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][j], b, c1, 0, 0, 0);
+      }
+      epilogue(p0, p1, prev_key);   // the store is skipped before the first N-tile
+      acc[u & 1][0] = c0;
+      acc[u & 1][1] = c1;
+      prev_key = k0 + 32 * u;
+      // interleave: per pair of k-steps one B read, and four epilogue VALU
+      // instructions behind each MFMA
+#pragma unroll
+      for (int g = 0; g < KS; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0002, 4, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0002, 4, 0);   // VALU
+      }
+    }
+  }
+  epilogue(acc[(kIdxKT / 32 - 1) & 1][0], acc[(kIdxKT / 32 - 1) & 1][1], prev_key);
+  idx_wait_vmcnt<0>();   // no load may land in LDS after the workgroup has left
+}
+
+static hipError_t launch_idx_h64(const IdxArgs& A, hipStream_t st) {
+  const int n_qblocks = (A.n_q + kIdxWaves - 1) / kIdxWaves;
+  int n_chunks = 1;
+  const int target_wgs = 1024;
+  if (n_qblocks < target_wgs) n_chunks = (target_wgs + n_qblocks - 1) / n_qblocks;
+  int chunk_keys = (int)((A.n_k + n_chunks - 1) / n_chunks);
+  chunk_keys = ((chunk_keys + kIdxKT - 1) / kIdxKT) * kIdxKT;
+  if (chunk_keys < 4 * kIdxKT) chunk_keys = 4 * kIdxKT;
+  n_chunks = (int)((A.n_k + chunk_keys - 1) / chunk_keys);
+  const long long grid = (long long)n_qblocks * n_chunks;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(idx_score_h64_kernel, dim3((unsigned)grid), dim3(64 * kIdxWaves), 0, st, A.q_idx, A.w,
+                     A.w_stride, static_cast<const uint16_t*>(A.k_idx), A.q_pos, A.n_q, (int)A.n_k, A.scores, A.ld,
+                     n_qblocks, n_chunks, chunk_keys);
+  return hipGetLastError();
+}
+
 hipError_t launch_index_scores(const IdxArgs& A, hipStream_t st) {
   const bool f8 = A.fp8;
+  if (!f8 && A.h_idx == 64 && A.d_idx == 128) return launch_idx_h64(A, st);
 #define SMA_IDX_CASE(HH, DD)                                                          \
   if (A.h_idx == HH && A.d_idx == DD)                                                 \
     return f8 ? launch_idx<HH, DD, true>(A, st) : launch_idx<HH, DD, false>(A, st);
