@@ -6,20 +6,24 @@
 // ou DP ?", with the tie-break reading).
 //
 // One 1024-thread workgroup per row, no atomics outside LDS, deterministic:
-//  1. scores become order-preserving uint32 keys (-0.0 folded onto +0.0);
-//  2. the key range [lo, hi] of the row is found (min/max reduce);
-//  3. radix refinement: the range is cut into <= 2048 equal-width bins,
-//     an LDS histogram locates the bin holding the K-th largest key, and the
+//  1. scores become order-preserving uint32 keys (-0.0 folded onto +0.0) and
+//     the key range [lo, hi] of the row is found while they are loaded;
+//  2. radix refinement: the range is cut into <= 2048 equal-width bins, an
+//     LDS histogram locates the bin holding the K-th largest key, and the
 //     range shrinks to that bin, until it is a single key T (at most three
 //     11-bit rounds for 32-bit keys).  Because the bins span the row's
 //     actual range rather than fixed bit fields, the first histogram is
-//     spread over the scores' distribution and LDS atomics rarely collide;
-//  4. an ordered compaction writes every position with key > T plus the
+//     spread over the scores' distribution and LDS atomics rarely collide.
+//     After the first round the keys of the selected bin (normally a few
+//     dozen) are copied to an LDS list and the later rounds run on that list
+//     alone; a bin too full for the list is refined over the whole row;
+//  3. an ordered compaction writes every position with key > T plus the
 //     first (K - #greater) positions with key == T, each to the slot given by
 //     a block-wide prefix count, so the output is ascending by position.
 // Rows up to 1024*V scores are read once into registers (blocked: thread t
-// owns positions [t*V, t*V+V)); longer rows are streamed from memory in
-// every pass.
+// owns positions [t*V, t*V+V), so a wave whose positions all lie past the
+// row end skips every pass); longer rows are streamed from memory in every
+// full pass.
 #include "sma_device.h"
 #include "sma_launch.h"
 
@@ -92,6 +96,7 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
   // Keys of positions THREADS*V + tid*VL + j live in LDS at word j*THREADS + tid
   // (consecutive threads hit consecutive banks).
   __shared__ uint32_t lds_keys[VL > 0 ? VL * THREADS : 1];
+  __shared__ uint32_t cand[kBins];   // keys of the selected bin after round 1
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;
   int p = q_pos[row];
@@ -106,55 +111,76 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
   }
 
   // Positions past the row end carry key 0, below every real key (score_key
-  // never returns 0), so no pass needs a per-position bound check.
+  // never returns 0), so no pass needs a per-position bound check.  A wave
+  // whose positions of a segment all lie past the row end skips it.
+  constexpr int kSeg2 = THREADS * V;   // first position held in LDS
+  const bool act1 = V > 0 && wave * 64 * V < n;
+  const bool act2 = VL > 0 && kSeg2 + wave * 64 * VL < n;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  auto note = [&](uint32_t k) {
+    kmin = min(kmin, k ? k : 0xFFFFFFFFu);
+    kmax = max(kmax, k);
+  };
   RowSource<V> rs;
   if constexpr (V > 0) {
-    const int base = tid * V;
+    if (act1) {
+      const int base = tid * V;
 #pragma unroll
-    for (int v = 0; v < V; v += 4) {
-      const int p0 = base + v;
-      f32x4 x;
-      if (p0 + 3 < n) {
-        x = *reinterpret_cast<const f32x4*>(src + p0);
-      } else {
+      for (int v = 0; v < V; v += 4) {
+        const int p0 = base + v;
+        f32x4 x;
+        if (p0 + 3 < n) {
+          x = *reinterpret_cast<const f32x4*>(src + p0);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = p0 + e < n ? src[p0 + e] : 0.f;
+          for (int e = 0; e < 4; ++e) x[e] = p0 + e < n ? src[p0 + e] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          rs.key[v + e] = p0 + e < n ? score_key(x[e]) : 0u;
+          note(rs.key[v + e]);
+        }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rs.key[v + e] = p0 + e < n ? score_key(x[e]) : 0u;
     }
   }
-
-  constexpr int kSeg2 = THREADS * V;   // first position held in LDS
   if constexpr (VL > 0) {
-    const int base = kSeg2 + tid * VL;
+    if (act2) {
+      const int base = kSeg2 + tid * VL;
 #pragma unroll
-    for (int v = 0; v < VL; v += 4) {
-      const int p0 = base + v;
-      f32x4 x;
-      if (p0 + 3 < n) {
-        x = *reinterpret_cast<const f32x4*>(src + p0);
-      } else {
+      for (int v = 0; v < VL; v += 4) {
+        const int p0 = base + v;
+        f32x4 x;
+        if (p0 + 3 < n) {
+          x = *reinterpret_cast<const f32x4*>(src + p0);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = p0 + e < n ? src[p0 + e] : 0.f;
+          for (int e = 0; e < 4; ++e) x[e] = p0 + e < n ? src[p0 + e] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t k = p0 + e < n ? score_key(x[e]) : 0u;
+          lds_keys[(v + e) * THREADS + tid] = k;
+          note(k);
+        }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) lds_keys[(v + e) * THREADS + tid] = p0 + e < n ? score_key(x[e]) : 0u;
     }
-    __syncthreads();
   }
 
   // Visit every (position, key) of this thread; within each segment
   // (registers, then LDS) in ascending position.  Keys of positions >= n are 0.
   auto for_seg1 = [&](auto&& fn) {
-    const int base = tid * V;
+    if (act1) {
+      const int base = tid * V;
 #pragma unroll
-    for (int v = 0; v < V; ++v) fn(base + v, rs.key[v]);
+      for (int v = 0; v < V; ++v) fn(base + v, rs.key[v]);
+    }
   };
   auto for_seg2 = [&](auto&& fn) {
-    const int base = kSeg2 + tid * VL;
+    if (act2) {
+      const int base = kSeg2 + tid * VL;
 #pragma unroll 4
-    for (int v = 0; v < VL; ++v) fn(base + v, lds_keys[v * THREADS + tid]);
+      for (int v = 0; v < VL; ++v) fn(base + v, lds_keys[v * THREADS + tid]);
+    }
   };
   auto for_each = [&](auto&& fn) {
     if constexpr (V > 0) {
@@ -169,12 +195,8 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
     }
   };
 
-  // ---- 2. key range ----
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for_each([&](int, uint32_t k) {
-    kmin = min(kmin, k ? k : 0xFFFFFFFFu);
-    kmax = max(kmax, k);
-  });
+  // ---- 1. key range ----
+  if constexpr (V == 0) for_each([&](int, uint32_t k) { note(k); });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
@@ -184,7 +206,7 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
     sh.red[wave] = kmin;
     sh.red[kTopkWaves + wave] = kmax;
   }
-  __syncthreads();
+  __syncthreads();   // also publishes the LDS-resident keys
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
   for (int w = 0; w < kTopkWaves; ++w) {
@@ -193,11 +215,10 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
   }
   __syncthreads();
 
-  // ---- 3. radix refinement of [lo, hi] down to the threshold key ----
+  // ---- 2. radix refinement of [lo, hi] down to the threshold key ----
   uint32_t remaining = (uint32_t)K;   // still to take from keys inside [lo, hi]
-  // Each round shrinks the range by 11 bits: three rounds reach a single key;
-  // the bound keeps the loop finite whatever the data.
-  for (int round = 0; round < 4 && hi != lo; ++round) {
+  uint32_t in_range = 0;              // keys inside [lo, hi] after the last round
+  auto refine = [&](auto&& visit) {
     const uint32_t width = hi - lo;
     const int bits = 32 - __clz(width);
     const int shift = bits > 11 ? bits - 11 : 0;
@@ -206,9 +227,10 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
     if (tid == 0) {
       sh.bcast[0] = 0u;
       sh.bcast[1] = 0u;
+      sh.bcast[2] = 0u;
     }
     __syncthreads();
-    for_each([&](int, uint32_t k) {
+    visit([&](int, uint32_t k) {
       if (k >= lo && k <= hi) atomicAdd(&sh.hist[(k - lo) >> shift], 1u);
     });
     __syncthreads();
@@ -231,22 +253,44 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
       if (b < nbins && above < remaining && remaining <= above + hb[e]) {
         sh.bcast[0] = (uint32_t)b;
         sh.bcast[1] = above;
+        sh.bcast[2] = hb[e];
       }
       above += hb[e];
     }
     __syncthreads();
     const uint32_t bsel = sh.bcast[0], above_sel = sh.bcast[1];
+    in_range = sh.bcast[2];
     __syncthreads();
     remaining -= above_sel;
     const uint64_t nlo = (uint64_t)lo + ((uint64_t)bsel << shift);
     const uint64_t nhi = nlo + ((uint64_t)1 << shift) - 1;
     lo = (uint32_t)nlo;
     hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+  };
+  // Each round shrinks the range by 11 bits: three rounds reach a single key;
+  // the bound keeps the loops finite whatever the data.
+  if (hi != lo) refine(for_each);
+  if (hi != lo) {
+    if (in_range <= (uint32_t)kBins) {
+      if (tid == 0) sh.bcast[3] = 0u;
+      __syncthreads();
+      for_each([&](int, uint32_t k) {
+        if (k >= lo && k <= hi) cand[atomicAdd(&sh.bcast[3], 1u)] = k;
+      });
+      __syncthreads();
+      const int n_cand = (int)in_range;
+      auto for_cand = [&](auto&& fn) {
+        for (int c = tid; c < n_cand; c += kTopkThreads) fn(c, cand[c]);
+      };
+      for (int round = 1; round < 4 && hi != lo; ++round) refine(for_cand);
+    } else {
+      for (int round = 1; round < 4 && hi != lo; ++round) refine(for_each);
+    }
   }
   const uint32_t T = lo;
   const uint32_t need_ties = remaining;   // >= 1 keys equal to T are taken
 
-  // ---- 4. ordered compaction ----
+  // ---- 3. ordered compaction ----
   if constexpr (V > 0) {
     uint32_t g_run = 0, e_run = 0;   // totals of earlier segments
     auto compact = [&](auto&& seg) {
