@@ -24,6 +24,8 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
 
 def _log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -40,7 +42,33 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="query rows in the CPU-oracle sample (0: a per-workload default of ~10-30 s)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the steps (a known-size "
+                         "reference for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = {"index_scores": ("idx_score", "idx_score.hip"), "topk_select": ("topk_kernel", "topk.hip"),
+                  "sparse_mla": ("sparse_mla", "sparse_mla.hip")}
+
+
+def measured_traffic(workload_name, kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
+    summary of this workload, or None when there is none or the kernel's source
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    substr, src = KERNEL_SOURCES[kernel]
+    if rec.get("kernel") != substr:
+        return None
+    with open(os.path.join(ROOT, "sparse_mla_attention_index_amd", "csrc", src), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec.get("source_sha256"):
+            return None
+    return round(float(rec["traffic_bytes_per_launch"]), 1)
 
 
 def main():
@@ -140,6 +168,16 @@ def main():
             sma.prefill(q_idx, wts, k_idx, q, kv, q_pos, w.top_k, w.sm_scale, k_scale=k_scale,
                         kv_scale=kv_scale, out=out, idx_out=idx, workspace=ws)
 
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        cal_src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        cal_dst = torch.empty_like(cal_src)
+        torch.cuda.synchronize()
+        cal_dst.copy_(cal_src)
+        torch.cuda.synchronize()
+        del cal_src, cal_dst
+        _log(f"calibration copy of {nbytes} bytes done")
+
     # ------------------------------------------------------ timed steps --
     for _ in range(args.warmup):
         step()
@@ -204,7 +242,7 @@ def main():
     dom = max(kern, key=lambda k: kern[k]["ms"])
     roof = {"kernel": dom, "bound": kern[dom]["bound"], "achieved": round(kern[dom]["achieved"], 3),
             "peak": kern[dom]["peak"], "unit": kern[dom]["unit"], "frac": round(kern[dom]["frac"], 4),
-            "traffic": None}
+            "traffic": measured_traffic(w.name, dom)}
 
     # ---------------------------------------- CPU oracle on a sample --
     cpu = None

@@ -1,0 +1,135 @@
+"""Summaries of rocprofv3 output for the files under profiles/.
+
+Two commands (run from the repository root on the CSV output of rocprofv3):
+
+  python -m sparse_mla_attention_index_amd.rocprof_summary stats \\
+      --stats gpurun_out/prof_k/run_kernel_stats.csv --out profiles/<name>.md --command "<cmd>"
+
+writes a kernel-time table (calls, average / min / max ms, share of the total);
+
+  python -m sparse_mla_attention_index_amd.rocprof_summary traffic \\
+      --fetch <FETCH_SIZE run>/run_counter_collection.csv \\
+      --write <WRITE_SIZE run>/run_counter_collection.csv \\
+      --kernel idx_score --source sparse_mla_attention_index_amd/csrc/idx_score.hip \\
+      --copy-bytes N --workload prefill-L65536-k2048 --out profiles/traffic_<workload>.json
+
+averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the named kernel,
+scales each by bytes / counter of the plain copy kernel of N bytes that the
+same run executed (torch's device copy), and records the result with the
+SHA-256 of the kernel's source file, so that a reader can tell whether the
+kernel changed since the counters were taken.
+"""
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+
+def _per_dispatch(path, counter):
+    """{dispatch_id: (kernel_name, value)} for one counter of a counter-collection CSV."""
+    out = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = r["Dispatch_Id"]
+            name, val = out.get(d, (r["Kernel_Name"], 0.0))
+            out[d] = (name, val + float(r["Counter_Value"]))
+    return out
+
+
+def _kernel_avg(disp, substr):
+    vals = [v for (name, v) in disp.values() if substr in name]
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel matching {substr!r}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def _copy_counter(disp):
+    """Counter value of the largest dispatch of a copy kernel."""
+    vals = [v for (name, v) in disp.values() if "copy" in name.lower()]
+    if not vals:
+        raise SystemExit("no copy kernel in the counter file")
+    return max(vals)
+
+
+def cmd_traffic(a):
+    fetch = _per_dispatch(a.fetch, "FETCH_SIZE")
+    write = _per_dispatch(a.write, "WRITE_SIZE")
+    f_kib, nf = _kernel_avg(fetch, a.kernel)
+    w_kib, nw = _kernel_avg(write, a.kernel)
+    f_copy, w_copy = _copy_counter(fetch), _copy_counter(write)
+    f_factor = a.copy_bytes / (f_copy * 1024.0)
+    w_factor = a.copy_bytes / (w_copy * 1024.0)
+    with open(a.source, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    rec = {
+        "workload": a.workload,
+        "kernel": a.kernel,
+        "source": a.source,
+        "source_sha256": sha,
+        "dispatches": {"fetch_run": nf, "write_run": nw},
+        "fetch_kib_per_dispatch": f_kib,
+        "write_kib_per_dispatch": w_kib,
+        "copy_bytes": a.copy_bytes,
+        "copy_fetch_kib": f_copy,
+        "copy_write_kib": w_copy,
+        "fetch_factor": f_factor,
+        "write_factor": w_factor,
+        "traffic_bytes_per_launch": f_kib * 1024.0 * f_factor + w_kib * 1024.0 * w_factor,
+        "commands": a.command,
+    }
+    with open(a.out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def cmd_stats(a):
+    rows = []
+    with open(a.stats, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append(r)
+    tot = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+    lines = [f"# {a.title}", "", "Command (from the repository root, on the GPU host):", "", "```"]
+    lines += [c for c in a.command] + ["```", ""]
+    lines += ["| kernel | calls | average ms | min ms | max ms | share |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].split("(")[0]
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+                     f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | "
+                     f"{100 * float(r['TotalDurationNs']) / tot:.1f}% |")
+    if a.note:
+        lines += ["", a.note]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--source", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--command", action="append", default=[])
+    s = sub.add_parser("stats")
+    s.add_argument("--stats", required=True)
+    s.add_argument("--out", required=True)
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", action="append", default=[])
+    s.add_argument("--note", default="")
+    a = ap.parse_args(argv)
+    (cmd_traffic if a.cmd == "traffic" else cmd_stats)(a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
