@@ -17,9 +17,11 @@
 //     After the first round the keys of the selected bin (normally a few
 //     dozen) are copied to an LDS list and the later rounds run on that list
 //     alone; a bin too full for the list is refined over the whole row;
+//     When the bin holds at most 64 keys one wave ranks them directly;
 //  3. an ordered compaction writes every position with key > T plus the
 //     first (K - #greater) positions with key == T, each to the slot given by
-//     a block-wide prefix count, so the output is ascending by position.
+//     a block-wide prefix count, so the output is ascending by position (for
+//     rows held on chip each thread marks its positions in bit masks first).
 // Rows up to 1024*V scores are read once into registers (blocked: thread t
 // owns positions [t*V, t*V+V), so a wave whose positions all lie past the
 // row end skips every pass); longer rows are streamed from memory in every
@@ -279,10 +281,32 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
       });
       __syncthreads();
       const int n_cand = (int)in_range;
-      auto for_cand = [&](auto&& fn) {
-        for (int c = tid; c < n_cand; c += kTopkThreads) fn(c, cand[c]);
-      };
-      for (int round = 1; round < 4 && hi != lo; ++round) refine(for_cand);
+      if (n_cand <= 64) {
+        // One wave ranks the candidates against each other: T is the key
+        // with fewer than `remaining` candidates above it and at least
+        // `remaining` at or above it.
+        if (wave == 0) {
+          const uint32_t x = lane < n_cand ? cand[lane] : 0u;
+          uint32_t gt = 0, ge = 0;
+          for (int j = 0; j < n_cand; ++j) {
+            const uint32_t y = (uint32_t)__shfl((int)x, j, 64);
+            gt += y > x;
+            ge += y >= x;
+          }
+          if (lane < n_cand && gt < remaining && remaining <= ge) {   // every such lane holds T
+            sh.bcast[0] = x;
+            sh.bcast[1] = remaining - gt;
+          }
+        }
+        __syncthreads();
+        lo = hi = sh.bcast[0];
+        remaining = sh.bcast[1];
+      } else {
+        auto for_cand = [&](auto&& fn) {
+          for (int c = tid; c < n_cand; c += kTopkThreads) fn(c, cand[c]);
+        };
+        for (int round = 1; round < 4 && hi != lo; ++round) refine(for_cand);
+      }
     } else {
       for (int round = 1; round < 4 && hi != lo; ++round) refine(for_each);
     }
@@ -292,32 +316,45 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
 
   // ---- 3. ordered compaction ----
   if constexpr (V > 0) {
-    uint32_t g_run = 0, e_run = 0;   // totals of earlier segments
-    auto compact = [&](auto&& seg) {
-      uint32_t cg = 0, ce = 0;
-      seg([&](int, uint32_t k) {
-        cg += k > T;
-        ce += k == T;
+    // Per segment, a thread's positions are consecutive: one bit per
+    // position marks key > T, another key == T.  The block-wide prefix of the
+    // counts (packed: greater in the low 12 bits, at most K - 1 in total;
+    // equal above them) gives each thread its first output slot.
+    uint32_t mg1 = 0, me1 = 0, mg2 = 0, me2 = 0;
+    for_seg1([&](int pos, uint32_t k) {
+      const int b = pos - tid * V;
+      mg1 |= (uint32_t)(k > T) << b;
+      me1 |= (uint32_t)(k == T) << b;
+    });
+    if constexpr (VL > 0) {
+      for_seg2([&](int pos, uint32_t k) {
+        const int b = pos - (kSeg2 + tid * VL);
+        mg2 |= (uint32_t)(k > T) << b;
+        me2 |= (uint32_t)(k == T) << b;
       });
-      uint32_t g_before, e_before, tg, te;
-      block_excl_scan2<THREADS>(cg, ce, g_before, e_before, tg, te, sh);
-      g_before += g_run;
-      e_before += e_run;
-      seg([&](int pos, uint32_t k) {
-        if (k > T) {
+    }
+    const uint32_t c1 = __popc(mg1) | ((uint32_t)__popc(me1) << 12);
+    const uint32_t c2 = __popc(mg2) | ((uint32_t)__popc(me2) << 12);
+    uint32_t b1, b2, t1, t2;
+    block_excl_scan2<THREADS>(c1, c2, b1, b2, t1, t2, sh);
+    auto emit = [&](uint32_t mg, uint32_t me, int base, uint32_t g_before, uint32_t e_before) {
+      uint32_t m = mg | me;
+      while (m) {
+        const int b = __builtin_ctz(m);
+        m &= m - 1;
+        if ((mg >> b) & 1u) {
           const uint32_t slot = g_before + min(e_before, need_ties);
-          if (slot < (uint32_t)K) out[slot] = pos;
+          if (slot < (uint32_t)K) out[slot] = base + b;
           ++g_before;
-        } else if (k == T) {
-          if (e_before < need_ties && g_before + e_before < (uint32_t)K) out[g_before + e_before] = pos;
+        } else {
+          if (e_before < need_ties && g_before + e_before < (uint32_t)K) out[g_before + e_before] = base + b;
           ++e_before;
         }
-      });
-      g_run += tg;
-      e_run += te;
+      }
     };
-    compact(for_seg1);
-    if constexpr (VL > 0) compact(for_seg2);
+    emit(mg1, me1, tid * V, b1 & 0xFFFu, b1 >> 12);
+    if constexpr (VL > 0)
+      emit(mg2, me2, kSeg2 + tid * VL, (t1 & 0xFFFu) + (b2 & 0xFFFu), (t1 >> 12) + (b2 >> 12));
   } else {
     uint32_t g_run = 0, e_run = 0;   // totals of earlier chunks
     for (int c0 = 0; c0 < n; c0 += kTopkThreads * kStreamV) {
