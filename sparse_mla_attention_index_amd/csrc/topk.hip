@@ -389,6 +389,248 @@ __global__ __launch_bounds__(THREADS, 1) void topk_kernel(const float* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// Rows of at most 4*THREADS*(S1+S2) positions, held on chip: thread t owns
+// positions 4*THREADS*s + 4t + e (e < 4), steps s < S1 in registers and the
+// next S2 steps in LDS, so every load reads 1 KiB per wave contiguously.
+// The ordered output comes from two LDS bit maps over the row's positions
+// (key > T, key == T) that the threads fill with atomic ORs; each thread then
+// owns 64 consecutive positions of the maps.
+// ---------------------------------------------------------------------------
+template <int THREADS, int S1, int S2>
+__global__ __launch_bounds__(THREADS, 1) void topk_chip_kernel(const float* __restrict__ scores, int64_t ld,
+                                                               const int32_t* __restrict__ q_pos, int n_k,
+                                                               int K, int32_t* __restrict__ idx) {
+  constexpr int kWaves = THREADS / 64, kStep = 4 * THREADS;
+  static_assert(kBins % THREADS == 0, "whole histogram bins per thread");
+  static_assert(kStep * (S1 + S2) <= 32 * kBins, "bit maps cover the row");
+  __shared__ TopkShared<THREADS> sh;
+  __shared__ u32x4 lds_keys[S2 > 0 ? S2 * THREADS : 1];
+  __shared__ uint32_t cand[kBins];   // keys of the selected bin; later the key > T bit map
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  int p = q_pos[row];
+  p = p < -1 ? -1 : (p > n_k - 1 ? n_k - 1 : p);
+  const int n = p + 1;
+  int32_t* out = idx + (int64_t)row * K;
+  const float* src = scores + (int64_t)row * ld;
+
+  if (n <= K) {
+    for (int e = tid; e < K; e += THREADS) out[e] = e < n ? e : -1;
+    return;
+  }
+
+  // Positions past the row end carry key 0, below every real key (score_key
+  // never returns 0).  A wave whose first position of a step lies past the
+  // row end skips that step in every pass.
+  auto active = [&](int s) { return kStep * s + 256 * wave < n; };
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  auto load4 = [&](int s) -> u32x4 {
+    const int p0 = kStep * s + 4 * tid;
+    f32x4 x;
+    if (p0 + 3 < n) {
+      x = *reinterpret_cast<const f32x4*>(src + p0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = p0 + e < n ? src[p0 + e] : 0.f;
+    }
+    u32x4 k;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      k[e] = p0 + e < n ? score_key(x[e]) : 0u;
+      kmin = min(kmin, k[e] ? k[e] : 0xFFFFFFFFu);
+      kmax = max(kmax, k[e]);
+    }
+    return k;
+  };
+  u32x4 rk[S1];
+#pragma unroll
+  for (int s = 0; s < S1; ++s)
+    if (active(s)) rk[s] = load4(s);
+#pragma unroll
+  for (int s = 0; s < S2; ++s)
+    if (active(S1 + s)) lds_keys[s * THREADS + tid] = load4(S1 + s);
+
+  // Visit every (position, key) of this thread in ascending position.
+  auto for_each = [&](auto&& fn) {
+#pragma unroll
+    for (int s = 0; s < S1; ++s)
+      if (active(s)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fn(kStep * s + 4 * tid + e, rk[s][e]);
+      }
+#pragma unroll 2
+    for (int s = 0; s < S2; ++s)
+      if (active(S1 + s)) {
+        const u32x4 k = lds_keys[s * THREADS + tid];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fn(kStep * (S1 + s) + 4 * tid + e, k[e]);
+      }
+  };
+
+  // ---- 1. key range ----
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  if (lane == 0) {
+    sh.red[wave] = kmin;
+    sh.red[kWaves + wave] = kmax;
+  }
+  __syncthreads();   // also publishes the LDS-resident keys
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    lo = min(lo, sh.red[w]);
+    hi = max(hi, sh.red[kWaves + w]);
+  }
+  __syncthreads();
+
+  // ---- 2. threshold key T ----
+  uint32_t remaining = (uint32_t)K, in_range = 0;
+  auto refine = [&](auto&& visit) {
+    const uint32_t width = hi - lo;
+    const int bits = 32 - __clz(width);
+    const int shift = bits > 11 ? bits - 11 : 0;
+    const int nbins = (int)(width >> shift) + 1;
+    for (int b = tid; b < nbins; b += THREADS) sh.hist[b] = 0u;
+    if (tid == 0) sh.bcast[0] = sh.bcast[1] = sh.bcast[2] = 0u;
+    __syncthreads();
+    visit([&](int, uint32_t k) {
+      if (k >= lo && k <= hi) atomicAdd(&sh.hist[(k - lo) >> shift], 1u);
+    });
+    __syncthreads();
+    constexpr int BPT = kBins / THREADS;
+    uint32_t hb[BPT], hsum = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      const int b = BPT * tid + e;
+      hb[e] = b < nbins ? sh.hist[b] : 0u;
+      hsum += hb[e];
+    }
+    uint32_t ex, dummy_e, tot, dummy_t;
+    block_excl_scan2<THREADS>(hsum, 0u, ex, dummy_e, tot, dummy_t, sh);
+    uint32_t above = tot - (ex + hsum);
+#pragma unroll
+    for (int e = BPT - 1; e >= 0; --e) {
+      const int b = BPT * tid + e;
+      if (b < nbins && above < remaining && remaining <= above + hb[e]) {
+        sh.bcast[0] = (uint32_t)b;
+        sh.bcast[1] = above;
+        sh.bcast[2] = hb[e];
+      }
+      above += hb[e];
+    }
+    __syncthreads();
+    const uint32_t bsel = sh.bcast[0], above_sel = sh.bcast[1];
+    in_range = sh.bcast[2];
+    __syncthreads();
+    remaining -= above_sel;
+    const uint64_t nlo = (uint64_t)lo + ((uint64_t)bsel << shift);
+    const uint64_t nhi = nlo + ((uint64_t)1 << shift) - 1;
+    lo = (uint32_t)nlo;
+    hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+  };
+  if (hi != lo) refine(for_each);
+  if (hi != lo) {
+    if (in_range <= (uint32_t)kBins) {
+      if (tid == 0) sh.bcast[3] = 0u;
+      __syncthreads();
+      for_each([&](int, uint32_t k) {
+        if (k >= lo && k <= hi) cand[atomicAdd(&sh.bcast[3], 1u)] = k;
+      });
+      __syncthreads();
+      const int n_cand = (int)in_range;
+      if (n_cand <= 64) {
+        // One wave ranks the candidates against each other: T is the key
+        // with fewer than `remaining` candidates above it and at least
+        // `remaining` at or above it.
+        if (wave == 0) {
+          const uint32_t x = lane < n_cand ? cand[lane] : 0u;
+          uint32_t gt = 0, ge = 0;
+          for (int j = 0; j < n_cand; ++j) {
+            const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
+            gt += y > x;
+            ge += y >= x;
+          }
+          if (lane < n_cand && gt < remaining && remaining <= ge) {   // every such lane holds T
+            sh.bcast[0] = x;
+            sh.bcast[1] = remaining - gt;
+          }
+        }
+        __syncthreads();
+        lo = hi = sh.bcast[0];
+        remaining = sh.bcast[1];
+      } else {
+        auto for_cand = [&](auto&& fn) {
+          for (int c = tid; c < n_cand; c += THREADS) fn(c, cand[c]);
+        };
+        for (int round = 1; round < 4 && hi != lo; ++round) refine(for_cand);
+      }
+    } else {
+      for (int round = 1; round < 4 && hi != lo; ++round) refine(for_each);
+    }
+  }
+  const uint32_t T = lo;
+  const uint32_t need_ties = remaining;   // >= 1 keys equal to T are taken
+
+  // ---- 3. ordered compaction through two bit maps ----
+  uint32_t* gmap = cand;      // key > T
+  uint32_t* emap = sh.hist;   // key == T
+  __syncthreads();            // every read of cand / hist is done
+  for (int w = tid; w < kBins; w += THREADS) gmap[w] = emap[w] = 0u;
+  __syncthreads();
+  auto mark = [&](int s, const u32x4& k) {
+    uint32_t g = 0, q = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      g |= (uint32_t)(k[e] > T) << e;
+      q |= (uint32_t)(k[e] == T) << e;
+    }
+    const int word = (kStep * s + 4 * tid) >> 5, sh4 = 4 * (tid & 7);
+    if (g) atomicOr(&gmap[word], g << sh4);
+    if (q) atomicOr(&emap[word], q << sh4);
+  };
+#pragma unroll
+  for (int s = 0; s < S1; ++s)
+    if (active(s)) mark(s, rk[s]);
+#pragma unroll 2
+  for (int s = 0; s < S2; ++s)
+    if (active(S1 + s)) mark(S1 + s, lds_keys[s * THREADS + tid]);
+  __syncthreads();
+  // thread t owns positions [64t, 64t + 64): map words 2t, 2t + 1
+  uint32_t gw[2], ew[2];
+  uint32_t cg = 0, ce = 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int w = 2 * tid + j;
+    gw[j] = w < kBins ? gmap[w] : 0u;
+    ew[j] = w < kBins ? emap[w] : 0u;
+    cg += __popc(gw[j]);
+    ce += __popc(ew[j]);
+  }
+  uint32_t g_before, e_before, tg, te;
+  block_excl_scan2<THREADS>(cg, ce, g_before, e_before, tg, te, sh);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t m = gw[j] | ew[j];
+    while (m) {
+      const int b = __builtin_ctz(m);
+      m &= m - 1;
+      const int pos = 64 * tid + 32 * j + b;
+      if ((gw[j] >> b) & 1u) {
+        const uint32_t slot = g_before + min(e_before, need_ties);
+        if (slot < (uint32_t)K) out[slot] = pos;
+        ++g_before;
+      } else {
+        if (e_before < need_ties && g_before + e_before < (uint32_t)K) out[g_before + e_before] = pos;
+        ++e_before;
+      }
+    }
+  }
+}
+
 hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   if (A.n_q <= 0) return hipSuccess;
   const dim3 grid((unsigned)A.n_q);
@@ -397,14 +639,14 @@ hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   // with 16-byte loads, so rows must start 16-byte aligned); longer or
   // unaligned rows are streamed from memory in every pass.
   const bool rows_aligned = (reinterpret_cast<uintptr_t>(A.scores) % 16 == 0) && (A.ld % 4 == 0);
-  if (rows_aligned && A.n_k <= 1024 * 16) {
-    hipLaunchKernelGGL((topk_kernel<1024, 16, 0>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
+  if (rows_aligned && A.n_k <= 4 * 1024 * 4) {
+    hipLaunchKernelGGL((topk_chip_kernel<1024, 4, 0>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
                        (int)A.n_k, A.top_k, A.idx);
-  } else if (rows_aligned && A.n_k <= 1024 * 32) {
-    hipLaunchKernelGGL((topk_kernel<1024, 32, 0>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
+  } else if (rows_aligned && A.n_k <= 4 * 1024 * 8) {
+    hipLaunchKernelGGL((topk_chip_kernel<1024, 8, 0>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
                        (int)A.n_k, A.top_k, A.idx);
-  } else if (rows_aligned && A.n_k <= 1024 * 64) {
-    hipLaunchKernelGGL((topk_kernel<1024, 32, 32>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
+  } else if (rows_aligned && A.n_k <= 4 * 1024 * 16) {
+    hipLaunchKernelGGL((topk_chip_kernel<1024, 8, 8>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
                        (int)A.n_k, A.top_k, A.idx);
   } else {
     hipLaunchKernelGGL((topk_kernel<1024, 0, 0>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
