@@ -228,6 +228,10 @@ constexpr int kIdxKT = 64;                                  // keys per tile
 constexpr int kIdxStages = 8;                               // ring depth
 constexpr int kIdxTileB = kIdxKT * 256;                     // 16 KiB
 constexpr int kIdxLoadsPerWave = kIdxTileB / 1024 / kIdxWaves;   // 2
+#ifndef SMA_IDX_READ_AHEAD
+#define SMA_IDX_READ_AHEAD 1
+#endif
+constexpr int kIdxReadAhead = SMA_IDX_READ_AHEAD;           // B reads in flight ahead of the MFMAs
 
 typedef __attribute__((address_space(3))) uint8_t idx_lds_u8;
 
@@ -329,7 +333,10 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_kernel(
       part = fmaf(wv[0][jj], __int_as_float(max(__float_as_int(c0[jj]), 0)), part);
       part = fmaf(wv[1][jj], __int_as_float(max(__float_as_int(c1[jj]), 0)), part);
     }
-    part += __shfl_xor(part, 32, 64);
+    // lanes 0..31 add the other 32 head rows, held by the lane 32 above
+    // (v_permlane32_swap: no LDS round trip inside the MFMA stream)
+    part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
+                                                             false)[1]);
     const int key = key0 + lrow;
     if (khalf == 0 && key0 >= 0 && q0 + wave < n_q && key <= mypos && key < k_end)
       scores[(int64_t)(q0 + wave) * ld + key] = part;
@@ -355,15 +362,17 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_kernel(
       acc[u & 1][0] = c0;
       acc[u & 1][1] = c1;
       prev_key = k0 + 32 * u;
-      // interleave: per pair of k-steps one B read, and four epilogue VALU
-      // instructions behind each MFMA
+      // interleave: B reads kIdxReadAhead k-steps ahead of their MFMAs, and
+      // four epilogue VALU instructions behind each MFMA
+#pragma unroll
+      for (int g = 0; g < kIdxReadAhead; ++g) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
 #pragma unroll
       for (int g = 0; g < KS; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
         __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
         __builtin_amdgcn_sched_group_barrier(0x0002, 4, 0);   // VALU
         __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
         __builtin_amdgcn_sched_group_barrier(0x0002, 4, 0);   // VALU
+        if (g + kIdxReadAhead < KS) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
       }
     }
   }
