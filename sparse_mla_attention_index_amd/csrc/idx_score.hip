@@ -228,10 +228,6 @@ constexpr int kIdxKT = 64;                                  // keys per tile
 constexpr int kIdxStages = 8;                               // ring depth
 constexpr int kIdxTileB = kIdxKT * 256;                     // 16 KiB
 constexpr int kIdxLoadsPerWave = kIdxTileB / 1024 / kIdxWaves;   // 2
-#ifndef SMA_IDX_READ_AHEAD
-#define SMA_IDX_READ_AHEAD 1
-#endif
-constexpr int kIdxReadAhead = SMA_IDX_READ_AHEAD;           // B reads in flight ahead of the MFMAs
 
 typedef __attribute__((address_space(3))) uint8_t idx_lds_u8;
 
@@ -341,9 +337,17 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_kernel(
     if (khalf == 0 && key0 >= 0 && q0 + wave < n_q && key <= mypos && key < k_end)
       scores[(int64_t)(q0 + wave) * ld + key] = part;
   };
+  // B operands are read one N-tile ahead of their MFMAs (bn), so the last
+  // N-tile of tile i reads tile i + 1: the wait below therefore covers tiles
+  // i and i + 1, leaving kIdxStages - 3 tiles in flight.
+  idx_wait_vmcnt<(kIdxStages - 2) * kIdxLoadsPerWave>();
+  idx_sync_lds();
+  bf16x8 bn[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) bn[j] = *reinterpret_cast<const bf16x8*>(s_k[0] + boff[j]);
   for (int i = 0; i < ntiles; ++i) {
-    // tile i has landed once at most the kIdxStages - 2 younger tiles are outstanding
-    idx_wait_vmcnt<(kIdxStages - 2) * kIdxLoadsPerWave>();
+    // tiles i and i + 1 have landed once at most the kIdxStages - 3 younger tiles are outstanding
+    idx_wait_vmcnt<(kIdxStages - 3) * kIdxLoadsPerWave>();
     idx_sync_lds();             // for every wave; slot (i - 1) % kIdxStages is free
     issue(i + kIdxStages - 1);  // past the range these load clamped keys into a free slot
     const uint8_t* tile = s_k[i % kIdxStages];
@@ -351,10 +355,13 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_kernel(
 #pragma unroll
     for (int u = 0; u < kIdxKT / 32; ++u) {
       const f32x16 p0 = acc[(u + 1) & 1][0], p1 = acc[(u + 1) & 1][1];
+      // the N-tile after this one: (tile i, u + 1) or (tile i + 1, 0)
+      const uint8_t* nxt = u + 1 < kIdxKT / 32 ? tile + 8192 * (u + 1) : s_k[(i + 1) % kIdxStages];
       f32x16 c0 = f32x16{}, c1 = f32x16{};
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(tile + 8192 * u + boff[j]);
+        const bf16x8 b = bn[j];
+        bn[j] = *reinterpret_cast<const bf16x8*>(nxt + boff[j]);
         c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][j], b, c0, 0, 0, 0);
         c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][j], b, c1, 0, 0, 0);
       }
@@ -362,17 +369,15 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_kernel(
       acc[u & 1][0] = c0;
       acc[u & 1][1] = c1;
       prev_key = k0 + 32 * u;
-      // interleave: B reads kIdxReadAhead k-steps ahead of their MFMAs, and
-      // four epilogue VALU instructions behind each MFMA
-#pragma unroll
-      for (int g = 0; g < kIdxReadAhead; ++g) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
+      // interleave: one B read (for the next N-tile) and four epilogue VALU
+      // instructions per pair of MFMAs
 #pragma unroll
       for (int g = 0; g < KS; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
         __builtin_amdgcn_sched_group_barrier(0x0002, 4, 0);   // VALU
         __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
         __builtin_amdgcn_sched_group_barrier(0x0002, 4, 0);   // VALU
-        if (g + kIdxReadAhead < KS) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
       }
     }
   }
