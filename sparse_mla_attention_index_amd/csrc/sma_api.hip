@@ -152,7 +152,7 @@ sma_status run_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride, 
     if (e != hipSuccess) return hip_fail(e, "topk launch");
   }
   sma::MlaArgs ma{q, kv, kv_scale, kv_dtype == SMA_DT_FP8_E4M3, n_k, idx, n_q, top_k, sm_scale,
-                  out, out_dtype == SMA_DT_FP32, lse};
+                  out, out_dtype == SMA_DT_FP32, lse, pos};
   hipError_t e = sma::launch_sparse_mla(ma, st);
   if (e != hipSuccess) return hip_fail(e, "sparse_mla launch");
   return SMA_OK;

@@ -44,6 +44,9 @@ struct MlaArgs {
   void* out;
   bool out_f32;
   float* lse;
+  // Query positions when the caller has them (they set the bf16 kernel's tile
+  // visiting order); null: the query index stands in for the position.
+  const int32_t* q_pos = nullptr;
 };
 
 hipError_t launch_index_scores(const IdxArgs& a, hipStream_t s);

@@ -358,7 +358,7 @@ template <bool OUT_F32>
 __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int n_k,
     const int32_t* __restrict__ idx, int n_q, int K, float scale_log2, void* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, const int32_t* __restrict__ q_pos) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_kv[2][kDmaTileB];
   __shared__ __attribute__((aligned(1024))) uint8_t s_x[4096];
   __shared__ __attribute__((aligned(1024))) int s_idx[2][kIdxChunk];
@@ -398,6 +398,20 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     return;
   }
   const int ntiles = (n_ext + kMlaRows - 1) / kMlaRows;
+  // Tiles are visited in a rotated order, starting at tile t0 = (p / 8) mod
+  // ntiles (p: the query's position, or its index when no positions are
+  // given).  Workgroups are dealt
+  // to the 8 XCDs in turn and each XCD runs 64 of them at a time, so on one
+  // XCD a new query starts about every 1/64 of a query's duration and the
+  // query started next is 8 positions later: with this rotation the queries
+  // resident on an XCD work on the same tile index at the same time, and as
+  // their sorted selections of nearly the same prefix walk the same
+  // position window, rows fetched by one of them are L2 hits for the others.
+  // The softmax reference is per query and the sum is over all tiles, so
+  // only the order of the fp32 accumulation depends on t0 (deterministic).
+  const int qpos = q_pos ? max(q_pos[qi], 0) : qi;
+  const int t0 = (int)((uint32_t)(qpos >> 3) % (uint32_t)ntiles);
+  auto real_tile = [&](int t) { return t + t0 < ntiles ? t + t0 : t + t0 - ntiles; };
 
   // ---- Q: block 0 = own heads 32d+c32, block 1 = partner heads; dims 288d + 16ks + 8h .. +7 ----
   bf16x8 qf[2][kPairKs];
@@ -414,18 +428,23 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
   // The entries are staged through LDS in chunks of 8 tiles (one chunk
   // ahead), so the per-tile index reads are LDS reads and the only
   // vector-memory operations in flight are the gathers and chunk loads.
+  // Entries are staged in visiting order: staged position v holds the entry
+  // (v mod 32) of the real tile real_tile(v / 32).
   auto stage_chunk = [&](int c) {
     const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)&s_idx[c & 1][kIdxChunk / 2 * d];
 #pragma unroll
-    for (int i = 0; i < kIdxChunk / 2 / 64; ++i)
-      dma_load4(irow + min(c * kIdxChunk + kIdxChunk / 2 * d + 64 * i + lane, K - 1), dst + 256 * i);
+    for (int i = 0; i < kIdxChunk / 2 / 64; ++i) {
+      const int v = c * kIdxChunk + kIdxChunk / 2 * d + 64 * i + lane;
+      const int tv = min(v / kMlaRows, ntiles - 1);
+      dma_load4(irow + min(real_tile(tv) * kMlaRows + v % kMlaRows, K - 1), dst + 256 * i);
+    }
   };
   auto entry_raw = [&](int t, int half) -> int {
     const int e = t * kMlaRows + 16 * half + rsel;
     return s_idx[(e / kIdxChunk) & 1][e % kIdxChunk];
   };
   auto entry_ok = [&](int t, int half, int x) -> bool {
-    return t * kMlaRows + 16 * half + rsel < n_ext && x >= 0 && x < n_k;
+    return real_tile(t) * kMlaRows + 16 * half + rsel < n_ext && x >= 0 && x < n_k;
   };
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv) + 16 * (lane >> 4) + 64 * (kPairLoads / 2) * d;
   auto issue_tile = [&](int t, int b) -> uint32_t {   // returns the tile's row mask
@@ -479,7 +498,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     for (int t = 0; t < ntiles; ++t) {
       wait_vmcnt<0>();     // tile t (and any index chunk) has landed
       block_sync_lds();    // for both waves; tile t-1's slot and the exchange buffers are free
-      if (t % (kIdxChunk / kMlaRows) == 0 && (t / (kIdxChunk / kMlaRows) + 1) * kIdxChunk < n_ext)
+      if (t % (kIdxChunk / kMlaRows) == 0 && (t / (kIdxChunk / kMlaRows) + 1) * (kIdxChunk / kMlaRows) < ntiles)
         stage_chunk(t / (kIdxChunk / kMlaRows) + 1);
       uint32_t mask_next = 0;
       if (t + 1 < ntiles) mask_next = issue_tile(t + 1, (t + 1) & 1);
@@ -636,10 +655,10 @@ hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
     const dim3 block2(kPairThreads);
     if (A.out_f32)
       hipLaunchKernelGGL((sparse_mla_bf16_kernel<true>), grid, block2, 0, st, A.q, kv, (int)A.n_k, A.idx, A.n_q,
-                         A.top_k, scale_log2, A.out, A.lse);
+                         A.top_k, scale_log2, A.out, A.lse, A.q_pos);
     else
       hipLaunchKernelGGL((sparse_mla_bf16_kernel<false>), grid, block2, 0, st, A.q, kv, (int)A.n_k, A.idx,
-                         A.n_q, A.top_k, scale_log2, A.out, A.lse);
+                         A.n_q, A.top_k, scale_log2, A.out, A.lse, A.q_pos);
   }
   return hipGetLastError();
 }
