@@ -210,7 +210,8 @@ def main():
     t_topk = timed(lambda: sma.topk_select(scores, q_pos[:nb], w.top_k, idx=idx[:nb]), reps) * (n_q / nb)
     # the full index list for the attention kernel comes from the timed steps
     step()
-    t_mla = timed(lambda: sma.sparse_mla_prefill(q, kv, idx, w.sm_scale, kv_scale=kv_scale, out=out), reps)
+    t_mla = timed(lambda: sma.sparse_mla_prefill(q, kv, idx, w.sm_scale, kv_scale=kv_scale, out=out,
+                                                 workspace=ws), reps)
     _log(f"kernels: index_scores {t_idx:.2f} ms, topk {t_topk:.2f} ms, sparse_mla {t_mla:.2f} ms")
     pcp = None
     if args.workload == "pcp":

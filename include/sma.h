@@ -139,7 +139,11 @@ sma_status sma_topk_select(const float* scores, int64_t ld_scores, const int32_t
  *  Softmax and accumulation are fp32; QK and PV run on bf16 MFMA (an FP8
  *  row is widened to bf16 exactly; its scale multiplies the logit and the
  *  softmax weight).
- *  Supported: 1 <= top_k <= 2048.  ws may be NULL (ws_bytes 0).
+ *  Supported: 1 <= top_k <= 2048.  ws may be NULL (ws_bytes 0).  With at
+ *  least sma_workspace_bytes(SMA_OP_SPARSE_MLA, ...) bytes (256-byte
+ *  aligned), a small FP8 batch splits each query's rows into slices whose
+ *  partial results are merged by log-sum-exp; results are the same up to
+ *  fp32 summation order.
  */
 sma_status sma_sparse_mla_prefill(const uint16_t* q, const void* kv, const float* kv_scale,
                                   int32_t kv_dtype, int64_t n_k, const int32_t* idx,
@@ -186,7 +190,9 @@ sma_status sma_pcp_rank_share(int32_t rank, int32_t pcp_size, int64_t L_total,
 
 /* Minimum workspace in bytes for `op` (an sma_op) at these sizes.  For
  * SMA_OP_PREFILL / SMA_OP_PCP_SHARE, n_q is the number of query rows and the
- * figure assumes idx_out == NULL (the index list lives in the workspace). */
+ * figure assumes idx_out == NULL (the index list lives in the workspace).
+ * For SMA_OP_SPARSE_MLA the workspace is optional: the figure is what lets a
+ * small FP8 batch split its queries' rows (0 when no split is used). */
 size_t sma_workspace_bytes(int32_t op, int32_t n_q, int64_t n_k, int32_t top_k,
                            int32_t h_idx, int32_t d_idx);
 

@@ -147,8 +147,12 @@ def topk_select(scores, q_pos, top_k: int, *, n_k: int | None = None, idx=None):
 
 
 def sparse_mla_prefill(q, kv, idx, sm_scale: float, *, kv_scale=None, out=None, out_dtype=torch.bfloat16,
-                       lse=None, want_lse: bool = False):
-    """Sparse MLA over idx: returns (out [n_q, 64, 512], lse [n_q, 64] or None)."""
+                       lse=None, want_lse: bool = False, workspace=None):
+    """Sparse MLA over idx: returns (out [n_q, 64, 512], lse [n_q, 64] or None).
+
+    `workspace` (uint8 device tensor, optional): with at least
+    workspace_bytes(SMA_OP_SPARSE_MLA, n_q, n_k, top_k) bytes, small FP8
+    batches split each query's rows across workgroups."""
     n_q = q.shape[0]
     _bf16(q, "q")
     kdt = _keys(kv, kv_scale, "kv")
@@ -159,9 +163,10 @@ def sparse_mla_prefill(q, kv, idx, sm_scale: float, *, kv_scale=None, out=None, 
     odt = SMA_DT_FP32 if out.dtype == torch.float32 else SMA_DT_BF16
     if lse is None and want_lse:
         lse = torch.empty((n_q, HEADS), dtype=torch.float32, device=q.device)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().sma_sparse_mla_prefill(_ptr(q), _ptr(kv), _ptr(kv_scale), kdt, kv.shape[0], _ptr(idx), n_q,
-                                        idx.shape[1], float(sm_scale), _ptr(out), odt, _ptr(lse), None, 0,
-                                        _stream(q.device)))
+                                        idx.shape[1], float(sm_scale), _ptr(out), odt, _ptr(lse),
+                                        _ptr(workspace), ws_n, _stream(q.device)))
     return out, lse
 
 

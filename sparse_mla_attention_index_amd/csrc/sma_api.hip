@@ -151,8 +151,10 @@ sma_status run_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride, 
     e = sma::launch_topk(ta, st);
     if (e != hipSuccess) return hip_fail(e, "topk launch");
   }
+  // the score blocks are dead once the index lists exist: their space holds
+  // the attention kernel's split partials for small batches
   sma::MlaArgs ma{q, kv, kv_scale, kv_dtype == SMA_DT_FP8_E4M3, n_k, idx, n_q, top_k, sm_scale,
-                  out, out_dtype == SMA_DT_FP32, lse, pos};
+                  out, out_dtype == SMA_DT_FP32, lse, pos, score_ws, score_ws_bytes};
   hipError_t e = sma::launch_sparse_mla(ma, st);
   if (e != hipSuccess) return hip_fail(e, "sparse_mla launch");
   return SMA_OK;
@@ -200,16 +202,15 @@ sma_status sma_sparse_mla_prefill(const uint16_t* q, const void* kv, const float
                                   int32_t kv_dtype, int64_t n_k, const int32_t* idx, int32_t n_q,
                                   int32_t top_k, float sm_scale, void* out, int32_t out_dtype,
                                   float* lse, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   g_err.clear();
   sma_status s = validate_mla(q, kv, kv_scale, kv_dtype, n_k, idx, n_q, top_k, sm_scale, out,
                               out_dtype, false);
   if (s != SMA_OK) return s;
   if (n_q == 0) return SMA_OK;
   if ((s = check_device()) != SMA_OK) return s;
+  if (ws && !aligned(ws, 256)) return fail(SMA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   sma::MlaArgs a{q, kv, kv_scale, kv_dtype == SMA_DT_FP8_E4M3, n_k, idx, n_q, top_k, sm_scale,
-                 out, out_dtype == SMA_DT_FP32, lse};
+                 out, out_dtype == SMA_DT_FP32, lse, nullptr, ws, ws ? ws_bytes : 0};
   hipError_t e = sma::launch_sparse_mla(a, (hipStream_t)stream);
   return e == hipSuccess ? SMA_OK : hip_fail(e, "sparse_mla launch");
 }
@@ -222,8 +223,9 @@ size_t sma_workspace_bytes(int32_t op, int32_t n_q, int64_t n_k, int32_t top_k, 
   switch (op) {
     case SMA_OP_INDEX_SCORES:
     case SMA_OP_TOPK:
-    case SMA_OP_SPARSE_MLA:
       return 0;
+    case SMA_OP_SPARSE_MLA:   // optional: lets small FP8 batches split each query's rows
+      return align_up(sma::mla_split_bytes(n_q, sma::mla_split_count(n_q, top_k, true)), 256);
     case SMA_OP_PREFILL:
     case SMA_OP_PCP_SHARE: {
       const int32_t blk = n_q < kMinScoreBlock ? n_q : kMinScoreBlock;

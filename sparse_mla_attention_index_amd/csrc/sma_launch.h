@@ -47,7 +47,15 @@ struct MlaArgs {
   // Query positions when the caller has them (they set the bf16 kernel's tile
   // visiting order); null: the query index stands in for the position.
   const int32_t* q_pos = nullptr;
+  // Workspace for the split partials of small FP8 batches (may be null).
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
 };
+
+// Number of row slices per query the FP8 attention kernel uses for n_q
+// queries (1: no split), and the workspace bytes their partials take.
+int mla_split_count(int n_q, int top_k, bool fp8);
+size_t mla_split_bytes(int n_q, int n_split);
 
 hipError_t launch_index_scores(const IdxArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);

@@ -19,6 +19,8 @@
 // Writing the products transposed puts one head per lane column in both
 // accumulators, so the softmax statistics of a head and the output rows
 // they scale live in the same lanes.
+#include <algorithm>
+
 #include "sma_device.h"
 #include "sma_launch.h"
 
@@ -27,6 +29,9 @@ namespace sma {
 constexpr int kMlaRows = 32;                // gathered rows per tile
 constexpr int kMlaRowB = kDqk * 2 + 16;     // padded LDS row, bytes (1168)
 constexpr int kMlaThreads = 256;
+// Split partial of one (query, slice): O [64][512] unnormalised, then the
+// per-head exponent reference m (log2 domain) and sum l.
+constexpr int kMlaPartFloats = kHeads * kDv + 2 * kHeads;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -34,14 +39,17 @@ template <bool FP8, bool OUT_F32>
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv, const float* __restrict__ kv_scale,
     int n_k, const int32_t* __restrict__ idx, int n_q, int K, float scale_log2,
-    void* __restrict__ out, float* __restrict__ lse) {
+    void* __restrict__ out, float* __restrict__ lse, int n_split, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][kMlaRows * kMlaRowB];
   __shared__ int s_list[SMA_MAX_TOPK_DEV];
   __shared__ float s_scale[2][kMlaRows];
   __shared__ uint32_t s_cnt[kMlaThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qi = blockIdx.x;
+  // With n_split > 1 workgroup (qi, split) covers one slice of the query's
+  // compacted rows and leaves an unnormalised partial in `part` (merged by
+  // mla_merge_kernel); otherwise it covers all of them.
+  const int qi = blockIdx.x / n_split, split = blockIdx.x % n_split;
   const int g = lane >> 4, i = lane & 15;   // lane group (k slot) and column (head)
 
   // ---- compact the valid indices, keeping their order ----
@@ -75,8 +83,21 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     if (v[e] >= 0) s_list[before++] = v[e];
   __syncthreads();
   const int n_valid = (int)total;
+  // this workgroup's slice [lb, le) of the compacted list (whole tiles)
+  const int per = ((n_valid + n_split - 1) / n_split + kMlaRows - 1) / kMlaRows * kMlaRows;
+  const int lb = min(n_valid, split * per), le = min(n_valid, lb + per);
 
   const int head = 16 * wave + i;
+  float* mypart = part ? part + (int64_t)blockIdx.x * kMlaPartFloats : nullptr;
+  if (mypart && le == lb) {   // empty slice: zero partial, reference -inf
+    for (int mt = 0; mt < kDv / 16; ++mt)
+      *reinterpret_cast<f32x4*>(mypart + head * kDv + 16 * mt + 4 * g) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (g == 0) {
+      mypart[kHeads * kDv + head] = -INFINITY;
+      mypart[kHeads * kDv + kHeads + head] = 0.f;
+    }
+    return;
+  }
   if (n_valid == 0) {
     for (int mt = 0; mt < kDv / 16; ++mt) {
       const int64_t o_off = ((int64_t)qi * kHeads + head) * kDv + 16 * mt + 4 * g;
@@ -104,27 +125,27 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
   u32x4 stage[NCH];
   float stage_sc = 0.f;
   auto load_tile = [&](int t) {
-    const int r0 = t * kMlaRows;
+    const int r0 = lb + t * kMlaRows;
 #pragma unroll
     for (int r = 0; r < NCH; ++r) {
       const int c = tid + kMlaThreads * r;
       if constexpr (FP8) {
         if (c < kMlaRows * kDqk / 16) {
           const int row = c / (kDqk / 16), col = c % (kDqk / 16);
-          const int li = r0 + row < n_valid ? r0 + row : 0;
+          const int li = r0 + row < le ? r0 + row : lb;
           stage[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(kv) +
                                                      (int64_t)s_list[li] * kDqk + col * 16);
         }
       } else {
         const int row = c / (kDqk / 8), col = c % (kDqk / 8);
-        const int li = r0 + row < n_valid ? r0 + row : 0;
+        const int li = r0 + row < le ? r0 + row : lb;
         stage[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(kv) +
                                                    (int64_t)s_list[li] * kDqk + col * 8);
       }
     }
     if constexpr (FP8) {
       if (tid < kMlaRows) {
-        const int li = r0 + tid < n_valid ? r0 + tid : 0;
+        const int li = r0 + tid < le ? r0 + tid : lb;
         stage_sc = kv_scale[s_list[li]];
       }
     }
@@ -159,7 +180,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
   float m_run = -INFINITY;   // running max of the head's logits (log2 domain)
   float l_run = 0.f;         // this lane's share of the softmax denominator
 
-  const int ntiles = (n_valid + kMlaRows - 1) / kMlaRows;
+  const int ntiles = (le - lb + kMlaRows - 1) / kMlaRows;
   load_tile(0);
   store_tile(0);
   __syncthreads();
@@ -183,7 +204,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     }
 
     // online softmax (log2 domain)
-    const int valid_rows = n_valid - t * kMlaRows;
+    const int valid_rows = le - lb - t * kMlaRows;
     float s2[8];
     float mx = -INFINITY;
 #pragma unroll
@@ -235,9 +256,19 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     __syncthreads();
   }
 
-  // ---- normalise and write ----
+  // ---- normalise and write (or leave the partial) ----
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
+  if (mypart) {
+#pragma unroll
+    for (int mt = 0; mt < kDv / 16; ++mt)
+      *reinterpret_cast<f32x4*>(mypart + head * kDv + 16 * mt + 4 * g) = o[mt];
+    if (g == 0) {
+      mypart[kHeads * kDv + head] = m_run;
+      mypart[kHeads * kDv + kHeads + head] = l_tot;
+    }
+    return;
+  }
   const float inv = 1.f / l_tot;
 #pragma unroll
   for (int mt = 0; mt < kDv / 16; ++mt) {
@@ -252,6 +283,45 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
   }
   if (lse && g == 0)
     lse[(int64_t)qi * kHeads + head] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+}
+
+// Log-sum-exp merge of the n_split partials of each query: with
+// M = max_s m_s, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s and
+// lse = (M + log2 of that sum) * ln 2.  One 256-thread workgroup per query;
+// thread t handles head t/4, dims 128(t%4) .. +127.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void mla_merge_kernel(const float* __restrict__ part, int n_split,
+                                                        void* __restrict__ out, float* __restrict__ lse) {
+  constexpr int kMaxSplit = 16;
+  const int qi = blockIdx.x, h = threadIdx.x >> 2, q4 = threadIdx.x & 3;
+  const float* base = part + (int64_t)qi * n_split * kMlaPartFloats;
+  float m[kMaxSplit], wgt[kMaxSplit];
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) {
+    m[s] = base[s * kMlaPartFloats + kHeads * kDv + h];
+    M = fmaxf(M, m[s]);
+  }
+  float L = 0.f;
+  for (int s = 0; s < n_split; ++s) {
+    wgt[s] = m[s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[s] - M);
+    L += wgt[s] * base[s * kMlaPartFloats + kHeads * kDv + kHeads + h];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int64_t o_row = ((int64_t)qi * kHeads + h) * kDv + 128 * q4;
+  for (int c = 0; c < 32; ++c) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n_split; ++s)
+      acc += wgt[s] * *reinterpret_cast<const f32x4*>(base + s * kMlaPartFloats + h * kDv + 128 * q4 + 4 * c);
+    acc *= inv;
+    if constexpr (OUT_F32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o_row + 4 * c) = acc;
+    } else {
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o_row + 4 * c) =
+          u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    }
+  }
+  if (lse && q4 == 0)
+    lse[(int64_t)qi * kHeads + h] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -639,17 +709,57 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
   if (lse && h == 0) lse[(int64_t)qi * kHeads + 32 * d + c32] = (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
+// Compute units of the current device (cached per device).
+static int device_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int mla_split_count(int n_q, int top_k, bool fp8) {
+  if (!fp8 || n_q <= 0) return 1;
+  const int cus = device_cu_count();
+  if (n_q >= cus) return 1;
+  int s = (2 * cus + n_q - 1) / n_q;            // about two workgroups per CU
+  s = std::min(s, std::min(16, std::max(1, top_k / 128)));   // slices of at least 128 rows
+  return std::max(1, s);
+}
+
+size_t mla_split_bytes(int n_q, int n_split) {
+  return n_split > 1 ? (size_t)n_q * n_split * kMlaPartFloats * sizeof(float) : 0;
+}
+
 hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
   if (A.n_q <= 0) return hipSuccess;
   const float scale_log2 = A.sm_scale * 1.4426950408889634f;
   const dim3 grid((unsigned)A.n_q), block(kMlaThreads);
   if (A.fp8) {
+    // small batches split each query's rows across workgroups when the
+    // workspace holds the partials
+    int n_split = mla_split_count(A.n_q, A.top_k, true);
+    if (n_split > 1 && (A.ws == nullptr || A.ws_bytes < mla_split_bytes(A.n_q, n_split))) n_split = 1;
+    float* part = n_split > 1 ? static_cast<float*>(A.ws) : nullptr;
+    const dim3 grid_s((unsigned)(A.n_q * n_split));
     if (A.out_f32)
-      hipLaunchKernelGGL((sparse_mla_kernel<true, true>), grid, block, 0, st, A.q, A.kv, A.kv_scale, (int)A.n_k,
-                         A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
+      hipLaunchKernelGGL((sparse_mla_kernel<true, true>), grid_s, block, 0, st, A.q, A.kv, A.kv_scale,
+                         (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part);
     else
-      hipLaunchKernelGGL((sparse_mla_kernel<true, false>), grid, block, 0, st, A.q, A.kv, A.kv_scale,
-                         (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
+      hipLaunchKernelGGL((sparse_mla_kernel<true, false>), grid_s, block, 0, st, A.q, A.kv, A.kv_scale,
+                         (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part);
+    if (n_split > 1) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      if (A.out_f32)
+        hipLaunchKernelGGL((mla_merge_kernel<true>), grid, dim3(256), 0, st, part, n_split, A.out, A.lse);
+      else
+        hipLaunchKernelGGL((mla_merge_kernel<false>), grid, dim3(256), 0, st, part, n_split, A.out, A.lse);
+    }
   } else {
     const uint16_t* kv = static_cast<const uint16_t*>(A.kv);
     const dim3 block2(kPairThreads);

@@ -37,6 +37,10 @@ def test_workspace_sizes():
     assert sma.workspace_bytes(_lib.SMA_OP_TOPK, 10, 10, 5) == 0
     assert sma.workspace_bytes(_lib.SMA_OP_PREFILL, 10, 100, 5) == 256 + 4096   # 200 B and 4000 B, 256-aligned
     assert sma.workspace_bytes(99, 10, 10, 5) == 0
+    # attention partials for small batches: 64 queries on 256 CUs take 8 slices of
+    # 64*512 + 2*64 floats each (no device here: the library assumes 256 CUs)
+    assert sma.workspace_bytes(_lib.SMA_OP_SPARSE_MLA, 64, 1 << 20, 2048) == 64 * 8 * (64 * 512 + 128) * 4
+    assert sma.workspace_bytes(_lib.SMA_OP_SPARSE_MLA, 65536, 65536, 2048) == 0
 
 
 P = ctypes.c_void_p

@@ -91,6 +91,34 @@ def test_mla_fp8_kv():
     assert np.abs(host(lse) - ref_lse).max() < 5e-3
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_mla_fp8_kv_split_rows(out_dtype):
+    """A small FP8 batch given the workspace splits each query's rows into
+    slices merged by log-sum-exp; same tolerance as the unsplit kernel,
+    including empty lists and padding in the middle."""
+    w = synth.workload(5)
+    n_q, n_k, top_k = 12, 7000, 2048
+    q = synth.rows(synth.workload(2), "q", 0, n_q)
+    kv = synth.rows(w, "kv", 0, n_k)
+    idx = _idx_lists(n_q, n_k, top_k, 21, invalid=True)
+    kvc, kvs = dev(kv)
+    nb = sma.workspace_bytes(sma._lib.SMA_OP_SPARSE_MLA, n_q, n_k, top_k)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out, lse = sma.sparse_mla_prefill(dev(q), kvc, dev(idx), TAU, kv_scale=kvs, out_dtype=out_dtype,
+                                      want_lse=True, workspace=ws)
+    ref, ref_lse = _ref(q, kv, idx, fp8=True)
+    got = out_f64(out)
+    assert np.abs(got - ref).max() <= 3e-2 * np.abs(ref).max()
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(host(lse)), fin)
+    assert np.abs(host(lse)[fin] - ref_lse[fin]).max() < 5e-3
+    assert np.all(got[2] == 0)   # the empty list
+    # against the unsplit kernel on the same inputs
+    one, _ = sma.sparse_mla_prefill(dev(q), kvc, dev(idx), TAU, kv_scale=kvs, out_dtype=out_dtype)
+    assert np.abs(out_f64(one) - got).max() <= 1e-2 * np.abs(ref).max()
+
+
 def test_mla_deterministic():
     w = synth.workload(2)
     q, kv = _inputs(w, 16, 3000)
