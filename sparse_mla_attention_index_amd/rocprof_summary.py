@@ -17,7 +17,13 @@ averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the named kernel,
 scales each by bytes / counter of the plain copy kernel of N bytes that the
 same run executed (torch's device copy), and records the result with the
 SHA-256 of the kernel's source file, so that a reader can tell whether the
-kernel changed since the counters were taken.
+kernel changed since the counters were taken;
+
+  python -m sparse_mla_attention_index_amd.rocprof_summary table \\
+      --fetch ... --write ... --kernel idx_score --kernel topk --kernel sparse_mla \\
+      --copy-bytes N --out profiles/<name>.md --title "..." --command "<cmd>" ...
+
+writes the same scaled figures for several kernels as a Markdown table.
 """
 import argparse
 import csv
@@ -88,6 +94,32 @@ def cmd_traffic(a):
     print(json.dumps(rec, indent=1))
 
 
+def cmd_table(a):
+    fetch = _per_dispatch(a.fetch, "FETCH_SIZE")
+    write = _per_dispatch(a.write, "WRITE_SIZE")
+    f_copy, w_copy = _copy_counter(fetch), _copy_counter(write)
+    f_factor = a.copy_bytes / (f_copy * 1024.0)
+    w_factor = a.copy_bytes / (w_copy * 1024.0)
+    lines = [f"# {a.title}", "", "Commands (from the repository root, on the GPU host), one counter per run:", "",
+             "```"] + list(a.command) + ["```", "",
+             f"Calibration: the same runs copy {a.copy_bytes} bytes with a plain device copy, which reads "
+             f"{f_copy:.0f} KiB by FETCH_SIZE and writes {w_copy:.0f} KiB by WRITE_SIZE, so FETCH_SIZE is "
+             f"scaled by {f_factor:.4f} and WRITE_SIZE by {w_factor:.4f}.", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB (scaled) | written GB (scaled) |",
+             "|---|---|---|---|---|---|"]
+    for k in a.kernel:
+        f_kib, nf = _kernel_avg(fetch, k)
+        w_kib, _ = _kernel_avg(write, k)
+        name = next(n for (n, _) in fetch.values() if k in n).split("(")[0]
+        lines.append(f"| `{name}` | {nf} | {f_kib:.0f} | {w_kib:.0f} | {f_kib * 1024 * f_factor / 1e9:.2f} | "
+                     f"{w_kib * 1024 * w_factor / 1e9:.2f} |")
+    if a.note:
+        lines += ["", a.note]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cmd_stats(a):
     rows = []
     with open(a.stats, newline="") as f:
@@ -127,8 +159,17 @@ def main(argv=None):
     s.add_argument("--title", required=True)
     s.add_argument("--command", action="append", default=[])
     s.add_argument("--note", default="")
+    b = sub.add_parser("table")
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--kernel", action="append", required=True)
+    b.add_argument("--copy-bytes", type=int, required=True)
+    b.add_argument("--out", required=True)
+    b.add_argument("--title", required=True)
+    b.add_argument("--command", action="append", default=[])
+    b.add_argument("--note", default="")
     a = ap.parse_args(argv)
-    (cmd_traffic if a.cmd == "traffic" else cmd_stats)(a)
+    {"traffic": cmd_traffic, "table": cmd_table, "stats": cmd_stats}[a.cmd](a)
 
 
 if __name__ == "__main__":
