@@ -154,7 +154,7 @@ sma_status run_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride, 
   // the score blocks are dead once the index lists exist: their space holds
   // the attention kernel's split partials for small batches
   sma::MlaArgs ma{q, kv, kv_scale, kv_dtype == SMA_DT_FP8_E4M3, n_k, idx, n_q, top_k, sm_scale,
-                  out, out_dtype == SMA_DT_FP32, lse, pos, score_ws, score_ws_bytes};
+                  out, out_dtype == SMA_DT_FP32, lse, score_ws, score_ws_bytes};
   hipError_t e = sma::launch_sparse_mla(ma, st);
   if (e != hipSuccess) return hip_fail(e, "sparse_mla launch");
   return SMA_OK;
@@ -210,7 +210,7 @@ sma_status sma_sparse_mla_prefill(const uint16_t* q, const void* kv, const float
   if ((s = check_device()) != SMA_OK) return s;
   if (ws && !aligned(ws, 256)) return fail(SMA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   sma::MlaArgs a{q, kv, kv_scale, kv_dtype == SMA_DT_FP8_E4M3, n_k, idx, n_q, top_k, sm_scale,
-                 out, out_dtype == SMA_DT_FP32, lse, nullptr, ws, ws ? ws_bytes : 0};
+                 out, out_dtype == SMA_DT_FP32, lse, ws, ws ? ws_bytes : 0};
   hipError_t e = sma::launch_sparse_mla(a, (hipStream_t)stream);
   return e == hipSuccess ? SMA_OK : hip_fail(e, "sparse_mla launch");
 }

@@ -44,9 +44,6 @@ struct MlaArgs {
   void* out;
   bool out_f32;
   float* lse;
-  // Query positions when the caller has them (they set the bf16 kernel's tile
-  // visiting order); null: the query index stands in for the position.
-  const int32_t* q_pos = nullptr;
   // Workspace for the split partials of small FP8 batches (may be null).
   void* ws = nullptr;
   size_t ws_bytes = 0;

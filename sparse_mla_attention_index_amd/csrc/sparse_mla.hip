@@ -393,17 +393,19 @@ __device__ __forceinline__ void block_sync_lds() {
 // Softmax weights use a fixed per-head reference (below), so the output
 // registers are only ever written by MFMAs.
 //
-// Tile layout (32 rows x 576 dims, 36 KiB): a 1-KiB block holds 16 rows x
-// 4 chunks of 16 bytes.  Chunk c of row r sits in block 2(c>>2) + (r>>4) at
-// slot 16(c&3) + ((r&15) ^ 4(c&3)).  A direct global->LDS load fills one
-// block, so each load reads 64 contiguous bytes from each of 16 rows (whole
-// 64-byte lines), and lane l of every load fetches one of the two rows
-// ((l&15) ^ 4(l>>4)) + {0, 16}: two indices per lane per tile.  A 16-byte
-// read serves 16 lanes per cycle and a transposed 8-byte read 32 lanes; the
-// swizzle puts each such group of the K operand reads and of the V^T reads
-// on distinct banks, and the reads need two base registers each plus
-// immediate offsets.  The rope
-// blocks (chunks 64..71, bytes 32768..36863) are dead after QK and carry the
+// Tile layout (32 rows x 576 dims, 36 KiB): a 1-KiB block holds 8 rows x
+// 128 bytes, block (rg, cg) = row group r >> 3 and 128-byte chunk group at
+// (4 cg + rg) KiB.  Inside a block row r takes 128 bytes at 128 (r & 7), and
+// its 16-byte chunk c sits at slot (c & 7) ^ swz(r), swz(r) = bit-reverse of
+// the 3 bits (r >> 1) & 7.  A direct global->LDS load fills one block: eight
+// consecutive lanes fetch the 128 contiguous bytes of one row (each lane the
+// chunk that belongs at its 16 bytes), which the memory path coalesces far
+// better than 16-byte pieces of 16 rows.  Wave d gathers row groups 2d and
+// 2d+1: two indices per lane per tile.  A 16-byte read serves 16 lanes per
+// cycle and a transposed 8-byte read 32 lanes; the swizzle puts each such
+// group of the K operand reads and of the V^T reads on distinct banks, and
+// the reads need four base registers each plus immediate offsets.  The rope
+// chunk group (cg 8, bytes 32768..36863) is dead after QK and carries the
 // S/P exchange of one direction; a 4-KiB buffer carries the other.
 //
 // Entries are used in their given order without compaction: invalid ones
@@ -424,11 +426,18 @@ __device__ __forceinline__ void dma_load4(const void* gaddr, uint32_t lds_base) 
 
 typedef f32x16v_t f32x16v;
 
+// swz(r): bit-reverse of (r >> 1) & 7 (the 16-byte slot swizzle of row r).
+__device__ __forceinline__ int tile_swz(int r) {
+  const int u = (r >> 1) & 7;
+  return ((u & 1) << 2) | (u & 2) | ((u >> 2) & 1);
+}
+__device__ __forceinline__ constexpr int tile_block(int rg, int cg) { return (4 * cg + rg) * 1024; }
+
 template <bool OUT_F32>
 __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int n_k,
     const int32_t* __restrict__ idx, int n_q, int K, float scale_log2, void* __restrict__ out,
-    float* __restrict__ lse, const int32_t* __restrict__ q_pos) {
+    float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_kv[2][kDmaTileB];
   __shared__ __attribute__((aligned(1024))) uint8_t s_x[4096];
   __shared__ __attribute__((aligned(1024))) int s_idx[2][kIdxChunk];
@@ -468,20 +477,6 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     return;
   }
   const int ntiles = (n_ext + kMlaRows - 1) / kMlaRows;
-  // Tiles are visited in a rotated order, starting at tile t0 = (p / 8) mod
-  // ntiles (p: the query's position, or its index when no positions are
-  // given).  Workgroups are dealt
-  // to the 8 XCDs in turn and each XCD runs 64 of them at a time, so on one
-  // XCD a new query starts about every 1/64 of a query's duration and the
-  // query started next is 8 positions later: with this rotation the queries
-  // resident on an XCD work on the same tile index at the same time, and as
-  // their sorted selections of nearly the same prefix walk the same
-  // position window, rows fetched by one of them are L2 hits for the others.
-  // The softmax reference is per query and the sum is over all tiles, so
-  // only the order of the fp32 accumulation depends on t0 (deterministic).
-  const int qpos = q_pos ? max(q_pos[qi], 0) : qi;
-  const int t0 = (int)((uint32_t)(qpos >> 3) % (uint32_t)ntiles);
-  auto real_tile = [&](int t) { return t + t0 < ntiles ? t + t0 : t + t0 - ntiles; };
 
   // ---- Q: block 0 = own heads 32d+c32, block 1 = partner heads; dims 288d + 16ks + 8h .. +7 ----
   bf16x8 qf[2][kPairKs];
@@ -492,62 +487,68 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     for (int ks = 0; ks < kPairKs; ++ks) qf[hb][ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
   }
 
-  // ---- gather: block B (wave d issues B = 18d..18d+17) lane l fetches row
-  // 16(B&1) + rsel, chunk 4(B>>1) + (l>>4) ----
-  const int rsel = (lane & 15) ^ (4 * (lane >> 4));
+  // ---- gather: wave d fills blocks (rg, cg) for rg = 2d, 2d+1 and all 9
+  // chunk groups; lane l fetches row 8rg + (l >> 3), chunk 8cg + ((l & 7) ^
+  // swz(row)) ----
+  const int rg_row = lane >> 3;
   // The entries are staged through LDS in chunks of 8 tiles (one chunk
   // ahead), so the per-tile index reads are LDS reads and the only
   // vector-memory operations in flight are the gathers and chunk loads.
-  // Entries are staged in visiting order: staged position v holds the entry
-  // (v mod 32) of the real tile real_tile(v / 32).
   auto stage_chunk = [&](int c) {
     const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)&s_idx[c & 1][kIdxChunk / 2 * d];
 #pragma unroll
     for (int i = 0; i < kIdxChunk / 2 / 64; ++i) {
       const int v = c * kIdxChunk + kIdxChunk / 2 * d + 64 * i + lane;
-      const int tv = min(v / kMlaRows, ntiles - 1);
-      dma_load4(irow + min(real_tile(tv) * kMlaRows + v % kMlaRows, K - 1), dst + 256 * i);
+      dma_load4(irow + min(v, K - 1), dst + 256 * i);
     }
   };
-  auto entry_raw = [&](int t, int half) -> int {
-    const int e = t * kMlaRows + 16 * half + rsel;
-    return s_idx[(e / kIdxChunk) & 1][e % kIdxChunk];
-  };
-  auto entry_ok = [&](int t, int half, int x) -> bool {
-    return real_tile(t) * kMlaRows + 16 * half + rsel < n_ext && x >= 0 && x < n_k;
-  };
-  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv) + 16 * (lane >> 4) + 64 * (kPairLoads / 2) * d;
+  auto entry_raw = [&](int e) -> int { return s_idx[(e / kIdxChunk) & 1][e % kIdxChunk]; };
+  auto entry_ok = [&](int e, int x) -> bool { return e < n_ext && x >= 0 && x < n_k; };
+  const uint8_t* kv_bytes = reinterpret_cast<const uint8_t*>(kv);
+  const int r_lo = 16 * d + rg_row, r_hi = r_lo + 8;   // rows of row groups 2d and 2d+1
+  const int c_lo = 16 * ((lane & 7) ^ tile_swz(r_lo)), c_hi = 16 * ((lane & 7) ^ tile_swz(r_hi));
   auto issue_tile = [&](int t, int b) -> uint32_t {   // returns the tile's row mask
-    const int raw_lo = entry_raw(t, 0), raw_hi = entry_raw(t, 1);
-    const bool ok_lo = entry_ok(t, 0, raw_lo), ok_hi = entry_ok(t, 1, raw_hi);
-    const uint8_t* src_lo = kvb + (int64_t)(ok_lo ? raw_lo : 0) * kDmaRowB;
-    const uint8_t* src_hi = kvb + (int64_t)(ok_hi ? raw_hi : 0) * kDmaRowB;
-    const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)&s_kv[b][kPairLoads * 1024 * d];
+    const int raw_lo = entry_raw(t * kMlaRows + r_lo), raw_hi = entry_raw(t * kMlaRows + r_hi);
+    const bool ok_lo = entry_ok(t * kMlaRows + r_lo, raw_lo), ok_hi = entry_ok(t * kMlaRows + r_hi, raw_hi);
+    const uint8_t* src_lo = kv_bytes + (int64_t)(ok_lo ? raw_lo : 0) * kDmaRowB + c_lo;
+    const uint8_t* src_hi = kv_bytes + (int64_t)(ok_hi ? raw_hi : 0) * kDmaRowB + c_hi;
+    const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)&s_kv[b][tile_block(2 * d, 0)];
 #pragma unroll
-    for (int j = 0; j < kPairLoads; ++j) dma_load16((j & 1 ? src_hi : src_lo) + 64 * (j >> 1), dst + 1024 * j);
-    // rows 0..15: lanes 0..15 (rsel = lane) of the lo half; rows 16..31: of the hi half
-    return ((uint32_t)__ballot(ok_lo) & 0xFFFFu) | (((uint32_t)__ballot(ok_hi) & 0xFFFFu) << 16);
+    for (int cg = 0; cg < kDmaRowB / 128; ++cg) {
+      dma_load16(src_lo + 128 * cg, dst + 4096 * cg);
+      dma_load16(src_hi + 128 * cg, dst + 4096 * cg + 1024);
+    }
+    // row mask of the whole tile: lane r (< 32) checks row r
+    const int e_m = t * kMlaRows + (lane & 31);
+    return (uint32_t)__ballot(entry_ok(e_m, entry_raw(e_m)));
   };
   // Retire the Q and extent loads: from here on the wave's outstanding
   // vector-memory operations are gathers and index-chunk loads only.
   wait_vmcnt<0>();
 
-  // K operand of k-step ks (global 18d+ks): row c32, chunk 36d + 2ks + h.
-  // c&3 = 2(ks&1) + h, so even and odd k-steps use two bases.
-  int kb[2];
+  // K operand of k-step ks (global 18d+ks): row c32, chunk c = 36d + 2ks + h;
+  // for ks = 4j + p the chunk group is that of 36d + 2p + h plus j and the
+  // slot that of 36d + 2p + h, so four bases and immediate offsets 4096j.
+  int kb[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int c = 36 * d + 2 * p + h;
+    kb[p] = tile_block(c32 >> 3, c >> 3) + 128 * (c32 & 7) + 16 * ((c & 7) ^ tile_swz(c32));
+  }
+  // V^T operand of M-tile m (dims 256d+32m..), k-step kk, half e: 16-lane group b = lane>>4
+  // reads row 16kk + 8e + 4h + (L>>2) at dims 256d + 32m + 16(b&1) + 4(L&3), L = lane&15;
+  // chunk group 4d + (m>>1), slot from 4(m&1) + 2(b&1) + ((L&3)>>1): four bases
+  // (e, m&1) and immediate offsets 4096(m>>1) + 2048kk.
+  const int L = lane & 15;
+  int vb[2][2];
 #pragma unroll
   for (int e = 0; e < 2; ++e)
-    kb[e] = (kPairLoads * 1024) * d + (c32 >> 4) * 1024 + 256 * (2 * e + h) + 16 * ((c32 & 15) ^ (4 * (2 * e + h)));
-  // V^T operand of M-tile m (dims 256d+32m..), k-step kk, half e: 16-lane group b = lane>>4
-  // reads rows 16kk + 8e + 4h + (L>>2) at dims 32m + 16(b&1) + 4(L&3), L = lane&15.
-  const int L = lane & 15, pL = (L >> 1) & 1;
-  // c&3 = 2(b&1) + pL and r&15 = 8e + 4h + (L>>2), so the two row halves e use two bases.
-  int vb[2];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int b1 = (lane >> 4) & 1;
-    vb[e] = (kPairMt * 2048) * d + 512 * b1 + 256 * pL + 16 * (8 * (e ^ b1) + 4 * (h ^ pL) + (L >> 2)) + 8 * (L & 1);
-  }
+    for (int m1 = 0; m1 < 2; ++m1) {
+      const int r = 8 * e + 4 * h + (L >> 2);
+      const int c7 = 4 * m1 + 2 * ((lane >> 4) & 1) + ((L & 3) >> 1);
+      vb[e][m1] = tile_block(e, 4 * d) + 128 * (r & 7) + 16 * (c7 ^ tile_swz(r)) + 8 * (L & 1);
+    }
 
   f32x16v o[kPairMt][2];
   float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.f;
@@ -576,7 +577,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
 
       // ---- partial S^T over this wave's dims, both head blocks ----
       constexpr int kPf = 3;
-      auto kread = [&](int ks) { return *reinterpret_cast<const bf16x8*>(tile + kb[ks & 1] + (ks >> 1) * 2048); };
+      auto kread = [&](int ks) { return *reinterpret_cast<const bf16x8*>(tile + kb[ks & 3] + (ks >> 2) * 4096); };
       f32x16v s_own, s_oth;
       bf16x8 kop[kPf];
 #pragma unroll
@@ -643,9 +644,9 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
 
       // ---- O^T += V^T . P^T over this wave's dims, both head blocks ----
       auto vread = [&](int m, int kk) {
-        const int off = 2048 * m + 1024 * kk;
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb[0] + off));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb[1] + off));
+        const int off = 4096 * (m >> 1) + 2048 * kk;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb[0][m & 1] + off));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb[1][m & 1] + off));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       bf16x8 vop[2][2];
@@ -765,10 +766,10 @@ hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
     const dim3 block2(kPairThreads);
     if (A.out_f32)
       hipLaunchKernelGGL((sparse_mla_bf16_kernel<true>), grid, block2, 0, st, A.q, kv, (int)A.n_k, A.idx, A.n_q,
-                         A.top_k, scale_log2, A.out, A.lse, A.q_pos);
+                         A.top_k, scale_log2, A.out, A.lse);
     else
       hipLaunchKernelGGL((sparse_mla_bf16_kernel<false>), grid, block2, 0, st, A.q, kv, (int)A.n_k, A.idx,
-                         A.n_q, A.top_k, scale_log2, A.out, A.lse, A.q_pos);
+                         A.n_q, A.top_k, scale_log2, A.out, A.lse);
   }
   return hipGetLastError();
 }

@@ -25,6 +25,7 @@ def _idx_lists(n_q, n_k, top_k, seed, invalid=False):
         idx[1, 3] = n_k + 5          # out of range: skipped
         idx[2, :] = -1               # empty set
         idx[3, ::2] = -1             # padding in the middle
+        idx[5, :64] = -1             # leading padding: the first tiles hold no valid row
     return idx
 
 
