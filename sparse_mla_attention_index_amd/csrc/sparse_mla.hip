@@ -343,6 +343,17 @@ __device__ __forceinline__ void dma_load16(const void* gaddr, uint32_t lds_base)
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
                : "memory", "m0");
 }
+// The same from gaddr + OFF (OFF < 4096), with OFF in the instruction's
+// offset field so that loads along one row share an address register.  The
+// instruction adds its offset to the LDS address as well, so M0 is lowered
+// by OFF (lds_base >= OFF).
+template <int OFF>
+__device__ __forceinline__ void dma_load16_at(const void* gaddr, uint32_t lds_base) {
+  static_assert(OFF >= 0 && OFF < 4096, "global instruction offset range");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(gaddr), "s"(lds_base - OFF),
+               "i"(OFF)
+               : "memory", "m0");
+}
 
 // v_mfma_f32_32x32x16_bf16 with its accumulator in VGPRs.  The compiler
 // emits every MFMA builtin of a kernel that also uses AGPRs in the AGPR
@@ -513,11 +524,14 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     const uint8_t* src_lo = kv_bytes + (int64_t)(ok_lo ? raw_lo : 0) * kDmaRowB + c_lo;
     const uint8_t* src_hi = kv_bytes + (int64_t)(ok_hi ? raw_hi : 0) * kDmaRowB + c_hi;
     const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)&s_kv[b][tile_block(2 * d, 0)];
-#pragma unroll
-    for (int cg = 0; cg < kDmaRowB / 128; ++cg) {
-      dma_load16(src_lo + 128 * cg, dst + 4096 * cg);
-      dma_load16(src_hi + 128 * cg, dst + 4096 * cg + 1024);
-    }
+    // chunk group cg of both rows: global offset 128 cg, LDS block (rg, cg)
+#define SMA_TILE_CG(cg)                                           \
+  dma_load16_at<128 * (cg)>(src_lo, dst + 4096 * (cg));           \
+  dma_load16_at<128 * (cg)>(src_hi, dst + 4096 * (cg) + 1024);
+    SMA_TILE_CG(0) SMA_TILE_CG(1) SMA_TILE_CG(2) SMA_TILE_CG(3) SMA_TILE_CG(4)
+    SMA_TILE_CG(5) SMA_TILE_CG(6) SMA_TILE_CG(7) SMA_TILE_CG(8)
+#undef SMA_TILE_CG
+    static_assert(kDmaRowB / 128 == 9, "nine chunk groups per row");
     // row mask of the whole tile: lane r (< 32) checks row r
     const int e_m = t * kMlaRows + (lane & 31);
     return (uint32_t)__ballot(entry_ok(e_m, entry_raw(e_m)));
@@ -612,23 +626,29 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
       }
 
       // ---- softmax weights of the own heads: element j is row 8(j>>2) + 4h + (j&3) ----
+      // A full tile (every row valid; the mask is the same in every lane)
+      // needs no masking.  Weights are 2^(s tau log2e - m_ref); scale_log2 > 0,
+      // so the row maximum is taken on the raw sums.  No clamp is needed: a
+      // weight can only exceed 2^kRefGap when `far` is set, and then the
+      // sweep's results are discarded.
+      const bool full = mask == 0xFFFFFFFFu;
       const uint32_t mh = mask >> (4 * h);
-      float x[16], mx = -INFINITY;
+      auto row_ok = [&](int j) { return full || ((mh >> (8 * (j >> 2) + (j & 3))) & 1u); };
+      float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const bool v = (mh >> (8 * (j >> 2) + (j & 3))) & 1u;
-        x[j] = v ? s_own[j] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[j]);
-      }
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, row_ok(j) ? s_own[j] : -INFINITY);
+      mx *= scale_log2;
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       if (m_ref == -INFINITY) m_ref = mx;   // first tile holding a valid row
       m_max = fmaxf(m_max, mx);
       far |= mx > m_ref + kRefGap;
       bf16x8 pb[2];
       float ps = 0.f;
+      const float neg_ref = -m_ref;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float pe = x[j] > -INFINITY ? __builtin_amdgcn_exp2f(fminf(x[j] - m_ref, kRefGap)) : 0.f;
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s_own[j], scale_log2, neg_ref));
+        if (!full) pe = row_ok(j) ? pe : 0.f;
         ps += pe;
         pb[j >> 3][j & 7] = (__bf16)pe;
       }
