@@ -154,7 +154,12 @@ def main():
     out = torch.empty((n_q, 64, 512), dtype=out_dtype, device=dev)
     idx = torch.empty((n_q, w.top_k), dtype=torch.int32, device=dev)
     blk = n_q if args.score_block <= 0 else max(64, min(args.score_block, n_q))
-    ws = torch.empty(blk * n_k * 4 + n_q * 4 + 4096, dtype=torch.uint8, device=dev)
+    # one score block of `blk` rows, the split top-k's buffers for that block
+    # (rows longer than 65,536 scores), the PCP share's positions
+    score_b = (blk * n_k * 4 + 255) // 256 * 256
+    topk_b = sma.workspace_bytes(sma._lib.SMA_OP_TOPK, blk, n_k, w.top_k)
+    ws = torch.empty(score_b + topk_b + (n_q * 4 + 255) // 256 * 256 + 4096, dtype=torch.uint8, device=dev)
+    topk_ws = ws[score_b:score_b + topk_b] if topk_b > 0 else None
 
     if args.workload == "pcp":
         def run_share(r, qi_, w_, q_):
@@ -207,7 +212,8 @@ def main():
     nb = scores.shape[0]
     t_idx = timed(lambda: sma.index_scores(q_idx[:nb], wts[:nb], k_idx, q_pos[:nb], k_scale=k_scale,
                                            scores=scores), reps) * (n_q / nb)
-    t_topk = timed(lambda: sma.topk_select(scores, q_pos[:nb], w.top_k, idx=idx[:nb]), reps) * (n_q / nb)
+    t_topk = timed(lambda: sma.topk_select(scores, q_pos[:nb], w.top_k, idx=idx[:nb], workspace=topk_ws),
+                   reps) * (n_q / nb)
     # the full index list for the attention kernel comes from the timed steps
     step()
     t_mla = timed(lambda: sma.sparse_mla_prefill(q, kv, idx, w.sm_scale, kv_scale=kv_scale, out=out,

@@ -131,8 +131,12 @@ def index_scores(q_idx, w, k_idx, q_pos, *, k_scale=None, scores=None):
     return scores
 
 
-def topk_select(scores, q_pos, top_k: int, *, n_k: int | None = None, idx=None):
-    """Top-k positions per row, ascending, -1 padded: int32 [n_q, top_k]."""
+def topk_select(scores, q_pos, top_k: int, *, n_k: int | None = None, idx=None, workspace=None):
+    """Top-k positions per row, ascending, -1 padded: int32 [n_q, top_k].
+
+    `workspace` (uint8 device tensor): rows longer than 65,536 scores are
+    split across workgroups when it holds workspace_bytes(SMA_OP_TOPK, ...)
+    bytes; one of that size is allocated here when none is given."""
     n_q = scores.shape[0]
     n_k = scores.shape[1] if n_k is None else n_k
     if scores.dtype != torch.float32 or scores.stride(1) != 1:
@@ -141,8 +145,13 @@ def topk_select(scores, q_pos, top_k: int, *, n_k: int | None = None, idx=None):
         raise ValueError("q_pos must be contiguous int32")
     if idx is None:
         idx = torch.empty((n_q, top_k), dtype=torch.int32, device=scores.device)
+    if workspace is None and n_q > 0:
+        nbytes = workspace_bytes(SMA_OP_TOPK, n_q, n_k, top_k)
+        if nbytes > 0:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=scores.device)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().sma_topk_select(_ptr(scores), scores.stride(0), _ptr(q_pos), n_q, n_k, top_k, _ptr(idx),
-                                 None, 0, _stream(scores.device)))
+                                 _ptr(workspace), ws_n, _stream(scores.device)))
     return idx
 
 

@@ -120,6 +120,15 @@ sma::IdxArgs idx_args(const uint16_t* q_idx, const float* w, int64_t w_stride, c
   return a;
 }
 
+// Workspace of one block of qb query rows in the composed path: their scores
+// plus, for rows longer than the on-chip top-k holds, the split top-k's
+// buffers.
+size_t score_block_bytes(int64_t qb, int64_t n_k, int32_t top_k) {
+  size_t b = align_up((size_t)qb * (size_t)n_k * 4, 256);
+  if (sma::topk_multi_wanted(n_k)) b += align_up(sma::topk_multi_bytes((int32_t)qb, n_k, top_k), 256);
+  return b;
+}
+
 size_t prefill_fixed_bytes(int32_t n_q, int32_t top_k, bool need_idx, bool need_pos) {
   size_t b = 0;
   if (need_pos) b += align_up((size_t)n_q * 4, 256);
@@ -135,19 +144,24 @@ sma_status run_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride, 
                        int64_t n_k, int32_t h_idx, int32_t d_idx, int32_t top_k, float sm_scale,
                        void* out, int32_t out_dtype, float* lse, int32_t* idx, uint8_t* score_ws,
                        size_t score_ws_bytes, hipStream_t st) {
-  const size_t row_bytes = (size_t)n_k * 4;
+  // the largest block of query rows (all of them, or a multiple of 16) whose
+  // scores and top-k buffers fit
+  const size_t row_bytes = score_block_bytes(1, n_k, top_k);
   int64_t qb = (int64_t)(score_ws_bytes / row_bytes);
   if (qb >= n_q) qb = n_q;
   else qb = qb / 16 * 16;
+  while (qb > 0 && score_block_bytes(qb, n_k, top_k) > score_ws_bytes) qb = qb > 16 ? qb - 16 : qb - 1;
   if (qb < 1) return fail(SMA_ERR_WORKSPACE, "workspace holds no score block");
   float* scores = reinterpret_cast<float*>(score_ws);
+  uint8_t* topk_ws = score_ws + align_up((size_t)qb * (size_t)n_k * 4, 256);
+  const size_t topk_ws_bytes = score_ws_bytes - align_up((size_t)qb * (size_t)n_k * 4, 256);
   for (int64_t q0 = 0; q0 < n_q; q0 += qb) {
     const int32_t nb = (int32_t)((n_q - q0) < qb ? (n_q - q0) : qb);
     sma::IdxArgs ia = idx_args(q_idx + q0 * h_idx * d_idx, w + q0 * w_stride, w_stride, k_idx, k_scale,
                                k_dtype, pos + q0, nb, n_k, h_idx, d_idx, scores, n_k);
     hipError_t e = sma::launch_index_scores(ia, st);
     if (e != hipSuccess) return hip_fail(e, "index_scores launch");
-    sma::TopkArgs ta{scores, n_k, pos + q0, nb, n_k, top_k, idx + q0 * top_k};
+    sma::TopkArgs ta{scores, n_k, pos + q0, nb, n_k, top_k, idx + q0 * top_k, topk_ws, topk_ws_bytes};
     e = sma::launch_topk(ta, st);
     if (e != hipSuccess) return hip_fail(e, "topk launch");
   }
@@ -184,16 +198,15 @@ sma_status sma_index_scores(const uint16_t* q_idx, const float* w, int64_t w_str
 sma_status sma_topk_select(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t n_q,
                            int64_t n_k, int32_t top_k, int32_t* idx, void* ws, size_t ws_bytes,
                            void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   g_err.clear();
   sma_status s = validate_topk(n_q, n_k, top_k);
   if (s != SMA_OK) return s;
   SMA_CHECK(ld_scores >= n_k, "ld_scores = %lld < n_k = %lld", (long long)ld_scores, (long long)n_k);
   if (n_q > 0) SMA_CHECK(scores && q_pos && idx, "scores, q_pos and idx must be non-NULL");
   if (n_q == 0) return SMA_OK;
+  if (ws) SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
   if ((s = check_device()) != SMA_OK) return s;
-  sma::TopkArgs a{scores, ld_scores, q_pos, n_q, n_k, top_k, idx};
+  sma::TopkArgs a{scores, ld_scores, q_pos, n_q, n_k, top_k, idx, ws, ws ? ws_bytes : 0};
   hipError_t e = sma::launch_topk(a, (hipStream_t)stream);
   return e == hipSuccess ? SMA_OK : hip_fail(e, "topk launch");
 }
@@ -222,15 +235,15 @@ size_t sma_workspace_bytes(int32_t op, int32_t n_q, int64_t n_k, int32_t top_k, 
   if (n_q < 0 || n_k < 1 || top_k < 1) return 0;
   switch (op) {
     case SMA_OP_INDEX_SCORES:
-    case SMA_OP_TOPK:
       return 0;
+    case SMA_OP_TOPK:   // optional: lets rows longer than 65,536 scores split across workgroups
+      return sma::topk_multi_wanted(n_k) ? align_up(sma::topk_multi_bytes(n_q, n_k, top_k), 256) : 0;
     case SMA_OP_SPARSE_MLA:   // optional: lets small FP8 batches split each query's rows
       return align_up(sma::mla_split_bytes(n_q, sma::mla_split_count(n_q, top_k, true)), 256);
     case SMA_OP_PREFILL:
     case SMA_OP_PCP_SHARE: {
       const int32_t blk = n_q < kMinScoreBlock ? n_q : kMinScoreBlock;
-      return prefill_fixed_bytes(n_q, top_k, true, op == SMA_OP_PCP_SHARE) +
-             align_up((size_t)blk * (size_t)n_k * 4, 256);
+      return prefill_fixed_bytes(n_q, top_k, true, op == SMA_OP_PCP_SHARE) + score_block_bytes(blk, n_k, top_k);
     }
     default:
       return 0;
@@ -252,7 +265,7 @@ sma_status sma_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride, 
   if (n_q == 0) return SMA_OK;
   const size_t fixed = prefill_fixed_bytes(n_q, top_k, idx_out == nullptr, false);
   const int32_t blk = n_q < kMinScoreBlock ? n_q : kMinScoreBlock;
-  const size_t need = fixed + align_up((size_t)blk * (size_t)n_k * 4, 256);
+  const size_t need = fixed + score_block_bytes(blk, n_k, top_k);
   if (ws_bytes < need || (ws == nullptr && need > 0))
     return fail(SMA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
   SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
@@ -292,7 +305,7 @@ sma_status sma_pcp_rank_share(int32_t rank, int32_t pcp_size, int64_t L_total, c
     return s;
   const size_t fixed = prefill_fixed_bytes(n_q, top_k, idx_share == nullptr, true);
   const int32_t blk = n_q < kMinScoreBlock ? n_q : kMinScoreBlock;
-  const size_t need = fixed + align_up((size_t)blk * (size_t)L_total * 4, 256);
+  const size_t need = fixed + score_block_bytes(blk, L_total, top_k);
   if (ws_bytes < need || ws == nullptr)
     return fail(SMA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
   SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");

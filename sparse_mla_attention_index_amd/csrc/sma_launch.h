@@ -30,6 +30,10 @@ struct TopkArgs {
   int64_t n_k;
   int32_t top_k;
   int32_t* idx;
+  // Workspace for rows split across workgroups (may be null: then long rows
+  // take the single-workgroup streaming kernel).
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
 };
 
 struct MlaArgs {
@@ -56,6 +60,11 @@ size_t mla_split_bytes(int n_q, int n_split);
 
 hipError_t launch_index_scores(const IdxArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// Rows longer than the on-chip top-k holds (n_k > 65,536) are split across
+// workgroups when the workspace holds topk_multi_bytes(n_q, n_k, top_k).
+bool topk_multi_wanted(int64_t n_k);
+size_t topk_multi_bytes(int32_t n_q, int64_t n_k, int32_t top_k);
+hipError_t launch_topk_multi(const TopkArgs& a, void* ws, hipStream_t s);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t s);
 hipError_t launch_pcp_positions(int32_t* pos, int32_t rank, int32_t pcp_size, int64_t L_total,
                                 hipStream_t s);

@@ -631,8 +631,12 @@ __global__ __launch_bounds__(THREADS, 1) void topk_chip_kernel(const float* __re
   }
 }
 
+bool topk_multi_wanted(int64_t n_k) { return n_k > 4 * 1024 * 16; }
+
 hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   if (A.n_q <= 0) return hipSuccess;
+  if (topk_multi_wanted(A.n_k) && A.ws && A.ws_bytes >= topk_multi_bytes(A.n_q, A.n_k, A.top_k))
+    return launch_topk_multi(A, A.ws, st);
   const dim3 grid((unsigned)A.n_q);
   // Rows that fit are read once and kept on chip: 1024 x 16 or 1024 x 32
   // keys in registers, or 1024 x 32 in registers plus 1024 x 32 in LDS (read

@@ -32,9 +32,17 @@ def test_library_exports_every_symbol():
 def test_workspace_sizes():
     # prefill: idx list + one 64-row score block (256-byte aligned pieces)
     assert sma.workspace_bytes(_lib.SMA_OP_PREFILL, 65536, 65536, 2048) == 65536 * 2048 * 4 + 64 * 65536 * 4
+    # rows longer than 65,536 scores: the 64-row block also holds the split
+    # top-k's buffers (per row: 32-B state, 2,048-bin histogram, and per
+    # 16,384-score chunk two counts, top_k positions and top_k (position, key))
+    def split_topk(n_q, n_k, k):
+        nch = -(-n_k // 16384)
+        return n_q * 32 + n_q * 2048 * 4 + n_q * nch * 8 + n_q * nch * k * 4 + n_q * nch * k * 8
     assert sma.workspace_bytes(_lib.SMA_OP_PCP_SHARE, 16384, 131072, 2048) == \
-        16384 * 4 + 16384 * 2048 * 4 + 64 * 131072 * 4
+        16384 * 4 + 16384 * 2048 * 4 + 64 * 131072 * 4 + split_topk(64, 131072, 2048)
     assert sma.workspace_bytes(_lib.SMA_OP_TOPK, 10, 10, 5) == 0
+    assert sma.workspace_bytes(_lib.SMA_OP_TOPK, 10, 65536, 2048) == 0
+    assert sma.workspace_bytes(_lib.SMA_OP_TOPK, 64, 1 << 20, 2048) == split_topk(64, 1 << 20, 2048)
     assert sma.workspace_bytes(_lib.SMA_OP_PREFILL, 10, 100, 5) == 256 + 4096   # 200 B and 4000 B, 256-aligned
     assert sma.workspace_bytes(99, 10, 10, 5) == 0
     # attention partials for small batches: 64 queries on 256 CUs take 8 slices of
