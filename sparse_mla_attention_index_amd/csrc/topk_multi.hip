@@ -77,20 +77,34 @@ __device__ __forceinline__ void excl_scan2(uint32_t a, uint32_t b, uint32_t& ea,
   __syncthreads();
 }
 
-// The 4 keys of positions p0..p0+3 (key 0 past the row end: below every real key).
+// The 4 keys of positions p0..p0+3 (p0 a multiple of 4; key 0 past the row
+// end: below every real key).  Branch-free, so that a thread's loads are all
+// in flight together: the address is clamped into the row and the keys past
+// its end masked.  With 16-byte aligned rows and a row stride that is a
+// multiple of 4, a vector at p0 <= n - 1 stays inside the row's storage.
 template <bool ALIGNED>
 __device__ __forceinline__ u32x4 load_keys4(const float* __restrict__ src, int p0, int n) {
   f32x4 x;
-  if (ALIGNED && p0 + 3 < n) {
-    x = *reinterpret_cast<const f32x4*>(src + p0);
+  if constexpr (ALIGNED) {
+    x = *reinterpret_cast<const f32x4*>(src + min(p0, (n - 1) & ~3));
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = p0 + e < n ? src[p0 + e] : 0.f;
+    for (int e = 0; e < 4; ++e) x[e] = src[min(p0 + e, n - 1)];
   }
   u32x4 k;
 #pragma unroll
   for (int e = 0; e < 4; ++e) k[e] = p0 + e < n ? score_key(x[e]) : 0u;
   return k;
+}
+
+constexpr int kSteps = kChunk / (4 * kTkmThreads);   // 8 vectors of 4 scores per thread
+
+// Every key of this thread in chunk [base, base + kChunk): vector i covers
+// positions base + 4 kTkmThreads i + 4 tid + 0..3.
+template <bool ALIGNED>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ src, int base, int n, u32x4 (&k)[kSteps]) {
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) k[i] = load_keys4<ALIGNED>(src, base + i * 4 * kTkmThreads + 4 * (int)threadIdx.x, n);
 }
 
 __global__ void tkm_init(RowState* __restrict__ st, uint32_t* __restrict__ ghist, const int32_t* __restrict__ q_pos,
@@ -122,17 +136,15 @@ __global__ __launch_bounds__(kTkmThreads) void tkm_minmax(const float* __restric
   if (base >= n) return;
   const float* src = scores + (int64_t)row * ld;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll 2
-  for (int s = 0; s < kChunk / (4 * kTkmThreads); ++s) {
-    const int p0 = base + s * 4 * kTkmThreads + 4 * threadIdx.x;
-    if (p0 >= n) break;
-    const u32x4 k = load_keys4<ALIGNED>(src, p0, n);
+  u32x4 kc[kSteps];
+  load_chunk<ALIGNED>(src, base, n, kc);
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      kmin = min(kmin, k[e] ? k[e] : 0xFFFFFFFFu);
-      kmax = max(kmax, k[e]);
+      kmin = min(kmin, kc[i][e] ? kc[i][e] : 0xFFFFFFFFu);
+      kmax = max(kmax, kc[i][e]);
     }
-  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -172,18 +184,16 @@ __global__ __launch_bounds__(kTkmThreads) void tkm_hist(const float* __restrict_
   if (base >= n) return;
   const int shift = range_shift(s.lo, s.hi);
   const int nbins = (int)((s.hi - s.lo) >> shift) + 1;
+  const float* src = scores + (int64_t)row * ld;
+  u32x4 kc[kSteps];
+  load_chunk<ALIGNED>(src, base, n, kc);
   for (int b = threadIdx.x; b < nbins; b += kTkmThreads) h[b] = 0u;
   __syncthreads();
-  const float* src = scores + (int64_t)row * ld;
-#pragma unroll 2
-  for (int i = 0; i < kChunk / (4 * kTkmThreads); ++i) {
-    const int p0 = base + i * 4 * kTkmThreads + 4 * threadIdx.x;
-    if (p0 >= n) break;
-    const u32x4 k = load_keys4<ALIGNED>(src, p0, n);
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (k[e] >= s.lo && k[e] <= s.hi) atomicAdd(&h[(k[e] - s.lo) >> shift], 1u);
-  }
+      if (kc[i][e] >= s.lo && kc[i][e] <= s.hi) atomicAdd(&h[(kc[i][e] - s.lo) >> shift], 1u);
   __syncthreads();
   uint32_t* g = ghist + (int64_t)row * kTkmBins;
   for (int b = threadIdx.x; b < nbins; b += kTkmThreads)
@@ -259,10 +269,13 @@ __global__ __launch_bounds__(kTkmThreads) void tkm_collect(const float* __restri
   int32_t* ab = abuf + ((int64_t)row * nch + c) * K;
   uint2* cb = cbuf + ((int64_t)row * nch + c) * K;
   uint32_t na = 0, nc = 0;
-  for (int i = 0; i < kChunk / (4 * kTkmThreads); ++i) {
+  // vector i + 1 is loaded while vector i is ranked
+  u32x4 k_next = load_keys4<ALIGNED>(src, base + 4 * (int)threadIdx.x, n);
+  for (int i = 0; i < kSteps; ++i) {
     const int p0 = base + i * 4 * kTkmThreads + 4 * threadIdx.x;
     if (base + i * 4 * kTkmThreads >= n) break;   // uniform
-    const u32x4 k = load_keys4<ALIGNED>(src, p0, n);
+    const u32x4 k = k_next;
+    if (i + 1 < kSteps) k_next = load_keys4<ALIGNED>(src, p0 + 4 * kTkmThreads, n);
     uint32_t a = 0, b = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
