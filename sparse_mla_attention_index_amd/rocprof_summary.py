@@ -23,7 +23,18 @@ kernel changed since the counters were taken;
       --fetch ... --write ... --kernel idx_score --kernel topk --kernel sparse_mla \\
       --copy-bytes N --out profiles/<name>.md --title "..." --command "<cmd>" ...
 
-writes the same scaled figures for several kernels as a Markdown table.
+writes the same scaled figures for several kernels as a Markdown table;
+
+  python -m sparse_mla_attention_index_amd.rocprof_summary counters \\
+      --pmc <run 1>/run_counter_collection.csv --pmc <run 2>/... \\
+      --stats <trace>/run_kernel_stats.csv --kernel idx_score ... --out profiles/<name>.md
+
+derives per kernel from SQ/GRBM counters (averaged per dispatch) and the
+trace's average duration: the shader clock (GRBM_GUI_ACTIVE summed over the
+8 XCDs / 8 / duration), the matrix-core busy fraction
+(SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x clock cycles)), and the share of wave
+time spent waiting (SQ_WAIT_ANY, SQ_WAIT_INST_ANY; SQ_WAVE_CYCLES counts in
+units of 4 cycles like them).
 """
 import argparse
 import csv
@@ -110,9 +121,51 @@ def cmd_table(a):
     for k in a.kernel:
         f_kib, nf = _kernel_avg(fetch, k)
         w_kib, _ = _kernel_avg(write, k)
-        name = next(n for (n, _) in fetch.values() if k in n).split("(")[0]
+        name = next(n for (n, _) in fetch.values() if k in n).replace("(anonymous namespace)::", "").split("(")[0]
         lines.append(f"| `{name}` | {nf} | {f_kib:.0f} | {w_kib:.0f} | {f_kib * 1024 * f_factor / 1e9:.2f} | "
                      f"{w_kib * 1024 * w_factor / 1e9:.2f} |")
+    if a.note:
+        lines += ["", a.note]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cmd_counters(a):
+    vals = defaultdict(dict)
+    for path in a.pmc:
+        with open(path, newline="") as f:
+            rows = list(csv.DictReader(f))
+        for k in a.kernel:
+            acc, disp = defaultdict(float), set()
+            for r in rows:
+                if k in r["Kernel_Name"]:
+                    acc[r["Counter_Name"]] += float(r["Counter_Value"])
+                    disp.add(r["Dispatch_Id"])
+            for c, v in acc.items():
+                vals[k][c] = v / max(len(disp), 1)
+    dur = {}
+    with open(a.stats, newline="") as f:
+        for r in csv.DictReader(f):
+            for k in a.kernel:
+                if k in r["Name"]:
+                    dur[k] = float(r["AverageNs"]) * 1e-9
+    lines = [f"# {a.title}", "", "Commands (from the repository root, on the GPU host):", "", "```"]
+    lines += list(a.command) + ["```", ""]
+    lines += ["| kernel | avg ms | clock GHz | MFMA busy | MFMA insts | VALU insts | LDS insts | wait (waitcnt/barrier) | wait (dependency) |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    for k in a.kernel:
+        v, t = vals[k], dur.get(k)
+        if not t or "GRBM_GUI_ACTIVE" not in v:
+            continue
+        cyc = v["GRBM_GUI_ACTIVE"] / a.xcds
+        ghz = cyc / t / 1e9
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (a.simds * cyc)
+        wave = v.get("SQ_WAVE_CYCLES", 0.0) or 1.0
+        name = next((r for r in [k]), k)
+        lines.append(f"| `{name}` | {t * 1e3:.2f} | {ghz:.2f} | {100 * busy:.0f}% | {v.get('SQ_INSTS_MFMA', 0):.3g} | "
+                     f"{v.get('SQ_INSTS_VALU', 0):.3g} | {v.get('SQ_INSTS_LDS', 0):.3g} | "
+                     f"{100 * v.get('SQ_WAIT_ANY', 0) / wave:.0f}% | {100 * v.get('SQ_WAIT_INST_ANY', 0) / wave:.0f}% |")
     if a.note:
         lines += ["", a.note]
     with open(a.out, "w") as f:
@@ -130,7 +183,7 @@ def cmd_stats(a):
     lines += [c for c in a.command] + ["```", ""]
     lines += ["| kernel | calls | average ms | min ms | max ms | share |", "|---|---|---|---|---|---|"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        name = r["Name"].split("(")[0]
+        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0]
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
                      f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | "
                      f"{100 * float(r['TotalDurationNs']) / tot:.1f}% |")
@@ -168,8 +221,18 @@ def main(argv=None):
     b.add_argument("--title", required=True)
     b.add_argument("--command", action="append", default=[])
     b.add_argument("--note", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("--pmc", action="append", required=True)
+    c.add_argument("--stats", required=True)
+    c.add_argument("--kernel", action="append", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", action="append", default=[])
+    c.add_argument("--note", default="")
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--simds", type=int, default=1024)
     a = ap.parse_args(argv)
-    {"traffic": cmd_traffic, "table": cmd_table, "stats": cmd_stats}[a.cmd](a)
+    {"traffic": cmd_traffic, "table": cmd_table, "stats": cmd_stats, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
