@@ -709,23 +709,48 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
   if (h == 0) s_l[32 * d + c32] = l_tot;
   block_sync_lds();
   const float inv[2] = {1.f / l_tot, 1.f / s_l[32 * (d ^ 1) + c32]};
+  if constexpr (OUT_F32) {
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int64_t row_off = ((int64_t)qi * kHeads + 32 * (d ^ hb) + c32) * kDv + 256 * d + 4 * h;
+    for (int hb = 0; hb < 2; ++hb) {
+      const int64_t row_off = ((int64_t)qi * kHeads + 32 * (d ^ hb) + c32) * kDv + 256 * d + 4 * h;
 #pragma unroll
-    for (int m = 0; m < kPairMt; ++m)
+      for (int m = 0; m < kPairMt; ++m)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 r = f32x4{o[m][hb][4 * jj], o[m][hb][4 * jj + 1], o[m][hb][4 * jj + 2], o[m][hb][4 * jj + 3]} *
-                        inv[hb];
-        const int64_t off = row_off + 32 * m + 8 * jj;
-        if constexpr (OUT_F32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = r;
-        } else {
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + off) =
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 r = f32x4{o[m][hb][4 * jj], o[m][hb][4 * jj + 1], o[m][hb][4 * jj + 2], o[m][hb][4 * jj + 3]} *
+                          inv[hb];
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + row_off + 32 * m + 8 * jj) = r;
+        }
+    }
+  } else {
+    // The query's bf16 output [64 heads][512 dims] is one contiguous 64 KiB
+    // block: stage it in the (now idle) tile ring as rows of 1 KiB whose
+    // 16-byte chunk c sits at slot c ^ (head & 63), then write it with
+    // 16-byte stores by consecutive lanes.  Lanes of one accumulator store
+    // hold 32 heads, which the slot rotation spreads over the banks.
+    uint8_t* obuf = &s_kv[0][0];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int head = 32 * (d ^ hb) + c32;
+      uint8_t* orow = obuf + head * 1024 + 8 * h;
+#pragma unroll
+      for (int m = 0; m < kPairMt; ++m)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 r = f32x4{o[m][hb][4 * jj], o[m][hb][4 * jj + 1], o[m][hb][4 * jj + 2], o[m][hb][4 * jj + 3]} *
+                          inv[hb];
+          const int chunk = 32 * d + 4 * m + jj;   // dims 8 chunk .. 8 chunk + 7
+          *reinterpret_cast<u32x2*>(orow + 16 * (chunk ^ (head & 63))) =
               u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
         }
-      }
+    }
+    block_sync_lds();
+    uint8_t* og = reinterpret_cast<uint8_t*>(out) + (int64_t)qi * kHeads * kDv * 2;
+#pragma unroll 8
+    for (int i = 0; i < kHeads * kDv * 2 / 16 / kPairThreads; ++i) {
+      const int c = tid + kPairThreads * i, head = c >> 6, cc = c & 63;
+      *reinterpret_cast<u32x4*>(og + 16 * c) = *reinterpret_cast<const u32x4*>(obuf + head * 1024 + 16 * (cc ^ (head & 63)));
+    }
   }
   if (lse && h == 0) lse[(int64_t)qi * kHeads + 32 * d + c32] = (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
 }
