@@ -373,6 +373,11 @@ __device__ __forceinline__ void mfma32_vgpr(f32x16v_t& acc, const bf16x8& a, con
 __device__ __forceinline__ void mfma32_vgpr_drain(f32x16v_t& x, f32x16v_t& y) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
+// Wait states after the last MFMA into x when one more MFMA is issued
+// before x is read (16 + 1 >= 11).
+__device__ __forceinline__ void mfma32_vgpr_drain1(f32x16v_t& x) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x));
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -597,18 +602,24 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
 #pragma unroll
       for (int ks = 0; ks < kPf; ++ks) kop[ks] = kread(ks);
 #pragma unroll
-      for (int ks = 0; ks < kPairKs; ++ks) {
+      for (int ks = 0; ks < kPairKs - 2; ++ks) {
         const bf16x8 a = kop[ks % kPf];
         if (ks + kPf < kPairKs) kop[ks % kPf] = kread(ks + kPf);
         if (ks == 0) {
-          mfma32_vgpr_first(s_own, a, qf[0][0]);
           mfma32_vgpr_first(s_oth, a, qf[1][0]);
+          mfma32_vgpr_first(s_own, a, qf[0][0]);
         } else {
-          mfma32_vgpr(s_own, a, qf[0][ks]);
           mfma32_vgpr(s_oth, a, qf[1][ks]);
+          mfma32_vgpr(s_own, a, qf[0][ks]);
         }
       }
-      mfma32_vgpr_drain(s_own, s_oth);
+      // The partner's block finishes first, so its half-sum goes out while
+      // the last own-block MFMAs run.
+      constexpr int kA = kPairKs - 2, kB = kPairKs - 1;
+      mfma32_vgpr(s_oth, kop[kA % kPf], qf[1][kA]);
+      mfma32_vgpr(s_oth, kop[kB % kPf], qf[1][kB]);
+      mfma32_vgpr(s_own, kop[kA % kPf], qf[0][kA]);
+      mfma32_vgpr_drain1(s_oth);
 
       // ---- exchange half-sums: wave 1 writes into the (now dead) rope blocks, wave 0 into s_x ----
       uint8_t* xw = d ? tile + kRopeOff : s_x;   // written by this wave
@@ -617,13 +628,16 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
       for (int p = 0; p < 4; ++p)
         *reinterpret_cast<f32x4*>(xw + 1024 * p + 16 * lane) =
             f32x4{s_oth[4 * p], s_oth[4 * p + 1], s_oth[4 * p + 2], s_oth[4 * p + 3]};
+      mfma32_vgpr(s_own, kop[kB % kPf], qf[0][kB]);
       block_sync_lds();
+      f32x4 y[4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const f32x4 y = *reinterpret_cast<const f32x4*>(xr + 1024 * p + 16 * lane);
+      for (int p = 0; p < 4; ++p) y[p] = *reinterpret_cast<const f32x4*>(xr + 1024 * p + 16 * lane);
+      mfma32_vgpr_drain(s_own, s_oth);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s_own[4 * p + r] += y[r];
-      }
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_own[4 * p + r] += y[p][r];
 
       // ---- softmax weights of the own heads: element j is row 8(j>>2) + 4h + (j&3) ----
       // A full tile (every row valid; the mask is the same in every lane)
@@ -638,7 +652,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, row_ok(j) ? s_own[j] : -INFINITY);
       mx *= scale_log2;
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      {   // lanes l and l ^ 32 hold the same head: v_permlane32_swap hands each the other's value
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
       if (m_ref == -INFINITY) m_ref = mx;   // first tile holding a valid row
       m_max = fmaxf(m_max, mx);
       far |= mx > m_ref + kRefGap;
