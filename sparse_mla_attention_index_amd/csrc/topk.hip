@@ -278,15 +278,17 @@ __global__ __launch_bounds__(THREADS, 1) void topk_stream_kernel(const float* __
 }
 
 // ---------------------------------------------------------------------------
-// Filtered top-k for 16-byte aligned rows of up to 65,536 scores.  One
-// 256-thread workgroup per row (four per CU), one pass over the row:
+// Filtered top-k for 16-byte aligned rows (16-bit positions and four
+// workgroups per CU up to 65,536 scores; 32-bit positions, a 4,096-score
+// sample and three per CU beyond).  One 256-thread workgroup per row, one
+// pass over the row:
 //  1. a row longer than kFtCap takes a threshold from a sample of itself:
-//     128 clusters of 16 consecutive scores spread evenly over the row.  One
-//     2,048-bin histogram over the samples' key range finds the bin holding
-//     the r0-th largest sample; its lower edge is the threshold, r0 chosen so
-//     that about 1.3 mu + 3 sqrt(mu) samples lie at or above it (mu = K * 2048
-//     / n, the samples expected among the row's K largest).  A shorter row
-//     keeps every key;
+//     S/16 clusters of 16 consecutive scores spread evenly over the row (S =
+//     2,048 or 4,096 samples).  One 2,048-bin histogram over the samples' key
+//     range finds the bin holding the r0-th largest sample; its lower edge is
+//     the threshold, r0 chosen so that about 1.3 mu + 3 sqrt(mu) samples lie at
+//     or above it (mu = K * S / n, the samples expected among the row's K
+//     largest).  A shorter row keeps every key;
 //  2. one coalesced pass keeps every position whose score is at or above the
 //     threshold, with its key, in ascending position order: wave ballots and
 //     a per-chunk table of wave counts give each kept position its LDS slot;
@@ -301,8 +303,7 @@ __global__ __launch_bounds__(THREADS, 1) void topk_stream_kernel(const float* __
 constexpr int kFtThreads = 256;
 constexpr int kFtWaves = kFtThreads / 64;
 constexpr int kFtCap = 5120;                      // kept positions held in LDS
-constexpr int kFtClusters = 128, kFtClusterLen = 16;
-constexpr int kFtSamples = kFtClusters * kFtClusterLen;
+constexpr int kFtClusterLen = 16;                 // consecutive scores per sample cluster
 constexpr int kFtU = 8;                           // 16-byte loads per thread per chunk
 constexpr int kFtChunk = kFtThreads * 4 * kFtU;   // 8,192 positions
 constexpr int kFtKeep = kFtCap / kFtThreads;      // kept keys per thread in the final select
@@ -394,12 +395,17 @@ __device__ uint32_t ft_round(const uint32_t (&key)[M], uint32_t& lo, uint32_t& h
   return in_bin;
 }
 
-__global__ __launch_bounds__(kFtThreads, 4) void topk_filter_kernel(const float* __restrict__ scores, int64_t ld,
-                                                                 const int32_t* __restrict__ q_pos, int n_k,
-                                                                 int K, int32_t* __restrict__ idx) {
+// PosT holds a position (uint16_t for rows of at most 65,536 scores); SPT
+// samples per thread (SPT * 256 in all).
+template <typename PosT, int SPT, int OCC>
+__global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                      const int32_t* __restrict__ q_pos, int n_k,
+                                                                      int K, int32_t* __restrict__ idx) {
+  constexpr int kSamples = kFtThreads * SPT, kClusters = kSamples / kFtClusterLen;
+  static_assert(SPT % 4 == 0 && kFtClusterLen % SPT == 0, "whole 16-byte loads within one cluster");
   __shared__ TopkShared<kFtThreads> sh;
   __shared__ uint32_t ckey[kFtCap];   // keys of the kept positions (the streaming fallback's scratch)
-  __shared__ uint16_t cpos[kFtCap];   // kept positions, ascending
+  __shared__ PosT cpos[kFtCap];       // kept positions, ascending
   __shared__ uint32_t tab[2][kFtU][kFtWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;
@@ -428,25 +434,27 @@ __global__ __launch_bounds__(kFtThreads, 4) void topk_filter_kernel(const float*
   };
 
   // ---- 1. threshold (the sample loads go out with the first chunk's) ----
-  f32x4 sa = {}, sb = {};
+  f32x4 sv[SPT / 4] = {};
   const bool sampled = n > kFtCap;
-  if (sampled) {
-    const int c = tid >> 1;
-    const int start = (int)(((int64_t)c * (n - kFtClusterLen)) / (kFtClusters - 1)) & ~3;
-    sa = *reinterpret_cast<const f32x4*>(src + start + 8 * (tid & 1));
-    sb = *reinterpret_cast<const f32x4*>(src + start + 8 * (tid & 1) + 4);
+  if (sampled) {   // thread t loads SPT consecutive scores of cluster t*SPT/16
+    const int c = tid * SPT / kFtClusterLen;
+    const int start = (int)(((int64_t)c * (n - kFtClusterLen)) / (kClusters - 1)) & ~3;
+#pragma unroll
+    for (int v = 0; v < SPT / 4; ++v)
+      sv[v] = *reinterpret_cast<const f32x4*>(src + start + (tid * SPT) % kFtClusterLen + 4 * v);
   }
   f32x4 xa[kFtU], xb[kFtU];
   load(0, xa);
   float thr = -INFINITY;
   if (sampled) {
-    const uint32_t sk[8] = {score_key(sa[0]), score_key(sa[1]), score_key(sa[2]), score_key(sa[3]),
-                            score_key(sb[0]), score_key(sb[1]), score_key(sb[2]), score_key(sb[3])};
-    const float mu = (float)K * (float)kFtSamples / (float)n;
-    const uint32_t r0 = (uint32_t)fminf(ceilf(1.3f * mu + 3.f * sqrtf(mu) + 4.f), (float)kFtSamples);
+    uint32_t sk[SPT];
+#pragma unroll
+    for (int v = 0; v < SPT; ++v) sk[v] = score_key(sv[v >> 2][v & 3]);
+    const float mu = (float)K * (float)kSamples / (float)n;
+    const uint32_t r0 = (uint32_t)fminf(ceilf(1.3f * mu + 3.f * sqrtf(mu) + 4.f), (float)kSamples);
     uint32_t lo, hi, rem = r0;
-    ft_range<8>(sk, lo, hi, sh);
-    if (hi != lo) ft_round<8>(sk, lo, hi, rem, sh);
+    ft_range<SPT>(sk, lo, hi, sh);
+    if (hi != lo) ft_round<SPT>(sk, lo, hi, rem, sh);
     thr = key_score(lo);   // at least r0 samples lie at or above it
   }
 
@@ -488,7 +496,7 @@ __global__ __launch_bounds__(kFtThreads, 4) void topk_filter_kernel(const float*
       for (int e = 0; e < 4; ++e)
         if ((fl[u] >> e) & 1u) {
           if (off < (uint32_t)kFtCap) {
-            cpos[off] = (uint16_t)(c0 + 1024 * u + 4 * tid + e);
+            cpos[off] = (PosT)(c0 + 1024 * u + 4 * tid + e);
             ckey[off] = score_key(x[u][e]);
           }
           ++off;
@@ -580,18 +588,38 @@ __global__ __launch_bounds__(kFtThreads, 4) void topk_filter_kernel(const float*
 
 bool topk_multi_wanted(int64_t n_k) { return n_k > 4 * 1024 * 16; }
 
+// Compute units of the current device (cached per device).
+static int topk_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   if (A.n_q <= 0) return hipSuccess;
+  const bool rows_aligned = (reinterpret_cast<uintptr_t>(A.scores) % 16 == 0) && (A.ld % 4 == 0);
+  const dim3 grid((unsigned)A.n_q);
+  // Long rows with enough of them to fill the device (a few workgroups per
+  // CU) take the filtered kernel too, with 32-bit positions.
+  if (rows_aligned && A.n_k > 65536 && A.n_k <= INT32_MAX && A.n_q >= 4 * topk_cu_count()) {
+    hipLaunchKernelGGL((topk_filter_kernel<uint32_t, 16, 3>), grid, dim3(kFtThreads), 0, st, A.scores, A.ld,
+                       A.q_pos, (int)A.n_k, A.top_k, A.idx);
+    return hipGetLastError();
+  }
   if (topk_multi_wanted(A.n_k) && A.ws && A.ws_bytes >= topk_multi_bytes(A.n_q, A.n_k, A.top_k))
     return launch_topk_multi(A, A.ws, st);
-  const dim3 grid((unsigned)A.n_q);
   // 16-byte aligned rows of up to 65,536 scores take the filtered kernel
   // (one pass over the row); longer or unaligned rows are streamed from
   // memory in every pass.
-  const bool rows_aligned = (reinterpret_cast<uintptr_t>(A.scores) % 16 == 0) && (A.ld % 4 == 0);
   if (rows_aligned && A.n_k <= 65536) {
-    hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kFtThreads), 0, st, A.scores, A.ld, A.q_pos, (int)A.n_k,
-                       A.top_k, A.idx);
+    hipLaunchKernelGGL((topk_filter_kernel<uint16_t, 8, 4>), grid, dim3(kFtThreads), 0, st, A.scores, A.ld,
+                       A.q_pos, (int)A.n_k, A.top_k, A.idx);
   } else {
     hipLaunchKernelGGL((topk_stream_kernel<1024>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
                        (int)A.n_k, A.top_k, A.idx);

@@ -55,3 +55,18 @@ def test_topk_clamped_positions():
     assert np.all(got[0] == -1) and np.all(got[1] == -1)
     assert np.array_equal(got[2], oracle.topk_row(sc[2], top_k))
     assert np.array_equal(got[3], oracle.topk_row(sc[3, :51], top_k))
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_topk_many_long_rows(kind):
+    """Rows longer than 65,536 scores, enough of them to fill the device (the
+    one-workgroup-per-row path with 32-bit positions); rows checked on a
+    spread sample."""
+    n_rows, n_k, top_k = 1100, 70000, 2048
+    sc = synth.random_scores(11 + len(kind), n_rows, n_k, kind)
+    pos = _positions(n_rows, n_k, top_k, 5)
+    pos[-4:] = [n_k - 1, n_k - 2, 65536, 65535]
+    got = host(sma.topk_select(dev(sc), dev(pos), top_k))
+    for r in list(range(0, n_rows, 37)) + list(range(n_rows - 4, n_rows)):
+        ref = oracle.topk_row(sc[r, : pos[r] + 1], top_k)
+        assert np.array_equal(got[r], ref), (kind, r, pos[r])
