@@ -23,6 +23,9 @@ Sources, by page and section:
 * same page, footnote 1: QK runs over 576 dims, PV over 512; indices are
   4 bytes; q and o are bf16.
 * same page, footnote 3: an FP8 key is 128 values plus a 4-byte scale.
+* same page, section "DCP : sharder aussi le cache KV": tokens are dealt
+  round-robin over the ranks, each rank attends over its own shard and the
+  partial results are merged by their log-sum-exp.
 * DeepSeek multi-node deployment page (Perplexity), sections
   "Parallélisme de tenseurs" and "Travaux futurs": the latent is shared by
   all heads; kv_b_proj maps it to each head; decode absorbs the projection.
@@ -182,6 +185,51 @@ def prefill(q_idx, w, k_idx, q, kv, q_pos, top_k: int, sm_scale: float):
     idx = topk_select(scores, top_k)
     out, lse = sparse_mla(q, kv, idx, sm_scale)
     return scores, idx, out, lse
+
+
+def dcp_shard_rows(rank: int, dcp_size: int, kv: np.ndarray) -> np.ndarray:
+    """The latent rows one DCP rank stores: tokens are dealt round-robin over
+    the ranks, so rank r holds tokens r, r + P, r + 2P, ... (local row j is
+    token j*P + r) (GLM-5.3 part 2, "DCP : sharder aussi le cache KV")."""
+    if not (0 <= rank < dcp_size):
+        raise ValueError("rank out of range")
+    return kv[rank::dcp_size]
+
+
+def dcp_shard_partial(rank: int, dcp_size: int, q: np.ndarray, kv: np.ndarray, idx: np.ndarray,
+                      sm_scale: float):
+    """One DCP rank's partial attention: over the selected tokens it stores
+    (those s in S_i with s mod P = rank), the same softmax attention as
+    sparse_mla, with its own normaliser; a query none of whose tokens the
+    rank stores gets o = 0 and lse = -inf.  In decode each rank attends over
+    its own shard and the partial results are merged by their log-sum-exp
+    (same page and section).  kv is the whole context here; the rank reads
+    the same rows from its shard (dcp_shard_rows)."""
+    if not (0 <= rank < dcp_size):
+        raise ValueError("rank out of range")
+    idx = np.asarray(idx)
+    own = np.where((idx >= 0) & (idx % dcp_size == rank), idx, -1)
+    return sparse_mla(q, kv, own, sm_scale)
+
+
+def lse_merge(parts: np.ndarray, lses: np.ndarray):
+    """Merge partial attentions by log-sum-exp (same page and section): with
+    L = log sum_r exp(lse_r), o = sum_r exp(lse_r - L) * o_r and the merged
+    log-sum-exp is L.  parts [P, n_q, H, D], lses [P, n_q, H]; a (query,
+    head) whose partials are all empty (lse = -inf) gets o = 0, L = -inf."""
+    parts = np.asarray(parts, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    m = lses.max(axis=0)                                   # [n_q, H]
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    a = np.where(np.isfinite(lses), np.exp(lses - m_safe[None]), 0.0)   # [P, n_q, H]
+    s = a.sum(axis=0)
+    out = np.zeros(parts.shape[1:], dtype=np.float64)
+    lse = np.full(m.shape, -np.inf, dtype=np.float64)
+    w = np.where(finite[None], a / np.where(finite, s, 1.0)[None], 0.0)
+    out[...] = np.einsum("pqh,pqhd->qhd", w, parts)
+    lse[finite] = m[finite] + np.log(s[finite])
+    return out, lse
 
 
 def pcp_positions(rank: int, pcp_size: int, L_total: int) -> np.ndarray:
