@@ -68,7 +68,8 @@ typedef enum {
   SMA_OP_TOPK = 1,
   SMA_OP_SPARSE_MLA = 2,
   SMA_OP_PREFILL = 3,
-  SMA_OP_PCP_SHARE = 4
+  SMA_OP_PCP_SHARE = 4,
+  SMA_OP_DCP_PARTIAL = 5
 } sma_op;
 
 /* Fixed MLA geometry: 64 heads share one 576-wide latent row (512 latent +
@@ -187,6 +188,47 @@ sma_status sma_pcp_rank_share(int32_t rank, int32_t pcp_size, int64_t L_total,
                               int32_t kv_dtype, int32_t h_idx, int32_t d_idx, int32_t top_k,
                               float sm_scale, void* out_share, int32_t out_dtype, float* lse_share,
                               int32_t* idx_share, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sma_dcp_shard_partial — one DCP rank's share of sparse MLA (same article,
+ * "DCP : sharder aussi le cache KV": tokens are dealt round-robin over the
+ * dcp_size ranks, so rank r stores tokens r, r + P, r + 2P, ...; in decode
+ * each rank attends over its own shard and the partial results are merged
+ * by their log-sum-exp, sma_lse_merge).
+ *
+ *  kv_local  [n_k_local, 576] the rank's shard: local row j is token
+ *            j*dcp_size + rank (bf16, or e4m3fn codes with kv_scale_local)
+ *  idx       [n_q, top_k] int32 global token positions of each query's
+ *            selection (as sma_topk_select writes them); the rank keeps the
+ *            entries it stores, other entries, negative ones and rows past
+ *            the shard are skipped
+ *  out_partial [n_q, 64, 512] fp32 and lse_partial [n_q, 64] fp32: the
+ *            attention over the kept rows alone, normalised over them, as in
+ *            sma_sparse_mla_prefill; a query the rank stores none of gets
+ *            0 and -inf
+ *  ws        at least sma_workspace_bytes(SMA_OP_DCP_PARTIAL, n_q, n_k_local,
+ *            top_k, 0, 0) bytes, 256-byte aligned (the rank's local index
+ *            list, and an FP8 batch's row slices)
+ *  Requires 0 <= rank < dcp_size.
+ */
+sma_status sma_dcp_shard_partial(int32_t rank, int32_t dcp_size, const uint16_t* q, const void* kv_local,
+                                 const float* kv_scale_local, int32_t kv_dtype, int64_t n_k_local,
+                                 const int32_t* idx, int32_t n_q, int32_t top_k, float sm_scale,
+                                 float* out_partial, float* lse_partial, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/*
+ * sma_lse_merge — merge n_part partial attention results by their
+ * log-sum-exp (same article and section):
+ *   L[i,h]   = log(sum_r exp(lses[r,i,h]))
+ *   out[i,h] = sum_r exp(lses[r,i,h] - L[i,h]) * parts[r,i,h,:]
+ *  parts [n_part, n_q, 64, 512] fp32, lses [n_part, n_q, 64] fp32 (natural
+ *  log, -inf for an empty partial); out [n_q, 64, 512] bf16 or fp32 (out_dtype);
+ *  lse_out [n_q, 64] fp32 or NULL.  A (query, head) whose partials are all
+ *  empty gets 0 and -inf.  Requires 1 <= n_part <= 64.
+ */
+sma_status sma_lse_merge(const float* parts, const float* lses, int32_t n_part, int32_t n_q, void* out,
+                         int32_t out_dtype, float* lse_out, void* stream);
 
 /* Minimum workspace in bytes for `op` (an sma_op) at these sizes.  For
  * SMA_OP_PREFILL / SMA_OP_PCP_SHARE, n_q is the number of query rows and the

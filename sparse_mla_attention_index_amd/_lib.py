@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libsma.so")
 
 SMA_DT_BF16, SMA_DT_FP8_E4M3, SMA_DT_FP32 = 0, 1, 2
 SMA_OP_INDEX_SCORES, SMA_OP_TOPK, SMA_OP_SPARSE_MLA, SMA_OP_PREFILL, SMA_OP_PCP_SHARE = 0, 1, 2, 3, 4
+SMA_OP_DCP_PARTIAL = 5
 HEADS, D_QK, D_V = 64, 576, 512
 
 # (name, restype, argtypes) of every entry point declared in include/sma.h
@@ -31,6 +32,9 @@ SIGNATURES = {
                            _P, _I32, _P, _P, _P, _SZ, _P]),
     "sma_pcp_rank_share": (_I32, [_I32, _I32, _I64, _P, _P, _I64, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
                                   _I32, _F, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "sma_dcp_shard_partial": (_I32, [_I32, _I32, _P, _P, _P, _I32, _I64, _P, _I32, _I32, _F, _P, _P, _P, _SZ,
+                                     _P]),
+    "sma_lse_merge": (_I32, [_P, _P, _I32, _I32, _P, _I32, _P, _P]),
     "sma_workspace_bytes": (_SZ, [_I32, _I32, _I64, _I32, _I32, _I32]),
     "sma_last_error": (ctypes.c_char_p, []),
     "sma_version": (_I32, []),
@@ -228,3 +232,46 @@ def pcp_rank_share(rank: int, pcp_size: int, q_idx_share, w_share, k_idx, q_shar
                                     _ptr(lse), _ptr(idx_share), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(dev)))
     return out, lse, idx_share
+
+
+def dcp_shard_partial(rank: int, dcp_size: int, q, kv_local, idx, sm_scale: float, *, kv_scale_local=None,
+                      out=None, lse=None, workspace=None):
+    """One DCP rank's partial sparse MLA over the tokens of idx (global
+    positions) it stores; kv_local row j is token j*dcp_size + rank.  Returns
+    (out [n_q, 64, 512] fp32, lse [n_q, 64] fp32)."""
+    n_q = q.shape[0]
+    _bf16(q, "q")
+    kdt = _keys(kv_local, kv_scale_local, "kv_local")
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32")
+    dev = q.device
+    if out is None:
+        out = torch.empty((n_q, HEADS, D_V), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((n_q, HEADS), dtype=torch.float32, device=dev)
+    top_k = idx.shape[1]
+    if workspace is None:
+        nbytes = workspace_bytes(SMA_OP_DCP_PARTIAL, n_q, kv_local.shape[0], top_k)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().sma_dcp_shard_partial(rank, dcp_size, _ptr(q), _ptr(kv_local), _ptr(kv_scale_local), kdt,
+                                       kv_local.shape[0], _ptr(idx), n_q, top_k, float(sm_scale), _ptr(out),
+                                       _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(dev)))
+    return out, lse
+
+
+def lse_merge(parts, lses, *, out=None, out_dtype=torch.bfloat16, want_lse: bool = False):
+    """Merge partial results parts [P, n_q, 64, 512] fp32 with their lses
+    [P, n_q, 64] by log-sum-exp; returns (out [n_q, 64, 512], lse or None)."""
+    if parts.dtype != torch.float32 or lses.dtype != torch.float32:
+        raise ValueError("parts and lses must be float32")
+    if not parts.is_contiguous() or not lses.is_contiguous():
+        raise ValueError("parts and lses must be contiguous")
+    n_part, n_q = parts.shape[0], parts.shape[1]
+    dev = parts.device
+    if out is None:
+        out = torch.empty((n_q, HEADS, D_V), dtype=out_dtype, device=dev)
+    odt = SMA_DT_FP32 if out.dtype == torch.float32 else SMA_DT_BF16
+    lse = torch.empty((n_q, HEADS), dtype=torch.float32, device=dev) if want_lse else None
+    _check(lib().sma_lse_merge(_ptr(parts), _ptr(lses), n_part, n_q, _ptr(out), odt, _ptr(lse), _stream(dev)))
+    return out, lse

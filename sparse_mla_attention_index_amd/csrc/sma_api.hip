@@ -228,6 +228,53 @@ sma_status sma_sparse_mla_prefill(const uint16_t* q, const void* kv, const float
   return e == hipSuccess ? SMA_OK : hip_fail(e, "sparse_mla launch");
 }
 
+sma_status sma_dcp_shard_partial(int32_t rank, int32_t dcp_size, const uint16_t* q, const void* kv_local,
+                                 const float* kv_scale_local, int32_t kv_dtype, int64_t n_k_local,
+                                 const int32_t* idx, int32_t n_q, int32_t top_k, float sm_scale,
+                                 float* out_partial, float* lse_partial, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  g_err.clear();
+  SMA_CHECK(dcp_size >= 1, "dcp_size = %d < 1", dcp_size);
+  SMA_CHECK(rank >= 0 && rank < dcp_size, "rank = %d not in [0, %d)", rank, dcp_size);
+  sma_status s = validate_mla(q, kv_local, kv_scale_local, kv_dtype, n_k_local, idx, n_q, top_k, sm_scale,
+                              out_partial, SMA_DT_FP32, false);
+  if (s != SMA_OK) return s;
+  if (n_q == 0) return SMA_OK;
+  SMA_CHECK(lse_partial != nullptr, "lse_partial is NULL");
+  const size_t idx_bytes = align_up((size_t)n_q * (size_t)top_k * 4, 256);
+  if (ws == nullptr || ws_bytes < idx_bytes)
+    return fail(SMA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws ? ws_bytes : 0, idx_bytes);
+  SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
+  if ((s = check_device()) != SMA_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* local = static_cast<int32_t*>(ws);
+  hipError_t e = sma::launch_dcp_local_idx(idx, n_q, top_k, rank, dcp_size, n_k_local, local, st);
+  if (e != hipSuccess) return hip_fail(e, "dcp_local_idx launch");
+  sma::MlaArgs a{q, kv_local, kv_scale_local, kv_dtype == SMA_DT_FP8_E4M3, n_k_local, local, n_q, top_k,
+                 sm_scale, out_partial, true, lse_partial, static_cast<uint8_t*>(ws) + idx_bytes,
+                 ws_bytes - idx_bytes};
+  e = sma::launch_sparse_mla(a, st);
+  return e == hipSuccess ? SMA_OK : hip_fail(e, "sparse_mla launch");
+}
+
+sma_status sma_lse_merge(const float* parts, const float* lses, int32_t n_part, int32_t n_q, void* out,
+                         int32_t out_dtype, float* lse_out, void* stream) {
+  g_err.clear();
+  SMA_CHECK(n_part >= 1 && n_part <= sma::kMaxMergeParts, "n_part = %d out of [1, %d]", n_part,
+            sma::kMaxMergeParts);
+  SMA_CHECK(n_q >= 0, "n_q = %d < 0", n_q);
+  SMA_CHECK(out_dtype == SMA_DT_BF16 || out_dtype == SMA_DT_FP32, "out_dtype = %d", out_dtype);
+  if (n_q == 0) return SMA_OK;
+  SMA_CHECK(parts && lses && out, "parts, lses and out must be non-NULL");
+  SMA_CHECK(aligned(parts, 16), "parts not 16-byte aligned");
+  SMA_CHECK(aligned(out, out_dtype == SMA_DT_FP32 ? 16 : 8), "out not aligned");
+  sma_status s = check_device();
+  if (s != SMA_OK) return s;
+  hipError_t e = sma::launch_lse_merge(parts, lses, n_part, n_q, out, out_dtype == SMA_DT_FP32, lse_out,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? SMA_OK : hip_fail(e, "lse_merge launch");
+}
+
 size_t sma_workspace_bytes(int32_t op, int32_t n_q, int64_t n_k, int32_t top_k, int32_t h_idx,
                            int32_t d_idx) {
   (void)h_idx;
@@ -240,6 +287,9 @@ size_t sma_workspace_bytes(int32_t op, int32_t n_q, int64_t n_k, int32_t top_k, 
       return sma::topk_multi_wanted(n_k) ? align_up(sma::topk_multi_bytes(n_q, n_k, top_k), 256) : 0;
     case SMA_OP_SPARSE_MLA:   // optional: lets small FP8 batches split each query's rows
       return align_up(sma::mla_split_bytes(n_q, sma::mla_split_count(n_q, top_k, true)), 256);
+    case SMA_OP_DCP_PARTIAL:   // the rank's local index list, then an FP8 batch's row slices
+      return align_up((size_t)n_q * (size_t)top_k * 4, 256) +
+             align_up(sma::mla_split_bytes(n_q, sma::mla_split_count(n_q, top_k, true)), 256);
     case SMA_OP_PREFILL:
     case SMA_OP_PCP_SHARE: {
       const int32_t blk = n_q < kMinScoreBlock ? n_q : kMinScoreBlock;

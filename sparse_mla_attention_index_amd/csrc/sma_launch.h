@@ -66,6 +66,16 @@ bool topk_multi_wanted(int64_t n_k);
 size_t topk_multi_bytes(int32_t n_q, int64_t n_k, int32_t top_k);
 hipError_t launch_topk_multi(const TopkArgs& a, void* ws, hipStream_t s);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t s);
+
+// DCP share: the tokens of a query's selection that rank `rank` of P stores
+// (s mod P == rank), as local rows s / P, ascending, -1 padded.
+hipError_t launch_dcp_local_idx(const int32_t* idx, int n_q, int K, int rank, int P, int64_t n_k_local,
+                                int32_t* local, hipStream_t s);
+// Log-sum-exp merge of n_part partial results [n_part, n_q, 64, 512] fp32
+// with their lse [n_part, n_q, 64].
+constexpr int kMaxMergeParts = 64;
+hipError_t launch_lse_merge(const float* parts, const float* lses, int n_part, int n_q, void* out, bool out_f32,
+                            float* lse_out, hipStream_t s);
 hipError_t launch_pcp_positions(int32_t* pos, int32_t rank, int32_t pcp_size, int64_t L_total,
                                 hipStream_t s);
 

@@ -106,3 +106,25 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libsma.so"))
     with pytest.raises(ImportError):
         _lib.lib()
+
+
+@pytest.mark.parametrize("rank,P,msg", [(3, 3, "rank"), (-1, 3, "rank"), (0, 0, "dcp_size")])
+def test_dcp_validation(rank, P, msg):
+    r = sma.lib().sma_dcp_shard_partial(rank, P, FAKE, FAKE, None, 0, 100, FAKE, 1, 8, 0.1, FAKE, FAKE, FAKE,
+                                        1 << 20, None)
+    assert r == -1 and msg in sma.last_error()
+
+
+def test_dcp_workspace_check():
+    r = sma.lib().sma_dcp_shard_partial(0, 2, FAKE, FAKE, None, 0, 100, FAKE, 4, 8, 0.1, FAKE, FAKE, FAKE, 64,
+                                        None)
+    assert r == -3 and "workspace" in sma.last_error()
+    # the local index list (256-byte aligned), then an FP8 batch's row slices
+    assert sma.workspace_bytes(_lib.SMA_OP_DCP_PARTIAL, 4, 100, 8) >= 256
+    assert sma.workspace_bytes(_lib.SMA_OP_DCP_PARTIAL, 65536, 65536, 2048) == 65536 * 2048 * 4
+
+
+@pytest.mark.parametrize("n_part,odt,msg", [(0, 0, "n_part"), (65, 0, "n_part"), (2, 7, "out_dtype")])
+def test_lse_merge_validation(n_part, odt, msg):
+    r = sma.lib().sma_lse_merge(FAKE, FAKE, n_part, 3, FAKE, odt, None, None)
+    assert r == -1 and msg in sma.last_error()
