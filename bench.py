@@ -227,6 +227,40 @@ def main():
         pcp = {"rank7_ms": round(t_r7, 3), "rank0_ms": round(t_r0, 3), "rank0_over_rank7": round(t_r0 / t_r7, 4)}
         _log(f"pcp: rank0 {t_r0:.2f} ms, rank7 {t_r7:.2f} ms")
 
+    dcp = None
+    if args.workload == "decode":
+        # One-GPU DCP8 share: the KV dealt round-robin to 8 shards, each
+        # rank's partial attention on its shard over the same selection, and
+        # the log-sum-exp merge, against the unsharded call.
+        P = 8
+        shards = [(kv[r::P].contiguous(), kv_scale[r::P].contiguous() if kv_scale is not None else None)
+                  for r in range(P)]
+        parts = torch.empty((P, n_q, 64, 512), dtype=torch.float32, device=dev)
+        lses = torch.empty((P, n_q, 64), dtype=torch.float32, device=dev)
+        dws_n = max(sma.workspace_bytes(sma._lib.SMA_OP_DCP_PARTIAL, n_q, shards[0][0].shape[0], w.top_k), 1)
+        dws = torch.empty(dws_n, dtype=torch.uint8, device=dev)
+        merged = torch.empty((n_q, 64, 512), dtype=out.dtype, device=dev)
+        unsharded = torch.empty((n_q, 64, 512), dtype=torch.float32, device=dev)
+
+        def dcp_partials():
+            for r, (kvl, kvs) in enumerate(shards):
+                sma.dcp_shard_partial(r, P, q, kvl, idx, w.sm_scale, kv_scale_local=kvs, out=parts[r], lse=lses[r],
+                                      workspace=dws)
+
+        t_part = timed(dcp_partials, reps)
+        t_merge = timed(lambda: sma.lse_merge(parts, lses, out=merged), reps)
+        sma.sparse_mla_prefill(q, kv, idx, w.sm_scale, kv_scale=kv_scale, out=unsharded, workspace=ws)
+        dcp_partials()
+        sma.lse_merge(parts, lses, out=merged)
+        torch.cuda.synchronize()
+        d_err = float((merged.float() - unsharded).abs().max() / unsharded.abs().max())
+        dcp = {"ranks": P, "partials_ms": round(t_part, 4), "per_rank_partial_ms": round(t_part / P, 4),
+               "merge_ms": round(t_merge, 4),
+               "total_ms": round(t_part + t_merge, 4), "unsharded_sparse_mla_ms": round(t_mla, 4),
+               "merged_vs_unsharded_max_err_rel": d_err}
+        _log(f"dcp{P}: partials {t_part:.3f} ms + merge {t_merge:.3f} ms (unsharded {t_mla:.3f} ms), "
+             f"max err {d_err:.2e}")
+
     pairs = acc.causal_pairs(pos_np)
     key_bytes = (w.d_idx + 4) if w.fp8 else 2 * w.d_idx
     row_bytes = (576 + 4) if w.fp8 else 1152
@@ -322,6 +356,8 @@ def main():
     }
     if pcp:
         res["pcp_load_balance"] = pcp
+    if dcp:
+        res["dcp_share"] = dcp
     print(json.dumps(res), flush=True)
 
 

@@ -225,7 +225,7 @@ sma_status sma_dcp_shard_partial(int32_t rank, int32_t dcp_size, const uint16_t*
  *  parts [n_part, n_q, 64, 512] fp32, lses [n_part, n_q, 64] fp32 (natural
  *  log, -inf for an empty partial); out [n_q, 64, 512] bf16 or fp32 (out_dtype);
  *  lse_out [n_q, 64] fp32 or NULL.  A (query, head) whose partials are all
- *  empty gets 0 and -inf.  Requires 1 <= n_part <= 64.
+ *  empty gets 0 and -inf.  Requires 1 <= n_part <= 64 and n_q <= 2^28.
  */
 sma_status sma_lse_merge(const float* parts, const float* lses, int32_t n_part, int32_t n_q, void* out,
                          int32_t out_dtype, float* lse_out, void* stream);

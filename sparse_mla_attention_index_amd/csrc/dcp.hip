@@ -59,43 +59,47 @@ __global__ __launch_bounds__(kDcpThreads) void dcp_local_idx_kernel(const int32_
   for (int e = (int)total + tid; e < K; e += kDcpThreads) out[e] = -1;
 }
 
-// One workgroup per query: the per-(rank, head) weights go to LDS, then each
-// thread merges consecutive 16-byte pieces of the query's [64, 512] outputs.
+// One workgroup per (query, group of 8 heads), so that a decode-sized batch
+// still spreads over the CUs: the per-(rank, head) weights go to LDS, then
+// each thread merges 16-byte pieces of the group's [8, 512] outputs.
+constexpr int kMergeHeads = 8;
 template <bool OUT_F32>
 __global__ __launch_bounds__(kDcpThreads) void lse_merge_kernel(const float* __restrict__ parts,
                                                                 const float* __restrict__ lses, int n_part,
                                                                 int n_q, void* __restrict__ out,
                                                                 float* __restrict__ lse_out) {
-  __shared__ float s_w[kMaxMergeParts][kHeads];
-  const int tid = threadIdx.x, qi = blockIdx.x;
+  __shared__ float s_w[kMaxMergeParts][kMergeHeads];
+  const int tid = threadIdx.x;
+  const int qi = blockIdx.x / (kHeads / kMergeHeads), h0 = kMergeHeads * (blockIdx.x % (kHeads / kMergeHeads));
   const int64_t part_stride = (int64_t)n_q * kHeads * kDv;
-  if (tid < kHeads) {
+  if (tid < kMergeHeads) {
+    const int h = h0 + tid;
     float m = -INFINITY;
-    for (int r = 0; r < n_part; ++r) m = fmaxf(m, lses[((int64_t)r * n_q + qi) * kHeads + tid]);
+    for (int r = 0; r < n_part; ++r) m = fmaxf(m, lses[((int64_t)r * n_q + qi) * kHeads + h]);
     float s = 0.f;
     for (int r = 0; r < n_part; ++r) {
-      const float l = lses[((int64_t)r * n_q + qi) * kHeads + tid];
+      const float l = lses[((int64_t)r * n_q + qi) * kHeads + h];
       const float a = m == -INFINITY || l == -INFINITY ? 0.f : __expf(l - m);
       s_w[r][tid] = a;
       s += a;
     }
     const float inv = s > 0.f ? 1.f / s : 0.f;
     for (int r = 0; r < n_part; ++r) s_w[r][tid] *= inv;
-    if (lse_out) lse_out[(int64_t)qi * kHeads + tid] = s > 0.f ? m + __logf(s) : -INFINITY;
+    if (lse_out) lse_out[(int64_t)qi * kHeads + h] = s > 0.f ? m + __logf(s) : -INFINITY;
   }
   __syncthreads();
-  const float* base = parts + (int64_t)qi * kHeads * kDv;
-  for (int f = tid; f < kHeads * kDv / 4; f += kDcpThreads) {
-    const int h = f / (kDv / 4);
+  const int64_t base = ((int64_t)qi * kHeads + h0) * kDv;   // first float of the group
+  for (int f = tid; f < kMergeHeads * kDv / 4; f += kDcpThreads) {
+    const int hh = f / (kDv / 4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int r = 0; r < n_part; ++r) {
-      const float wr = s_w[r][h];
-      if (wr != 0.f) acc += wr * reinterpret_cast<const f32x4*>(base + r * part_stride)[f];
+      const float wr = s_w[r][hh];
+      if (wr != 0.f) acc += wr * reinterpret_cast<const f32x4*>(parts + r * part_stride + base)[f];
     }
     if constexpr (OUT_F32) {
-      reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)qi * kHeads * kDv)[f] = acc;
+      reinterpret_cast<f32x4*>(static_cast<float*>(out) + base)[f] = acc;
     } else {
-      reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (int64_t)qi * kHeads * kDv)[f] =
+      reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + base)[f] =
           u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
     }
   }
@@ -112,12 +116,13 @@ hipError_t launch_dcp_local_idx(const int32_t* idx, int n_q, int K, int rank, in
 hipError_t launch_lse_merge(const float* parts, const float* lses, int n_part, int n_q, void* out, bool out_f32,
                             float* lse_out, hipStream_t st) {
   if (n_q <= 0) return hipSuccess;
+  const dim3 grid((unsigned)n_q * (kHeads / kMergeHeads));
   if (out_f32)
-    hipLaunchKernelGGL((lse_merge_kernel<true>), dim3((unsigned)n_q), dim3(kDcpThreads), 0, st, parts, lses,
-                       n_part, n_q, out, lse_out);
+    hipLaunchKernelGGL((lse_merge_kernel<true>), grid, dim3(kDcpThreads), 0, st, parts, lses, n_part, n_q, out,
+                       lse_out);
   else
-    hipLaunchKernelGGL((lse_merge_kernel<false>), dim3((unsigned)n_q), dim3(kDcpThreads), 0, st, parts, lses,
-                       n_part, n_q, out, lse_out);
+    hipLaunchKernelGGL((lse_merge_kernel<false>), grid, dim3(kDcpThreads), 0, st, parts, lses, n_part, n_q, out,
+                       lse_out);
   return hipGetLastError();
 }
 

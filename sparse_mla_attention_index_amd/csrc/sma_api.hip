@@ -262,7 +262,7 @@ sma_status sma_lse_merge(const float* parts, const float* lses, int32_t n_part, 
   g_err.clear();
   SMA_CHECK(n_part >= 1 && n_part <= sma::kMaxMergeParts, "n_part = %d out of [1, %d]", n_part,
             sma::kMaxMergeParts);
-  SMA_CHECK(n_q >= 0, "n_q = %d < 0", n_q);
+  SMA_CHECK(n_q >= 0 && n_q <= (1 << 28), "n_q = %d out of [0, 2^28]", n_q);
   SMA_CHECK(out_dtype == SMA_DT_BF16 || out_dtype == SMA_DT_FP32, "out_dtype = %d", out_dtype);
   if (n_q == 0) return SMA_OK;
   SMA_CHECK(parts && lses && out, "parts, lses and out must be non-NULL");
