@@ -23,6 +23,8 @@ Sources, by page and section:
 * same page, footnote 1: QK runs over 576 dims, PV over 512; indices are
   4 bytes; q and o are bf16.
 * same page, footnote 3: an FP8 key is 128 values plus a 4-byte scale.
+* DeepSeek multi-node deployment page, section "Quantification": activations
+  are quantised on the fly with one scale per 128-element vector.
 * same page, section "DCP : sharder aussi le cache KV": tokens are dealt
   round-robin over the ranks, each rank attends over its own shard and the
   partial results are merged by their log-sum-exp.
@@ -40,7 +42,9 @@ Readings where the pages are silent (each also listed in the design notes):
 * attention scale tau = 1/sqrt(192); value = the first 512 latent dims;
   LSE is the natural-log log-sum-exp of the scaled logits;
 * FP8 is OCP e4m3fn (bias 7, max 448, no infinities) times a per-token fp32
-  scale; the oracle dequantises first, then runs the same steps.
+  scale; the oracle dequantises first, then runs the same steps;
+* FP8 queries of the indexer carry one scale per (query, head) row, set to
+  amax/448 with round-to-nearest-even codes (quantize_fp8_rows).
 
 Pins: tests/test_oracle_*.py check each function against what the pages and
 the mathematics fix (integer brute force, library routines for the dense and
@@ -93,6 +97,51 @@ def keys_f64(k, fp8: bool) -> np.ndarray:
     return fp8_rows_to_f64(*k) if fp8 else bf16_bits_to_f64(k)
 
 
+FP8_MAX = 448.0   # largest finite e4m3fn magnitude
+
+
+def e4m3fn_encode(v) -> np.ndarray:
+    """Nearest OCP E4M3FN code to each finite value with |v| <= 448, ties to
+    the even code, the sign of zero kept.
+
+    The format's grid, written out: in the binade [2^e, 2^(e+1)), e >= -6,
+    the 8 codes are spaced 2^(e-3) apart; below 2^-6 the subnormals continue
+    with spacing 2^-9.  So with e = max(floor(log2|v|), -6) and
+    n = round_half_even(|v| / 2^(e-3)), the magnitude code is 8*(e+6) + n
+    (n = 16, a value rounded up into the next binade, lands on that binade's
+    first code).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if not np.all(a <= FP8_MAX):
+        raise ValueError("e4m3fn_encode takes finite values with |v| <= 448")
+    _, ex = np.frexp(a)                       # a = m * 2^ex, m in [0.5, 1)
+    e = np.maximum(ex - 1, -6)
+    n = np.rint(a / np.ldexp(1.0, e - 3))     # np.rint: round half to even
+    mag = np.where(a == 0, 0, 8 * (e + 6) + n).astype(np.int64)
+    sign = np.signbit(v).astype(np.int64) << 7
+    return (sign | mag).astype(np.uint8)
+
+
+def quantize_fp8_rows(x) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row FP8 quantisation of activations: one fp32 scale per row (the
+    DeepSeek multi-node page, section "Quantification": activation scales are
+    taken on the fly over vectors of 128 elements; an indexer head's q_I row
+    is one such vector).  The decisions are taken in fp32, as the GPU takes
+    them: scale = amax / 448, y = x / scale (both correctly rounded fp32
+    divisions), y clamped to [-448, 448], code = nearest e4m3fn value.  A row
+    of zeros gets scale 0 and zero codes.  x [n, d] (any float dtype, taken
+    as fp32) -> codes uint8 [n, d], scale float32 [n]."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=1)
+    scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
+    nz = scale > 0
+    y = np.zeros_like(x)
+    y[nz] = x[nz] / scale[nz][:, None]
+    y = np.clip(y, -np.float32(FP8_MAX), np.float32(FP8_MAX))
+    return e4m3fn_encode(y), scale
+
+
 # ----------------------------------------------------------------- a1 -----
 
 def index_scores(q_idx: np.ndarray, w: np.ndarray, k_idx: np.ndarray, q_pos: np.ndarray) -> list:
@@ -110,6 +159,19 @@ def index_scores(q_idx: np.ndarray, w: np.ndarray, k_idx: np.ndarray, q_pos: np.
         dots = q_idx[i] @ k_idx[: p + 1].T          # [H_I, p+1]
         out.append(w[i] @ np.maximum(dots, 0.0))    # [p+1]
     return out
+
+
+def index_scores_fp8(q8: np.ndarray, q_scale: np.ndarray, w: np.ndarray, k8: np.ndarray,
+                     k_scale: np.ndarray, q_pos: np.ndarray) -> list:
+    """Indexer scores with FP8 queries and FP8 keys: q_I[i,h,:] =
+    e4m3(q8[i,h,:]) * q_scale[i,h] (one scale per head row of 128 values, the
+    DeepSeek page's activation blocks) and k_I[s,:] = e4m3(k8[s,:]) *
+    k_scale[s] (GLM-5.3 part 2, footnote 3); then index_scores on the
+    dequantised values.  q8 uint8 [n_q, H_I, d_I], q_scale [n_q, H_I]."""
+    n_q, h, d = q8.shape
+    q = fp8_rows_to_f64(np.asarray(q8).reshape(n_q * h, d), np.asarray(q_scale).reshape(-1))
+    return index_scores(q.reshape(n_q, h, d), np.asarray(w, dtype=np.float64),
+                        fp8_rows_to_f64(k8, k_scale), q_pos)
 
 
 # ----------------------------------------------------------------- a2 -----
