@@ -106,6 +106,47 @@ sma_status sma_index_scores(const uint16_t* q_idx, const float* w, int64_t w_str
                             float* scores, int64_t ld_scores, void* stream);
 
 /*
+ * sma_quantize_fp8_rows — per-row FP8 quantisation of bf16 rows, the way the
+ * FP8 indexer's operands are stored: one fp32 scale per row of d values
+ * (DeepSeek multi-node page, "Quantification": activation scales over
+ * 128-element vectors; GLM-5.3 part 2, footnote 3: a key row is 128 FP8
+ * values plus a 4-byte scale).
+ *
+ *   scale[r]   = amax_j |x[r,j]| / 448                       (fp32, rounded)
+ *   codes[r,j] = e4m3fn(clamp(x[r,j] / scale[r], -448, 448)) (fp32 division,
+ *                nearest-even code); a row of zeros gets scale 0, codes 0
+ *
+ *  x      [n_rows, d] bf16, 16-byte aligned; inputs must be finite
+ *  codes  [n_rows, d] uint8, 8-byte aligned;  scale [n_rows] fp32
+ *  Supported: d in {64, 128}, 0 <= n_rows <= 2^36.  A query's 64 head rows
+ *  of q_I are 64 rows here (scale index i*64 + h).
+ */
+sma_status sma_quantize_fp8_rows(const uint16_t* x, int64_t n_rows, int32_t d, uint8_t* codes, float* scale,
+                                 void* stream);
+
+/*
+ * sma_index_scores_fp8 — the indexer scores of sma_index_scores with FP8
+ * queries and FP8 keys (footnote 3 of the same article stores the keys so;
+ * the queries carry one scale per head row, as sma_quantize_fp8_rows makes
+ * them):
+ *
+ *   scores[i*ld + s] = sum_h w[i*w_stride + h]
+ *                      * max(0, (q_scale[i*64+h] * e4m3(q_idx[i,h,:]))
+ *                               . (k_scale[s] * e4m3(k_idx[s,:])))
+ *
+ *  q_idx [n_q, 64, 128] e4m3fn codes (16-byte aligned), q_scale [n_q, 64]
+ *  fp32 >= 0; k_idx [n_k, 128] codes, k_scale [n_k] fp32 >= 0; the rest as
+ *  sma_index_scores.  The dot products run on e4m3 x e4m3 MFMA with fp32
+ *  accumulation (exact products); the scales, ReLU, head weights and head
+ *  sum are fp32.
+ *  Supported: h_idx = 64, d_idx = 128 only (SMA_ERR_UNSUPPORTED otherwise).
+ */
+sma_status sma_index_scores_fp8(const uint8_t* q_idx, const float* q_scale, const float* w, int64_t w_stride,
+                                const uint8_t* k_idx, const float* k_scale, const int32_t* q_pos, int32_t n_q,
+                                int64_t n_k, int32_t h_idx, int32_t d_idx, float* scores, int64_t ld_scores,
+                                void* stream);
+
+/*
  * sma_topk_select — per-query top-k of the causal scores (same article,
  * "Pourquoi pas TP ou DP ?"; 4-byte indices, footnote 1).
  *
@@ -167,6 +208,19 @@ sma_status sma_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride,
                        int32_t h_idx, int32_t d_idx, int32_t top_k, float sm_scale,
                        void* out, int32_t out_dtype, float* lse, int32_t* idx_out,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sma_prefill_fp8_indexer — sma_prefill with the indexer of
+ * sma_index_scores_fp8 (FP8 queries and keys, h_idx = 64, d_idx = 128);
+ * top-k and sparse MLA as in sma_prefill, the same workspace
+ * (sma_workspace_bytes(SMA_OP_PREFILL, ...)).
+ */
+sma_status sma_prefill_fp8_indexer(const uint8_t* q_idx, const float* q_scale, const float* w, int64_t w_stride,
+                                   const uint8_t* k_idx, const float* k_scale, const uint16_t* q, const void* kv,
+                                   const float* kv_scale, int32_t kv_dtype, const int32_t* q_pos, int32_t n_q,
+                                   int64_t n_k, int32_t h_idx, int32_t d_idx, int32_t top_k, float sm_scale,
+                                   void* out, int32_t out_dtype, float* lse, int32_t* idx_out, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /*
  * sma_pcp_rank_share — one PCP rank's share of a prompt of L_total tokens

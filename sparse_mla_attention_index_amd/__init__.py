@@ -1,6 +1,9 @@
 """MI355X (gfx950) sparse-MLA prefill path: indexer scores -> per-query
 top-k -> sparse MLA over the selected latent rows, plus one PCP rank's
-share and one DCP rank's partial attention with the log-sum-exp merge.  The compute runs in hand-written HIP kernels behind the C ABI of
-include/sma.h (libsma.so); this package is the thin Python binding."""
-from ._lib import (SmaError, dcp_shard_partial, index_scores, last_error, lib, lse_merge,  # noqa: F401
-                   pcp_rank_share, prefill, sparse_mla_prefill, topk_select, version, workspace_bytes)
+share, one DCP rank's partial attention with the log-sum-exp merge, and the
+FP8 indexer (per-row FP8 quantisation, e4m3 x e4m3 scores).  The compute
+runs in hand-written HIP kernels behind the C ABI of include/sma.h
+(libsma.so); this package is the thin Python binding."""
+from ._lib import (SmaError, dcp_shard_partial, index_scores, index_scores_fp8, last_error, lib,  # noqa: F401
+                   lse_merge, pcp_rank_share, prefill, prefill_fp8_indexer, quantize_fp8_rows,
+                   sparse_mla_prefill, topk_select, version, workspace_bytes)

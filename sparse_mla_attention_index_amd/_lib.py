@@ -35,6 +35,10 @@ SIGNATURES = {
     "sma_dcp_shard_partial": (_I32, [_I32, _I32, _P, _P, _P, _I32, _I64, _P, _I32, _I32, _F, _P, _P, _P, _SZ,
                                      _P]),
     "sma_lse_merge": (_I32, [_P, _P, _I32, _I32, _P, _I32, _P, _P]),
+    "sma_quantize_fp8_rows": (_I32, [_P, _I64, _I32, _P, _P, _P]),
+    "sma_index_scores_fp8": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _I64, _P]),
+    "sma_prefill_fp8_indexer": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _I32, _P, _I32, _I64, _I32, _I32,
+                                       _I32, _F, _P, _I32, _P, _P, _P, _SZ, _P]),
     "sma_workspace_bytes": (_SZ, [_I32, _I32, _I64, _I32, _I32, _I32]),
     "sma_last_error": (ctypes.c_char_p, []),
     "sma_version": (_I32, []),
@@ -135,6 +139,58 @@ def index_scores(q_idx, w, k_idx, q_pos, *, k_scale=None, scores=None):
     return scores
 
 
+def _fp8(t, name):
+    if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError(f"{name}: expected e4m3fn codes (float8_e4m3fn or uint8), got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _f32(t, name):
+    if t is None or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous fp32 tensor")
+
+
+def quantize_fp8_rows(x, *, codes=None, scale=None):
+    """Per-row FP8: x bf16 [..., d] (d = 64 or 128) -> (codes uint8 [..., d],
+    scale fp32 [...]) with scale = amax/448 and nearest-even e4m3fn codes."""
+    _bf16(x, "x")
+    d = x.shape[-1]
+    n_rows = x.numel() // d if d else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _fp8(codes, "codes")
+    _f32(scale, "scale")
+    if codes.numel() != x.numel() or scale.numel() != n_rows:
+        raise ValueError("codes / scale sizes do not match x")
+    _check(lib().sma_quantize_fp8_rows(_ptr(x), n_rows, d, _ptr(codes), _ptr(scale), _stream(x.device)))
+    return codes, scale
+
+
+def index_scores_fp8(q_idx, q_scale, w, k_idx, k_scale, q_pos, *, scores=None):
+    """Indexer scores [n_q, n_k] fp32 from FP8 queries [n_q, 64, 128] with
+    per-(query, head) scales [n_q, 64] and FP8 keys [n_k, 128] with per-key
+    scales; only s <= q_pos[i] is written."""
+    n_q, h, d = q_idx.shape
+    n_k = k_idx.shape[0]
+    _fp8(q_idx, "q_idx")
+    _fp8(k_idx, "k_idx")
+    _f32(q_scale, "q_scale")
+    _f32(k_scale, "k_scale")
+    if q_pos.dtype != torch.int32 or not q_pos.is_contiguous():
+        raise ValueError("q_pos must be contiguous int32")
+    if scores is None:
+        scores = torch.empty((n_q, n_k), dtype=torch.float32, device=q_idx.device)
+    if scores.dtype != torch.float32 or scores.stride(1) != 1:
+        raise ValueError("scores must be fp32 with unit column stride")
+    _check(lib().sma_index_scores_fp8(_ptr(q_idx), _ptr(q_scale), _ptr(w), _w_stride(w, n_q, h), _ptr(k_idx),
+                                      _ptr(k_scale), _ptr(q_pos), n_q, n_k, h, d, _ptr(scores), scores.stride(0),
+                                      _stream(q_idx.device)))
+    return scores
+
+
 def topk_select(scores, q_pos, top_k: int, *, n_k: int | None = None, idx=None, workspace=None):
     """Top-k positions per row, ascending, -1 padded: int32 [n_q, top_k].
 
@@ -204,6 +260,35 @@ def prefill(q_idx, w, k_idx, q, kv, q_pos, top_k: int, sm_scale: float, *, k_sca
                              _ptr(q), _ptr(kv), _ptr(kv_scale), vdt, _ptr(q_pos), n_q, n_k, h, d, top_k,
                              float(sm_scale), _ptr(out), odt, _ptr(lse), _ptr(idx_out), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, lse, idx_out
+
+
+def prefill_fp8_indexer(q_idx, q_scale, w, k_idx, k_scale, q, kv, q_pos, top_k: int, sm_scale: float, *,
+                        kv_scale=None, out=None, out_dtype=torch.bfloat16, want_lse=False, idx_out=None,
+                        workspace=None):
+    """prefill() with the FP8 indexer (FP8 queries + per-head scales, FP8
+    keys + per-key scales); returns (out, lse or None, idx or None)."""
+    n_q, h, d = q_idx.shape
+    n_k = k_idx.shape[0]
+    _fp8(q_idx, "q_idx")
+    _fp8(k_idx, "k_idx")
+    _f32(q_scale, "q_scale")
+    _f32(k_scale, "k_scale")
+    vdt = _keys(kv, kv_scale, "kv")
+    _bf16(q, "q")
+    dev = q.device
+    if out is None:
+        out = torch.empty((n_q, HEADS, D_V), dtype=out_dtype, device=dev)
+    odt = SMA_DT_FP32 if out.dtype == torch.float32 else SMA_DT_BF16
+    lse = torch.empty((n_q, HEADS), dtype=torch.float32, device=dev) if want_lse else None
+    if workspace is None:
+        nbytes = workspace_bytes(SMA_OP_PREFILL, n_q, n_k, top_k, h, d)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().sma_prefill_fp8_indexer(_ptr(q_idx), _ptr(q_scale), _ptr(w), _w_stride(w, n_q, h), _ptr(k_idx),
+                                         _ptr(k_scale), _ptr(q), _ptr(kv), _ptr(kv_scale), vdt, _ptr(q_pos), n_q,
+                                         n_k, h, d, top_k, float(sm_scale), _ptr(out), odt, _ptr(lse),
+                                         _ptr(idx_out), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(dev)))
     return out, lse, idx_out
 
 

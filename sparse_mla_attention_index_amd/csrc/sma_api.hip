@@ -60,7 +60,7 @@ constexpr int32_t kMinScoreBlock = 64;   // query rows of scores the prefill wor
     if (!(cond)) return fail(SMA_ERR_INVALID_ARG, __VA_ARGS__); \
   } while (0)
 
-sma_status validate_indexer(const uint16_t* q_idx, const float* w, int64_t w_stride, const void* k_idx,
+sma_status validate_indexer(const void* q_idx, const float* w, int64_t w_stride, const void* k_idx,
                             const float* k_scale, int32_t k_dtype, const int32_t* q_pos, int32_t n_q,
                             int64_t n_k, int32_t h_idx, int32_t d_idx, bool pos_from_caller = true) {
   SMA_CHECK(n_q >= 0, "n_q = %d < 0", n_q);
@@ -79,6 +79,20 @@ sma_status validate_indexer(const uint16_t* q_idx, const float* w, int64_t w_str
     SMA_CHECK(q_idx && w && (q_pos || !pos_from_caller), "q_idx, w and q_pos must be non-NULL");
     SMA_CHECK(aligned(q_idx, 16), "q_idx not 16-byte aligned");
   }
+  return SMA_OK;
+}
+
+// FP8 queries: FP8 keys, the 64 x 128 shape, one scale per (query, head).
+sma_status validate_indexer_fp8(const uint8_t* q_idx, const float* q_scale, const float* w, int64_t w_stride,
+                                const uint8_t* k_idx, const float* k_scale, const int32_t* q_pos, int32_t n_q,
+                                int64_t n_k, int32_t h_idx, int32_t d_idx) {
+  sma_status s = validate_indexer(q_idx, w, w_stride, k_idx, k_scale, SMA_DT_FP8_E4M3, q_pos, n_q, n_k, h_idx,
+                                  d_idx);
+  if (s != SMA_OK) return s;
+  SMA_CHECK(k_scale != nullptr && aligned(k_scale, 4), "k_scale is NULL or not 4-byte aligned");
+  if (h_idx != 64 || d_idx != 128)
+    return fail(SMA_ERR_UNSUPPORTED, "FP8 queries: h_idx = %d, d_idx = %d (supported: 64 x 128)", h_idx, d_idx);
+  if (n_q > 0) SMA_CHECK(q_scale != nullptr, "q_scale is NULL");
   return SMA_OK;
 }
 
@@ -110,11 +124,11 @@ sma_status validate_mla(const uint16_t* q, const void* kv, const float* kv_scale
   return SMA_OK;
 }
 
-sma::IdxArgs idx_args(const uint16_t* q_idx, const float* w, int64_t w_stride, const void* k_idx,
-                      const float* k_scale, int32_t k_dtype, const int32_t* q_pos, int32_t n_q,
-                      int64_t n_k, int32_t h_idx, int32_t d_idx, float* scores, int64_t ld) {
+sma::IdxArgs idx_args(const void* q_idx, const float* q_scale, const float* w, int64_t w_stride,
+                      const void* k_idx, const float* k_scale, int32_t k_dtype, const int32_t* q_pos,
+                      int32_t n_q, int64_t n_k, int32_t h_idx, int32_t d_idx, float* scores, int64_t ld) {
   sma::IdxArgs a;
-  a.q_idx = q_idx; a.w = w; a.w_stride = w_stride; a.k_idx = k_idx; a.k_scale = k_scale;
+  a.q_idx = q_idx; a.q_scale = q_scale; a.w = w; a.w_stride = w_stride; a.k_idx = k_idx; a.k_scale = k_scale;
   a.fp8 = k_dtype == SMA_DT_FP8_E4M3; a.q_pos = q_pos; a.n_q = n_q; a.n_k = n_k;
   a.h_idx = h_idx; a.d_idx = d_idx; a.scores = scores; a.ld = ld;
   return a;
@@ -138,7 +152,8 @@ size_t prefill_fixed_bytes(int32_t n_q, int32_t top_k, bool need_idx, bool need_
 
 // The composed path shared by sma_prefill and sma_pcp_rank_share.  `pos` is
 // a device array of n_q positions; `ws` past `fixed` holds score blocks.
-sma_status run_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride, const void* k_idx,
+sma_status run_prefill(const void* q_idx, const float* q_scale, const float* w, int64_t w_stride,
+                       const void* k_idx,
                        const float* k_scale, int32_t k_dtype, const uint16_t* q, const void* kv,
                        const float* kv_scale, int32_t kv_dtype, const int32_t* pos, int32_t n_q,
                        int64_t n_k, int32_t h_idx, int32_t d_idx, int32_t top_k, float sm_scale,
@@ -157,8 +172,11 @@ sma_status run_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride, 
   const size_t topk_ws_bytes = score_ws_bytes - align_up((size_t)qb * (size_t)n_k * 4, 256);
   for (int64_t q0 = 0; q0 < n_q; q0 += qb) {
     const int32_t nb = (int32_t)((n_q - q0) < qb ? (n_q - q0) : qb);
-    sma::IdxArgs ia = idx_args(q_idx + q0 * h_idx * d_idx, w + q0 * w_stride, w_stride, k_idx, k_scale,
-                               k_dtype, pos + q0, nb, n_k, h_idx, d_idx, scores, n_k);
+    // bf16 query rows take 2 bytes an element, FP8 ones 1 plus a scale per head
+    const size_t q_row_bytes = (size_t)h_idx * d_idx * (q_scale ? 1 : 2);
+    sma::IdxArgs ia = idx_args(static_cast<const uint8_t*>(q_idx) + q0 * q_row_bytes,
+                               q_scale ? q_scale + q0 * h_idx : nullptr, w + q0 * w_stride, w_stride, k_idx,
+                               k_scale, k_dtype, pos + q0, nb, n_k, h_idx, d_idx, scores, n_k);
     hipError_t e = sma::launch_index_scores(ia, st);
     if (e != hipSuccess) return hip_fail(e, "index_scores launch");
     sma::TopkArgs ta{scores, n_k, pos + q0, nb, n_k, top_k, idx + q0 * top_k, topk_ws, topk_ws_bytes};
@@ -172,6 +190,35 @@ sma_status run_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride, 
   hipError_t e = sma::launch_sparse_mla(ma, st);
   if (e != hipSuccess) return hip_fail(e, "sparse_mla launch");
   return SMA_OK;
+}
+
+
+// sma_prefill and sma_prefill_fp8_indexer after their indexer checks.
+sma_status prefill_entry(const void* q_idx, const float* q_scale, const float* w, int64_t w_stride,
+                         const void* k_idx, const float* k_scale, int32_t k_dtype, const uint16_t* q,
+                         const void* kv, const float* kv_scale, int32_t kv_dtype, const int32_t* q_pos,
+                         int32_t n_q, int64_t n_k, int32_t h_idx, int32_t d_idx, int32_t top_k, float sm_scale,
+                         void* out, int32_t out_dtype, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                         void* stream) {
+  sma_status s = validate_mla(q, kv, kv_scale, kv_dtype, n_k, idx_out, n_q, top_k, sm_scale, out, out_dtype, true);
+  if (s != SMA_OK) return s;
+  if (n_q == 0) return SMA_OK;
+  const size_t fixed = prefill_fixed_bytes(n_q, top_k, idx_out == nullptr, false);
+  const int32_t blk = n_q < kMinScoreBlock ? n_q : kMinScoreBlock;
+  const size_t need = fixed + score_block_bytes(blk, n_k, top_k);
+  if (ws_bytes < need || (ws == nullptr && need > 0))
+    return fail(SMA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
+  if ((s = check_device()) != SMA_OK) return s;
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  int32_t* idx = idx_out;
+  if (!idx) {
+    idx = reinterpret_cast<int32_t*>(p);
+    p += align_up((size_t)n_q * top_k * 4, 256);
+  }
+  return run_prefill(q_idx, q_scale, w, w_stride, k_idx, k_scale, k_dtype, q, kv, kv_scale, kv_dtype, q_pos,
+                     n_q, n_k, h_idx, d_idx, top_k, sm_scale, out, out_dtype, lse, idx, p,
+                     ws_bytes - (size_t)(p - static_cast<uint8_t*>(ws)), (hipStream_t)stream);
 }
 
 }  // namespace
@@ -190,9 +237,43 @@ sma_status sma_index_scores(const uint16_t* q_idx, const float* w, int64_t w_str
   if (n_q == 0) return SMA_OK;
   if ((s = check_device()) != SMA_OK) return s;
   hipError_t e = sma::launch_index_scores(
-      idx_args(q_idx, w, w_stride, k_idx, k_scale, k_dtype, q_pos, n_q, n_k, h_idx, d_idx, scores, ld_scores),
+      idx_args(q_idx, nullptr, w, w_stride, k_idx, k_scale, k_dtype, q_pos, n_q, n_k, h_idx, d_idx, scores,
+               ld_scores),
       (hipStream_t)stream);
   return e == hipSuccess ? SMA_OK : hip_fail(e, "index_scores launch");
+}
+
+sma_status sma_index_scores_fp8(const uint8_t* q_idx, const float* q_scale, const float* w, int64_t w_stride,
+                                const uint8_t* k_idx, const float* k_scale, const int32_t* q_pos, int32_t n_q,
+                                int64_t n_k, int32_t h_idx, int32_t d_idx, float* scores, int64_t ld_scores,
+                                void* stream) {
+  g_err.clear();
+  sma_status s = validate_indexer_fp8(q_idx, q_scale, w, w_stride, k_idx, k_scale, q_pos, n_q, n_k, h_idx, d_idx);
+  if (s != SMA_OK) return s;
+  SMA_CHECK(ld_scores >= n_k, "ld_scores = %lld < n_k = %lld", (long long)ld_scores, (long long)n_k);
+  if (n_q > 0) SMA_CHECK(scores != nullptr, "scores is NULL");
+  if (n_q == 0) return SMA_OK;
+  if ((s = check_device()) != SMA_OK) return s;
+  hipError_t e = sma::launch_index_scores(idx_args(q_idx, q_scale, w, w_stride, k_idx, k_scale, SMA_DT_FP8_E4M3,
+                                                   q_pos, n_q, n_k, h_idx, d_idx, scores, ld_scores),
+                                          (hipStream_t)stream);
+  return e == hipSuccess ? SMA_OK : hip_fail(e, "index_scores_fp8 launch");
+}
+
+sma_status sma_quantize_fp8_rows(const uint16_t* x, int64_t n_rows, int32_t d, uint8_t* codes, float* scale,
+                                 void* stream) {
+  g_err.clear();
+  SMA_CHECK(n_rows >= 0 && n_rows <= ((int64_t)1 << 36), "n_rows = %lld out of [0, 2^36]", (long long)n_rows);
+  if (d != 64 && d != 128) return fail(SMA_ERR_UNSUPPORTED, "d = %d (supported: 64, 128)", d);
+  if (n_rows == 0) return SMA_OK;
+  SMA_CHECK(x && codes && scale, "x, codes and scale must be non-NULL");
+  SMA_CHECK(aligned(x, 16), "x not 16-byte aligned");
+  SMA_CHECK(aligned(codes, 8), "codes not 8-byte aligned");
+  SMA_CHECK(aligned(scale, 4), "scale not 4-byte aligned");
+  sma_status s = check_device();
+  if (s != SMA_OK) return s;
+  hipError_t e = sma::launch_quantize_fp8_rows(x, n_rows, d, codes, scale, (hipStream_t)stream);
+  return e == hipSuccess ? SMA_OK : hip_fail(e, "quantize_fp8_rows launch");
 }
 
 sma_status sma_topk_select(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t n_q,
@@ -309,26 +390,23 @@ sma_status sma_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride, 
   g_err.clear();
   sma_status s = validate_indexer(q_idx, w, w_stride, k_idx, k_scale, k_dtype, q_pos, n_q, n_k, h_idx, d_idx);
   if (s != SMA_OK) return s;
-  if ((s = validate_mla(q, kv, kv_scale, kv_dtype, n_k, idx_out, n_q, top_k, sm_scale, out, out_dtype,
-                        true)) != SMA_OK)
-    return s;
-  if (n_q == 0) return SMA_OK;
-  const size_t fixed = prefill_fixed_bytes(n_q, top_k, idx_out == nullptr, false);
-  const int32_t blk = n_q < kMinScoreBlock ? n_q : kMinScoreBlock;
-  const size_t need = fixed + score_block_bytes(blk, n_k, top_k);
-  if (ws_bytes < need || (ws == nullptr && need > 0))
-    return fail(SMA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
-  SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
-  if ((s = check_device()) != SMA_OK) return s;
-  uint8_t* p = static_cast<uint8_t*>(ws);
-  int32_t* idx = idx_out;
-  if (!idx) {
-    idx = reinterpret_cast<int32_t*>(p);
-    p += align_up((size_t)n_q * top_k * 4, 256);
-  }
-  return run_prefill(q_idx, w, w_stride, k_idx, k_scale, k_dtype, q, kv, kv_scale, kv_dtype, q_pos, n_q,
-                     n_k, h_idx, d_idx, top_k, sm_scale, out, out_dtype, lse, idx, p,
-                     ws_bytes - (size_t)(p - static_cast<uint8_t*>(ws)), (hipStream_t)stream);
+  return prefill_entry(q_idx, nullptr, w, w_stride, k_idx, k_scale, k_dtype, q, kv, kv_scale, kv_dtype, q_pos,
+                       n_q, n_k, h_idx, d_idx, top_k, sm_scale, out, out_dtype, lse, idx_out, ws, ws_bytes,
+                       stream);
+}
+
+sma_status sma_prefill_fp8_indexer(const uint8_t* q_idx, const float* q_scale, const float* w, int64_t w_stride,
+                                   const uint8_t* k_idx, const float* k_scale, const uint16_t* q, const void* kv,
+                                   const float* kv_scale, int32_t kv_dtype, const int32_t* q_pos, int32_t n_q,
+                                   int64_t n_k, int32_t h_idx, int32_t d_idx, int32_t top_k, float sm_scale,
+                                   void* out, int32_t out_dtype, float* lse, int32_t* idx_out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  g_err.clear();
+  sma_status s = validate_indexer_fp8(q_idx, q_scale, w, w_stride, k_idx, k_scale, q_pos, n_q, n_k, h_idx, d_idx);
+  if (s != SMA_OK) return s;
+  return prefill_entry(q_idx, q_scale, w, w_stride, k_idx, k_scale, SMA_DT_FP8_E4M3, q, kv, kv_scale, kv_dtype,
+                       q_pos, n_q, n_k, h_idx, d_idx, top_k, sm_scale, out, out_dtype, lse, idx_out, ws, ws_bytes,
+                       stream);
 }
 
 sma_status sma_pcp_rank_share(int32_t rank, int32_t pcp_size, int64_t L_total, const uint16_t* q_idx_share,
@@ -371,7 +449,7 @@ sma_status sma_pcp_rank_share(int32_t rank, int32_t pcp_size, int64_t L_total, c
   }
   hipError_t e = sma::launch_pcp_positions(pos, rank, pcp_size, L_total, st);
   if (e != hipSuccess) return hip_fail(e, "pcp positions launch");
-  return run_prefill(q_idx_share, w_share, w_stride, k_idx, k_scale, k_dtype, q_share, kv, kv_scale,
+  return run_prefill(q_idx_share, nullptr, w_share, w_stride, k_idx, k_scale, k_dtype, q_share, kv, kv_scale,
                      kv_dtype, pos, n_q, L_total, h_idx, d_idx, top_k, sm_scale, out_share, out_dtype,
                      lse_share, idx, p, ws_bytes - (size_t)(p - static_cast<uint8_t*>(ws)), st);
 }

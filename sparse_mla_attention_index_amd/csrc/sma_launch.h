@@ -8,7 +8,8 @@
 namespace sma {
 
 struct IdxArgs {
-  const uint16_t* q_idx;
+  const void* q_idx;        // bf16 rows, or e4m3fn codes when q_scale is set
+  const float* q_scale = nullptr;   // FP8 queries: one scale per (query, head) row
   const float* w;
   int64_t w_stride;
   const void* k_idx;
@@ -59,6 +60,9 @@ int mla_split_count(int n_q, int top_k, bool fp8);
 size_t mla_split_bytes(int n_q, int n_split);
 
 hipError_t launch_index_scores(const IdxArgs& a, hipStream_t s);
+// e4m3fn rows of d = 64 or 128 values -> codes + one fp32 scale per row.
+hipError_t launch_quantize_fp8_rows(const uint16_t* x, int64_t n_rows, int d, uint8_t* codes, float* scale,
+                                    hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 // Rows longer than the on-chip top-k holds (n_k > 65,536) are split across
 // workgroups when the workspace holds topk_multi_bytes(n_q, n_k, top_k).

@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(sma_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(sma_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_header_and_binding_agree():
@@ -128,3 +128,30 @@ def test_dcp_workspace_check():
 def test_lse_merge_validation(n_part, odt, msg):
     r = sma.lib().sma_lse_merge(FAKE, FAKE, n_part, 3, FAKE, odt, None, None)
     assert r == -1 and msg in sma.last_error()
+
+
+@pytest.mark.parametrize("n,d,code,msg", [(10, 96, -2, "d = 96"), (-1, 128, -1, "n_rows"), (10, 128, -1, "NULL")])
+def test_quantize_validation(n, d, code, msg):
+    r = sma.lib().sma_quantize_fp8_rows(FAKE, n, d, None if msg == "NULL" else FAKE, FAKE, None)
+    assert r == code and msg in sma.last_error()
+
+
+@pytest.mark.parametrize("args,code,msg", [
+    (dict(h=32), -2, "64 x 128"),
+    (dict(d=64), -2, "64 x 128"),
+    (dict(qs=None), -1, "q_scale"),
+    (dict(ks=None), -1, "k_scale"),
+    (dict(ld=5), -1, "ld_scores"),
+])
+def test_index_scores_fp8_validation(args, code, msg):
+    a = dict(h=64, d=128, qs=FAKE, ks=FAKE, ld=10)
+    a.update(args)
+    r = sma.lib().sma_index_scores_fp8(FAKE, a["qs"], FAKE, 64, FAKE, a["ks"], FAKE, 1, 10, a["h"], a["d"], FAKE,
+                                       a["ld"], None)
+    assert r == code and msg in sma.last_error()
+
+
+def test_prefill_fp8_indexer_workspace_check():
+    r = sma.lib().sma_prefill_fp8_indexer(FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 16, 1000,
+                                          64, 128, 64, 0.1, FAKE, 0, None, None, FAKE, 100, None)
+    assert r == -3 and "workspace" in sma.last_error()
