@@ -48,7 +48,7 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = {"index_scores": ("idx_score", "idx_score.hip"), "topk_select": ("topk_kernel", "topk.hip"),
+KERNEL_SOURCES = {"index_scores": ("idx_score_h64_kernel", "idx_score.hip"), "topk_select": ("topk_kernel", "topk.hip"),
                   "sparse_mla": ("sparse_mla", "sparse_mla.hip")}
 
 
@@ -261,6 +261,42 @@ def main():
         _log(f"dcp{P}: partials {t_part:.3f} ms + merge {t_merge:.3f} ms (unsharded {t_mla:.3f} ms), "
              f"max err {d_err:.2e}")
 
+    # FP8 indexer leg: q_I (and bf16 keys) quantised per row on the GPU, the
+    # e4m3 x e4m3 indexer, and a whole step with it (quantisers included).
+    f8 = None
+    if w.h_idx == 64 and w.d_idx == 128:
+        q8 = torch.empty((n_q, 64, 128), dtype=torch.uint8, device=dev)
+        qs8 = torch.empty((n_q, 64), dtype=torch.float32, device=dev)
+        if w.fp8:
+            k8, ks8 = k_idx, k_scale
+        else:
+            k8 = torch.empty((n_k, 128), dtype=torch.uint8, device=dev)
+            ks8 = torch.empty((n_k,), dtype=torch.float32, device=dev)
+        idx8 = torch.empty_like(idx)
+        out8 = torch.empty_like(out)
+
+        def quant():
+            sma.quantize_fp8_rows(q_idx, codes=q8, scale=qs8)
+            if not w.fp8:
+                sma.quantize_fp8_rows(k_idx, codes=k8, scale=ks8)
+
+        def step8():
+            quant()
+            sma.prefill_fp8_indexer(q8, qs8, wts, k8, ks8, q, kv, q_pos, w.top_k, w.sm_scale, kv_scale=kv_scale,
+                                    out=out8, idx_out=idx8, workspace=ws)
+
+        t_qq = timed(lambda: sma.quantize_fp8_rows(q_idx, codes=q8, scale=qs8), reps)
+        t_qk = 0.0 if w.fp8 else timed(lambda: sma.quantize_fp8_rows(k_idx, codes=k8, scale=ks8), reps)
+        t_idx8 = timed(lambda: sma.index_scores_fp8(q8[:nb], qs8[:nb], wts[:nb], k8, ks8, q_pos[:nb],
+                                                    scores=scores), reps) * (n_q / nb)
+        t_step8 = timed(step8, max(2, min(args.steps, 3)))
+        step8()
+        torch.cuda.synchronize()
+        f8 = {"quantize_q_ms": round(t_qq, 4), "quantize_k_ms": round(t_qk, 4), "index_scores_ms": round(t_idx8, 4),
+              "step_ms": round(t_step8, 3), "tokens_per_s": round(n_q / (t_step8 * 1e-3), 2)}
+        _log(f"fp8 indexer: quantize q {t_qq:.3f} ms, k {t_qk:.3f} ms, index_scores {t_idx8:.2f} ms, "
+             f"step {t_step8:.2f} ms")
+
     pairs = acc.causal_pairs(pos_np)
     key_bytes = (w.d_idx + 4) if w.fp8 else 2 * w.d_idx
     row_bytes = (576 + 4) if w.fp8 else 1152
@@ -289,6 +325,18 @@ def main():
     }
     for v in kern.values():
         v["frac"] = v["achieved"] / v["peak"]
+    if f8:
+        t8 = f8["index_scores_ms"]
+        f8["tflops"] = round(idx_flops / (t8 * 1e-3) / 1e12, 2)
+        f8["peak_tflops"] = acc.PEAK_FP8_TFLOPS
+        f8["frac_fp8_peak"] = round(f8["tflops"] / acc.PEAK_FP8_TFLOPS, 4)
+        f8["keys_per_s"] = round(pairs / (t8 * 1e-3), 1)
+        if args.workload == "decode":
+            # bytes as if each request streamed its own prefix; the synthetic
+            # batch shares one context, so a key tile serves the workgroup's
+            # 12 queries and this figure can exceed what HBM delivers
+            fb = acc.indexer_bytes_per_request(pos_np, w.h_idx, w.d_idx, w.d_idx + 4, q_bytes_per_elem=1)
+            f8["gbs_per_request_counted"] = round(fb / (t8 * 1e-3) / 1e9, 1)
     dom = max(kern, key=lambda k: kern[k]["ms"])
     roof = {"kernel": dom, "bound": kern[dom]["bound"], "achieved": round(kern[dom]["achieved"], 3),
             "peak": kern[dom]["peak"], "unit": kern[dom]["unit"], "frac": round(kern[dom]["frac"], 4),
@@ -334,6 +382,29 @@ def main():
         parity = {"rows": int(sample.size), "topk_threshold_rule": bool(rule), "topk_sets_identical": exact_sets,
                   "mla_max_err_rel_to_max_ref": err, "tolerance": 3e-2 if w.fp8 else 1e-2,
                   "ok": bool(rule and err <= (3e-2 if w.fp8 else 1e-2))}
+        if f8:
+            # the FP8 path on part of the sample: its selections against the
+            # oracle's FP8 scores (same codes), its attention output, and how
+            # much of the bf16 indexer's selection it keeps
+            sub = sample[:: max(1, sample.size // 256)]
+            s8 = torch.from_numpy(sub).to(dev)
+            q8_s, qs8_s = host(q8[s8], np.uint8), host(qs8[s8])
+            k8_h, ks8_h = host(k8, np.uint8), host(ks8)
+            t_c8 = time.perf_counter()
+            sc8 = oracle.index_scores_fp8(q8_s, qs8_s, host(wts[s8]), k8_h, ks8_h, pos_np[sub])
+            cpu8_s = time.perf_counter() - t_c8
+            g8 = host(idx8[s8])
+            rule8 = all(_threshold_rule_ok(oracle, g8[j], sc8[j], w.top_k) for j in range(sub.size))
+            own8, _ = oracle.sparse_mla(f(host(q[s8], np.uint16)), kvv, g8, w.sm_scale)
+            err8 = float(np.abs(host(out8[s8].float()).astype(np.float64) - own8).max() / np.abs(own8).max())
+            gb = host(idx[s8])
+            keep = [np.intersect1d(g8[j][g8[j] >= 0], gb[j][gb[j] >= 0]).size / max(1, (gb[j] >= 0).sum())
+                    for j in range(sub.size)]
+            f8["parity"] = {"rows": int(sub.size), "topk_threshold_rule": bool(rule8),
+                            "mla_max_err_rel_to_max_ref": err8, "ok": bool(rule8 and err8 <= parity["tolerance"]),
+                            "oracle_fp8_indexer_s": round(cpu8_s, 2)}
+            f8["bf16_selection_kept"] = round(float(np.mean(keep)), 4)
+            _log(f"fp8 parity: rule {rule8}, mla err {err8:.2e}, kept {np.mean(keep):.4f} of the bf16 selection")
 
     tokens_s = n_q / (ms_step * 1e-3)
     res = {
@@ -358,6 +429,8 @@ def main():
         res["pcp_load_balance"] = pcp
     if dcp:
         res["dcp_share"] = dcp
+    if f8:
+        res["fp8_indexer"] = f8
     print(json.dumps(res), flush=True)
 
 

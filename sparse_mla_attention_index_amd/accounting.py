@@ -78,13 +78,16 @@ def indexer_bytes(q_pos, h_idx: int, d_idx: int, key_bytes: int, score_bytes: in
     return n_q * h_idx * (2 * d_idx + 4) + n_k * key_bytes + causal_pairs(q_pos) * score_bytes
 
 
-def indexer_bytes_per_request(q_pos, h_idx: int, d_idx: int, key_bytes: int, score_bytes: int = 4) -> int:
+def indexer_bytes_per_request(q_pos, h_idx: int, d_idx: int, key_bytes: int, score_bytes: int = 4,
+                              q_bytes_per_elem: int = 2) -> int:
     """HBM bytes of one index_scores launch when every query streams its own
     causal prefix of keys (the decode batch, where each request would own
     its KV): q_I and w once per query, key_bytes per causal pair read, one
-    fp32 score written per causal pair."""
+    fp32 score written per causal pair.  FP8 queries (q_bytes_per_elem = 1)
+    add a 4-byte scale per head row."""
     q_pos = np.asarray(q_pos, dtype=np.int64)
-    return q_pos.size * h_idx * (2 * d_idx + 4) + causal_pairs(q_pos) * (key_bytes + score_bytes)
+    q_row = q_bytes_per_elem * d_idx + (4 if q_bytes_per_elem == 1 else 0)
+    return q_pos.size * h_idx * (q_row + 4) + causal_pairs(q_pos) * (key_bytes + score_bytes)
 
 
 def topk_bytes(q_pos, top_k: int) -> int:

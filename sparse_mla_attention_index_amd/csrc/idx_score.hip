@@ -406,21 +406,30 @@ static hipError_t launch_idx_h64(const IdxArgs& A, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// FP8 queries and FP8 keys, 64 heads x d_I = 128: the same structure as the
-// bf16 kernel above (eight waves, one query each, a ring of key tiles filled
-// by direct global->LDS loads) on v_mfma_scale_f32_32x32x64_f8f6f4, whose
-// e4m3 x e4m3 products run at twice the bf16 rate.  Its block scales are
-// left at 2^0: the per-row fp32 scales act outside the dot product,
+// FP8 queries and FP8 keys, 64 heads x d_I = 128, on
+// v_mfma_scale_f32_32x32x64_f8f6f4, whose e4m3 x e4m3 products run at twice
+// the bf16 rate.  Its block scales are left at 2^0: the per-row fp32 scales
+// act outside the dot product,
 //   w_h * ReLU(sq_h * sk_s * d) = sk_s * (w_h * sq_h) * ReLU(d),  sq, sk >= 0,
 // so the head weight absorbs the query row's scale and the key's scale
 // multiplies the head sum once.
 //
-// Tile: 128 keys x 128 bytes (16 KiB) plus the 128 key scales.  16-byte
-// chunk c of key r sits at slot c ^ (r & 7) of its 128-byte row, so the 8
-// lanes of a B read that share a chunk hit 8 distinct bank groups; a 1-KiB
-// load covers 8 keys, lane l fetching key 8b + (l >> 3), slot l & 7.  Each
-// wave also loads 16 of the tile's scales (lanes 0..15), so every wave
-// issues the same three loads per tile and waits on the same counts.
+// At twice the MFMA rate the epilogue (a ReLU and an FMA per head and key,
+// fp32) issues more VALU cycles than the MFMAs take, so the kernel is laid
+// out to keep the VALU busy: twelve waves (three per SIMD), one query each,
+// share a ring of 96-key tiles filled by direct global->LDS loads; inside a
+// wave the epilogue of one 32-key N-tile is interleaved with the MFMAs of
+// the next; stores take their row base and lane mask in scalar registers.
+//
+// Tile: 96 keys x 128 bytes (12 KiB) plus the 96 key scales.  16-byte chunk
+// c of key r sits at slot c ^ ((r >> 1) & 7) of its 128-byte row.  The LDS
+// serves 16 lanes of a 16-byte read per cycle over a 256-byte bank period
+// (two keys' rows): the 16 lanes that read one chunk of keys r .. r + 15
+// then hit 16 distinct 16-byte bank groups (key parity picks the half of
+// the period, (r >> 1) & 7 the slot).  Wave v loads keys
+// 8v .. 8v + 7 of the tile (one 1-KiB load, lane l taking key 8v + (l >> 3),
+// slot l & 7) and their 8 scales (lanes 0..7): every wave issues the same two
+// loads per tile and waits on the same counts.
 //
 // The MFMA's 64-wide K step takes 32 bytes per lane from A and from B.  The
 // lane (row, half) loads bytes 64j + 32 half .. +31 of its row for step j in
@@ -429,15 +438,33 @@ static hipError_t launch_idx_h64(const IdxArgs& A, hipStream_t st) {
 // over exactly the 64 products of matching elements.
 // ---------------------------------------------------------------------------
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-constexpr int kF8KT = 128;                                   // keys per tile
-constexpr int kF8Stages = 8;                                 // ring depth
-constexpr int kF8TileB = kF8KT * 128;                        // 16 KiB
-constexpr int kF8KeyLoads = kF8TileB / 1024 / kIdxWaves;     // 2 per wave
-constexpr int kF8Loads = kF8KeyLoads + 1;                    // + the scale load
+constexpr int kF8Waves = 12;                                 // queries per workgroup
+// KL key loads of 1 KiB per wave per tile: KT = 96 KL keys, NT = 3 KL
+// N-tiles; a ring of S tiles (a power of two).
+template <int KL, int S>
+struct F8Geom {
+  static constexpr int KT = 8 * kF8Waves * KL;   // keys per tile
+  static constexpr int NT = KT / 32;             // 32-key N-tiles per tile
+  static constexpr int TileB = KT * 128;         // bytes of a tile
+  static constexpr int Loads = KL + 1;           // loads per wave per tile: keys, scales
+  static_assert((S & (S - 1)) == 0, "ring depth is a power of two");
+};
 
 __device__ __forceinline__ void idx_dma4(const void* gaddr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gaddr), "s"(lds_base)
                : "memory", "m0");
+}
+
+// Store v at base + off on the lanes set in `mask` (a subset of the active
+// lanes), without a branch: exec is narrowed around the one store and
+// restored.  base is uniform (scalar registers), off a per-lane byte offset.
+// Nothing in the kernel reads the stored memory, hence no memory clobber.
+__device__ __forceinline__ void store_lanes(const float* base, uint32_t off, float v, uint64_t mask) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\ts_mov_b64 exec, %4\n\tglobal_store_dword %1, %2, %3\n\ts_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(off), "v"(v), "s"(base), "s"(mask));
 }
 
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
@@ -445,23 +472,26 @@ __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-__global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_fp8_kernel(
+template <int KL, int S>
+__global__ __launch_bounds__(64 * kF8Waves, 1) void idx_score_h64_fp8_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale, const float* __restrict__ w,
     int64_t w_stride, const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
     const int32_t* __restrict__ q_pos, int n_q, int n_k, float* __restrict__ scores, int64_t ld,
     int n_qblocks, int n_chunks, int chunk_keys) {
   constexpr int H = 64, DI = 128;
-  __shared__ __attribute__((aligned(1024))) uint8_t s_k[kF8Stages][kF8TileB];
-  __shared__ __attribute__((aligned(16))) float s_sc[kF8Stages][kF8KT];
-  __shared__ int s_pos[kIdxWaves];
+  using G = F8Geom<KL, S>;
+  constexpr int kF8KT = G::KT, kF8NT = G::NT, kF8Stages = S, kF8Loads = G::Loads;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_k[S][G::TileB];
+  __shared__ __attribute__((aligned(16))) float s_sc[S][G::KT];
+  __shared__ int s_pos[kF8Waves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qb = n_qblocks - 1 - (int)(blockIdx.x / n_chunks);
   const int chunk = (int)(blockIdx.x % n_chunks);
-  const int q0 = qb * kIdxWaves;
+  const int q0 = qb * kF8Waves;
 
-  if (tid < kIdxWaves) {
+  if (tid < kF8Waves) {
     const int qi = q0 + tid;
     const int p = qi < n_q ? q_pos[qi] : -1;
     s_pos[tid] = p < -1 ? -1 : (p > n_k - 1 ? n_k - 1 : p);
@@ -469,12 +499,14 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_fp8_kernel(
   __syncthreads();
   int pmax = -1;
 #pragma unroll
-  for (int t = 0; t < kIdxWaves; ++t) pmax = max(pmax, s_pos[t]);
+  for (int t = 0; t < kF8Waves; ++t) pmax = max(pmax, s_pos[t]);
   const int k_begin = chunk * chunk_keys;
   const int k_end = min(k_begin + chunk_keys, pmax + 1);
   if (k_begin >= k_end) return;   // uniform across the workgroup
   const int ntiles = (k_end - k_begin + kF8KT - 1) / kF8KT;
-  const int mypos = s_pos[wave];
+  // the wave's query: position (scalar), row (clamped for the operand reads)
+  const int mypos = __builtin_amdgcn_readfirstlane(s_pos[wave]);
+  const bool q_ok = q0 + wave < n_q;
   const int qi = min(q0 + wave, n_q - 1);
 
   // ---- A operands: head row 32t + lrow, bytes 64j + 32 khalf .. +31 ----
@@ -501,37 +533,36 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_fp8_kernel(
       wv[t][jj] = w[(int64_t)qi * w_stride + h] * q_scale[(int64_t)qi * H + h];
     }
 
-  // ---- gather of tile i (keys k_begin + 128i ..) into slot i % kF8Stages ----
-  const int dkey = kF8KeyLoads * 8 * wave + (lane >> 3);   // key of load 0 within the tile
+  // ---- gather of tile i (keys k_begin + 96i ..) into slot i % kF8Stages ----
+  const int dkey = 8 * KL * wave + (lane >> 3);   // this lane's key within the tile, load 0
   auto issue = [&](int i) {
-    const int slot = i % kF8Stages;
-    const uint32_t dst = (uint32_t)(uintptr_t)(idx_lds_u8*)&s_k[slot][1024 * kF8KeyLoads * wave];
+    const int slot = i & (S - 1);
     const int kt = k_begin + kF8KT * i;
+    const uint32_t dst = (uint32_t)(uintptr_t)(idx_lds_u8*)&s_k[slot][1024 * KL * wave];
 #pragma unroll
-    for (int j = 0; j < kF8KeyLoads; ++j) {
-      const int key = min(kt + dkey + 8 * j, n_k - 1);
-      const int c = (lane & 7) ^ ((dkey + 8 * j) & 7);
-      idx_dma16(k8 + (int64_t)key * DI + 16 * c, dst + 1024 * j);
-    }
-    const uint32_t sdst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&s_sc[slot][16 * wave];
-    if (lane < 16) idx_dma4(k_scale + min(kt + 16 * wave + lane, n_k - 1), sdst);
+    for (int j = 0; j < KL; ++j)   // keys 8j apart share (key >> 1) & 7's parity pattern: 8j >> 1 = 4j
+      idx_dma16(k8 + (int64_t)min(kt + dkey + 8 * j, n_k - 1) * DI + 16 * ((lane & 7) ^ (((dkey + 8 * j) >> 1) & 7)),
+                dst + 1024 * j);
+    const uint32_t sdst =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&s_sc[slot][8 * KL * wave];
+    if (lane < 8 * KL) idx_dma4(k_scale + min(kt + 8 * KL * wave + lane, n_k - 1), sdst);
   };
   idx_wait_vmcnt<0>();   // operand loads retired: only gathers are outstanding below
 #pragma unroll
   for (int i = 0; i < kF8Stages - 1; ++i) issue(i);
 
   // B operand of N-tile u, k-step j: key 32u + lrow, chunks 4j + 2khalf and
-  // 4j + 2khalf + 1 at their swizzled slots (key & 7 = lrow & 7).
+  // 4j + 2khalf + 1 at their swizzled slots ((key >> 1) & 7 = (lrow >> 1) & 7).
   int boff[2][2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) boff[j][h] = lrow * 128 + 16 * ((4 * j + 2 * khalf + h) ^ (lrow & 7));
+    for (int h = 0; h < 2; ++h) boff[j][h] = lrow * 128 + 16 * ((4 * j + 2 * khalf + h) ^ ((lrow >> 1) & 7));
 
-  f32x16 acc[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};   // [buffer][M tile]
-  int prev_key = -1;
-  float prev_sc = 0.f;
-  auto epilogue = [&](const f32x16& c0, const f32x16& c1, int key0, float sc) {
+  // ReLU, head weights, sum over the lane's 32 head rows and the other 32
+  // held by the lane 32 apart; times the key scale.  Both halves end with
+  // the head sum of key column lrow.
+  auto head_sum = [&](const f32x16& c0, const f32x16& c1, float sc) {
     float part = 0.f;
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
@@ -540,9 +571,16 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_fp8_kernel(
     }
     part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
                                                              false)[1]);
-    const int key = key0 + lrow;
-    if (khalf == 0 && key0 >= 0 && q0 + wave < n_q && key <= mypos && key < k_end)
-      scores[(int64_t)(q0 + wave) * ld + key] = part * sc;
+    return part * sc;
+  };
+  // keys key0 .. key0 + 31 of the wave's row, from the lower half's lanes,
+  // up to the query's position; base and mask are scalar
+  const float* row = scores + (int64_t)qi * ld;
+  const uint32_t lane_off = 4u * (uint32_t)lrow;
+  auto store = [&](float v, int key0) {
+    const int nv = q_ok ? min(max(mypos - key0 + 1, 0), 32) : 0;
+    const uint64_t m = nv >= 32 ? 0xFFFFFFFFull : ((1ull << nv) - 1);
+    store_lanes(row + key0, lane_off, v, m);
   };
   // B operands and the key scale are read one N-tile ahead of their MFMAs,
   // so the last N-tile of tile i reads tile i + 1: the waits cover tiles i
@@ -555,17 +593,25 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_fp8_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) bn[j][h] = *reinterpret_cast<const u32x4*>(s_k[0] + boff[j][h]);
   float scn = s_sc[0][lrow];
+  // Each N-tile's MFMAs are followed by its own epilogue; the three waves of
+  // a SIMD overlap one wave's MFMAs with another's epilogue.  A tile's sums
+  // are stored at the top of the next iteration, beside the wait, barrier
+  // and loads, so that the N-tile loop is one scheduling region.
+  float res[kF8NT];
   for (int i = 0; i < ntiles; ++i) {
-    idx_wait_vmcnt<(kF8Stages - 3) * kF8Loads>();
-    idx_sync_lds();             // for every wave; slot (i - 1) % kF8Stages is free
-    issue(i + kF8Stages - 1);   // past the range these load clamped keys into a free slot
-    const uint8_t* tile = s_k[i % kF8Stages];
     const int k0 = k_begin + kF8KT * i;
+    if (i > 0) {
 #pragma unroll
-    for (int u = 0; u < kF8KT / 32; ++u) {
-      const f32x16 p0 = acc[(u + 1) & 1][0], p1 = acc[(u + 1) & 1][1];
-      const bool last = u + 1 == kF8KT / 32;
-      const int nslot = last ? (i + 1) % kF8Stages : i % kF8Stages;
+      for (int u = 0; u < kF8NT; ++u) store(res[u], k0 - kF8KT + 32 * u);
+    }
+    idx_wait_vmcnt<(kF8Stages - 3) * kF8Loads>();
+    idx_sync_lds();             // for every wave; slot (i - 1) % S is free
+    issue(i + kF8Stages - 1);   // past the range these load clamped keys into a free slot
+    const uint8_t* tile = s_k[i & (S - 1)];
+#pragma unroll
+    for (int u = 0; u < kF8NT; ++u) {
+      const bool last = u + 1 == kF8NT;
+      const int nslot = (last ? i + 1 : i) & (S - 1);
       const uint8_t* nxt = last ? s_k[nslot] : tile + 4096 * (u + 1);
       const float* nsc = &s_sc[nslot][last ? 0 : 32 * (u + 1)];
       const float sc = scn;
@@ -581,42 +627,38 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_fp8_kernel(
         c1 = mfma_f8(a[1][j], b, c1);
       }
       scn = nsc[lrow];
-      epilogue(p0, p1, prev_key, prev_sc);   // the store is skipped before the first N-tile
-      acc[u & 1][0] = c0;
-      acc[u & 1][1] = c1;
-      prev_key = k0 + 32 * u;
-      prev_sc = sc;
-      // one MFMA, then a quarter of the epilogue's VALU work and one B read
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);    // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x0002, 16, 0);   // VALU
-        __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);    // DS read
-      }
+      res[u] = head_sum(c0, c1, sc);
     }
   }
-  epilogue(acc[(kF8KT / 32 - 1) & 1][0], acc[(kF8KT / 32 - 1) & 1][1], prev_key, prev_sc);
+#pragma unroll
+  for (int u = 0; u < kF8NT; ++u) store(res[u], k_begin + kF8KT * (ntiles - 1) + 32 * u);
   idx_wait_vmcnt<0>();   // no load may land in LDS after the workgroup has left
 }
 
-hipError_t launch_index_scores_fp8(const IdxArgs& A, hipStream_t st) {
-  if (A.h_idx != 64 || A.d_idx != 128 || !A.fp8 || !A.q_scale) return hipErrorInvalidValue;
-  const int n_qblocks = (A.n_q + kIdxWaves - 1) / kIdxWaves;
+template <int KL, int S>
+static hipError_t launch_f8(const IdxArgs& A, hipStream_t st) {
+  constexpr int KT = F8Geom<KL, S>::KT;
+  const int n_qblocks = (A.n_q + kF8Waves - 1) / kF8Waves;
   int n_chunks = 1;
   const int target_wgs = 1024;
   if (n_qblocks < target_wgs) n_chunks = (target_wgs + n_qblocks - 1) / n_qblocks;
   int chunk_keys = (int)((A.n_k + n_chunks - 1) / n_chunks);
-  chunk_keys = ((chunk_keys + kF8KT - 1) / kF8KT) * kF8KT;
-  if (chunk_keys < 4 * kF8KT) chunk_keys = 4 * kF8KT;
+  chunk_keys = ((chunk_keys + KT - 1) / KT) * KT;
+  if (chunk_keys < 4 * KT) chunk_keys = 4 * KT;
   n_chunks = (int)((A.n_k + chunk_keys - 1) / chunk_keys);
   const long long grid = (long long)n_qblocks * n_chunks;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(idx_score_h64_fp8_kernel, dim3((unsigned)grid), dim3(64 * kIdxWaves), 0, st,
+  hipLaunchKernelGGL((idx_score_h64_fp8_kernel<KL, S>), dim3((unsigned)grid), dim3(64 * kF8Waves), 0, st,
                      static_cast<const uint8_t*>(A.q_idx), A.q_scale, A.w, A.w_stride,
                      static_cast<const uint8_t*>(A.k_idx), A.k_scale, A.q_pos, A.n_q, (int)A.n_k, A.scores, A.ld,
                      n_qblocks, n_chunks, chunk_keys);
   return hipGetLastError();
+}
+
+hipError_t launch_index_scores_fp8(const IdxArgs& A, hipStream_t st) {
+  if (A.h_idx != 64 || A.d_idx != 128 || !A.fp8 || !A.q_scale) return hipErrorInvalidValue;
+  return launch_f8<1, 8>(A, st);   // 96-key tiles, 8 in the ring (~99 KiB of LDS)
 }
 
 hipError_t launch_index_scores(const IdxArgs& A, hipStream_t st) {
