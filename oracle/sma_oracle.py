@@ -23,6 +23,10 @@ Sources, by page and section:
 * same page, footnote 1: QK runs over 576 dims, PV over 512; indices are
   4 bytes; q and o are bf16.
 * same page, footnote 3: an FP8 key is 128 values plus a 4-byte scale.
+* same page, footnote 1: FlashMLA's fp8_ds_mla KV row of 656 bytes (its
+  layout, not given on the page, is taken from FlashMLA's public
+  description: 512 e4m3 codes, 4 fp32 scales of 128 dims each, 64 bf16 rope
+  values).
 * DeepSeek multi-node deployment page, section "Quantification": activations
   are quantised on the fly with one scale per 128-element vector.
 * same page, section "DCP : sharder aussi le cache KV": tokens are dealt
@@ -91,6 +95,26 @@ def fp8_rows_to_f64(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     """Dequantise per-token FP8 rows: x[s, :] = e4m3(code[s, :]) * scale[s]
     (GLM-5.3 part 2, footnote 3: 128 FP8 values plus a 4-byte scale)."""
     return _E4M3[np.asarray(codes, dtype=np.uint8)] * np.asarray(scale, dtype=np.float64)[:, None]
+
+
+DS_ROW_BYTES = 656   # 512 e4m3 codes + 4 fp32 scales + 64 bf16 rope values
+
+
+def fp8_ds_mla_rows_to_f64(rows: np.ndarray) -> np.ndarray:
+    """Decode FlashMLA's 656-byte fp8_ds_mla latent rows (GLM-5.3 part 2,
+    footnote 1, names the format and its 656 bytes; the layout is the one
+    FlashMLA's public description gives): bytes 0..511 are the e4m3fn codes
+    of latent dims 0..511, bytes 512..527 four little-endian fp32 scales,
+    scale b for dims 128b .. 128b+127, and bytes 528..655 the 64 rope dims
+    512..575 as bf16, unscaled.  rows uint8 [n, 656] -> float64 [n, 576]."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint8)
+    if rows.ndim != 2 or rows.shape[1] != DS_ROW_BYTES:
+        raise ValueError("fp8_ds_mla rows are uint8 [n, 656]")
+    n = rows.shape[0]
+    scales = rows[:, 512:528].copy().view("<f4").astype(np.float64)          # [n, 4]
+    nope = _E4M3[rows[:, :512]] * np.repeat(scales, 128, axis=1)              # [n, 512]
+    rope = bf16_bits_to_f64(rows[:, 528:656].copy().view("<u2"))              # [n, 64]
+    return np.concatenate([nope, rope], axis=1).reshape(n, D_QK)
 
 
 def keys_f64(k, fp8: bool) -> np.ndarray:

@@ -159,6 +159,31 @@ def to_fp8_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return codes, scale
 
 
+def to_fp8_ds_mla_rows(x: np.ndarray) -> np.ndarray:
+    """Latent rows [n, 576] (fp32) in FlashMLA's 656-byte fp8_ds_mla storage:
+    dims 0..511 as e4m3fn codes with one fp32 scale per 128 dims (amax/448,
+    codes by torch's float8_e4m3fn cast), the four scales, then dims 512..575
+    as bf16 (nearest-even).  -> uint8 [n, 656]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n = x.shape[0]
+    out = np.empty((n, 656), dtype=np.uint8)
+    blocks = x[:, :512].reshape(n, 4, 128)
+    amax = np.abs(blocks).max(axis=2)
+    scale = (amax / np.float32(FP8_MAX)).astype(np.float32)                   # [n, 4]
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    y = np.clip(blocks / safe[:, :, None], -FP8_MAX, FP8_MAX).reshape(n, 512)
+    out[:, :512] = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    out[:, 512:528] = np.ascontiguousarray(scale.astype("<f4")).view(np.uint8)
+    out[:, 528:] = np.ascontiguousarray(to_bf16_bits(x[:, 512:]).astype("<u2")).view(np.uint8)
+    return out
+
+
+def latent_rows_fp8_ds_mla(w: Workload, start: int, stop: int, threads: int = 8) -> np.ndarray:
+    """Rows [start, stop) of the workload's latent KV in fp8_ds_mla storage
+    (the same fp32 draws the other storage formats quantise)."""
+    return to_fp8_ds_mla_rows(_gen_f32_rows(w, "kv", start, stop, threads))
+
+
 def rows(w: Workload, tensor: str, start: int, stop: int, threads: int = 8):
     """Rows [start, stop) of one input tensor in its storage format.
 

@@ -9,6 +9,7 @@ FP8 (footnote 3 of the same page: 128 FP8 values plus a 4-byte scale): the
 oracle's e4m3fn table is compared with torch's float8_e4m3fn cast.
 """
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -91,3 +92,53 @@ def test_fp8_generator_roundtrip():
     deq = oracle.fp8_rows_to_f64(codes, scale)
     assert np.all(np.abs(deq - x32) <= np.abs(x32) * 2.0 ** -4 + scale[:, None] * 2.0 ** -9 + 1e-12)
     assert np.all(np.abs(oracle.e4m3fn_table()[codes]).max(axis=1) == 448.0)
+
+
+# --------------------------------------------- fp8_ds_mla (656-byte rows) --
+
+def test_fp8_ds_mla_layout_markers():
+    """A row built byte by byte: codes 0x38 (= 1.0) everywhere, scales
+    1, 2, 4, 8, rope bf16 0.5 (0x3F00) -> dims 0..127 = 1, 128..255 = 2,
+    256..383 = 4, 384..511 = 8, 512..575 = 0.5."""
+    row = np.zeros((1, 656), np.uint8)
+    row[0, :512] = 0x38
+    row[0, 512:528] = np.array([1, 2, 4, 8], "<f4").view(np.uint8)
+    row[0, 528:] = np.full(64, 0x3F00, "<u2").view(np.uint8)
+    x = oracle.fp8_ds_mla_rows_to_f64(row)[0]
+    assert np.array_equal(x, np.concatenate([np.full(128, 1.0), np.full(128, 2.0), np.full(128, 4.0),
+                                             np.full(128, 8.0), np.full(64, 0.5)]))
+
+
+def test_fp8_ds_mla_decode_of_torch_packed_rows():
+    """Rows packed here with torch's casts (codes per 128-dim block, its
+    scale, bf16 rope) decode to e4m3(code)*scale and the bf16 rope exactly,
+    within the format's half-spacing of the fp32 source."""
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((40, 576)) * np.exp2(rng.integers(-6, 6, (40, 1)))).astype(np.float32)
+    x[3, 128:256] = 0.0                                   # an all-zero block: scale 0
+    rows = np.zeros((40, 656), np.uint8)
+    dec_ref = np.zeros((40, 576))
+    for b in range(4):
+        blk = x[:, 128 * b:128 * (b + 1)]
+        s = (np.abs(blk).max(axis=1) / np.float32(448)).astype(np.float32)
+        safe = np.where(s > 0, s, 1).astype(np.float32)
+        c = torch.from_numpy(np.clip(blk / safe[:, None], -448, 448).astype(np.float32)).to(torch.float8_e4m3fn)
+        rows[:, 128 * b:128 * (b + 1)] = c.view(torch.uint8).numpy()
+        rows[:, 512 + 4 * b:516 + 4 * b] = s.astype("<f4").view(np.uint8).reshape(40, 4)
+        dec_ref[:, 128 * b:128 * (b + 1)] = c.to(torch.float64).numpy() * s.astype(np.float64)[:, None]
+    rb = torch.from_numpy(x[:, 512:]).to(torch.bfloat16)
+    rows[:, 528:] = rb.view(torch.int16).numpy().view(np.uint8).reshape(40, 128)
+    dec_ref[:, 512:] = rb.to(torch.float64).numpy()
+    got = oracle.fp8_ds_mla_rows_to_f64(rows)
+    assert np.array_equal(got, dec_ref)
+    assert np.all(got[3, 128:256] == 0)
+    err = np.abs(got[:, :512] - x[:, :512])
+    bound = np.repeat(np.abs(x[:, :512]).reshape(40, 4, 128).max(axis=2) / 448, 128, axis=1)
+    assert np.all(err <= (2.0 ** -4 * np.abs(x[:, :512]) + 2.0 ** -10 * bound) * (1 + 1e-6))
+    # the input generator's packer gives the same bytes
+    assert np.array_equal(synth.to_fp8_ds_mla_rows(x), rows)
+
+
+def test_fp8_ds_mla_rejects_other_shapes():
+    with pytest.raises(ValueError):
+        oracle.fp8_ds_mla_rows_to_f64(np.zeros((2, 580), np.uint8))
