@@ -261,6 +261,27 @@ def main():
         _log(f"dcp{P}: partials {t_part:.3f} ms + merge {t_merge:.3f} ms (unsharded {t_mla:.3f} ms), "
              f"max err {d_err:.2e}")
 
+    # fp8_ds_mla leg (decode): the same selection attended over FlashMLA's
+    # 656-byte rows of the same latent (512 codes + 4 block scales + 64 bf16)
+    ds = None
+    if args.workload == "decode":
+        t_g = time.time()
+        ds_rows = torch.empty((n_k, 656), dtype=torch.uint8, device=dev)
+        for a in range(0, n_k, 65536):
+            b = min(n_k, a + 65536)
+            ds_rows[a:b].copy_(torch.from_numpy(synth.latent_rows_fp8_ds_mla(w, a, b)))
+        out_ds = torch.empty_like(out)
+        torch.cuda.synchronize()
+        t_ds = timed(lambda: sma.sparse_mla_prefill(q, ds_rows, idx, w.sm_scale, out=out_ds, workspace=ws), reps)
+        sma.sparse_mla_prefill(q, ds_rows, idx, w.sm_scale, out=out_ds, workspace=ws)
+        torch.cuda.synchronize()
+        sel = acc.selected_rows(pos_np, w.top_k)
+        ds = {"row_bytes": 656, "sparse_mla_ms": round(t_ds, 4), "fp8_row_format_ms": round(t_mla, 4),
+              "gather_gbs": round(sel * 660 / (t_ds * 1e-3) / 1e9, 1),
+              "tflops": round(acc.mla_flops(pos_np, w.top_k) / (t_ds * 1e-3) / 1e12, 2)}
+        _log(f"fp8_ds_mla: rows packed in {time.time() - t_g:.1f}s, sparse_mla {t_ds:.3f} ms "
+             f"(per-row FP8 format {t_mla:.3f} ms)")
+
     # FP8 indexer leg: q_I (and bf16 keys) quantised per row on the GPU, the
     # e4m3 x e4m3 indexer, and a whole step with it (quantisers included).
     f8 = None
@@ -382,6 +403,19 @@ def main():
         parity = {"rows": int(sample.size), "topk_threshold_rule": bool(rule), "topk_sets_identical": exact_sets,
                   "mla_max_err_rel_to_max_ref": err, "tolerance": 3e-2 if w.fp8 else 1e-2,
                   "ok": bool(rule and err <= (3e-2 if w.fp8 else 1e-2))}
+        if ds:
+            # the 656-byte rows: attention on the GPU's own lists against the
+            # oracle over the decoded rows those lists select
+            g_all = host(idx[s_idx])
+            used = np.unique(g_all[g_all >= 0])
+            dec = oracle.fp8_ds_mla_rows_to_f64(host(ds_rows[torch.from_numpy(used).to(dev)], np.uint8))
+            remap = np.where(g_all >= 0, np.searchsorted(used, np.maximum(g_all, 0)), -1)
+            ref_ds, _ = oracle.sparse_mla(q_s, dec, remap, w.sm_scale)
+            err_ds = float(np.abs(host(out_ds[s_idx].float()).astype(np.float64) - ref_ds).max() /
+                           np.abs(ref_ds).max())
+            ds["parity"] = {"rows": int(sample.size), "mla_max_err_rel_to_max_ref": err_ds, "tolerance": 3e-2,
+                            "ok": bool(err_ds <= 3e-2)}
+            _log(f"fp8_ds_mla parity: err {err_ds:.2e}")
         if f8:
             # the FP8 path on part of the sample: its selections against the
             # oracle's FP8 scores (same codes), its attention output, and how
@@ -431,6 +465,8 @@ def main():
         res["dcp_share"] = dcp
     if f8:
         res["fp8_indexer"] = f8
+    if ds:
+        res["fp8_ds_mla"] = ds
     print(json.dumps(res), flush=True)
 
 

@@ -61,7 +61,13 @@ typedef enum {
   SMA_ERR_HIP = -4
 } sma_status;
 
-typedef enum { SMA_DT_BF16 = 0, SMA_DT_FP8_E4M3 = 1, SMA_DT_FP32 = 2 } sma_dtype;
+/* SMA_DT_FP8_DS_MLA: FlashMLA's 656-byte fp8_ds_mla latent row (GLM-5.3
+ * part 2, footnote 1, names it; the layout is FlashMLA's public one): bytes
+ * 0..511 the e4m3fn codes of latent dims 0..511, bytes 512..527 four fp32
+ * scales (scale b for dims 128b .. 128b+127), bytes 528..655 rope dims
+ * 512..575 as bf16.  Accepted as the KV of the sparse-MLA entry points
+ * (kv_scale must then be NULL); rows are 656 bytes apart. */
+typedef enum { SMA_DT_BF16 = 0, SMA_DT_FP8_E4M3 = 1, SMA_DT_FP32 = 2, SMA_DT_FP8_DS_MLA = 3 } sma_dtype;
 
 typedef enum {
   SMA_OP_INDEX_SCORES = 0,
@@ -173,14 +179,18 @@ sma_status sma_topk_select(const float* scores, int64_t ld_scores, const int32_t
  *   lse[i,h] = log(sum_s exp(z_s))                          (natural log)
  *
  *  q        [n_q, 64, 576] bf16
- *  kv       [n_k, 576] bf16, or e4m3fn codes with kv_scale [n_k] fp32
+ *  kv       [n_k, 576] bf16, or e4m3fn codes with kv_scale [n_k] fp32, or
+ *           [n_k] 656-byte fp8_ds_mla rows (kv_dtype SMA_DT_FP8_DS_MLA,
+ *           kv_scale NULL)
  *  idx      [n_q, top_k] int32; entries < 0 or >= n_k are skipped
  *  out      [n_q, 64, 512], out_dtype SMA_DT_BF16 or SMA_DT_FP32
  *  lse      [n_q, 64] fp32, or NULL.  A query with no valid index gets
  *           out = 0 and lse = -inf.
  *  Softmax and accumulation are fp32; QK and PV run on bf16 MFMA (an FP8
  *  row is widened to bf16 exactly; its scale multiplies the logit and the
- *  softmax weight).
+ *  softmax weight; an fp8_ds_mla row's QK is summed per 128-dim block and
+ *  each block's scale applied to its part, its PV takes the softmax weight
+ *  times the block's scale).
  *  Supported: 1 <= top_k <= 2048.  ws may be NULL (ws_bytes 0).  With at
  *  least sma_workspace_bytes(SMA_OP_SPARSE_MLA, ...) bytes (256-byte
  *  aligned), a small FP8 batch splits each query's rows into slices whose

@@ -17,7 +17,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsma.so")
 
-SMA_DT_BF16, SMA_DT_FP8_E4M3, SMA_DT_FP32 = 0, 1, 2
+SMA_DT_BF16, SMA_DT_FP8_E4M3, SMA_DT_FP32, SMA_DT_FP8_DS_MLA = 0, 1, 2, 3
+DS_ROW_BYTES = 656   # fp8_ds_mla latent row: 512 e4m3 codes, 4 fp32 scales, 64 bf16 rope dims
 SMA_OP_INDEX_SCORES, SMA_OP_TOPK, SMA_OP_SPARSE_MLA, SMA_OP_PREFILL, SMA_OP_PCP_SHARE = 0, 1, 2, 3, 4
 SMA_OP_DCP_PARTIAL = 5
 HEADS, D_QK, D_V = 64, 576, 512
@@ -102,7 +103,12 @@ def _bf16(t, name):
 
 
 def _keys(t, scale, name):
-    """-> dtype code for a key/KV tensor (bf16 or FP8 codes + per-row scale)."""
+    """-> dtype code for a key/KV tensor: bf16, FP8 codes + per-row scale, or
+    (uint8 [n, 656] with no scale) fp8_ds_mla latent rows."""
+    if t.dtype == torch.uint8 and scale is None and t.dim() == 2 and t.shape[1] == DS_ROW_BYTES:
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return SMA_DT_FP8_DS_MLA
     if t.dtype in (torch.float8_e4m3fn, torch.uint8):
         if scale is None or scale.dtype != torch.float32 or not scale.is_contiguous():
             raise ValueError(f"{name}: FP8 data needs a contiguous fp32 per-row scale")

@@ -109,10 +109,11 @@ sma_status validate_mla(const uint16_t* q, const void* kv, const float* kv_scale
   SMA_CHECK(n_q >= 0, "n_q = %d < 0", n_q);
   SMA_CHECK(n_k >= 1 && n_k <= kMaxKeys, "n_k = %lld out of [1, 2^31)", (long long)n_k);
   SMA_CHECK(top_k >= 1 && top_k <= SMA_MAX_TOPK, "top_k = %d out of [1, %d]", top_k, SMA_MAX_TOPK);
-  SMA_CHECK(kv_dtype == SMA_DT_BF16 || kv_dtype == SMA_DT_FP8_E4M3, "kv_dtype = %d", kv_dtype);
+  SMA_CHECK(kv_dtype == SMA_DT_BF16 || kv_dtype == SMA_DT_FP8_E4M3 || kv_dtype == SMA_DT_FP8_DS_MLA,
+            "kv_dtype = %d", kv_dtype);
   SMA_CHECK(out_dtype == SMA_DT_BF16 || out_dtype == SMA_DT_FP32, "out_dtype = %d", out_dtype);
   SMA_CHECK(kv != nullptr, "kv is NULL");
-  SMA_CHECK((kv_dtype == SMA_DT_FP8_E4M3) == (kv_scale != nullptr),
+  SMA_CHECK((kv_dtype == SMA_DT_FP8_E4M3) == (kv_scale != nullptr),   // fp8_ds_mla rows carry their scales
             "kv_scale must be given exactly when the KV is FP8");
   SMA_CHECK(aligned(kv, 16), "kv not 16-byte aligned");
   SMA_CHECK(std::isfinite(sm_scale), "sm_scale not finite");
@@ -185,8 +186,9 @@ sma_status run_prefill(const void* q_idx, const float* q_scale, const float* w, 
   }
   // the score blocks are dead once the index lists exist: their space holds
   // the attention kernel's split partials for small batches
-  sma::MlaArgs ma{q, kv, kv_scale, kv_dtype == SMA_DT_FP8_E4M3, n_k, idx, n_q, top_k, sm_scale,
+  sma::MlaArgs ma{q, kv, kv_scale, kv_dtype != SMA_DT_BF16, n_k, idx, n_q, top_k, sm_scale,
                   out, out_dtype == SMA_DT_FP32, lse, score_ws, score_ws_bytes};
+  ma.ds_mla = kv_dtype == SMA_DT_FP8_DS_MLA;
   hipError_t e = sma::launch_sparse_mla(ma, st);
   if (e != hipSuccess) return hip_fail(e, "sparse_mla launch");
   return SMA_OK;
@@ -303,8 +305,9 @@ sma_status sma_sparse_mla_prefill(const uint16_t* q, const void* kv, const float
   if (n_q == 0) return SMA_OK;
   if ((s = check_device()) != SMA_OK) return s;
   if (ws && !aligned(ws, 256)) return fail(SMA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-  sma::MlaArgs a{q, kv, kv_scale, kv_dtype == SMA_DT_FP8_E4M3, n_k, idx, n_q, top_k, sm_scale,
+  sma::MlaArgs a{q, kv, kv_scale, kv_dtype != SMA_DT_BF16, n_k, idx, n_q, top_k, sm_scale,
                  out, out_dtype == SMA_DT_FP32, lse, ws, ws ? ws_bytes : 0};
+  a.ds_mla = kv_dtype == SMA_DT_FP8_DS_MLA;
   hipError_t e = sma::launch_sparse_mla(a, (hipStream_t)stream);
   return e == hipSuccess ? SMA_OK : hip_fail(e, "sparse_mla launch");
 }
@@ -331,9 +334,10 @@ sma_status sma_dcp_shard_partial(int32_t rank, int32_t dcp_size, const uint16_t*
   int32_t* local = static_cast<int32_t*>(ws);
   hipError_t e = sma::launch_dcp_local_idx(idx, n_q, top_k, rank, dcp_size, n_k_local, local, st);
   if (e != hipSuccess) return hip_fail(e, "dcp_local_idx launch");
-  sma::MlaArgs a{q, kv_local, kv_scale_local, kv_dtype == SMA_DT_FP8_E4M3, n_k_local, local, n_q, top_k,
+  sma::MlaArgs a{q, kv_local, kv_scale_local, kv_dtype != SMA_DT_BF16, n_k_local, local, n_q, top_k,
                  sm_scale, out_partial, true, lse_partial, static_cast<uint8_t*>(ws) + idx_bytes,
                  ws_bytes - idx_bytes};
+  a.ds_mla = kv_dtype == SMA_DT_FP8_DS_MLA;
   e = sma::launch_sparse_mla(a, st);
   return e == hipSuccess ? SMA_OK : hip_fail(e, "sparse_mla launch");
 }

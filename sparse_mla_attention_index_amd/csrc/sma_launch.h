@@ -52,6 +52,8 @@ struct MlaArgs {
   // Workspace for the split partials of small FP8 batches (may be null).
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  // fp8 && ds_mla: 656-byte fp8_ds_mla rows (scales inside the row, kv_scale unused)
+  bool ds_mla = false;
 };
 
 // Number of row slices per query the FP8 attention kernel uses for n_q

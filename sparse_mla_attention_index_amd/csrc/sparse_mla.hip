@@ -7,11 +7,18 @@
 // over 512).
 //
 // Two kernels share that computation:
-//  * sparse_mla_kernel (FP8-e4m3 KV with a per-row scale): one 4-wave
+//  * sparse_mla_kernel (FP8-e4m3 KV, two storage formats): one 4-wave
 //    workgroup per query, wave w owns heads
 //    16w..16w+15, rows staged through registers into a padded row-major
-//    LDS tile and dequantised to bf16 on the way; v_mfma_f32_16x16x32_bf16
-//    for S^T = K.Q^T and O^T += V^T.P^T with an online softmax.
+//    LDS tile, the codes widened to bf16 exactly on the way;
+//    v_mfma_f32_16x16x32_bf16 for S^T = K.Q^T and O^T += V^T.P^T with an
+//    online softmax.  The scales stay out of the bf16 operands: a row's
+//    scale multiplies its logit and its softmax weight.  Formats: 576 codes
+//    with one fp32 scale per row (a separate array), or FlashMLA's 656-byte
+//    fp8_ds_mla row (512 codes, four fp32 scales of 128 dims each, 64 bf16
+//    rope dims; GLM-5.3 part 2, footnote 1, names it), whose QK sums run per
+//    128-dim block so each block's scale meets its own partial logit, and
+//    whose PV uses one scaled P per block.
 //  * sparse_mla_bf16_kernel (bf16 KV): one 2-wave workgroup per query that
 //    splits both contractions by dims, gathers with direct global->LDS
 //    loads and uses v_mfma_f32_32x32x16_bf16 (twice the rate of the 16x16
@@ -35,14 +42,22 @@ constexpr int kMlaPartFloats = kHeads * kDv + 2 * kHeads;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <bool FP8, bool OUT_F32>
+// KV formats of sparse_mla_kernel
+constexpr int kKvBf16 = 0;      // bf16 rows (576 x 2 bytes)
+constexpr int kKvFp8Row = 1;    // 576 e4m3 codes, one fp32 scale per row in a separate array
+constexpr int kKvFp8Ds = 2;     // 656-byte fp8_ds_mla rows
+constexpr int kDsRowB = 656;    // 512 codes + 4 fp32 scales + 64 bf16
+constexpr int kDsChunks = kDsRowB / 16;   // 41 16-byte chunks: 32 of codes, 1 of scales, 8 of rope
+
+template <int KVF, bool OUT_F32>
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv, const float* __restrict__ kv_scale,
     int n_k, const int32_t* __restrict__ idx, int n_q, int K, float scale_log2,
     void* __restrict__ out, float* __restrict__ lse, int n_split, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][kMlaRows * kMlaRowB];
   __shared__ int s_list[SMA_MAX_TOPK_DEV];
-  __shared__ float s_scale[2][kMlaRows];
+  constexpr bool FP8 = KVF != kKvBf16, DS = KVF == kKvFp8Ds;
+  __shared__ __attribute__((aligned(16))) float s_scale[2][DS ? 4 * kMlaRows : kMlaRows];
   __shared__ uint32_t s_cnt[kMlaThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -120,8 +135,9 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
   }
 
   // ---- gather staging ----
-  constexpr int NCH = FP8 ? (kMlaRows * kDqk / 16 + kMlaThreads - 1) / kMlaThreads
-                          : kMlaRows * kDqk / 8 / kMlaThreads;   // 16-byte loads per thread
+  constexpr int NCH = DS    ? (kMlaRows * kDsChunks + kMlaThreads - 1) / kMlaThreads
+                      : FP8 ? (kMlaRows * kDqk / 16 + kMlaThreads - 1) / kMlaThreads
+                            : kMlaRows * kDqk / 8 / kMlaThreads;   // 16-byte loads per thread
   u32x4 stage[NCH];
   float stage_sc = 0.f;
   auto load_tile = [&](int t) {
@@ -129,7 +145,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
 #pragma unroll
     for (int r = 0; r < NCH; ++r) {
       const int c = tid + kMlaThreads * r;
-      if constexpr (FP8) {
+      if constexpr (DS) {
+        if (c < kMlaRows * kDsChunks) {
+          const int row = c / kDsChunks, col = c % kDsChunks;
+          const int li = r0 + row < le ? r0 + row : lb;
+          stage[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(kv) +
+                                                     (int64_t)s_list[li] * kDsRowB + col * 16);
+        }
+      } else if constexpr (FP8) {
         if (c < kMlaRows * kDqk / 16) {
           const int row = c / (kDqk / 16), col = c % (kDqk / 16);
           const int li = r0 + row < le ? r0 + row : lb;
@@ -143,7 +166,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
                                                    (int64_t)s_list[li] * kDqk + col * 8);
       }
     }
-    if constexpr (FP8) {
+    if constexpr (KVF == kKvFp8Row) {
       if (tid < kMlaRows) {
         const int li = r0 + tid < le ? r0 + tid : lb;
         stage_sc = kv_scale[s_list[li]];
@@ -154,7 +177,22 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
 #pragma unroll
     for (int r = 0; r < NCH; ++r) {
       const int c = tid + kMlaThreads * r;
-      if constexpr (FP8) {
+      if constexpr (DS) {
+        if (c < kMlaRows * kDsChunks) {
+          const int row = c / kDsChunks, col = c % kDsChunks;
+          if (col < 32) {          // codes of dims 16col .. 16col + 15, widened exactly
+            uint8_t* dst = &s_kv[buf][row * kMlaRowB + col * 32];
+            const u32x2 t0 = e4m3x4_to_bf16x4(stage[r][0]), t1 = e4m3x4_to_bf16x4(stage[r][1]);
+            const u32x2 t2 = e4m3x4_to_bf16x4(stage[r][2]), t3 = e4m3x4_to_bf16x4(stage[r][3]);
+            *reinterpret_cast<u32x4*>(dst) = u32x4{t0[0], t0[1], t1[0], t1[1]};
+            *reinterpret_cast<u32x4*>(dst + 16) = u32x4{t2[0], t2[1], t3[0], t3[1]};
+          } else if (col == 32) {  // the row's four block scales
+            *reinterpret_cast<u32x4*>(&s_scale[buf][4 * row]) = stage[r];
+          } else {                 // rope dims 512 + 8(col - 33) .., bf16 as stored
+            *reinterpret_cast<u32x4*>(&s_kv[buf][row * kMlaRowB + 1024 + 16 * (col - 33)]) = stage[r];
+          }
+        }
+      } else if constexpr (FP8) {
         if (c < kMlaRows * kDqk / 16) {
           const int row = c / (kDqk / 16), col = c % (kDqk / 16);
           uint8_t* dst = &s_kv[buf][row * kMlaRowB + col * 32];
@@ -168,7 +206,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         *reinterpret_cast<u32x4*>(&s_kv[buf][row * kMlaRowB + col * 16]) = stage[r];
       }
     }
-    if constexpr (FP8) {
+    if constexpr (KVF == kKvFp8Row) {
       if (tid < kMlaRows) s_scale[buf][tid] = stage_sc;
     }
   };
@@ -193,13 +231,36 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
 
     // S^T = K . Q^T : rows 16mt + 4g + r, head i
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if constexpr (DS) {
+      // block b (dims 128b .. +127, k-steps 4b .. 4b+3) carries the row's
+      // scale b; the rope dims (k-steps 16, 17) carry none
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) {
+      for (int b = 0; b < 5; ++b) {
+        f32x4 blk[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(tile + (16 * mt + i) * kMlaRowB + (32 * ks + 8 * g) * 2);
-        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
+        for (int ks = 4 * b; ks < (b < 4 ? 4 * b + 4 : kDqk / 32); ++ks) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            const bf16x8 a =
+                *reinterpret_cast<const bf16x8*>(tile + (16 * mt + i) * kMlaRowB + (32 * ks + 8 * g) * 2);
+            blk[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], blk[mt], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sacc[mt][r] += b < 4 ? blk[mt][r] * s_scale[buf][4 * (16 * mt + 4 * g + r) + b] : blk[mt][r];
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kDqk / 32; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(tile + (16 * mt + i) * kMlaRowB + (32 * ks + 8 * g) * 2);
+          sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
+        }
       }
     }
 
@@ -213,7 +274,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * mt + 4 * g + r;
         float x = sacc[mt][r] * scale_log2;
-        if constexpr (FP8) x *= s_scale[buf][row];
+        if constexpr (KVF == kKvFp8Row) x *= s_scale[buf][row];
         x = row < valid_rows ? x : -INFINITY;
         s2[4 * mt + r] = x;
         mx = fmaxf(mx, x);
@@ -229,7 +290,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
       const float pe = exp2f(s2[e] - m_new);
       psum += pe;
       pv[e] = pe;
-      if constexpr (FP8) pv[e] = pe * s_scale[buf][16 * (e / 4) + 4 * g + (e % 4)];
+      if constexpr (KVF == kKvFp8Row) pv[e] = pe * s_scale[buf][16 * (e / 4) + 4 * g + (e % 4)];
     }
     l_run = l_run * alpha + psum;
     if (__any(alpha != 1.f)) {
@@ -237,9 +298,19 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
       for (int mt = 0; mt < kDv / 16; ++mt) o[mt] *= alpha;
     }
     m_run = m_new;
-    bf16x8 pb;
+    // P^T operand: with fp8_ds_mla rows, one per 128-dim block of V, the
+    // softmax weight times that block's scale of the row
+    constexpr int NPB = DS ? 4 : 1;
+    bf16x8 pb[NPB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pv[e];
+    for (int b = 0; b < NPB; ++b)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (DS)
+          pb[b][e] = (__bf16)(pv[e] * s_scale[buf][4 * (16 * (e / 4) + 4 * g + (e % 4)) + b]);
+        else
+          pb[b][e] = (__bf16)pv[e];
+      }
 
     // O^T += V^T . P^T ; V^T columns read transposed from the row-major tile
     const uint8_t* va_base = tile + (4 * g + (i >> 2)) * kMlaRowB + 8 * (i & 3);
@@ -249,7 +320,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
       const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(va_base + 32 * mt));
       const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_base + 32 * mt));
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mt], 0, 0, 0);
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[DS ? mt / 8 : 0], o[mt], 0, 0, 0);
     }
 
     if (has_next) store_tile(buf ^ 1);
@@ -809,12 +880,17 @@ hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
     if (n_split > 1 && (A.ws == nullptr || A.ws_bytes < mla_split_bytes(A.n_q, n_split))) n_split = 1;
     float* part = n_split > 1 ? static_cast<float*>(A.ws) : nullptr;
     const dim3 grid_s((unsigned)(A.n_q * n_split));
-    if (A.out_f32)
-      hipLaunchKernelGGL((sparse_mla_kernel<true, true>), grid_s, block, 0, st, A.q, A.kv, A.kv_scale,
-                         (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part);
-    else
-      hipLaunchKernelGGL((sparse_mla_kernel<true, false>), grid_s, block, 0, st, A.q, A.kv, A.kv_scale,
-                         (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part);
+#define SMA_MLA_F8(KVF, F32)                                                                          \
+  hipLaunchKernelGGL((sparse_mla_kernel<KVF, F32>), grid_s, block, 0, st, A.q, A.kv, A.kv_scale, (int)A.n_k, \
+                     A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part)
+    if (A.ds_mla) {
+      if (A.out_f32) SMA_MLA_F8(kKvFp8Ds, true);
+      else SMA_MLA_F8(kKvFp8Ds, false);
+    } else {
+      if (A.out_f32) SMA_MLA_F8(kKvFp8Row, true);
+      else SMA_MLA_F8(kKvFp8Row, false);
+    }
+#undef SMA_MLA_F8
     if (n_split > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

@@ -80,7 +80,7 @@ def test_topk_validation(topk, ld, code):
 
 @pytest.mark.parametrize("kvdt,scale,odt,topk,msg", [
     (1, None, 0, 8, "kv_scale"), (0, FAKE, 0, 8, "kv_scale"), (0, None, 1, 8, "out_dtype"),
-    (0, None, 0, 0, "top_k"), (5, None, 0, 8, "kv_dtype")])
+    (0, None, 0, 0, "top_k"), (5, None, 0, 8, "kv_dtype"), (3, FAKE, 0, 8, "kv_scale")])
 def test_mla_validation(kvdt, scale, odt, topk, msg):
     r = sma.lib().sma_sparse_mla_prefill(FAKE, FAKE, scale, kvdt, 100, FAKE, 1, topk, 0.1, FAKE, odt, None,
                                          None, 0, None)
