@@ -273,6 +273,24 @@ def prefill(q_idx, w, k_idx, q, kv, q_pos, top_k: int, sm_scale: float):
     return scores, idx, out, lse
 
 
+def absorb_q(q_nope: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """Absorb the key half of kv_b_proj into the query (DeepSeek multi-node
+    page, "Couche MLA": kv_b_proj split into k_b_proj and v_b_proj, computed
+    as batched products; "Travaux futurs": decode absorbs the matrices).  A
+    head's no-rope key is k[s,h,:] = W_UK[h] c_s, so q_nope[i,h,:] . k[s,h,:]
+    = (W_UK[h]^T q_nope[i,h,:]) . c_s:  q_lat[i,h,:] = W_UK[h]^T q_nope[i,h,:].
+    q_nope [n, H, d_nope], w_uk [H, d_nope, d_lat] -> [n, H, d_lat]."""
+    return np.einsum("nhd,hdc->nhc", np.asarray(q_nope, np.float64), np.asarray(w_uk, np.float64))
+
+
+def project_out(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """Apply the value half of kv_b_proj to the attention's latent output
+    (same page and sections): v[s,h,:] = W_UV[h] c_s, so the head's output is
+    o[i,h,:] = W_UV[h] o_lat[i,h,:].  o_lat [n, H, d_lat], w_uv [H, d_v,
+    d_lat] -> [n, H, d_v]."""
+    return np.einsum("nhc,hvc->nhv", np.asarray(o_lat, np.float64), np.asarray(w_uv, np.float64))
+
+
 def dcp_shard_rows(rank: int, dcp_size: int, kv: np.ndarray) -> np.ndarray:
     """The latent rows one DCP rank stores: tokens are dealt round-robin over
     the ranks, so rank r holds tokens r, r + P, r + 2P, ... (local row j is

@@ -8,6 +8,8 @@
   random kv_b_proj split into W_UK / W_UV (DeepSeek multi-node deployment
   page, "Parallélisme de tenseurs", "Couche MLA", "Travaux futurs"), MHA over
   k = [W_UK c, k_rope], v = W_UV c equals W_UV applied to the absorbed output.
+  The absorption and output projections are the oracle's absorb_q and
+  project_out, also checked by integer brute force.
 * Invariants: constant values give that constant; the index order does not
   matter; one selected row returns that row's value; empty sets give 0/-inf.
 """
@@ -62,10 +64,10 @@ def test_absorbed_equals_expanded():
     for i in range(n_q):
         idx[i, :12] = np.sort(rng.choice(n_k, 12, replace=False))
     # absorbed: q_abs = [W_UK^T q_nope, q_rope], kv = [c, k_rope]
-    q_abs = np.concatenate([np.einsum("hnl,qhn->qhl", W_UK, q_nope), q_rope], axis=-1)
+    q_abs = np.concatenate([oracle.absorb_q(q_nope, W_UK), q_rope], axis=-1)
     kv = np.concatenate([c, k_rope], axis=-1)
     o_lat, _ = oracle.sparse_mla(q_abs, kv, idx, TAU)
-    o_abs = np.einsum("hvl,qhl->qhv", W_UV, o_lat)
+    o_abs = oracle.project_out(o_lat, W_UV)
     # expanded MHA with a mask of the selected set, via torch SDPA
     k_full = np.concatenate([np.einsum("hnl,sl->hsn", W_UK, c),
                              np.broadcast_to(k_rope, (H, n_k, d_rope))], axis=-1)   # [H, n_k, 192]
@@ -120,3 +122,21 @@ def test_softmax_weights_sum_to_one():
     for i in range(4):
         z = TAU * (q[i] @ kv[idx[i]].T)
         np.testing.assert_allclose(np.exp(z - lse[i][:, None]).sum(axis=1), 1.0, atol=1e-6)
+
+
+def test_absorb_and_project_integer_bruteforce():
+    """Python-integer loops on small integer inputs (exact)."""
+    rng = np.random.default_rng(5)
+    n, H, dn, dl, dv = 3, 2, 4, 6, 5
+    qn = rng.integers(-3, 4, (n, H, dn))
+    wuk = rng.integers(-3, 4, (H, dn, dl))
+    ol = rng.integers(-3, 4, (n, H, dl))
+    wuv = rng.integers(-3, 4, (H, dv, dl))
+    ql = oracle.absorb_q(qn, wuk)
+    o = oracle.project_out(ol, wuv)
+    for i in range(n):
+        for h in range(H):
+            for c in range(dl):
+                assert ql[i, h, c] == sum(int(qn[i, h, d]) * int(wuk[h, d, c]) for d in range(dn))
+            for v in range(dv):
+                assert o[i, h, v] == sum(int(ol[i, h, c]) * int(wuv[h, v, c]) for c in range(dl))
