@@ -282,6 +282,30 @@ def main():
         _log(f"fp8_ds_mla: rows packed in {time.time() - t_g:.1f}s, sparse_mla {t_ds:.3f} ms "
              f"(per-row FP8 format {t_mla:.3f} ms)")
 
+    # absorption leg (prefill): q_nope through W_UK into the latent part of a
+    # query, and the attention's latent output through W_UV, 64 heads
+    ab = None
+    if args.workload == "prefill64k":
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(synth.SEED_BASE + 9)
+        q_nope = torch.randn((n_q, 64, 128), generator=gen, device=dev).to(torch.bfloat16)
+        w_uk = (torch.randn((64, 128, 512), generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+        w_uv = (torch.randn((64, 128, 512), generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+        q_abs = torch.empty((n_q, 64, 576), dtype=torch.bfloat16, device=dev)
+        o_proj = torch.empty((n_q, 64, 128), dtype=torch.bfloat16, device=dev)
+        o_lat = out if out.dtype == torch.bfloat16 else out.to(torch.bfloat16)
+        t_aq = timed(lambda: sma.absorb_q(q_nope, w_uk, out=q_abs), reps)
+        t_po = timed(lambda: sma.project_out(o_lat, w_uv, out=o_proj), reps)
+        fl = 2 * n_q * 64 * 128 * 512
+        b_aq = n_q * 64 * (128 + 512) * 2 + w_uk.numel() * 2
+        b_po = n_q * 64 * (512 + 128) * 2 + w_uv.numel() * 2
+        ab = {"absorb_q_ms": round(t_aq, 4), "absorb_q_gbs": round(b_aq / (t_aq * 1e-3) / 1e9, 1),
+              "project_out_ms": round(t_po, 4), "project_out_gbs": round(b_po / (t_po * 1e-3) / 1e9, 1),
+              "bytes_per_launch": [b_aq, b_po], "flops_per_launch": fl,
+              "absorb_q_frac_hbm": round(b_aq / (t_aq * 1e-3) / 1e9 / acc.PEAK_HBM_GBS, 4),
+              "project_out_frac_hbm": round(b_po / (t_po * 1e-3) / 1e9 / acc.PEAK_HBM_GBS, 4)}
+        _log(f"absorption: absorb_q {t_aq:.3f} ms, project_out {t_po:.3f} ms")
+
     # FP8 indexer leg: q_I (and bf16 keys) quantised per row on the GPU, the
     # e4m3 x e4m3 indexer, and a whole step with it (quantisers included).
     f8 = None
@@ -403,6 +427,19 @@ def main():
         parity = {"rows": int(sample.size), "topk_threshold_rule": bool(rule), "topk_sets_identical": exact_sets,
                   "mla_max_err_rel_to_max_ref": err, "tolerance": 3e-2 if w.fp8 else 1e-2,
                   "ok": bool(rule and err <= (3e-2 if w.fp8 else 1e-2))}
+        if ab:
+            # absorption products on a few sampled rows against the oracle
+            sub = sample[:: max(1, sample.size // 32)]
+            sa_ = torch.from_numpy(sub).to(dev)
+            qn_h = f(host(q_nope[sa_], np.uint16))
+            ref_q = oracle.absorb_q(qn_h, f(host(w_uk, np.uint16)))
+            got_q = f(host(q_abs[sa_][:, :, :512].contiguous(), np.uint16))
+            ref_o = oracle.project_out(f(host(o_lat[sa_], np.uint16)), f(host(w_uv, np.uint16)))
+            got_o = f(host(o_proj[sa_], np.uint16))
+            e_q = float(np.abs(got_q - ref_q).max() / np.abs(ref_q).max())
+            e_o = float(np.abs(got_o - ref_o).max() / np.abs(ref_o).max())
+            ab["parity"] = {"rows": int(sub.size), "absorb_q_max_err_rel": e_q, "project_out_max_err_rel": e_o,
+                            "ok": bool(e_q <= 1e-2 and e_o <= 1e-2)}
         if ds:
             # the 656-byte rows: attention on the GPU's own lists against the
             # oracle over the decoded rows those lists select
@@ -467,6 +504,8 @@ def main():
         res["fp8_indexer"] = f8
     if ds:
         res["fp8_ds_mla"] = ds
+    if ab:
+        res["absorption"] = ab
     print(json.dumps(res), flush=True)
 
 

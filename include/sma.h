@@ -254,6 +254,30 @@ sma_status sma_pcp_rank_share(int32_t rank, int32_t pcp_size, int64_t L_total,
                               int32_t* idx_share, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sma_absorb_q / sma_project_out — the absorbed form's per-head batched
+ * products around sparse MLA (DeepSeek multi-node page, "Couche MLA":
+ * kv_b_proj split into k_b_proj and v_b_proj, computed as batched products;
+ * "Travaux futurs": decode absorbs the matrices).  With the key half
+ * W_UK[h] and the value half W_UV[h] of kv_b_proj, each [128, 512] bf16
+ * (row d of W_UK[h] maps the 512-dim latent to no-rope key dim d):
+ *
+ *   sma_absorb_q:    q_out[(i*heads + h)*ld_out + c] = sum_d q_nope[i,h,d] * W_UK[h,d,c]
+ *                    for c < 512 (the rest of each ld_out row is untouched,
+ *                    so ld_out = 576 writes the latent part of a sparse-MLA
+ *                    query [n, heads, 576] in place, beside its rope dims)
+ *   sma_project_out: out[i,h,d] = sum_c o_lat[i,h,c] * W_UV[h,d,c]
+ *
+ *  q_nope [n, heads, 128], w_uk / w_uv [heads, 128, 512], o_lat [n, heads,
+ *  512], out [n, heads, 128]: bf16, contiguous, 16-byte aligned.  fp32
+ *  accumulation on bf16 MFMA, one rounding to bf16 at the end.
+ *  Requires 1 <= heads <= 1024, ld_out >= 512 and a multiple of 8.
+ */
+sma_status sma_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, int32_t n, int32_t heads, uint16_t* q_out,
+                        int64_t ld_out, void* stream);
+sma_status sma_project_out(const uint16_t* o_lat, const uint16_t* w_uv, int32_t n, int32_t heads, uint16_t* out,
+                           void* stream);
+
+/*
  * sma_dcp_shard_partial — one DCP rank's share of sparse MLA (same article,
  * "DCP : sharder aussi le cache KV": tokens are dealt round-robin over the
  * dcp_size ranks, so rank r stores tokens r, r + P, r + 2P, ...; in decode

@@ -1,9 +1,10 @@
 """MI355X (gfx950) sparse-MLA prefill path: indexer scores -> per-query
 top-k -> sparse MLA over the selected latent rows, plus one PCP rank's
 share, one DCP rank's partial attention with the log-sum-exp merge, and the
-FP8 indexer (per-row FP8 quantisation, e4m3 x e4m3 scores).  The compute
+FP8 indexer (per-row FP8 quantisation, e4m3 x e4m3 scores) and the
+absorption products around sparse MLA.  The compute
 runs in hand-written HIP kernels behind the C ABI of include/sma.h
 (libsma.so); this package is the thin Python binding."""
-from ._lib import (SmaError, dcp_shard_partial, index_scores, index_scores_fp8, last_error, lib,  # noqa: F401
+from ._lib import (SmaError, absorb_q, dcp_shard_partial, index_scores, index_scores_fp8, last_error, lib,  # noqa: F401
                    lse_merge, pcp_rank_share, prefill, prefill_fp8_indexer, quantize_fp8_rows,
-                   sparse_mla_prefill, topk_select, version, workspace_bytes)
+                   project_out, sparse_mla_prefill, topk_select, version, workspace_bytes)

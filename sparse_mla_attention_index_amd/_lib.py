@@ -37,6 +37,8 @@ SIGNATURES = {
                                      _P]),
     "sma_lse_merge": (_I32, [_P, _P, _I32, _I32, _P, _I32, _P, _P]),
     "sma_quantize_fp8_rows": (_I32, [_P, _I64, _I32, _P, _P, _P]),
+    "sma_absorb_q": (_I32, [_P, _P, _I32, _I32, _P, _I64, _P]),
+    "sma_project_out": (_I32, [_P, _P, _I32, _I32, _P, _P]),
     "sma_index_scores_fp8": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _I64, _P]),
     "sma_prefill_fp8_indexer": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _I32, _P, _I32, _I64, _I32, _I32,
                                        _I32, _F, _P, _I32, _P, _P, _P, _SZ, _P]),
@@ -296,6 +298,39 @@ def prefill_fp8_indexer(q_idx, q_scale, w, k_idx, k_scale, q, kv, q_pos, top_k: 
                                          _ptr(idx_out), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(), _stream(dev)))
     return out, lse, idx_out
+
+
+def absorb_q(q_nope, w_uk, *, out=None):
+    """q_lat[i,h,:] = W_UK[h]^T q_nope[i,h,:]: q_nope bf16 [n, H, 128], w_uk
+    bf16 [H, 128, 512] -> bf16 [n, H, 512]; `out` may be a sparse-MLA query
+    [n, H, 576] (its first 512 dims are written, the rope dims kept)."""
+    n, heads, d = q_nope.shape
+    _bf16(q_nope, "q_nope")
+    _bf16(w_uk, "w_uk")
+    if d != 128 or tuple(w_uk.shape) != (heads, 128, 512):
+        raise ValueError("q_nope [n, H, 128] and w_uk [H, 128, 512] expected")
+    if out is None:
+        out = torch.empty((n, heads, 512), dtype=torch.bfloat16, device=q_nope.device)
+    _bf16(out, "out")
+    if out.dim() != 3 or tuple(out.shape[:2]) != (n, heads) or out.shape[2] < 512:
+        raise ValueError("out must be [n, H, >= 512]")
+    _check(lib().sma_absorb_q(_ptr(q_nope), _ptr(w_uk), n, heads, _ptr(out), out.shape[2], _stream(q_nope.device)))
+    return out
+
+
+def project_out(o_lat, w_uv, *, out=None):
+    """o[i,h,:] = W_UV[h] o_lat[i,h,:]: o_lat bf16 [n, H, 512], w_uv bf16
+    [H, 128, 512] -> bf16 [n, H, 128]."""
+    n, heads, d = o_lat.shape
+    _bf16(o_lat, "o_lat")
+    _bf16(w_uv, "w_uv")
+    if d != 512 or tuple(w_uv.shape) != (heads, 128, 512):
+        raise ValueError("o_lat [n, H, 512] and w_uv [H, 128, 512] expected")
+    if out is None:
+        out = torch.empty((n, heads, 128), dtype=torch.bfloat16, device=o_lat.device)
+    _bf16(out, "out")
+    _check(lib().sma_project_out(_ptr(o_lat), _ptr(w_uv), n, heads, _ptr(out), _stream(o_lat.device)))
+    return out
 
 
 def pcp_rank_share(rank: int, pcp_size: int, q_idx_share, w_share, k_idx, q_share, kv, top_k: int,

@@ -278,6 +278,39 @@ sma_status sma_quantize_fp8_rows(const uint16_t* x, int64_t n_rows, int32_t d, u
   return e == hipSuccess ? SMA_OK : hip_fail(e, "quantize_fp8_rows launch");
 }
 
+sma_status sma_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, int32_t n, int32_t heads, uint16_t* q_out,
+                        int64_t ld_out, void* stream) {
+  g_err.clear();
+  SMA_CHECK(n >= 0, "n = %d < 0", n);
+  SMA_CHECK(heads >= 1 && heads <= 1024, "heads = %d out of [1, 1024]", heads);
+  SMA_CHECK(ld_out >= 512 && ld_out % 8 == 0, "ld_out = %lld (>= 512, a multiple of 8)", (long long)ld_out);
+  if (n == 0) return SMA_OK;
+  SMA_CHECK(q_nope && w_uk && q_out, "q_nope, w_uk and q_out must be non-NULL");
+  SMA_CHECK(aligned(q_nope, 16) && aligned(w_uk, 16) && aligned(q_out, 16), "tensors must be 16-byte aligned");
+  sma_status s = check_device();
+  if (s != SMA_OK) return s;
+  sma::BmmArgs a{q_nope, (int64_t)heads * 128, 128, w_uk, 512, 128 * 512, true,
+                 q_out, (int64_t)heads * ld_out, ld_out, n, 512, 128, heads};
+  hipError_t e = sma::launch_bmm_bf16(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMA_OK : hip_fail(e, "absorb_q launch");
+}
+
+sma_status sma_project_out(const uint16_t* o_lat, const uint16_t* w_uv, int32_t n, int32_t heads, uint16_t* out,
+                           void* stream) {
+  g_err.clear();
+  SMA_CHECK(n >= 0, "n = %d < 0", n);
+  SMA_CHECK(heads >= 1 && heads <= 1024, "heads = %d out of [1, 1024]", heads);
+  if (n == 0) return SMA_OK;
+  SMA_CHECK(o_lat && w_uv && out, "o_lat, w_uv and out must be non-NULL");
+  SMA_CHECK(aligned(o_lat, 16) && aligned(w_uv, 16) && aligned(out, 16), "tensors must be 16-byte aligned");
+  sma_status s = check_device();
+  if (s != SMA_OK) return s;
+  sma::BmmArgs a{o_lat, (int64_t)heads * 512, 512, w_uv, 512, 128 * 512, false,
+                 out, (int64_t)heads * 128, 128, n, 128, 512, heads};
+  hipError_t e = sma::launch_bmm_bf16(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMA_OK : hip_fail(e, "project_out launch");
+}
+
 sma_status sma_topk_select(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t n_q,
                            int64_t n_k, int32_t top_k, int32_t* idx, void* ws, size_t ws_bytes,
                            void* stream) {

@@ -82,6 +82,23 @@ hipError_t launch_dcp_local_idx(const int32_t* idx, int n_q, int K, int rank, in
 constexpr int kMaxMergeParts = 64;
 hipError_t launch_lse_merge(const float* parts, const float* lses, int n_part, int n_q, void* out, bool out_f32,
                             float* lse_out, hipStream_t s);
+// Batched bf16 product C_h = A_h . B_h (fp32 accumulation, bf16 out) for
+// h < batch: A_h[m][k] at A + h*a_bs + m*lda + k; B_h[k][n] at
+// B + h*b_bs + k*ldb + n when b_kn, else at B + h*b_bs + n*ldb + k;
+// C_h[m][n] at C + h*c_bs + m*ldc + n.  Requires N % 128 == 0, K % 64 == 0,
+// 16-byte aligned rows.
+struct BmmArgs {
+  const uint16_t* A;
+  int64_t lda, a_bs;
+  const uint16_t* B;
+  int64_t ldb, b_bs;
+  bool b_kn;
+  uint16_t* C;
+  int64_t ldc, c_bs;
+  int M, N, K, batch;
+};
+hipError_t launch_bmm_bf16(const BmmArgs& a, hipStream_t s);
+
 hipError_t launch_pcp_positions(int32_t* pos, int32_t rank, int32_t pcp_size, int64_t L_total,
                                 hipStream_t s);
 

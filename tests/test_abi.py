@@ -155,3 +155,15 @@ def test_prefill_fp8_indexer_workspace_check():
     r = sma.lib().sma_prefill_fp8_indexer(FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 16, 1000,
                                           64, 128, 64, 0.1, FAKE, 0, None, None, FAKE, 100, None)
     assert r == -3 and "workspace" in sma.last_error()
+
+
+@pytest.mark.parametrize("n,heads,ld,msg", [(-1, 64, 576, "n ="), (4, 0, 576, "heads"), (4, 64, 500, "ld_out"),
+                                            (4, 64, 580, "ld_out")])
+def test_absorb_q_validation(n, heads, ld, msg):
+    r = sma.lib().sma_absorb_q(FAKE, FAKE, n, heads, FAKE, ld, None)
+    assert r == -1 and msg in sma.last_error()
+
+
+def test_project_out_validation():
+    assert sma.lib().sma_project_out(FAKE, FAKE, 4, 2000, FAKE, None) == -1 and "heads" in sma.last_error()
+    assert sma.lib().sma_project_out(None, FAKE, 4, 64, FAKE, None) == -1 and "NULL" in sma.last_error()
