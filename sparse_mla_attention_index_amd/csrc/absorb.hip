@@ -37,7 +37,7 @@ typedef __attribute__((address_space(3))) i16x4 bm_lds_i16x4;
 template <bool B_KN>
 __global__ __launch_bounds__(kBmThreads, 2) void bmm_bf16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int64_t a_bs, const uint16_t* __restrict__ B, int64_t ldb,
-    int64_t b_bs, uint16_t* __restrict__ C, int64_t ldc, int64_t c_bs, int M, int K, int m_tiles, int n_tiles) {
+    int64_t b_bs, uint16_t* __restrict__ C, int64_t ldc, int64_t c_bs, int M, int K, int batch, int n_tiles) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kBmABytes + kBmBBytes)];
   // chunk buffer b: A at b * kBmABytes, B at 2 * kBmABytes + b * kBmBBytes
   auto s_a = [&](int b) { return smem + b * kBmABytes; };
@@ -46,10 +46,12 @@ __global__ __launch_bounds__(kBmThreads, 2) void bmm_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;         // the wave's 64 x 64 quadrant
   const int lrow = lane & 31, khalf = lane >> 5;
-  // n fastest: the workgroups of one A tile run together and share it in L2
+  // n fastest, then the head: the workgroups of one A tile run together and
+  // share it in L2, and those running at once cover all heads of the same
+  // rows, whose A and C rows are contiguous in memory ([token][head][...])
   const int nt = (int)(blockIdx.x % n_tiles);
   const int rest = (int)(blockIdx.x / n_tiles);
-  const int mt = rest % m_tiles, h = rest / m_tiles;
+  const int h = rest % batch, mt = rest / batch;
   const int m0 = mt * kBmTM, n0 = nt * kBmTN;
   const uint16_t* Ah = A + h * a_bs;
   const uint16_t* Bh = B + h * b_bs;
@@ -167,10 +169,10 @@ hipError_t launch_bmm_bf16(const BmmArgs& a, hipStream_t st) {
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   if (a.b_kn)
     hipLaunchKernelGGL(bmm_bf16_kernel<true>, dim3((unsigned)grid), dim3(kBmThreads), 0, st, a.A, a.lda, a.a_bs,
-                       a.B, a.ldb, a.b_bs, a.C, a.ldc, a.c_bs, a.M, a.K, m_tiles, n_tiles);
+                       a.B, a.ldb, a.b_bs, a.C, a.ldc, a.c_bs, a.M, a.K, a.batch, n_tiles);
   else
     hipLaunchKernelGGL(bmm_bf16_kernel<false>, dim3((unsigned)grid), dim3(kBmThreads), 0, st, a.A, a.lda, a.a_bs,
-                       a.B, a.ldb, a.b_bs, a.C, a.ldc, a.c_bs, a.M, a.K, m_tiles, n_tiles);
+                       a.B, a.ldb, a.b_bs, a.C, a.ldc, a.c_bs, a.M, a.K, a.batch, n_tiles);
   return hipGetLastError();
 }
 
