@@ -117,14 +117,18 @@ __global__ __launch_bounds__(256, 2) void idx_score_kernel(
       const int c = tid + 256 * r;
       if constexpr (FP8) {
         const int key = c / (DI / 16), col = c % (DI / 16);
+        // codes widened by the hardware convert (exact in fp32 and in bf16)
         uint8_t* dst = &s_k[buf][key * ROWB + col * 32];
-        u32x4 lo, hi;
-        u32x2 t0 = e4m3x4_to_bf16x4(stage[r][0]), t1 = e4m3x4_to_bf16x4(stage[r][1]);
-        u32x2 t2 = e4m3x4_to_bf16x4(stage[r][2]), t3 = e4m3x4_to_bf16x4(stage[r][3]);
-        lo[0] = t0[0]; lo[1] = t0[1]; lo[2] = t1[0]; lo[3] = t1[1];
-        hi[0] = t2[0]; hi[1] = t2[1]; hi[2] = t3[0]; hi[3] = t3[1];
-        *reinterpret_cast<u32x4*>(dst) = lo;
-        *reinterpret_cast<u32x4*>(dst + 16) = hi;
+        uint32_t packed[8];
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[r][wd], false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[r][wd], true);
+          packed[2 * wd] = pack_bf16x2(lo[0], lo[1]);
+          packed[2 * wd + 1] = pack_bf16x2(hi[0], hi[1]);
+        }
+        *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+        *reinterpret_cast<u32x4*>(dst + 16) = u32x4{packed[4], packed[5], packed[6], packed[7]};
       } else {
         const int key = c / (DI / 8), col = c % (DI / 8);
         *reinterpret_cast<u32x4*>(&s_k[buf][key * ROWB + col * 16]) = stage[r];

@@ -28,31 +28,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// One OCP e4m3fn code -> bf16 bits, exactly.  Normal codes (exponent field
-// e >= 1) re-bias the exponent from 7 to 127 and widen the 3-bit mantissa;
-// subnormal codes m * 2^-9 (m = 1..7) are built through fp32, where they are
-// normal numbers.  The NaN code maps to a bf16 NaN.
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
-  const uint32_t sign = (c & 0x80u) << 8;
-  const uint32_t mag = c & 0x7Fu;
-  uint32_t r;
-  if (mag >= 8u) {
-    r = (mag << 4) + (120u << 7);              // (e + 120) << 7 | m << 4
-    if (mag == 0x7Fu) r = 0x7FC0u;             // NaN
-  } else {
-    r = __float_as_uint((float)mag * 0.001953125f) >> 16;   // m * 2^-9, exact in bf16
-  }
-  return sign | r;
-}
-
-// Four e4m3 codes packed in a dword -> four bf16 in two dwords (low first).
-__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
-  u32x2 r;
-  r[0] = e4m3_to_bf16_bits(w & 0xFFu) | (e4m3_to_bf16_bits((w >> 8) & 0xFFu) << 16);
-  r[1] = e4m3_to_bf16_bits((w >> 16) & 0xFFu) | (e4m3_to_bf16_bits(w >> 24) << 16);
-  return r;
-}
-
 // Order-preserving map of an fp32 score onto uint32 (larger score -> larger
 // key); -0.0 is folded onto +0.0 so the two zeros are one key.  The result
 // is never 0 (the one NaN pattern that would map there is moved up by one),

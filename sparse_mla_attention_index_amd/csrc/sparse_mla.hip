@@ -12,13 +12,13 @@
 //    16w..16w+15, rows staged through registers into a padded row-major
 //    LDS tile, the codes widened to bf16 exactly on the way;
 //    v_mfma_f32_16x16x32_bf16 for S^T = K.Q^T and O^T += V^T.P^T with an
-//    online softmax.  The scales stay out of the bf16 operands: a row's
-//    scale multiplies its logit and its softmax weight.  Formats: 576 codes
-//    with one fp32 scale per row (a separate array), or FlashMLA's 656-byte
-//    fp8_ds_mla row (512 codes, four fp32 scales of 128 dims each, 64 bf16
-//    rope dims; GLM-5.3 part 2, footnote 1, names it), whose QK sums run per
-//    128-dim block so each block's scale meets its own partial logit, and
-//    whose PV uses one scaled P per block.
+//    online softmax.  Formats: 576 codes with one fp32 scale per row (a
+//    separate array), whose scale stays out of the bf16 operands (it
+//    multiplies the row's logit and softmax weight, so the codes widen to
+//    bf16 exactly); or FlashMLA's 656-byte fp8_ds_mla row (512 codes, four
+//    fp32 scales of 128 dims each, 64 bf16 rope dims; GLM-5.3 part 2,
+//    footnote 1, names it), whose codes are staged as bf16(code x block
+//    scale), one rounding per element, so QK and PV run as for bf16 rows.
 //  * sparse_mla_bf16_kernel (bf16 KV): one 2-wave workgroup per query that
 //    splits both contractions by dims, gathers with direct global->LDS
 //    loads and uses v_mfma_f32_32x32x16_bf16 (twice the rate of the 16x16
@@ -178,28 +178,29 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     for (int r = 0; r < NCH; ++r) {
       const int c = tid + kMlaThreads * r;
       if constexpr (DS) {
+        // the row's four block scales and its rope dims (bf16 as stored);
+        // the codes follow once every scale of the tile is in LDS
         if (c < kMlaRows * kDsChunks) {
           const int row = c / kDsChunks, col = c % kDsChunks;
-          if (col < 32) {          // codes of dims 16col .. 16col + 15, widened exactly
-            uint8_t* dst = &s_kv[buf][row * kMlaRowB + col * 32];
-            const u32x2 t0 = e4m3x4_to_bf16x4(stage[r][0]), t1 = e4m3x4_to_bf16x4(stage[r][1]);
-            const u32x2 t2 = e4m3x4_to_bf16x4(stage[r][2]), t3 = e4m3x4_to_bf16x4(stage[r][3]);
-            *reinterpret_cast<u32x4*>(dst) = u32x4{t0[0], t0[1], t1[0], t1[1]};
-            *reinterpret_cast<u32x4*>(dst + 16) = u32x4{t2[0], t2[1], t3[0], t3[1]};
-          } else if (col == 32) {  // the row's four block scales
-            *reinterpret_cast<u32x4*>(&s_scale[buf][4 * row]) = stage[r];
-          } else {                 // rope dims 512 + 8(col - 33) .., bf16 as stored
-            *reinterpret_cast<u32x4*>(&s_kv[buf][row * kMlaRowB + 1024 + 16 * (col - 33)]) = stage[r];
-          }
+          if (col == 32) *reinterpret_cast<u32x4*>(&s_scale[buf][4 * row]) = stage[r];
+          else if (col > 32) *reinterpret_cast<u32x4*>(&s_kv[buf][row * kMlaRowB + 1024 + 16 * (col - 33)]) = stage[r];
         }
       } else if constexpr (FP8) {
+        // codes widened by the hardware convert: every e4m3 value is exact
+        // in fp32 and in bf16
         if (c < kMlaRows * kDqk / 16) {
           const int row = c / (kDqk / 16), col = c % (kDqk / 16);
           uint8_t* dst = &s_kv[buf][row * kMlaRowB + col * 32];
-          const u32x2 t0 = e4m3x4_to_bf16x4(stage[r][0]), t1 = e4m3x4_to_bf16x4(stage[r][1]);
-          const u32x2 t2 = e4m3x4_to_bf16x4(stage[r][2]), t3 = e4m3x4_to_bf16x4(stage[r][3]);
-          *reinterpret_cast<u32x4*>(dst) = u32x4{t0[0], t0[1], t1[0], t1[1]};
-          *reinterpret_cast<u32x4*>(dst + 16) = u32x4{t2[0], t2[1], t3[0], t3[1]};
+          uint32_t packed[8];
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[r][wd], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[r][wd], true);
+            packed[2 * wd] = pack_bf16x2(lo[0], lo[1]);
+            packed[2 * wd + 1] = pack_bf16x2(hi[0], hi[1]);
+          }
+          *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+          *reinterpret_cast<u32x4*>(dst + 16) = u32x4{packed[4], packed[5], packed[6], packed[7]};
         }
       } else {
         const int row = c / (kDqk / 8), col = c % (kDqk / 8);
@@ -208,6 +209,32 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     }
     if constexpr (KVF == kKvFp8Row) {
       if (tid < kMlaRows) s_scale[buf][tid] = stage_sc;
+    }
+    if constexpr (DS) {
+      // codes of dims 16col .. 16col + 15 times the row's scale of block
+      // col / 8, rounded once to bf16 (e4m3 -> fp32 is exact)
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < NCH; ++r) {
+        const int c = tid + kMlaThreads * r;
+        if (c < kMlaRows * kDsChunks) {
+          const int row = c / kDsChunks, col = c % kDsChunks;
+          if (col < 32) {
+            const float sc = s_scale[buf][4 * row + (col >> 3)];
+            uint32_t packed[8];
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+              const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[r][wd], false);
+              const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[r][wd], true);
+              packed[2 * wd] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+              packed[2 * wd + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
+            }
+            uint8_t* dst = &s_kv[buf][row * kMlaRowB + col * 32];
+            *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+            *reinterpret_cast<u32x4*>(dst + 16) = u32x4{packed[4], packed[5], packed[6], packed[7]};
+          }
+        }
+      }
     }
   };
 
@@ -231,36 +258,13 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
 
     // S^T = K . Q^T : rows 16mt + 4g + r, head i
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    if constexpr (DS) {
-      // block b (dims 128b .. +127, k-steps 4b .. 4b+3) carries the row's
-      // scale b; the rope dims (k-steps 16, 17) carry none
 #pragma unroll
-      for (int b = 0; b < 5; ++b) {
-        f32x4 blk[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int ks = 0; ks < kDqk / 32; ++ks) {
 #pragma unroll
-        for (int ks = 4 * b; ks < (b < 4 ? 4 * b + 4 : kDqk / 32); ++ks) {
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8*>(tile + (16 * mt + i) * kMlaRowB + (32 * ks + 8 * g) * 2);
-            blk[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], blk[mt], 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sacc[mt][r] += b < 4 ? blk[mt][r] * s_scale[buf][4 * (16 * mt + 4 * g + r) + b] : blk[mt][r];
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < kDqk / 32; ++ks) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(tile + (16 * mt + i) * kMlaRowB + (32 * ks + 8 * g) * 2);
-          sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
-        }
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(tile + (16 * mt + i) * kMlaRowB + (32 * ks + 8 * g) * 2);
+        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
       }
     }
 
@@ -298,19 +302,9 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
       for (int mt = 0; mt < kDv / 16; ++mt) o[mt] *= alpha;
     }
     m_run = m_new;
-    // P^T operand: with fp8_ds_mla rows, one per 128-dim block of V, the
-    // softmax weight times that block's scale of the row
-    constexpr int NPB = DS ? 4 : 1;
-    bf16x8 pb[NPB];
+    bf16x8 pb;
 #pragma unroll
-    for (int b = 0; b < NPB; ++b)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (DS)
-          pb[b][e] = (__bf16)(pv[e] * s_scale[buf][4 * (16 * (e / 4) + 4 * g + (e % 4)) + b]);
-        else
-          pb[b][e] = (__bf16)pv[e];
-      }
+    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pv[e];
 
     // O^T += V^T . P^T ; V^T columns read transposed from the row-major tile
     const uint8_t* va_base = tile + (4 * g + (i >> 2)) * kMlaRowB + 8 * (i & 3);
@@ -320,7 +314,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
       const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(va_base + 32 * mt));
       const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_base + 32 * mt));
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[DS ? mt / 8 : 0], o[mt], 0, 0, 0);
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mt], 0, 0, 0);
     }
 
     if (has_next) store_tile(buf ^ 1);
