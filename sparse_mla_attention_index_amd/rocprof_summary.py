@@ -66,10 +66,12 @@ def _kernel_avg(disp, substr):
 
 
 def _copy_counter(disp):
-    """Counter value of the largest dispatch of a copy kernel."""
-    vals = [v for (name, v) in disp.values() if "copy" in name.lower()]
+    """Counter value of the largest dispatch of the runtime's device-to-device
+    copy kernel (the calibration copy; torch's dtype-conversion kernels also
+    carry "copy" in their names and are not it)."""
+    vals = [v for (name, v) in disp.values() if "copybuffer" in name.lower()]
     if not vals:
-        raise SystemExit("no copy kernel in the counter file")
+        raise SystemExit("no device copy kernel (copyBuffer) in the counter file")
     return max(vals)
 
 
