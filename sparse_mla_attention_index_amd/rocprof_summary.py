@@ -3,7 +3,7 @@
 Two commands (run from the repository root on the CSV output of rocprofv3):
 
   python -m sparse_mla_attention_index_amd.rocprof_summary stats \\
-      --stats gpurun_out/prof_k/run_kernel_stats.csv --out profiles/<name>.md --command "<cmd>"
+      --stats <run dir>/run_kernel_stats.csv --out profiles/<name>.md --command "<cmd>"
 
 writes a kernel-time table (calls, average / min / max ms, share of the total);
 
