@@ -161,12 +161,146 @@ __global__ __launch_bounds__(kBmThreads, 2) void bmm_bf16_kernel(
   }
 }
 
+// K = 128 with an N-contiguous B (absorb_q): one workgroup computes every
+// 128-column n-tile of its 128-row A tile.  A (both 64-wide K chunks) stays
+// in LDS for the whole sweep, so it is read from memory once instead of once
+// per n-tile; the next n-tile's B chunks are loaded into registers while the
+// current one is multiplied, and the bf16 output tile is staged through the
+// B buffers (then refilled), keeping LDS at two workgroups per CU.
+__global__ __launch_bounds__(kBmThreads, 2) void bmm_k128_nsweep_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, int64_t a_bs, const uint16_t* __restrict__ B, int64_t ldb,
+    int64_t b_bs, uint16_t* __restrict__ C, int64_t ldc, int64_t c_bs, int M, int batch, int n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kBmABytes + kBmBBytes)];
+  auto s_a = [&](int c) { return smem + c * kBmABytes; };
+  auto s_b = [&](int c) { return smem + 2 * kBmABytes + c * kBmBBytes; };
+  uint8_t* s_c = smem + 2 * kBmABytes;   // the two B buffers, 36,864 bytes >= 128 x 272
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lrow = lane & 31, khalf = lane >> 5;
+  // head fastest: the workgroups running at once cover all heads of the
+  // same token rows, contiguous in memory
+  const int h = (int)(blockIdx.x % batch), mt = (int)(blockIdx.x / batch);
+  const int m0 = mt * kBmTM;
+  const uint16_t* Ah = A + h * a_bs;
+  const uint16_t* Bh = B + h * b_bs;
+  uint16_t* Ch = C + h * c_bs;
+
+  u32x4 sb[2][4];
+  auto load_b = [&](int n0) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = tid + kBmThreads * r;
+        const int kr = p >> 4, n16 = p & 15;
+        sb[c][r] = *reinterpret_cast<const u32x4*>(Bh + (int64_t)(64 * c + kr) * ldb + n0 + 8 * n16);
+      }
+  };
+  auto store_b = [&]() {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = tid + kBmThreads * r;
+        const int kr = p >> 4, n16 = p & 15;
+        *reinterpret_cast<u32x4*>(s_b(c) + kr * kBmRowN + 16 * n16) = sb[c][r];
+      }
+  };
+  {   // A, both K chunks, once
+    u32x4 sa[2][4];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = tid + kBmThreads * r;
+        const int row = p >> 3, c16 = p & 7;
+        sa[c][r] = *reinterpret_cast<const u32x4*>(Ah + (int64_t)min(m0 + row, M - 1) * lda + 64 * c + 8 * c16);
+      }
+    load_b(0);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = tid + kBmThreads * r;
+        const int row = p >> 3, c16 = p & 7;
+        *reinterpret_cast<u32x4*>(s_a(c) + row * kBmRowK + 16 * c16) = sa[c][r];
+      }
+    store_b();
+  }
+  __syncthreads();
+
+  for (int nt = 0; nt < n_tiles; ++nt) {
+    const int n0 = nt * kBmTN;
+    if (nt + 1 < n_tiles) load_b(n0 + kBmTN);   // in flight during this n-tile
+    f32x16 acc[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint8_t* ta = s_a(c);
+      const uint8_t* tb = s_b(c);
+#pragma unroll
+      for (int ks = 0; ks < kBmTK / 16; ++ks) {
+        bf16x8 fa[2], fb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          fa[t] = *reinterpret_cast<const bf16x8*>(ta + (64 * wm + 32 * t + lrow) * kBmRowK + (16 * ks + 8 * khalf) * 2);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int j = lane & 15, grp = lane >> 4;
+          const int col = 64 * wn + 32 * t + 16 * (grp & 1) + 4 * (j & 3);
+          const int kr = 16 * ks + 8 * (grp >> 1) + (j >> 2);
+          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bm_lds_i16x4*)(tb + kr * kBmRowN + 2 * col));
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bm_lds_i16x4*)(tb + (kr + 4) * kBmRowN + 2 * col));
+          fb[t] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < 2; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // every wave is done with the B buffers
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 64 * wm + 32 * tm + lrow;
+          const int col = 64 * wn + 32 * tn + 8 * q + 4 * khalf;
+          const f32x16& a = acc[tm][tn];
+          *reinterpret_cast<u32x2*>(s_c + row * kBmRowC + 2 * col) =
+              u32x2{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
+        }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kBmTM * kBmTN / 8 / kBmThreads; ++r) {
+      const int p = tid + kBmThreads * r;
+      const int row = p >> 4, c16 = p & 15;
+      if (m0 + row < M)
+        *reinterpret_cast<u32x4*>(Ch + (int64_t)(m0 + row) * ldc + n0 + 8 * c16) =
+            *reinterpret_cast<const u32x4*>(s_c + row * kBmRowC + 16 * c16);
+    }
+    if (nt + 1 < n_tiles) {
+      __syncthreads();   // the staged tile has been read out
+      store_b();
+      __syncthreads();
+    }
+  }
+}
+
 hipError_t launch_bmm_bf16(const BmmArgs& a, hipStream_t st) {
   if (a.M <= 0 || a.batch <= 0) return hipSuccess;
   if (a.N % kBmTN || a.K % kBmTK) return hipErrorInvalidValue;
   const int m_tiles = (a.M + kBmTM - 1) / kBmTM, n_tiles = a.N / kBmTN;
   const long long grid = (long long)a.batch * m_tiles * n_tiles;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  if (a.K == 128 && a.b_kn) {
+    hipLaunchKernelGGL(bmm_k128_nsweep_kernel, dim3((unsigned)(grid / n_tiles)), dim3(kBmThreads), 0, st, a.A, a.lda,
+                       a.a_bs, a.B, a.ldb, a.b_bs, a.C, a.ldc, a.c_bs, a.M, a.batch, n_tiles);
+    return hipGetLastError();
+  }
   if (a.b_kn)
     hipLaunchKernelGGL(bmm_bf16_kernel<true>, dim3((unsigned)grid), dim3(kBmThreads), 0, st, a.A, a.lda, a.a_bs,
                        a.B, a.ldb, a.b_bs, a.C, a.ldc, a.c_bs, a.M, a.K, a.batch, n_tiles);
