@@ -349,17 +349,18 @@ def main():
     idx_flops = pairs * acc.indexer_flops_per_pair(w.h_idx, w.d_idx)
     mla_flops = acc.mla_flops(pos_np, w.top_k)
     topk_b = acc.topk_bytes(pos_np, w.top_k)
-    # The decode batch's queries each scan their own ~1M-key prefix (bytes
-    # counted per request): that scan is bound by HBM, the prefill indexer
-    # (key tiles shared by query blocks) by the matrix cores.
+    # The indexer is placed against the matrix cores.  In the decode batch the
+    # 64 queries scan one shared ~1M-key context and a workgroup's queries
+    # share each key tile, so the keys it reads are far fewer than the bytes
+    # counted per request (as if every request streamed its own prefix);
+    # that per-request rate is reported beside it, not as the roofline.
     idx_tflops = idx_flops / (t_idx * 1e-3) / 1e12
+    idx_k = {"bound": "mfma", "achieved": idx_tflops, "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     if args.workload == "decode":
-        idx_gbs = acc.indexer_bytes_per_request(pos_np, w.h_idx, w.d_idx, key_bytes) / (t_idx * 1e-3) / 1e9
-        idx_k = {"bound": "hbm", "achieved": idx_gbs, "peak": acc.PEAK_HBM_GBS, "unit": "GB/s", "tflops": idx_tflops}
+        idx_k["gbs_per_request_counted"] = \
+            acc.indexer_bytes_per_request(pos_np, w.h_idx, w.d_idx, key_bytes) / (t_idx * 1e-3) / 1e9
     else:
-        idx_gbs = acc.indexer_bytes(pos_np, w.h_idx, w.d_idx, key_bytes) / (t_idx * 1e-3) / 1e9
-        idx_k = {"bound": "mfma", "achieved": idx_tflops, "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                 "hbm_gbs": idx_gbs}
+        idx_k["hbm_gbs"] = acc.indexer_bytes(pos_np, w.h_idx, w.d_idx, key_bytes) / (t_idx * 1e-3) / 1e9
     kern = {
         "index_scores": dict(ms=t_idx, **idx_k),
         "topk_select": {"ms": t_topk, "bound": "hbm", "achieved": topk_b / (t_topk * 1e-3) / 1e9,
