@@ -245,6 +245,11 @@ __device__ __forceinline__ void idx_wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+__device__ __forceinline__ void idx_dma4(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ void idx_sync_lds() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt not waited
@@ -390,6 +395,186 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_kernel(
   idx_wait_vmcnt<0>();   // no load may land in LDS after the workgroup has left
 }
 
+// ---------------------------------------------------------------------------
+// bf16 queries over FP8 keys, 64 heads x d_I = 128 (the decode batch): the
+// kernel above with an FP8 key ring.  Each wave's direct global->LDS load
+// brings 8 keys (1 KiB of codes) and their 8 scales per 64-key tile; once a
+// tile has landed, the workgroup widens its codes to bf16 (the hardware
+// convert, exact) into one of two bf16 tiles laid out and swizzled as above,
+// so the MFMA loop is unchanged; the key's scale multiplies the head sum.
+// ---------------------------------------------------------------------------
+constexpr int kF8kTileB = kIdxKT * 128;   // 8 KiB of codes per 64-key tile
+
+__global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_f8k_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int64_t w_stride,
+    const uint8_t* __restrict__ k8, const float* __restrict__ k_scale, const int32_t* __restrict__ q_pos, int n_q,
+    int n_k, float* __restrict__ scores, int64_t ld, int n_qblocks, int n_chunks, int chunk_keys) {
+  constexpr int H = 64, DI = 128, KS = DI / 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_c8[kIdxStages][kF8kTileB];   // codes, as stored
+  __shared__ __attribute__((aligned(16))) float s_sc[kIdxStages][kIdxKT];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_k[2][kIdxTileB];             // widened, swizzled
+  __shared__ int s_pos[kIdxWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qb = n_qblocks - 1 - (int)(blockIdx.x / n_chunks);
+  const int chunk = (int)(blockIdx.x % n_chunks);
+  const int q0 = qb * kIdxWaves;
+
+  if (tid < kIdxWaves) {
+    const int qi = q0 + tid;
+    const int p = qi < n_q ? q_pos[qi] : -1;
+    s_pos[tid] = p < -1 ? -1 : (p > n_k - 1 ? n_k - 1 : p);
+  }
+  __syncthreads();
+  int pmax = -1;
+#pragma unroll
+  for (int t = 0; t < kIdxWaves; ++t) pmax = max(pmax, s_pos[t]);
+  const int k_begin = chunk * chunk_keys;
+  const int k_end = min(k_begin + chunk_keys, pmax + 1);
+  if (k_begin >= k_end) return;   // uniform across the workgroup
+  const int ntiles = (k_end - k_begin + kIdxKT - 1) / kIdxKT;
+  const int mypos = s_pos[wave];
+  const int qi = min(q0 + wave, n_q - 1);
+
+  const int lrow = lane & 31, khalf = lane >> 5;
+  bf16x8 a[2][KS];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint16_t* src = q_idx + ((int64_t)qi * H + 32 * t + lrow) * DI + khalf * 8;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) a[t][j] = *reinterpret_cast<const bf16x8*>(src + j * 16);
+  }
+  float wv[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) wv[t][jj] = w[(int64_t)qi * w_stride + 32 * t + 8 * (jj >> 2) + 4 * khalf + (jj & 3)];
+
+  // ---- tile i (keys k_begin + 64i ..): codes and scales into ring slot i % kIdxStages ----
+  auto issue = [&](int i) {
+    const int slot = i % kIdxStages;
+    const int kt = k_begin + kIdxKT * i;
+    const uint32_t dst = (uint32_t)(uintptr_t)(idx_lds_u8*)&s_c8[slot][1024 * wave];
+    idx_dma16(k8 + (int64_t)min(kt + 8 * wave + (lane >> 3), n_k - 1) * DI + 16 * (lane & 7), dst);
+    const uint32_t sdst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&s_sc[slot][8 * wave];
+    if (lane < 8) idx_dma4(k_scale + min(kt + 8 * wave + lane, n_k - 1), sdst);
+  };
+  constexpr int kLoads = 2;   // per wave per tile: codes, scales
+  // widen tile i: thread t takes 16 codes (key t >> 3, 16-byte chunk t & 7)
+  // into bf16 chunks 2c and 2c + 1 of the key at slots (2c + h) ^ (key & 15)
+  auto widen = [&](int i) {
+    const int key = tid >> 3, c = tid & 7;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&s_c8[i % kIdxStages][key * 128 + 16 * c]);
+    uint32_t packed[8];
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[wd], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[wd], true);
+      packed[2 * wd] = pack_bf16x2(lo[0], lo[1]);
+      packed[2 * wd + 1] = pack_bf16x2(hi[0], hi[1]);
+    }
+    uint8_t* row = &s_k[i & 1][key * 256];
+    *reinterpret_cast<u32x4*>(row + 16 * ((2 * c) ^ (key & 15))) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    *reinterpret_cast<u32x4*>(row + 16 * ((2 * c + 1) ^ (key & 15))) =
+        u32x4{packed[4], packed[5], packed[6], packed[7]};
+  };
+  idx_wait_vmcnt<0>();
+#pragma unroll
+  for (int i = 0; i < kIdxStages - 1; ++i) issue(i);
+  int boff[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) boff[j] = lrow * 256 + 16 * ((2 * j + khalf) ^ (lrow & 15));
+
+  f32x16 acc[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};
+  int prev_key = -1;
+  float prev_sc = 0.f;
+  auto epilogue = [&](const f32x16& c0, const f32x16& c1, int key0, float sc) {
+    float part = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      part = fmaf(wv[0][jj], __int_as_float(max(__float_as_int(c0[jj]), 0)), part);
+      part = fmaf(wv[1][jj], __int_as_float(max(__float_as_int(c1[jj]), 0)), part);
+    }
+    part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
+                                                             false)[1]);
+    const int key = key0 + lrow;
+    if (khalf == 0 && key0 >= 0 && q0 + wave < n_q && key <= mypos && key < k_end)
+      scores[(int64_t)(q0 + wave) * ld + key] = part * sc;
+  };
+  // tile 0 widened before the loop; iteration i widens tile i + 1 (whose B
+  // operands the last N-tile of tile i reads), so the waits cover tiles i
+  // and i + 1, leaving kIdxStages - 3 tiles in flight
+  idx_wait_vmcnt<(kIdxStages - 2) * kLoads>();
+  idx_sync_lds();
+  widen(0);
+  idx_sync_lds();
+  bf16x8 bn[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) bn[j] = *reinterpret_cast<const bf16x8*>(s_k[0] + boff[j]);
+  float scn = s_sc[0][lrow];
+  for (int i = 0; i < ntiles; ++i) {
+    idx_wait_vmcnt<(kIdxStages - 3) * kLoads>();
+    idx_sync_lds();             // tile i + 1 landed; bf16 tile (i + 1) & 1 is no longer read
+    widen(i + 1);               // past the range this widens clamped keys, never stored
+    idx_sync_lds();
+    issue(i + kIdxStages - 1);  // into slot (i - 1) % kIdxStages, whose codes were widened at i - 2
+    const uint8_t* tile = s_k[i & 1];
+    const int slot = i % kIdxStages;
+    const int k0 = k_begin + kIdxKT * i;
+#pragma unroll
+    for (int u = 0; u < kIdxKT / 32; ++u) {
+      const f32x16 p0 = acc[(u + 1) & 1][0], p1 = acc[(u + 1) & 1][1];
+      const bool last = u + 1 == kIdxKT / 32;
+      const uint8_t* nxt = last ? s_k[(i + 1) & 1] : tile + 8192 * (u + 1);
+      const float* nsc = last ? &s_sc[(i + 1) % kIdxStages][0] : &s_sc[slot][32 * (u + 1)];
+      const float sc = scn;
+      f32x16 c0 = f32x16{}, c1 = f32x16{};
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const bf16x8 b = bn[j];
+        bn[j] = *reinterpret_cast<const bf16x8*>(nxt + boff[j]);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][j], b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][j], b, c1, 0, 0, 0);
+      }
+      scn = nsc[lrow];
+      epilogue(p0, p1, prev_key, prev_sc);
+      acc[u & 1][0] = c0;
+      acc[u & 1][1] = c1;
+      prev_key = k0 + 32 * u;
+      prev_sc = sc;
+#pragma unroll
+      for (int g = 0; g < KS; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0002, 4, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0002, 4, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
+      }
+    }
+  }
+  epilogue(acc[(kIdxKT / 32 - 1) & 1][0], acc[(kIdxKT / 32 - 1) & 1][1], prev_key, prev_sc);
+  idx_wait_vmcnt<0>();
+}
+
+static hipError_t launch_idx_h64_f8k(const IdxArgs& A, hipStream_t st) {
+  const int n_qblocks = (A.n_q + kIdxWaves - 1) / kIdxWaves;
+  int n_chunks = 1;
+  const int target_wgs = 1024;
+  if (n_qblocks < target_wgs) n_chunks = (target_wgs + n_qblocks - 1) / n_qblocks;
+  int chunk_keys = (int)((A.n_k + n_chunks - 1) / n_chunks);
+  chunk_keys = ((chunk_keys + kIdxKT - 1) / kIdxKT) * kIdxKT;
+  if (chunk_keys < 4 * kIdxKT) chunk_keys = 4 * kIdxKT;
+  n_chunks = (int)((A.n_k + chunk_keys - 1) / chunk_keys);
+  const long long grid = (long long)n_qblocks * n_chunks;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(idx_score_h64_f8k_kernel, dim3((unsigned)grid), dim3(64 * kIdxWaves), 0, st,
+                     static_cast<const uint16_t*>(A.q_idx), A.w, A.w_stride, static_cast<const uint8_t*>(A.k_idx),
+                     A.k_scale, A.q_pos, A.n_q, (int)A.n_k, A.scores, A.ld, n_qblocks, n_chunks, chunk_keys);
+  return hipGetLastError();
+}
+
 static hipError_t launch_idx_h64(const IdxArgs& A, hipStream_t st) {
   const int n_qblocks = (A.n_q + kIdxWaves - 1) / kIdxWaves;
   int n_chunks = 1;
@@ -454,10 +639,6 @@ struct F8Geom {
   static_assert((S & (S - 1)) == 0, "ring depth is a power of two");
 };
 
-__device__ __forceinline__ void idx_dma4(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gaddr), "s"(lds_base)
-               : "memory", "m0");
-}
 
 // Store v at base + off on the lanes set in `mask` (a subset of the active
 // lanes), without a branch: exec is narrowed around the one store and
@@ -668,7 +849,7 @@ hipError_t launch_index_scores_fp8(const IdxArgs& A, hipStream_t st) {
 hipError_t launch_index_scores(const IdxArgs& A, hipStream_t st) {
   const bool f8 = A.fp8;
   if (A.q_scale) return launch_index_scores_fp8(A, st);
-  if (!f8 && A.h_idx == 64 && A.d_idx == 128) return launch_idx_h64(A, st);
+  if (A.h_idx == 64 && A.d_idx == 128) return f8 ? launch_idx_h64_f8k(A, st) : launch_idx_h64(A, st);
 #define SMA_IDX_CASE(HH, DD)                                                          \
   if (A.h_idx == HH && A.d_idx == DD)                                                 \
     return f8 ? launch_idx<HH, DD, true>(A, st) : launch_idx<HH, DD, false>(A, st);
