@@ -121,3 +121,27 @@ def test_positions_clamped_and_empty():
     for i in (2, 3, 4, 5, 20):
         p = min(max(pos[i], -1), 63)
         assert np.array_equal(got[i, : p + 1].astype(np.float64), ref[i])
+
+
+def test_fp8_keys_prefill_shape_exact():
+    """64 heads x 128 over FP8 keys at a causal prefill shape (1,100 queries:
+    many query blocks, a ragged last tile): integer q_I, keys whose codes are
+    small integers with power-of-two scales, w = k/16 -> every score is exact
+    in fp32, so the GPU must reproduce the oracle bit for bit."""
+    rng = np.random.default_rng(77)
+    n = 1100
+    q = synth.to_bf16_bits(rng.integers(-3, 4, size=(n, 64, 128)).astype(np.float32))
+    table = oracle.e4m3fn_table()
+    ints = {int(v): c for c, v in enumerate(table[:0x7F]) if v == int(v) and v <= 4}
+    ints.update({-v: c | 0x80 for v, c in list(ints.items()) if v > 0})
+    keys = np.array(sorted(ints))
+    lut = np.array([ints[k] for k in keys], np.uint8)
+    k8 = lut[rng.integers(0, keys.size, (n, 128))]
+    ks = rng.choice(np.array([0.5, 1.0, 2.0], np.float32), n)
+    wt = (rng.integers(0, 17, size=(n, 64)) / 16).astype(np.float32)
+    pos = np.arange(n, dtype=np.int32)
+    got = _run(q, wt, (k8, ks), pos)
+    ref = _oracle(q, wt, (k8, ks), pos, fp8=True)
+    for i in range(n):
+        assert np.array_equal(got[i, : i + 1].astype(np.float64), ref[i]), i
+        assert np.all(np.isnan(got[i, i + 1:])), i
