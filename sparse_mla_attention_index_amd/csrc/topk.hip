@@ -290,8 +290,10 @@ __global__ __launch_bounds__(THREADS, 1) void topk_stream_kernel(const float* __
 //     or above it (mu = K * S / n, the samples expected among the row's K
 //     largest).  A shorter row keeps every key;
 //  2. one coalesced pass keeps every position whose score is at or above the
-//     threshold, with its key, in ascending position order: wave ballots and
-//     a per-chunk table of wave counts give each kept position its LDS slot;
+//     threshold, with the score, in ascending position order: each wave owns
+//     a contiguous quarter of an 8,192-score chunk, and wave ballots plus a
+//     per-chunk table of the waves' counts give each kept position its LDS
+//     slot (scores become keys only once kept);
 //  3. if between K and kFtCap positions were kept, the threshold key T comes
 //     from the kept keys alone (one histogram round, then one wave ranks the
 //     few keys of the selected bin) and an ordered compaction over them
@@ -306,6 +308,7 @@ constexpr int kFtCap = 5120;                      // kept positions held in LDS
 constexpr int kFtClusterLen = 16;                 // consecutive scores per sample cluster
 constexpr int kFtU = 8;                           // 16-byte loads per thread per chunk
 constexpr int kFtChunk = kFtThreads * 4 * kFtU;   // 8,192 positions
+constexpr int kFtWaveSpan = 256 * kFtU;           // a wave's contiguous share of a chunk
 constexpr int kFtKeep = kFtCap / kFtThreads;      // kept keys per thread in the final select
 
 // The score whose key is k (the inverse of score_key for finite scores).
@@ -404,9 +407,9 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
   constexpr int kSamples = kFtThreads * SPT, kClusters = kSamples / kFtClusterLen;
   static_assert(SPT % 4 == 0 && kFtClusterLen % SPT == 0, "whole 16-byte loads within one cluster");
   __shared__ TopkShared<kFtThreads> sh;
-  __shared__ uint32_t ckey[kFtCap];   // keys of the kept positions (the streaming fallback's scratch)
-  __shared__ PosT cpos[kFtCap];       // kept positions, ascending
-  __shared__ uint32_t tab[2][kFtU][kFtWaves];
+  __shared__ uint32_t ckey[kFtCap + 4];   // score bits of the kept positions (the streaming fallback's scratch)
+  __shared__ PosT cpos[kFtCap + 4];       // kept positions, ascending
+  __shared__ uint32_t tab[2][kFtWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;
   int p = q_pos[row];
@@ -419,16 +422,24 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
     return;
   }
 
-  // Thread t's step u of the chunk at c0 covers positions c0 + 1024u + 4t .. +3.
+  // Wave w's step u of the chunk at c0 covers positions c0 + 2048w + 256u ..
+  // + 255, lane l the four at + 4l; positions at or past n read as NaN, which
+  // no threshold keeps.
   auto load = [&](int c0, f32x4 (&x)[kFtU]) {
+    const int pw = c0 + kFtWaveSpan * wave + 4 * lane;
+    if (c0 + kFtChunk <= n) {
 #pragma unroll
-    for (int u = 0; u < kFtU; ++u) {
-      const int p0 = c0 + 1024 * u + 4 * tid;
-      if (p0 + 3 < n) {
-        x[u] = *reinterpret_cast<const f32x4*>(src + p0);
-      } else {
+      for (int u = 0; u < kFtU; ++u) x[u] = *reinterpret_cast<const f32x4*>(src + pw + 256 * u);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[u][e] = p0 + e < n ? src[p0 + e] : 0.f;
+      for (int u = 0; u < kFtU; ++u) {
+        const int p0 = pw + 256 * u;
+        if (p0 + 3 < n) {
+          x[u] = *reinterpret_cast<const f32x4*>(src + p0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[u][e] = p0 + e < n ? src[p0 + e] : __builtin_nanf("");
+        }
       }
     }
   };
@@ -461,49 +472,50 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
   // ---- 2. one pass: positions with score >= thr, in ascending order ----
   uint32_t kept = 0;   // positions kept by earlier chunks
   // Keep the chunk at c0 (held in x), then load the chunk two ahead into x.
+  // The kept list holds raw score bits; keys are formed for kept entries only.
   auto step = [&](int c0, int ci, f32x4 (&x)[kFtU]) {
-    uint32_t fl[kFtU];    // bit e: position c0 + 1024u + 4t + e is kept
-    uint32_t pre[kFtU];   // kept positions of lower lanes in step u
+    // off[u]: this lane's first slot for step u within the wave's kept
+    // entries of the chunk (ballot prefix counts, accumulated by mbcnt)
+    uint32_t off[kFtU];
+    uint32_t wcnt = 0;
 #pragma unroll
     for (int u = 0; u < kFtU; ++u) {
-      const int p0 = c0 + 1024 * u + 4 * tid;
-      fl[u] = 0;
-      pre[u] = 0;
-      uint32_t cnt = 0;
+      uint32_t o = wcnt;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bool f = p0 + e < n && x[u][e] >= thr;
-        const uint64_t m = __ballot(f);
-        fl[u] |= (uint32_t)f << e;
-        pre[u] += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        cnt += (uint32_t)__popcll(m);
+        const uint64_t m = __ballot(x[u][e] >= thr);
+        o = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, o));
+        wcnt += (uint32_t)__popcll(m);
       }
-      if (lane == 0) tab[ci & 1][u][wave] = cnt;
+      asm volatile("" : "+v"(o));   // keep the offset in a register (not recomputed after the barrier)
+      off[u] = o;
     }
+    if (lane == 0) tab[ci & 1][wave] = wcnt;
     __syncthreads();
-    uint32_t base = kept;
+    uint32_t base = kept, all = 0;
+#pragma unroll
+    for (int w = 0; w < kFtWaves; ++w) {
+      const uint32_t v = tab[ci & 1][w];
+      base += w < wave ? v : 0u;
+      all += v;
+    }
+    const int pw = c0 + kFtWaveSpan * wave + 4 * lane;
+    // a position not kept writes to this thread's own words of the
+    // histogram, idle during this pass, so that no lane branches
 #pragma unroll
     for (int u = 0; u < kFtU; ++u) {
-      uint32_t before = 0, all = 0;
+      uint32_t slot = min(base + off[u], (uint32_t)kFtCap);   // slots kFtCap.. absorb an overflow
 #pragma unroll
-      for (int w = 0; w < kFtWaves; ++w) {
-        const uint32_t v = tab[ci & 1][u][w];
-        before += w < wave ? v : 0u;
-        all += v;
+      for (int e = 0; e < 4; ++e) {
+        const bool f = x[u][e] >= thr;
+        uint32_t* kp = f ? &ckey[slot] : &sh.hist[tid];
+        PosT* pp = f ? &cpos[slot] : reinterpret_cast<PosT*>(&sh.hist[kFtThreads + tid]);
+        *pp = (PosT)(pw + 256 * u + e);
+        *kp = __float_as_uint(x[u][e]);
+        slot += f;
       }
-      uint32_t off = base + before + pre[u];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((fl[u] >> e) & 1u) {
-          if (off < (uint32_t)kFtCap) {
-            cpos[off] = (PosT)(c0 + 1024 * u + 4 * tid + e);
-            ckey[off] = score_key(x[u][e]);
-          }
-          ++off;
-        }
-      base += all;
     }
-    kept = base;
+    kept += all;
     if (c0 + 2 * kFtChunk < n) load(c0 + 2 * kFtChunk, x);
   };
   if (kFtChunk < n) load(kFtChunk, xb);
@@ -524,7 +536,7 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
 #pragma unroll
   for (int j = 0; j < kFtKeep; ++j) {
     const int i = tid + kFtThreads * j;
-    kk[j] = i < C ? ckey[i] : 0u;
+    kk[j] = i < C ? score_key(__uint_as_float(ckey[i])) : 0u;
   }
   uint32_t lo, hi, need_ties = (uint32_t)K;
   ft_range<kFtKeep>(kk, lo, hi, sh);
@@ -563,23 +575,26 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
   const uint32_t T = lo;
 
   // ---- 4. ordered compaction: thread t owns kept entries [t*M, t*M + M) ----
+  // (kept scores are never NaN, so comparing them as floats with T's score
+  // orders them as their keys do, -0.0 == +0.0 included)
+  const float Tf = key_score(T);
   const int M = (C + kFtThreads - 1) / kFtThreads;
   const int i0 = min(C, tid * M), i1 = min(C, i0 + M);
   uint32_t cg = 0, ce = 0;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t k = ckey[i];
-    cg += k > T;
-    ce += k == T;
+    const float v = __uint_as_float(ckey[i]);
+    cg += v > Tf;
+    ce += v == Tf;
   }
   uint32_t g_before, e_before, tg, te;
   block_excl_scan2<kFtThreads>(cg, ce, g_before, e_before, tg, te, sh);
   for (int i = i0; i < i1; ++i) {
-    const uint32_t k = ckey[i];
-    if (k > T) {
+    const float v = __uint_as_float(ckey[i]);
+    if (v > Tf) {
       const uint32_t slot = g_before + min(e_before, need_ties);
       if (slot < (uint32_t)K) out[slot] = cpos[i];
       ++g_before;
-    } else if (k == T) {
+    } else if (v == Tf) {
       if (e_before < need_ties && g_before + e_before < (uint32_t)K) out[g_before + e_before] = cpos[i];
       ++e_before;
     }
