@@ -329,7 +329,8 @@ __global__ __launch_bounds__(kFinalThreads) void tkm_final(const RowState* __res
   __shared__ int32_t s_cpos[SMA_MAX_TOPK_DEV];
   __shared__ uint32_t s_flag[SMA_MAX_TOPK_DEV];
   __shared__ uint32_t red[2 * (kFinalThreads / 64)];
-  __shared__ uint32_t s_off[2];
+  __shared__ uint32_t s_goa[kFinalThreads], s_goc[kFinalThreads];   // a chunk group's list offsets
+  __shared__ uint32_t s_gna[kFinalThreads], s_gnc[kFinalThreads];   // and counts
   const int row = blockIdx.x, tid = threadIdx.x;
   const RowState s = st[row];
   const int n = (int)s.n;
@@ -340,33 +341,44 @@ __global__ __launch_bounds__(kFinalThreads) void tkm_final(const RowState* __res
   }
   // Concatenate the chunks' lists (chunks in position order): positions
   // above hi, then the candidates; with one key left (lo == hi) only the
-  // first `rem` candidates can be taken.
+  // first `rem` candidates can be taken.  The chunks' counts are read and
+  // scanned kFinalThreads at a time, so every chunk's offsets are known
+  // before any entry moves and the copies need no barrier between chunks.
   const uint32_t* rc = cnt + (int64_t)row * nch * 2;
-  if (tid == 0) s_off[0] = s_off[1] = 0u;
-  __syncthreads();
   const uint32_t want_c = s.lo == s.hi ? s.rem : (uint32_t)K;
-  for (int c = 0; c < nch; ++c) {
-    const uint32_t na = rc[2 * c], nc = rc[2 * c + 1];
-    const uint32_t oa = s_off[0], oc = s_off[1];
-    const int32_t* ab = abuf + ((int64_t)row * nch + c) * K;
-    const uint2* cb = cbuf + ((int64_t)row * nch + c) * K;
-    for (uint32_t e = tid; e < na; e += kFinalThreads)
-      if (oa + e < (uint32_t)K) s_above[oa + e] = ab[e];
-    const uint32_t take = oc < want_c ? min(nc, want_c - oc) : 0u;
-    for (uint32_t e = tid; e < take; e += kFinalThreads) {
-      const uint2 v = cb[e];
-      s_cpos[oc + e] = (int32_t)v.x;
-      s_ckey[oc + e] = v.y;
+  uint32_t run_a = 0, run_c = 0;   // entries of earlier chunk groups
+  for (int g0 = 0; g0 < nch; g0 += kFinalThreads) {
+    const int c = g0 + tid;
+    const uint32_t na = c < nch ? rc[2 * c] : 0u, nc = c < nch ? rc[2 * c + 1] : 0u;
+    uint32_t ea, ec, ta, tc;
+    excl_scan2<kFinalThreads>(na, nc, ea, ec, ta, tc, red);
+    if (c < nch) {
+      s_goa[tid] = run_a + ea;
+      s_goc[tid] = run_c + ec;
+      s_gna[tid] = na;
+      s_gnc[tid] = nc;
     }
     __syncthreads();
-    if (tid == 0) {
-      s_off[0] = oa + na;
-      s_off[1] = oc + take;
+    const int gn = min(kFinalThreads, nch - g0);
+    for (int k = 0; k < gn; ++k) {
+      const uint32_t oa = s_goa[k], oc = s_goc[k], ka = s_gna[k], kc = s_gnc[k];
+      const int32_t* ab = abuf + ((int64_t)row * nch + g0 + k) * K;
+      const uint2* cb = cbuf + ((int64_t)row * nch + g0 + k) * K;
+      for (uint32_t e = tid; e < ka; e += kFinalThreads)
+        if (oa + e < (uint32_t)K) s_above[oa + e] = ab[e];
+      const uint32_t take = oc < want_c ? min(kc, want_c - oc) : 0u;
+      for (uint32_t e = tid; e < take; e += kFinalThreads) {
+        const uint2 v = cb[e];
+        s_cpos[oc + e] = (int32_t)v.x;
+        s_ckey[oc + e] = v.y;
+      }
     }
+    run_a += ta;
+    run_c += tc;
     __syncthreads();
   }
-  const int A = (int)min(s_off[0], (uint32_t)K);   // = K - rem
-  const int C = (int)s_off[1];
+  const int A = (int)min(run_a, (uint32_t)K);   // = K - rem
+  const int C = (int)min(run_c, want_c);
   const int R = min((int)s.rem, K - A);              // candidates taken (= rem)
   // ---- which candidates are taken ----
   if (s.lo == s.hi) {
