@@ -330,7 +330,6 @@ __global__ __launch_bounds__(kFinalThreads) void tkm_final(const RowState* __res
   __shared__ uint32_t s_flag[SMA_MAX_TOPK_DEV];
   __shared__ uint32_t red[2 * (kFinalThreads / 64)];
   __shared__ uint32_t s_goa[kFinalThreads], s_goc[kFinalThreads];   // a chunk group's list offsets
-  __shared__ uint32_t s_gna[kFinalThreads], s_gnc[kFinalThreads];   // and counts
   const int row = blockIdx.x, tid = threadIdx.x;
   const RowState s = st[row];
   const int n = (int)s.n;
@@ -343,7 +342,7 @@ __global__ __launch_bounds__(kFinalThreads) void tkm_final(const RowState* __res
   // above hi, then the candidates; with one key left (lo == hi) only the
   // first `rem` candidates can be taken.  The chunks' counts are read and
   // scanned kFinalThreads at a time, so every chunk's offsets are known
-  // before any entry moves and the copies need no barrier between chunks.
+  // before any entry moves.
   const uint32_t* rc = cnt + (int64_t)row * nch * 2;
   const uint32_t want_c = s.lo == s.hi ? s.rem : (uint32_t)K;
   uint32_t run_a = 0, run_c = 0;   // entries of earlier chunk groups
@@ -355,23 +354,32 @@ __global__ __launch_bounds__(kFinalThreads) void tkm_final(const RowState* __res
     if (c < nch) {
       s_goa[tid] = run_a + ea;
       s_goc[tid] = run_c + ec;
-      s_gna[tid] = na;
-      s_gnc[tid] = nc;
     }
     __syncthreads();
+    // Entry g of the group's list lies in the last chunk whose offset is
+    // <= g (an empty chunk shares its offset with the next one); threads
+    // take entries of the whole group, so all the loads are in flight at once.
     const int gn = min(kFinalThreads, nch - g0);
-    for (int k = 0; k < gn; ++k) {
-      const uint32_t oa = s_goa[k], oc = s_goc[k], ka = s_gna[k], kc = s_gnc[k];
-      const int32_t* ab = abuf + ((int64_t)row * nch + g0 + k) * K;
-      const uint2* cb = cbuf + ((int64_t)row * nch + g0 + k) * K;
-      for (uint32_t e = tid; e < ka; e += kFinalThreads)
-        if (oa + e < (uint32_t)K) s_above[oa + e] = ab[e];
-      const uint32_t take = oc < want_c ? min(kc, want_c - oc) : 0u;
-      for (uint32_t e = tid; e < take; e += kFinalThreads) {
-        const uint2 v = cb[e];
-        s_cpos[oc + e] = (int32_t)v.x;
-        s_ckey[oc + e] = v.y;
+    auto chunk_of = [&](const uint32_t* off, uint32_t g) {
+      int lo = 0, hi = gn - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= g) lo = mid;
+        else hi = mid - 1;
       }
+      return lo;
+    };
+    const uint32_t a_end = min(run_a + ta, (uint32_t)K);
+    for (uint32_t g = run_a + tid; g < a_end; g += kFinalThreads) {
+      const int k = chunk_of(s_goa, g);
+      s_above[g] = abuf[((int64_t)row * nch + g0 + k) * K + (g - s_goa[k])];
+    }
+    const uint32_t c_end = min(run_c + tc, want_c);
+    for (uint32_t g = run_c + tid; g < c_end; g += kFinalThreads) {
+      const int k = chunk_of(s_goc, g);
+      const uint2 v = cbuf[((int64_t)row * nch + g0 + k) * K + (g - s_goc[k])];
+      s_cpos[g] = (int32_t)v.x;
+      s_ckey[g] = v.y;
     }
     run_a += ta;
     run_c += tc;
