@@ -70,3 +70,33 @@ def test_topk_many_long_rows(kind):
     for r in list(range(0, n_rows, 37)) + list(range(n_rows - 4, n_rows)):
         ref = oracle.topk_row(sc[r, : pos[r] + 1], top_k)
         assert np.array_equal(got[r], ref), (kind, r, pos[r])
+
+
+def _sampled_positions(n, n_samples=2048, cluster=16):
+    """Positions the filtered top-k samples in a row of n scores (n <= 65,536):
+    n_samples / 16 clusters of 16 consecutive scores whose starts are spread
+    evenly over the row (rounded down to a multiple of 4)."""
+    k = n_samples // cluster
+    starts = [((c * (n - cluster)) // (k - 1)) & ~3 for c in range(k)]
+    return np.unique(np.concatenate([np.arange(s, s + cluster) for s in starts]))
+
+
+def test_topk_misleading_sample():
+    """Rows whose sample misleads the filtered pass's threshold: every
+    unsampled score lies above all sampled ones (far more than the 5,120 LDS
+    slots are kept: the overflow slots absorb the excess and the row is redone
+    by the streaming selection), or the samples hold the largest scores (fewer
+    than K kept, redone too).  Both stay exact."""
+    n_k, top_k = 60000, 2048
+    rng = np.random.default_rng(17)
+    sc = rng.random((4, n_k)).astype(np.float32)
+    samp = _sampled_positions(n_k)
+    rest = np.setdiff1d(np.arange(n_k), samp)
+    sc[0, rest] += 10.0          # threshold far too low
+    sc[1, samp] += 10.0          # threshold far too high
+    sc[2, rest[::3]] += 10.0     # ~19,000 kept
+    sc[3, :] = rng.random(n_k)   # an ordinary row beside them
+    pos = np.array([n_k - 1, n_k - 1, n_k - 3, 40001], dtype=np.int32)
+    got = host(sma.topk_select(dev(sc), dev(pos), top_k))
+    for r in range(4):
+        assert np.array_equal(got[r], oracle.topk_row(sc[r, : pos[r] + 1], top_k)), r
