@@ -269,13 +269,15 @@ __global__ __launch_bounds__(kTkmThreads) void tkm_collect(const float* __restri
   int32_t* ab = abuf + ((int64_t)row * nch + c) * K;
   uint2* cb = cbuf + ((int64_t)row * nch + c) * K;
   uint32_t na = 0, nc = 0;
-  // vector i + 1 is loaded while vector i is ranked
+  // vectors i + 1 and i + 2 are loaded while vector i is ranked
   u32x4 k_next = load_keys4<ALIGNED>(src, base + 4 * (int)threadIdx.x, n);
+  u32x4 k_next2 = load_keys4<ALIGNED>(src, base + 4 * kTkmThreads + 4 * (int)threadIdx.x, n);
   for (int i = 0; i < kSteps; ++i) {
     const int p0 = base + i * 4 * kTkmThreads + 4 * threadIdx.x;
     if (base + i * 4 * kTkmThreads >= n) break;   // uniform
     const u32x4 k = k_next;
-    if (i + 1 < kSteps) k_next = load_keys4<ALIGNED>(src, p0 + 4 * kTkmThreads, n);
+    k_next = k_next2;
+    if (i + 2 < kSteps) k_next2 = load_keys4<ALIGNED>(src, p0 + 8 * kTkmThreads, n);
     uint32_t a = 0, b = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
