@@ -62,7 +62,8 @@ typedef enum {
 } sma_status;
 
 /* SMA_DT_FP8_DS_MLA: FlashMLA's 656-byte fp8_ds_mla latent row (GLM-5.3
- * part 2, footnote 1, names it; the layout is FlashMLA's public one): bytes
+ * part 2, footnote 1, names it and gives its 656 bytes; the internal layout
+ * is not on the page and is taken from FlashMLA's public description): bytes
  * 0..511 the e4m3fn codes of latent dims 0..511, bytes 512..527 four fp32
  * scales (scale b for dims 128b .. 128b+127), bytes 528..655 rope dims
  * 512..575 as bf16.  Accepted as the KV of the sparse-MLA entry points
@@ -160,8 +161,11 @@ sma_status sma_index_scores_fp8(const uint8_t* q_idx, const float* q_scale, cons
  *  scores[i*ld_scores + 0 .. n_i-1].  idx[i*top_k + 0 .. m_i-1] receives the
  *  m_i = min(top_k, n_i) positions with the largest scores, in ascending
  *  position order; slots m_i .. top_k-1 receive -1.  Ties at the threshold
- *  go to the lowest positions; -0.0 and +0.0 are one value; a NaN ranks
- *  above every number.
+ *  go to the lowest positions; -0.0 and +0.0 are one value; a NaN (either
+ *  sign, any payload) ranks below every number, -inf included, so NaN
+ *  positions are selected only when a row holds fewer than m_i numbers, the
+ *  lowest NaN positions first.  Every row length and alignment follows this
+ *  one rule.
  *  Supported: 1 <= top_k <= 2048, ld_scores >= n_k, n_k < 2^31.
  *  ws/ws_bytes: workspace (sma_workspace_bytes(SMA_OP_TOPK, ...), may be 0).
  */
@@ -191,6 +195,7 @@ sma_status sma_topk_select(const float* scores, int64_t ld_scores, const int32_t
  *  softmax weight; an fp8_ds_mla row's QK is summed per 128-dim block and
  *  each block's scale applied to its part, its PV takes the softmax weight
  *  times the block's scale).
+ *  sm_scale must be finite and > 0 (SMA_ERR_INVALID_ARG otherwise).
  *  Supported: 1 <= top_k <= 2048.  ws may be NULL (ws_bytes 0).  With at
  *  least sma_workspace_bytes(SMA_OP_SPARSE_MLA, ...) bytes (256-byte
  *  aligned), a small FP8 batch splits each query's rows into slices whose
@@ -209,7 +214,8 @@ sma_status sma_sparse_mla_prefill(const uint16_t* q, const void* kv, const float
  *  idx_out  [n_q, top_k] int32 or NULL (then kept in the workspace).
  *  The scores are produced block by block in the workspace; a larger
  *  workspace allows larger query blocks (fewer launches), never different
- *  results.  Minimum size: sma_workspace_bytes(SMA_OP_PREFILL, ...).
+ *  results.  Minimum size: sma_workspace_bytes(SMA_OP_PREFILL, ...), which
+ *  holds the index list and a block of min(n_q, 64) rows, for any n_q.
  */
 sma_status sma_prefill(const uint16_t* q_idx, const float* w, int64_t w_stride,
                        const void* k_idx, const float* k_scale, int32_t k_dtype,

@@ -29,7 +29,7 @@ Sources, by page and section:
   values).
 * DeepSeek multi-node deployment page, section "Quantification": activations
   are quantised on the fly with one scale per 128-element vector.
-* same page, section "DCP : sharder aussi le cache KV": tokens are dealt
+* GLM-5.3 part 2, section "DCP : sharder aussi le cache KV": tokens are dealt
   round-robin over the ranks, each rank attends over its own shard and the
   partial results are merged by their log-sum-exp.
 * DeepSeek multi-node deployment page (Perplexity), sections
@@ -42,7 +42,7 @@ Readings where the pages are silent (each also listed in the design notes):
   0 <= s <= p_i (the query's own token included), no bias, no scaling;
 * top-k keeps the min(K, p_i+1) largest scores; ties at the threshold go to
   the lowest positions; the list is ascending by position, padded with -1;
-  -0.0 and +0.0 are the same value;
+  -0.0 and +0.0 are the same value; a NaN ranks below every number;
 * attention scale tau = 1/sqrt(192); value = the first 512 latent dims;
   LSE is the natural-log log-sum-exp of the scaled logits;
 * FP8 is OCP e4m3fn (bias 7, max 448, no infinities) times a per-token fp32
@@ -205,7 +205,9 @@ def topk_row(scores: np.ndarray, top_k: int) -> np.ndarray:
 
     Keeps m = min(top_k, len) positions: every position whose score is above
     the m-th largest value T, then the lowest positions whose score equals T
-    until m are kept.
+    until m are kept.  A NaN score ranks below every number (-inf included):
+    NaN positions are kept only when fewer than m scores are numbers, the
+    lowest NaN positions first.
     """
     s = np.asarray(scores, dtype=np.float64)
     n = s.size
@@ -213,11 +215,17 @@ def topk_row(scores: np.ndarray, top_k: int) -> np.ndarray:
     out = np.full(top_k, -1, dtype=np.int32)
     if m == 0:
         return out
-    t = np.partition(s, n - m)[n - m]               # m-th largest value
-    above = np.flatnonzero(s > t)
-    ties = np.flatnonzero(s == t)[: m - above.size]
-    sel = np.sort(np.concatenate([above, ties]))
-    out[:m] = sel
+    nan = np.isnan(s)
+    num = np.flatnonzero(~nan)                      # positions holding numbers
+    if num.size >= m:
+        v = s[num]
+        t = np.partition(v, v.size - m)[v.size - m]   # m-th largest number
+        above = num[v > t]
+        ties = num[v == t][: m - above.size]
+        sel = np.concatenate([above, ties])
+    else:
+        sel = np.concatenate([num, np.flatnonzero(nan)[: m - num.size]])
+    out[:m] = np.sort(sel)
     return out
 
 

@@ -3,6 +3,7 @@
 // contract of every entry point are in include/sma.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -32,20 +33,26 @@ sma_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int kMaxDevices = 64;
-int g_dev_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other (benign race: idempotent)
+// Per-device facts queried once: 0 = not yet known.  Concurrent first calls
+// may both query; they store the same value, and the atomics make that a
+// well-defined race.
+std::atomic<int> g_dev_ok[kMaxDevices];   // 1 gfx950, -1 other
+std::atomic<int> g_dev_cus[kMaxDevices];  // compute units
 
 sma_status check_device() {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev < 0 || dev >= kMaxDevices) return fail(SMA_ERR_UNSUPPORTED, "device ordinal %d", dev);
-  if (g_dev_ok[dev] == 0) {
+  int ok = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (ok == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
-    g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_dev_ok[dev].store(ok, std::memory_order_relaxed);
   }
-  if (g_dev_ok[dev] != 1) return fail(SMA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  if (ok != 1) return fail(SMA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
   return SMA_OK;
 }
 
@@ -116,7 +123,7 @@ sma_status validate_mla(const uint16_t* q, const void* kv, const float* kv_scale
   SMA_CHECK((kv_dtype == SMA_DT_FP8_E4M3) == (kv_scale != nullptr),   // fp8_ds_mla rows carry their scales
             "kv_scale must be given exactly when the KV is FP8");
   SMA_CHECK(aligned(kv, 16), "kv not 16-byte aligned");
-  SMA_CHECK(std::isfinite(sm_scale), "sm_scale not finite");
+  SMA_CHECK(std::isfinite(sm_scale) && sm_scale > 0.f, "sm_scale = %g (finite and > 0)", (double)sm_scale);
   if (n_q > 0) {
     SMA_CHECK(q && out && (idx || idx_may_be_null), "q, idx and out must be non-NULL");
     SMA_CHECK(aligned(q, 16), "q not 16-byte aligned");
@@ -160,13 +167,17 @@ sma_status run_prefill(const void* q_idx, const float* q_scale, const float* w, 
                        int64_t n_k, int32_t h_idx, int32_t d_idx, int32_t top_k, float sm_scale,
                        void* out, int32_t out_dtype, float* lse, int32_t* idx, uint8_t* score_ws,
                        size_t score_ws_bytes, hipStream_t st) {
-  // the largest block of query rows (all of them, or a multiple of 16) whose
-  // scores and top-k buffers fit
-  const size_t row_bytes = score_block_bytes(1, n_k, top_k);
-  int64_t qb = (int64_t)(score_ws_bytes / row_bytes);
-  if (qb >= n_q) qb = n_q;
-  else qb = qb / 16 * 16;
-  while (qb > 0 && score_block_bytes(qb, n_k, top_k) > score_ws_bytes) qb = qb > 16 ? qb - 16 : qb - 1;
+  // the largest block of query rows whose scores and top-k buffers fit (the
+  // size grows with the rows), rounded down to a multiple of 16 when it
+  // holds 16 or more but not all of them
+  int64_t lo = 0, hi = n_q;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    if (score_block_bytes(mid, n_k, top_k) <= score_ws_bytes) lo = mid;
+    else hi = mid - 1;
+  }
+  int64_t qb = lo;
+  if (qb < n_q && qb >= 16) qb = qb / 16 * 16;
   if (qb < 1) return fail(SMA_ERR_WORKSPACE, "workspace holds no score block");
   float* scores = reinterpret_cast<float*>(score_ws);
   uint8_t* topk_ws = score_ws + align_up((size_t)qb * (size_t)n_k * 4, 256);
@@ -512,6 +523,17 @@ hipError_t launch_pcp_positions(int32_t* pos, int32_t rank, int32_t pcp_size, in
   const int n = 2 * c;
   hipLaunchKernelGGL(pcp_positions_kernel, dim3((n + 255) / 256), dim3(256), 0, st, pos, rank, nchunk, c);
   return hipGetLastError();
+}
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_dev_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_dev_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 }  // namespace sma

@@ -29,14 +29,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // Order-preserving map of an fp32 score onto uint32 (larger score -> larger
-// key); -0.0 is folded onto +0.0 so the two zeros are one key.  The result
-// is never 0 (the one NaN pattern that would map there is moved up by one),
-// which leaves 0 free as a "no element" marker.
+// key); -0.0 is folded onto +0.0 so the two zeros are one key, and every NaN
+// (either sign, any payload) takes key 1, below -inf (key 0x007FFFFF), so a
+// NaN ranks below every number.  The result is never 0, which leaves 0 free
+// as a "no element" marker.
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t b = __float_as_uint(f);
   if (b == 0x80000000u) b = 0u;
   const uint32_t k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return k ? k : 1u;
+  return f != f ? 1u : k;
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -7,6 +7,10 @@
 
 namespace sma {
 
+// Compute units of the current device (queried once per device, kept in an
+// atomic per-device cache; 256 if the query fails).
+int device_cu_count();
+
 struct IdxArgs {
   const void* q_idx;        // bf16 rows, or e4m3fn codes when q_scale is set
   const float* q_scale = nullptr;   // FP8 queries: one scale per (query, head) row

@@ -837,19 +837,6 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
   if (lse && h == 0) lse[(int64_t)qi * kHeads + 32 * d + c32] = (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
-// Compute units of the current device (cached per device).
-static int device_cu_count() {
-  static int cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 int mla_split_count(int n_q, int top_k, bool fp8) {
   if (!fp8 || n_q <= 0) return 1;
   const int cus = device_cu_count();

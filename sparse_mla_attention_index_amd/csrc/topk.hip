@@ -310,6 +310,7 @@ constexpr int kFtU = 8;                           // 16-byte loads per thread pe
 constexpr int kFtChunk = kFtThreads * 4 * kFtU;   // 8,192 positions
 constexpr int kFtWaveSpan = 256 * kFtU;           // a wave's contiguous share of a chunk
 constexpr int kFtKeep = kFtCap / kFtThreads;      // kept keys per thread in the final select
+constexpr int64_t kFtLongMax = 1 << 18;           // longest rows the filtered kernel takes
 
 // The score whose key is k (the inverse of score_key for finite scores).
 __device__ __forceinline__ float key_score(uint32_t k) {
@@ -603,26 +604,18 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
 
 bool topk_multi_wanted(int64_t n_k) { return n_k > 4 * 1024 * 16; }
 
-// Compute units of the current device (cached per device).
-static int topk_cu_count() {
-  static int cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   if (A.n_q <= 0) return hipSuccess;
   const bool rows_aligned = (reinterpret_cast<uintptr_t>(A.scores) % 16 == 0) && (A.ld % 4 == 0);
   const dim3 grid((unsigned)A.n_q);
   // Long rows with enough of them to fill the device (a few workgroups per
-  // CU) take the filtered kernel too, with 32-bit positions.
-  if (rows_aligned && A.n_k > 65536 && A.n_k <= INT32_MAX && A.n_q >= 4 * topk_cu_count()) {
+  // CU) take the filtered kernel too, with 32-bit positions, up to the row
+  // length whose expected kept count stays well inside the LDS slots: the
+  // 4,096-sample threshold keeps about 1.3K + 3 sqrt(K n / 4096) + n / 1024
+  // scores of an n-score row (about 4,000 +- 510 at n = 2^18 with K = 2,048,
+  // 4,710 +- 780 at 2^19, against kFtCap = 5,120 slots); a row that
+  // overflows is redone by the streaming selection, several passes over it.
+  if (rows_aligned && A.n_k > 65536 && A.n_k <= kFtLongMax && A.n_q >= 4 * device_cu_count()) {
     hipLaunchKernelGGL((topk_filter_kernel<uint32_t, 16, 3>), grid, dim3(kFtThreads), 0, st, A.scores, A.ld,
                        A.q_pos, (int)A.n_k, A.top_k, A.idx);
     return hipGetLastError();

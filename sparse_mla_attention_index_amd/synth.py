@@ -254,7 +254,9 @@ def random_scores(seed: int, n_rows: int, n_cols: int, kind: str) -> np.ndarray:
 
     kind = "normal": continuous N(0,1) values; "ints": small integers with
     many ties; "ties": a handful of distinct values; "signed_zero": values in
-    {-0.0, +0.0, 1.0} to check that the two zeros are one key.
+    {-0.0, +0.0, 1.0} to check that the two zeros are one key; "nan" / "nan_heavy":
+    N(0,1) values with about 10% / 90% of entries replaced by NaNs of both
+    signs and several payloads, and a few +-inf.
     """
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_BASE, 100, seed])))
     if kind == "normal":
@@ -266,4 +268,13 @@ def random_scores(seed: int, n_rows: int, n_cols: int, kind: str) -> np.ndarray:
     if kind == "signed_zero":
         c = rng.integers(0, 3, size=(n_rows, n_cols))
         return np.where(c == 0, np.float32(-0.0), np.where(c == 1, np.float32(0.0), np.float32(1.0))).astype(np.float32)
+    if kind in ("nan", "nan_heavy"):
+        x = rng.standard_normal((n_rows, n_cols), dtype=np.float32)
+        u = rng.random((n_rows, n_cols))
+        frac = 0.1 if kind == "nan" else 0.9
+        pats = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF], dtype=np.uint32).view(np.float32)
+        x = np.where(u < frac, pats[rng.integers(0, 4, size=(n_rows, n_cols))], x)
+        infs = np.array([np.inf, -np.inf], dtype=np.float32)
+        x = np.where((u >= frac) & (u < frac + 0.002), infs[rng.integers(0, 2, size=(n_rows, n_cols))], x)
+        return x.astype(np.float32)
     raise KeyError(kind)

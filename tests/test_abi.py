@@ -167,3 +167,12 @@ def test_absorb_q_validation(n, heads, ld, msg):
 def test_project_out_validation():
     assert sma.lib().sma_project_out(FAKE, FAKE, 4, 2000, FAKE, None) == -1 and "heads" in sma.last_error()
     assert sma.lib().sma_project_out(None, FAKE, 4, 64, FAKE, None) == -1 and "NULL" in sma.last_error()
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1, float("inf"), float("nan")])
+def test_mla_scale_must_be_positive(scale):
+    r = sma.lib().sma_sparse_mla_prefill(FAKE, FAKE, None, 0, 100, FAKE, 1, 8, scale, FAKE, 0, None, None, 0, None)
+    assert r == -1 and "sm_scale" in sma.last_error()
+    r = sma.lib().sma_dcp_shard_partial(0, 2, FAKE, FAKE, None, 0, 100, FAKE, 1, 8, scale, FAKE, FAKE, FAKE,
+                                        1 << 20, None)
+    assert r == -1 and "sm_scale" in sma.last_error()

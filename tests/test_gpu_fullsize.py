@@ -15,10 +15,10 @@ from _gpuhelp import check_topk_threshold_rule, host, out_f64
 pytestmark = pytest.mark.gpu
 
 
-def _upload(w, tensor, n, chunk):
-    """Rows [0, n) of a workload tensor, generated in chunks straight into
-    device memory (bf16 bits as int16; FP8 as codes + scales)."""
-    first = synth.rows(w, tensor, 0, min(n, chunk))
+def _upload(w, tensor, n, chunk, start=0):
+    """Rows [start, start + n) of a workload tensor, generated in chunks
+    straight into device memory (bf16 bits as int16; FP8 as codes + scales)."""
+    first = synth.rows(w, tensor, start, start + min(n, chunk))
     if isinstance(first, tuple):
         codes = torch.empty((n,) + first[0].shape[1:], dtype=torch.uint8, device="cuda:0")
         scale = torch.empty((n,), dtype=torch.float32, device="cuda:0")
@@ -28,7 +28,7 @@ def _upload(w, tensor, n, chunk):
         out = torch.empty((n,) + first.shape[1:], dtype=dt, device="cuda:0")
     for a in range(0, n, chunk):
         b = min(n, a + chunk)
-        x = first if a == 0 else synth.rows(w, tensor, a, b)
+        x = first if a == 0 else synth.rows(w, tensor, start + a, start + b)
         if isinstance(x, tuple):
             out[0][a:b].copy_(torch.from_numpy(x[0]))
             out[1][a:b].copy_(torch.from_numpy(x[1]))
@@ -101,3 +101,47 @@ def test_decode_1m_fp8_sampled_queries():
     got = out_f64(out[sel])
     assert np.abs(got - ref).max() <= 3e-2 * np.abs(ref).max()
     assert np.abs(host(lse[sel]) - ref_lse).max() < 5e-3
+
+
+def test_pcp_share_131k_ranks_0_and_7():
+    """One PCP8 rank's share of a 131,072-token prompt (16 chunks of 8,192),
+    ranks 0 and 7 in the bench's configuration (one score block holding all
+    16,384 query rows), checked on rows at both chunks' first and last
+    positions and spread between: the selections follow the threshold rule
+    against the oracle's scores, attention on the GPU's own lists is within
+    1e-2 of max|ref| and the LSE within 2e-3."""
+    w = synth.workload(4)
+    L, P = w.n_keys, w.pcp_size
+    C = L // (2 * P)
+    k_idx = _upload(w, "k_idx", L, 65536)
+    kv = _upload(w, "kv", L, 16384)
+    f = oracle.bf16_bits_to_f64
+    kk = f(host(k_idx).view(np.uint16))
+    kvv = f(host(kv).view(np.uint16))
+    rows = np.unique(np.r_[0, 1, C - 1, C, C + 1, 2 * C - 2, 2 * C - 1,
+                           np.linspace(0, 2 * C - 1, 7).round().astype(int)])
+    sel = torch.from_numpy(rows).to("cuda:0")
+    for r in (0, 7):
+        pos_np = oracle.pcp_positions(r, P, L)
+        halves = [(r * C, C), ((2 * P - 1 - r) * C, C)]
+        q_idx = torch.cat([_upload(w, "q_idx", n, 1024, a) for a, n in halves])
+        wt = torch.cat([_upload(w, "w", n, 65536, a) for a, n in halves])
+        q = torch.cat([_upload(w, "q", n, 256, a) for a, n in halves])
+        idx = torch.empty((2 * C, w.top_k), dtype=torch.int32, device="cuda:0")
+        ws_n = 2 * C * 4 + 2 * C * L * 4 + sma.workspace_bytes(sma._lib.SMA_OP_TOPK, 2 * C, L, w.top_k) + 4096
+        ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda:0")
+        out, lse, _ = sma.pcp_rank_share(r, P, q_idx, wt, k_idx, q, kv, w.top_k, w.sm_scale, want_lse=True,
+                                         idx_share=idx, workspace=ws)
+        torch.cuda.synchronize()
+        del ws
+        sub = pos_np[rows]
+        sc = oracle.index_scores(f(host(q_idx[sel]).view(np.uint16)), host(wt[sel]).astype(np.float64), kk, sub)
+        gi = host(idx[sel])
+        for j, s_ in enumerate(sc):
+            check_topk_threshold_rule(gi[j], s_, w.top_k)
+        ref, ref_lse = oracle.sparse_mla(f(host(q[sel]).view(np.uint16)), kvv, gi, w.sm_scale)
+        got = out_f64(out[sel])
+        assert np.abs(got - ref).max() <= 1e-2 * np.abs(ref).max(), r
+        assert np.abs(host(lse[sel]) - ref_lse).max() < 2e-3, r
+        del q_idx, wt, q, out, lse, idx
+        torch.cuda.empty_cache()

@@ -20,7 +20,7 @@ def _positions(n_rows, n_k, top_k, seed):
     return pos.astype(np.int32)
 
 
-@pytest.mark.parametrize("kind", ["normal", "ints", "ties", "signed_zero"])
+@pytest.mark.parametrize("kind", ["normal", "ints", "ties", "signed_zero", "nan", "nan_heavy"])
 @pytest.mark.parametrize("n_k,top_k", [(300, 128), (5000, 2048), (20000, 2048), (40000, 1), (70000, 2048),
                                        (140000, 2048)])
 def test_topk_exact(kind, n_k, top_k):
@@ -34,11 +34,12 @@ def test_topk_exact(kind, n_k, top_k):
         assert np.array_equal(got[r], ref), (kind, n_k, top_k, r, pos[r])
 
 
-@pytest.mark.parametrize("pad", [1, 3, 64])
-def test_topk_row_stride(pad):
-    """Rows with a leading dimension larger than n_k (aligned or not)."""
+@pytest.mark.parametrize("pad,kind", [(1, "normal"), (3, "normal"), (64, "normal"), (1, "nan"), (3, "nan_heavy")])
+def test_topk_row_stride(pad, kind):
+    """Rows with a leading dimension larger than n_k (aligned or not; an
+    unaligned row takes the streaming selection)."""
     n_k, top_k, n_rows = 9000, 512, 16
-    sc = synth.random_scores(77, n_rows, n_k + pad, "normal")
+    sc = synth.random_scores(77, n_rows, n_k + pad, kind)
     pos = _positions(n_rows, n_k, top_k, pad)
     t = dev(sc)
     idx = sma.topk_select(t, dev(pos), top_k, n_k=n_k)
@@ -57,7 +58,7 @@ def test_topk_clamped_positions():
     assert np.array_equal(got[3], oracle.topk_row(sc[3, :51], top_k))
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "nan"])
 def test_topk_many_long_rows(kind):
     """Rows longer than 65,536 scores, enough of them to fill the device (the
     one-workgroup-per-row path with 32-bit positions); rows checked on a

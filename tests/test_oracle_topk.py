@@ -12,15 +12,18 @@ from sparse_mla_attention_index_amd import synth
 
 
 def _by_full_sort(row, k):
+    """Sort key: numbers before NaNs, then score descending, then position."""
     n = row.size
     m = min(k, n)
-    order = np.lexsort((np.arange(n), -row.astype(np.float64)))
+    r = row.astype(np.float64)
+    isnan = np.isnan(r)
+    order = np.lexsort((np.arange(n), -np.where(isnan, 0.0, r), isnan))
     out = np.full(k, -1, dtype=np.int32)
     out[:m] = np.sort(order[:m])
     return out
 
 
-@pytest.mark.parametrize("kind", ["normal", "ints", "ties", "signed_zero"])
+@pytest.mark.parametrize("kind", ["normal", "ints", "ties", "signed_zero", "nan", "nan_heavy"])
 def test_matches_full_sort(kind):
     sc = synth.random_scores(11, 40, 97, kind)
     for k in (1, 5, 16, 96, 97, 200):
@@ -76,3 +79,13 @@ def test_threshold_value():
     assert oracle.topk_threshold(row, 2) == 9.0
     assert oracle.topk_threshold(row, 3) == 5.0
     assert oracle.topk_threshold(row, 10) == 1.0
+
+
+def test_nan_ranks_below_every_number():
+    nan = np.float32(np.nan)
+    row = np.array([nan, -np.inf, nan, 2.0, nan], dtype=np.float32)
+    assert oracle.topk_row(row, 2).tolist() == [1, 3]          # -inf beats NaN
+    assert oracle.topk_row(row, 3).tolist() == [0, 1, 3]       # then the lowest NaN position
+    assert oracle.topk_row(row, 5).tolist() == [0, 1, 2, 3, 4]
+    neg = np.array([0xFFC00000, 0x7FC00000], dtype=np.uint32).view(np.float32)   # NaNs of both signs
+    assert oracle.topk_row(np.array([neg[0], neg[1], -1.0], dtype=np.float32), 2).tolist() == [0, 2]
