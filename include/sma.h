@@ -196,11 +196,14 @@ sma_status sma_topk_select(const float* scores, int64_t ld_scores, const int32_t
  *  each block's scale applied to its part, its PV takes the softmax weight
  *  times the block's scale).
  *  sm_scale must be finite and > 0 (SMA_ERR_INVALID_ARG otherwise).
- *  Supported: 1 <= top_k <= 2048.  ws may be NULL (ws_bytes 0).  With at
- *  least sma_workspace_bytes(SMA_OP_SPARSE_MLA, ...) bytes (256-byte
- *  aligned), a small FP8 batch splits each query's rows into slices whose
- *  partial results are merged by log-sum-exp; results are the same up to
- *  fp32 summation order.
+ *  Supported: 1 <= top_k <= 2048.  ws may be NULL (ws_bytes 0).  With a
+ *  workspace (256-byte aligned), a small FP8 batch splits each query's rows
+ *  into slices whose partial results are merged by log-sum-exp: with
+ *  sma_workspace_bytes(SMA_OP_SPARSE_MLA, ...) bytes into the preferred
+ *  number of slices, with less into as many as the workspace holds
+ *  partials for.  Slices change the result only by rounding: fp32
+ *  summation order, and the bf16 rounding of the softmax weights, which each
+ *  slice takes against its own running maximum.
  */
 sma_status sma_sparse_mla_prefill(const uint16_t* q, const void* kv, const float* kv_scale,
                                   int32_t kv_dtype, int64_t n_k, const int32_t* idx,
@@ -310,6 +313,39 @@ sma_status sma_dcp_shard_partial(int32_t rank, int32_t dcp_size, const uint16_t*
                                  const int32_t* idx, int32_t n_q, int32_t top_k, float sm_scale,
                                  float* out_partial, float* lse_partial, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/*
+ * sma_dcp_shard_partial_noalloc — sma_dcp_shard_partial for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): no workspace argument,
+ * and no allocation inside.
+ *
+ *  Scratch: a static device array of SMA_STATIC_SCRATCH_BYTES (64 MiB) per
+ *  device, part of the library's code object, so each device that runs the
+ *  library holds it until the process ends.  It holds the rank's local
+ *  index list (n_q*top_k*4 bytes, 256-byte aligned) and, in what remains,
+ *  the partials of an FP8 batch's row slices (as many slices as fit, up to
+ *  the count sma_dcp_shard_partial uses with a full workspace).  With the
+ *  same slice count the two entries give identical results; with fewer
+ *  slices they differ by the bf16 rounding of the softmax weights, which
+ *  each slice takes against its own running maximum (about 2^-8 relative).
+ *  Every buffer is written before it is read, so nothing from an earlier
+ *  call leaks into a result.
+ *  Limit: a call whose index list exceeds the scratch (n_q*top_k >
+ *  SMA_STATIC_SCRATCH_BYTES/4 = 16,777,216 entries) returns
+ *  SMA_ERR_WORKSPACE before any launch.
+ *  Concurrency: every call on one device shares that device's array.  Calls
+ *  ordered on one stream are safe; calls that overlap in time on one device
+ *  (different streams, or several host threads) race on it and give wrong
+ *  results.
+ *  Arguments, results and the other errors are those of
+ *  sma_dcp_shard_partial.
+ */
+#define SMA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+sma_status sma_dcp_shard_partial_noalloc(int32_t rank, int32_t dcp_size, const uint16_t* q, const void* kv_local,
+                                         const float* kv_scale_local, int32_t kv_dtype, int64_t n_k_local,
+                                         const int32_t* idx, int32_t n_q, int32_t top_k, float sm_scale,
+                                         float* out_partial, float* lse_partial, void* stream);
 
 /*
  * sma_lse_merge — merge n_part partial attention results by their

@@ -35,6 +35,7 @@ SIGNATURES = {
                                   _I32, _F, _P, _I32, _P, _P, _P, _SZ, _P]),
     "sma_dcp_shard_partial": (_I32, [_I32, _I32, _P, _P, _P, _I32, _I64, _P, _I32, _I32, _F, _P, _P, _P, _SZ,
                                      _P]),
+    "sma_dcp_shard_partial_noalloc": (_I32, [_I32, _I32, _P, _P, _P, _I32, _I64, _P, _I32, _I32, _F, _P, _P, _P]),
     "sma_lse_merge": (_I32, [_P, _P, _I32, _I32, _P, _I32, _P, _P]),
     "sma_quantize_fp8_rows": (_I32, [_P, _I64, _I32, _P, _P, _P]),
     "sma_absorb_q": (_I32, [_P, _P, _I32, _I32, _P, _I64, _P]),
@@ -383,6 +384,28 @@ def dcp_shard_partial(rank: int, dcp_size: int, q, kv_local, idx, sm_scale: floa
                                        kv_local.shape[0], _ptr(idx), n_q, top_k, float(sm_scale), _ptr(out),
                                        _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                        _stream(dev)))
+    return out, lse
+
+
+def dcp_shard_partial_noalloc(rank: int, dcp_size: int, q, kv_local, idx, sm_scale: float, *,
+                              kv_scale_local=None, out=None, lse=None):
+    """dcp_shard_partial with the library's static device scratch in place of
+    a workspace (no device allocation inside the call; `out` and `lse` must
+    then be given by the caller for the call to allocate nothing at all)."""
+    n_q = q.shape[0]
+    _bf16(q, "q")
+    kdt = _keys(kv_local, kv_scale_local, "kv_local")
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32")
+    dev = q.device
+    if out is None:
+        out = torch.empty((n_q, HEADS, D_V), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((n_q, HEADS), dtype=torch.float32, device=dev)
+    top_k = idx.shape[1]
+    _check(lib().sma_dcp_shard_partial_noalloc(rank, dcp_size, _ptr(q), _ptr(kv_local), _ptr(kv_scale_local), kdt,
+                                               kv_local.shape[0], _ptr(idx), n_q, top_k, float(sm_scale), _ptr(out),
+                                               _ptr(lse), _stream(dev)))
     return out, lse
 
 

@@ -8,10 +8,16 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/sma.h"
 #include "sma_launch.h"
+
+// Scratch of sma_dcp_shard_partial_noalloc (its callers cannot allocate):
+// the rank's local index list and the FP8 row slices' partials.
+constexpr size_t kStaticScratchBytes = SMA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -234,6 +240,65 @@ sma_status prefill_entry(const void* q_idx, const float* q_scale, const float* w
                      ws_bytes - (size_t)(p - static_cast<uint8_t*>(ws)), (hipStream_t)stream);
 }
 
+sma_status validate_dcp(int32_t rank, int32_t dcp_size, const uint16_t* q, const void* kv_local,
+                        const float* kv_scale_local, int32_t kv_dtype, int64_t n_k_local, const int32_t* idx,
+                        int32_t n_q, int32_t top_k, float sm_scale, float* out_partial, float* lse_partial) {
+  SMA_CHECK(dcp_size >= 1, "dcp_size = %d < 1", dcp_size);
+  SMA_CHECK(rank >= 0 && rank < dcp_size, "rank = %d not in [0, %d)", rank, dcp_size);
+  sma_status s = validate_mla(q, kv_local, kv_scale_local, kv_dtype, n_k_local, idx, n_q, top_k, sm_scale,
+                              out_partial, SMA_DT_FP32, false);
+  if (s != SMA_OK) return s;
+  if (n_q > 0) SMA_CHECK(lse_partial != nullptr, "lse_partial is NULL");
+  return SMA_OK;
+}
+
+// One DCP rank's partial after validation: the rank's local index list at the
+// start of `ws`, the FP8 row slices' partials in the rest.
+sma_status run_dcp_partial(int32_t rank, int32_t dcp_size, const uint16_t* q, const void* kv_local,
+                           const float* kv_scale_local, int32_t kv_dtype, int64_t n_k_local, const int32_t* idx,
+                           int32_t n_q, int32_t top_k, float sm_scale, float* out_partial, float* lse_partial,
+                           uint8_t* ws, size_t ws_bytes, hipStream_t st) {
+  const size_t idx_bytes = align_up((size_t)n_q * (size_t)top_k * 4, 256);
+  int32_t* local = reinterpret_cast<int32_t*>(ws);
+  hipError_t e = sma::launch_dcp_local_idx(idx, n_q, top_k, rank, dcp_size, n_k_local, local, st);
+  if (e != hipSuccess) return hip_fail(e, "dcp_local_idx launch");
+  sma::MlaArgs a{q, kv_local, kv_scale_local, kv_dtype != SMA_DT_BF16, n_k_local, local, n_q, top_k,
+                 sm_scale, out_partial, true, lse_partial, ws + idx_bytes, ws_bytes - idx_bytes};
+  a.ds_mla = kv_dtype == SMA_DT_FP8_DS_MLA;
+  e = sma::launch_sparse_mla(a, st);
+  return e == hipSuccess ? SMA_OK : hip_fail(e, "sparse_mla launch");
+}
+
+// The no-allocation entry's scratch: one static device array per device,
+// reached through the address hipGetSymbolAddress returns for the current
+// device (the array's name is only a host-side stand-in).  Taken once per
+// device, under a lock, at that device's first call; kept until the process
+// ends.
+std::atomic<uint8_t*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+sma_status static_scratch(uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SMA_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  uint8_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (addr == nullptr) return fail(SMA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+      p = static_cast<uint8_t*>(addr);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SMA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -362,28 +427,38 @@ sma_status sma_dcp_shard_partial(int32_t rank, int32_t dcp_size, const uint16_t*
                                  float* out_partial, float* lse_partial, void* ws, size_t ws_bytes,
                                  void* stream) {
   g_err.clear();
-  SMA_CHECK(dcp_size >= 1, "dcp_size = %d < 1", dcp_size);
-  SMA_CHECK(rank >= 0 && rank < dcp_size, "rank = %d not in [0, %d)", rank, dcp_size);
-  sma_status s = validate_mla(q, kv_local, kv_scale_local, kv_dtype, n_k_local, idx, n_q, top_k, sm_scale,
-                              out_partial, SMA_DT_FP32, false);
-  if (s != SMA_OK) return s;
-  if (n_q == 0) return SMA_OK;
-  SMA_CHECK(lse_partial != nullptr, "lse_partial is NULL");
+  sma_status s = validate_dcp(rank, dcp_size, q, kv_local, kv_scale_local, kv_dtype, n_k_local, idx, n_q, top_k,
+                              sm_scale, out_partial, lse_partial);
+  if (s != SMA_OK || n_q == 0) return s;
   const size_t idx_bytes = align_up((size_t)n_q * (size_t)top_k * 4, 256);
   if (ws == nullptr || ws_bytes < idx_bytes)
     return fail(SMA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws ? ws_bytes : 0, idx_bytes);
   SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
   if ((s = check_device()) != SMA_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
-  int32_t* local = static_cast<int32_t*>(ws);
-  hipError_t e = sma::launch_dcp_local_idx(idx, n_q, top_k, rank, dcp_size, n_k_local, local, st);
-  if (e != hipSuccess) return hip_fail(e, "dcp_local_idx launch");
-  sma::MlaArgs a{q, kv_local, kv_scale_local, kv_dtype != SMA_DT_BF16, n_k_local, local, n_q, top_k,
-                 sm_scale, out_partial, true, lse_partial, static_cast<uint8_t*>(ws) + idx_bytes,
-                 ws_bytes - idx_bytes};
-  a.ds_mla = kv_dtype == SMA_DT_FP8_DS_MLA;
-  e = sma::launch_sparse_mla(a, st);
-  return e == hipSuccess ? SMA_OK : hip_fail(e, "sparse_mla launch");
+  return run_dcp_partial(rank, dcp_size, q, kv_local, kv_scale_local, kv_dtype, n_k_local, idx, n_q, top_k,
+                         sm_scale, out_partial, lse_partial, static_cast<uint8_t*>(ws), ws_bytes,
+                         (hipStream_t)stream);
+}
+
+sma_status sma_dcp_shard_partial_noalloc(int32_t rank, int32_t dcp_size, const uint16_t* q, const void* kv_local,
+                                         const float* kv_scale_local, int32_t kv_dtype, int64_t n_k_local,
+                                         const int32_t* idx, int32_t n_q, int32_t top_k, float sm_scale,
+                                         float* out_partial, float* lse_partial, void* stream) {
+  g_err.clear();
+  sma_status s = validate_dcp(rank, dcp_size, q, kv_local, kv_scale_local, kv_dtype, n_k_local, idx, n_q, top_k,
+                              sm_scale, out_partial, lse_partial);
+  if (s != SMA_OK || n_q == 0) return s;
+  const size_t idx_bytes = align_up((size_t)n_q * (size_t)top_k * 4, 256);
+  if (idx_bytes > kStaticScratchBytes)
+    return fail(SMA_ERR_WORKSPACE,
+                "n_q * top_k = %lld index entries (%zu bytes) exceed the %zu-byte static scratch "
+                "(at most %zu entries)", (long long)n_q * top_k, idx_bytes, kStaticScratchBytes,
+                kStaticScratchBytes / 4);
+  if ((s = check_device()) != SMA_OK) return s;
+  uint8_t* ws = nullptr;
+  if ((s = static_scratch(&ws)) != SMA_OK) return s;
+  return run_dcp_partial(rank, dcp_size, q, kv_local, kv_scale_local, kv_dtype, n_k_local, idx, n_q, top_k,
+                         sm_scale, out_partial, lse_partial, ws, kStaticScratchBytes, (hipStream_t)stream);
 }
 
 sma_status sma_lse_merge(const float* parts, const float* lses, int32_t n_part, int32_t n_q, void* out,

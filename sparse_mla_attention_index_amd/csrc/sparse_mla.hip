@@ -855,10 +855,15 @@ hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
   const float scale_log2 = A.sm_scale * 1.4426950408889634f;
   const dim3 grid((unsigned)A.n_q), block(kMlaThreads);
   if (A.fp8) {
-    // small batches split each query's rows across workgroups when the
-    // workspace holds the partials
+    // small batches split each query's rows across workgroups, into as many
+    // slices as the workspace holds partials for (up to the preferred count)
     int n_split = mla_split_count(A.n_q, A.top_k, true);
-    if (n_split > 1 && (A.ws == nullptr || A.ws_bytes < mla_split_bytes(A.n_q, n_split))) n_split = 1;
+    if (n_split > 1) {
+      const size_t per_slice = mla_split_bytes(A.n_q, 2) / 2;
+      const size_t fit = A.ws ? A.ws_bytes / per_slice : 0;
+      if ((size_t)n_split > fit) n_split = (int)fit;
+      if (n_split < 2) n_split = 1;
+    }
     float* part = n_split > 1 ? static_cast<float*>(A.ws) : nullptr;
     const dim3 grid_s((unsigned)(A.n_q * n_split));
 #define SMA_MLA_F8(KVF, F32)                                                                          \

@@ -176,3 +176,13 @@ def test_mla_scale_must_be_positive(scale):
     r = sma.lib().sma_dcp_shard_partial(0, 2, FAKE, FAKE, None, 0, 100, FAKE, 1, 8, scale, FAKE, FAKE, FAKE,
                                         1 << 20, None)
     assert r == -1 and "sm_scale" in sma.last_error()
+
+
+def test_dcp_noalloc_limit():
+    """The no-allocation DCP partial rejects, before any launch, an index list
+    larger than its static scratch (64 MiB: 16,777,216 entries)."""
+    r = sma.lib().sma_dcp_shard_partial_noalloc(0, 2, FAKE, FAKE, None, 0, 100, FAKE, 8193, 2048, 0.1, FAKE, FAKE,
+                                                None)
+    assert r == -3 and "static scratch" in sma.last_error()
+    r = sma.lib().sma_dcp_shard_partial_noalloc(2, 2, FAKE, FAKE, None, 0, 100, FAKE, 1, 8, 0.1, FAKE, FAKE, None)
+    assert r == -1 and "rank" in sma.last_error()
