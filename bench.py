@@ -1,30 +1,42 @@
 #!/usr/bin/env python3
 """Benchmark of the sparse-MLA prefill path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill64k|pcp|decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--only]
 
-A step is one pass of the hot path over the workload's batch: indexer
-scores -> per-query top-k -> sparse MLA (sma_prefill), inputs resident in
-HBM before timing starts.  The default workload is a single-layer prefill of
-L = 65,536 tokens (top_k = 2,048, 64-head indexer of dim 128, 64-head MLA
-over a 576-wide bf16 latent), on seeded synthetic data.
+A step is one pass of the hot path over a workload's batch: indexer scores
+-> per-query top-k -> sparse MLA (sma_prefill, or sma_pcp_rank_share for the
+PCP share), inputs resident in HBM before timing starts.  The headline
+workload (default `prefill64k`) is a single-layer prefill of L = 65,536
+tokens (top_k = 2,048, 64-head indexer of dim 128, 64-head MLA over a
+576-wide bf16 latent), on seeded synthetic data; its figures are the
+top-level fields of the JSON line.  Unless --only is given, every other
+workload is then run the same way (W warm-up steps, K timed steps) and
+reported under "configs": `tiny` (L = 512, top_k = 128, integer indexer),
+`prefill16k`, `pcp` (one PCP8 rank's share of a 131,072-token prompt, ranks
+7 and 0) and `decode` (64 queries over a 1,048,576-token FP8 context).
 
-Besides the timed steps, each kernel is timed on its own (HIP events on the
+For each workload every kernel is also timed on its own (HIP events on the
 stream it runs on), the dominant kernel is placed against its roofline, the
-CPU oracle is timed on a bounded sample of query rows, and the GPU's outputs
-for those rows are checked against the oracle.  One JSON line is printed.
+CPU oracle is timed on a bounded sample of query rows (the whole prompt for
+`tiny`), and the GPU's outputs for those rows are checked against the
+oracle.  One JSON line is printed.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
 import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+WORKLOADS = {"tiny": 1, "prefill16k": 2, "prefill64k": 3, "pcp": 4, "decode": 5}
+# query rows of the CPU-oracle sample per workload (about 5-20 s each on 16
+# host cores; `tiny` is timed whole)
+CPU_ROWS = {"tiny": 512, "prefill16k": 2048, "prefill64k": 4096, "pcp": 1024, "decode": 16}
 
 
 def _log(msg):
@@ -36,11 +48,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="prefill64k", choices=["prefill64k", "prefill16k", "pcp", "decode"])
+    ap.add_argument("--workload", default="prefill64k", choices=sorted(WORKLOADS))
+    ap.add_argument("--only", action="store_true", help="run the headline workload only")
     ap.add_argument("--score-block", type=int, default=0,
                     help="query rows per score block inside sma_prefill (0: all rows at once)")
     ap.add_argument("--cpu-rows", type=int, default=0,
-                    help="query rows in the CPU-oracle sample (0: a per-workload default of ~10-30 s)")
+                    help="query rows in the headline's CPU-oracle sample (0: the per-workload default)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps (a known-size "
@@ -53,9 +66,10 @@ KERNEL_SOURCES = {"index_scores": ("idx_score_h64_kernel", "idx_score.hip"), "to
 
 
 def measured_traffic(workload_name, kernel):
-    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
-    summary of this workload, or None when there is none or the kernel's source
-    changed since the counters were taken."""
+    """Bytes per launch of `kernel` between its L2 and the memory fabric
+    (FETCH_SIZE + WRITE_SIZE, calibrated) from the committed summary of this
+    workload, or None when there is none or the kernel's source changed since
+    the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
     if not os.path.exists(path):
@@ -71,32 +85,71 @@ def measured_traffic(workload_name, kernel):
     return round(float(rec["traffic_bytes_per_launch"]), 1)
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
-                                   "(the PCP rank share is benchmarked on one GPU with --workload pcp)"}))
-        sys.exit(2)
+def host_info():
+    """What the CPU baseline ran on: cores this process may use, the CPU
+    model, the BLAS numpy calls and its thread count."""
+    info = {"host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": platform.processor() or None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas_threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                info["blas"] = f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer')})"
+                blas_threads = int(i.get("num_threads", 1))
+                break
+    except Exception:
+        pass
+    info["blas_threads"] = blas_threads
+    # threads the oracle's BLAS calls actually use (its loops are single-threaded)
+    info["cores"] = min(blas_threads or info["host_cores_available"], info["host_cores_available"])
+    return info
 
+
+def host(t, view=None):
+    import torch
+    a = t.detach().cpu()
+    if view is np.uint16:
+        return a.view(torch.int16).numpy().view(np.uint16)
+    if view is np.uint8:
+        return a.view(torch.uint8).numpy()
+    return a.numpy()
+
+
+def _threshold_rule_ok(oracle, got, ref_scores, top_k, rel=1e-3):
+    """GPU index list vs the oracle's: same length, ascending, and members
+    may differ only where the oracle score is within rel*|threshold| of it."""
+    n = ref_scores.size
+    m = min(top_k, n)
+    v = np.asarray(got[:m])
+    if np.any(np.asarray(got[m:]) != -1) or np.any(v < 0) or np.any(v >= n) or np.any(np.diff(v) <= 0):
+        return False
+    ref = oracle.topk_row(ref_scores, top_k)[:m]
+    t = oracle.topk_threshold(ref_scores, top_k)
+    diff = np.setxor1d(v, ref)
+    return bool(np.all(np.abs(ref_scores[diff] - t) <= rel * abs(t)))
+
+
+def run_workload(name, args, headline):
+    """Everything measured on one workload; returns its JSON record."""
     import torch
 
     import sparse_mla_attention_index_amd as sma
     from sparse_mla_attention_index_amd import accounting as acc
     from sparse_mla_attention_index_amd import synth
 
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
-        sys.exit(2)
-    sma.lib()   # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    cfg = {"prefill64k": 3, "prefill16k": 2, "pcp": 4, "decode": 5}[args.workload]
-    w = synth.workload(cfg)
+    w = synth.workload(WORKLOADS[name])
     # PCP: the step is rank 7's share (chunks 7 and 8); rank 0 (chunks 0 and
     # 15) is timed beside it for the load-balance ratio.
-    rank = 7 if args.workload == "pcp" else 0
+    rank = 7 if name == "pcp" else 0
     pos_np = synth.query_positions(w, rank)
     n_q, n_k = pos_np.size, w.n_keys
 
@@ -143,25 +196,27 @@ def main():
         k_idx, k_scale = k_idx
     if isinstance(kv, tuple):
         kv, kv_scale = kv
-    if args.workload == "pcp":
+    if name == "pcp":
         pos0 = synth.query_positions(w, 0)
         q_idx0, wts0, q0 = (upload_query("q_idx", pos0, 1024), upload_query("w", pos0, 65536),
                             upload_query("q", pos0, 256))
     torch.cuda.synchronize()
-    _log(f"inputs for {w.name} ready in {time.time() - t0:.1f}s (n_q={n_q}, n_k={n_k})")
+    _log(f"{name}: inputs for {w.name} ready in {time.time() - t0:.1f}s (n_q={n_q}, n_k={n_k})")
 
     out_dtype = torch.float32 if w.out_fp32 else torch.bfloat16
     out = torch.empty((n_q, 64, 512), dtype=out_dtype, device=dev)
     idx = torch.empty((n_q, w.top_k), dtype=torch.int32, device=dev)
-    blk = n_q if args.score_block <= 0 else max(64, min(args.score_block, n_q))
+    blk = n_q if (args.score_block <= 0 or not headline) else max(64, min(args.score_block, n_q))
     # one score block of `blk` rows, the split top-k's buffers for that block
     # (rows longer than 65,536 scores), the PCP share's positions
     score_b = (blk * n_k * 4 + 255) // 256 * 256
     topk_b = sma.workspace_bytes(sma._lib.SMA_OP_TOPK, blk, n_k, w.top_k)
-    ws = torch.empty(score_b + topk_b + (n_q * 4 + 255) // 256 * 256 + 4096, dtype=torch.uint8, device=dev)
+    mla_b = sma.workspace_bytes(sma._lib.SMA_OP_SPARSE_MLA, n_q, n_k, w.top_k)
+    ws = torch.empty(max(score_b + topk_b, mla_b) + (n_q * 4 + 255) // 256 * 256 + 4096, dtype=torch.uint8,
+                     device=dev)
     topk_ws = ws[score_b:score_b + topk_b] if topk_b > 0 else None
 
-    if args.workload == "pcp":
+    if name == "pcp":
         def run_share(r, qi_, w_, q_):
             sma.pcp_rank_share(r, w.pcp_size, qi_, w_, k_idx, q_, kv, w.top_k, w.sm_scale, k_scale=k_scale,
                                kv_scale=kv_scale, out=out, idx_share=idx, workspace=ws)
@@ -173,7 +228,7 @@ def main():
             sma.prefill(q_idx, wts, k_idx, q, kv, q_pos, w.top_k, w.sm_scale, k_scale=k_scale,
                         kv_scale=kv_scale, out=out, idx_out=idx, workspace=ws)
 
-    if args.copy_calibration_mib > 0:
+    if headline and args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
         cal_src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
         cal_dst = torch.empty_like(cal_src)
@@ -192,7 +247,7 @@ def main():
         step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t_start) * 1e3 / max(args.steps, 1)
-    _log(f"step {ms_step:.2f} ms over {args.steps} steps")
+    _log(f"{name}: step {ms_step:.3f} ms over {args.steps} steps")
 
     # ------------------------------------------- per-kernel breakdown --
     scores = ws[: blk * n_k * 4].view(torch.float32).view(blk, n_k)
@@ -218,17 +273,18 @@ def main():
     step()
     t_mla = timed(lambda: sma.sparse_mla_prefill(q, kv, idx, w.sm_scale, kv_scale=kv_scale, out=out,
                                                  workspace=ws), reps)
-    _log(f"kernels: index_scores {t_idx:.2f} ms, topk {t_topk:.2f} ms, sparse_mla {t_mla:.2f} ms")
+    _log(f"{name}: kernels: index_scores {t_idx:.3f} ms, topk {t_topk:.3f} ms, sparse_mla {t_mla:.3f} ms")
     pcp = None
-    if args.workload == "pcp":
+    if name == "pcp":
         t_r7 = timed(step, reps)
         t_r0 = timed(lambda: run_share(0, q_idx0, wts0, q0), reps)
         step()   # leave rank 7's results in out/idx for the parity sample
-        pcp = {"rank7_ms": round(t_r7, 3), "rank0_ms": round(t_r0, 3), "rank0_over_rank7": round(t_r0 / t_r7, 4)}
+        pcp = {"rank7_ms": round(t_r7, 3), "rank0_ms": round(t_r0, 3), "rank0_over_rank7": round(t_r0 / t_r7, 4),
+               "analytic_range": [0.9375, 1.0]}
         _log(f"pcp: rank0 {t_r0:.2f} ms, rank7 {t_r7:.2f} ms")
 
     dcp = None
-    if args.workload == "decode":
+    if name == "decode":
         # One-GPU DCP8 share: the KV dealt round-robin to 8 shards, each
         # rank's partial attention on its shard over the same selection, and
         # the log-sum-exp merge, against the unsharded call.
@@ -260,32 +316,56 @@ def main():
                "merged_vs_unsharded_max_err_rel": d_err}
         _log(f"dcp{P}: partials {t_part:.3f} ms + merge {t_merge:.3f} ms (unsharded {t_mla:.3f} ms), "
              f"max err {d_err:.2e}")
+        del shards, parts, lses, dws
 
-    # fp8_ds_mla leg (decode): the same selection attended over FlashMLA's
-    # 656-byte rows of the same latent (512 codes + 4 block scales + 64 bf16)
-    ds = None
-    if args.workload == "decode":
+    # FP8 latent rows, the same selection: FlashMLA's 656-byte rows (512
+    # codes + 4 block scales + 64 bf16) in decode, and at 64K both the
+    # per-token FP8 rows (576 codes + a scale) and the 656-byte rows of the
+    # same fp32 draws as the bf16 latent
+    fp8kv = None
+    if name in ("decode", "prefill64k"):
         t_g = time.time()
         ds_rows = torch.empty((n_k, 656), dtype=torch.uint8, device=dev)
         for a in range(0, n_k, 65536):
             b = min(n_k, a + 65536)
             ds_rows[a:b].copy_(torch.from_numpy(synth.latent_rows_fp8_ds_mla(w, a, b)))
+        rows8 = scale8 = None
+        if not w.fp8:
+            rows8 = torch.empty((n_k, 576), dtype=torch.uint8, device=dev)
+            scale8 = torch.empty((n_k,), dtype=torch.float32, device=dev)
+            for a in range(0, n_k, 16384):
+                b = min(n_k, a + 16384)
+                c8, s8 = synth.latent_rows_fp8(w, a, b)
+                rows8[a:b].copy_(torch.from_numpy(c8))
+                scale8[a:b].copy_(torch.from_numpy(s8))
         out_ds = torch.empty_like(out)
+        out_r8 = torch.empty_like(out) if rows8 is not None else None
         torch.cuda.synchronize()
+        sel_rows = acc.selected_rows(pos_np, w.top_k)
+        mfl = acc.mla_flops(pos_np, w.top_k)
         t_ds = timed(lambda: sma.sparse_mla_prefill(q, ds_rows, idx, w.sm_scale, out=out_ds, workspace=ws), reps)
+        fp8kv = {"fp8_ds_mla": {"row_bytes": 656, "sparse_mla_ms": round(t_ds, 4),
+                                "gather_gbs": round(sel_rows * 660 / (t_ds * 1e-3) / 1e9, 1),
+                                "tflops": round(mfl / (t_ds * 1e-3) / 1e12, 2)}}
+        if rows8 is not None:
+            t_r8 = timed(lambda: sma.sparse_mla_prefill(q, rows8, idx, w.sm_scale, kv_scale=scale8, out=out_r8,
+                                                        workspace=ws), reps)
+            fp8kv["fp8_row"] = {"row_bytes": 580, "sparse_mla_ms": round(t_r8, 4),
+                                "gather_gbs": round(sel_rows * 584 / (t_r8 * 1e-3) / 1e9, 1),
+                                "tflops": round(mfl / (t_r8 * 1e-3) / 1e12, 2)}
+        fp8kv["bf16_sparse_mla_ms"] = round(t_mla, 4) if not w.fp8 else None
+        fp8kv["fp8_row_format_ms"] = round(t_mla, 4) if w.fp8 else fp8kv.get("fp8_row", {}).get("sparse_mla_ms")
         sma.sparse_mla_prefill(q, ds_rows, idx, w.sm_scale, out=out_ds, workspace=ws)
+        if rows8 is not None:
+            sma.sparse_mla_prefill(q, rows8, idx, w.sm_scale, kv_scale=scale8, out=out_r8, workspace=ws)
         torch.cuda.synchronize()
-        sel = acc.selected_rows(pos_np, w.top_k)
-        ds = {"row_bytes": 656, "sparse_mla_ms": round(t_ds, 4), "fp8_row_format_ms": round(t_mla, 4),
-              "gather_gbs": round(sel * 660 / (t_ds * 1e-3) / 1e9, 1),
-              "tflops": round(acc.mla_flops(pos_np, w.top_k) / (t_ds * 1e-3) / 1e12, 2)}
-        _log(f"fp8_ds_mla: rows packed in {time.time() - t_g:.1f}s, sparse_mla {t_ds:.3f} ms "
-             f"(per-row FP8 format {t_mla:.3f} ms)")
+        _log(f"{name}: FP8 latent rows packed in {time.time() - t_g:.1f}s; sparse_mla fp8_ds_mla {t_ds:.3f} ms"
+             + (f", per-token FP8 {fp8kv['fp8_row']['sparse_mla_ms']:.3f} ms" if rows8 is not None else ""))
 
-    # absorption leg (prefill): q_nope through W_UK into the latent part of a
-    # query, and the attention's latent output through W_UV, 64 heads
+    # absorption leg (64K prefill): q_nope through W_UK into the latent part
+    # of a query, and the attention's latent output through W_UV, 64 heads
     ab = None
-    if args.workload == "prefill64k":
+    if name == "prefill64k":
         gen = torch.Generator(device=dev)
         gen.manual_seed(synth.SEED_BASE + 9)
         q_nope = torch.randn((n_q, 64, 128), generator=gen, device=dev).to(torch.bfloat16)
@@ -309,7 +389,7 @@ def main():
     # FP8 indexer leg: q_I (and bf16 keys) quantised per row on the GPU, the
     # e4m3 x e4m3 indexer, and a whole step with it (quantisers included).
     f8 = None
-    if w.h_idx == 64 and w.d_idx == 128:
+    if w.h_idx == 64 and w.d_idx == 128 and name != "prefill16k":
         q8 = torch.empty((n_q, 64, 128), dtype=torch.uint8, device=dev)
         qs8 = torch.empty((n_q, 64), dtype=torch.float32, device=dev)
         if w.fp8:
@@ -327,6 +407,8 @@ def main():
 
         def step8():
             quant()
+            if name == "pcp":
+                return   # the share's FP8 indexer is timed on its own below
             sma.prefill_fp8_indexer(q8, qs8, wts, k8, ks8, q, kv, q_pos, w.top_k, w.sm_scale, kv_scale=kv_scale,
                                     out=out8, idx_out=idx8, workspace=ws)
 
@@ -334,13 +416,13 @@ def main():
         t_qk = 0.0 if w.fp8 else timed(lambda: sma.quantize_fp8_rows(k_idx, codes=k8, scale=ks8), reps)
         t_idx8 = timed(lambda: sma.index_scores_fp8(q8[:nb], qs8[:nb], wts[:nb], k8, ks8, q_pos[:nb],
                                                     scores=scores), reps) * (n_q / nb)
-        t_step8 = timed(step8, max(2, min(args.steps, 3)))
-        step8()
+        f8 = {"quantize_q_ms": round(t_qq, 4), "quantize_k_ms": round(t_qk, 4), "index_scores_ms": round(t_idx8, 4)}
+        if name != "pcp":
+            t_step8 = timed(step8, max(2, min(args.steps, 3)))
+            step8()
+            f8.update(step_ms=round(t_step8, 3), tokens_per_s=round(n_q / (t_step8 * 1e-3), 2))
         torch.cuda.synchronize()
-        f8 = {"quantize_q_ms": round(t_qq, 4), "quantize_k_ms": round(t_qk, 4), "index_scores_ms": round(t_idx8, 4),
-              "step_ms": round(t_step8, 3), "tokens_per_s": round(n_q / (t_step8 * 1e-3), 2)}
-        _log(f"fp8 indexer: quantize q {t_qq:.3f} ms, k {t_qk:.3f} ms, index_scores {t_idx8:.2f} ms, "
-             f"step {t_step8:.2f} ms")
+        _log(f"{name}: fp8 indexer: quantize q {t_qq:.3f} ms, k {t_qk:.3f} ms, index_scores {t_idx8:.3f} ms")
 
     pairs = acc.causal_pairs(pos_np)
     key_bytes = (w.d_idx + 4) if w.fp8 else 2 * w.d_idx
@@ -356,7 +438,7 @@ def main():
     # that per-request rate is reported beside it, not as the roofline.
     idx_tflops = idx_flops / (t_idx * 1e-3) / 1e12
     idx_k = {"bound": "mfma", "achieved": idx_tflops, "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    if args.workload == "decode":
+    if name == "decode":
         idx_k["gbs_per_request_counted"] = \
             acc.indexer_bytes_per_request(pos_np, w.h_idx, w.d_idx, key_bytes) / (t_idx * 1e-3) / 1e9
     else:
@@ -377,12 +459,16 @@ def main():
         f8["peak_tflops"] = acc.PEAK_FP8_TFLOPS
         f8["frac_fp8_peak"] = round(f8["tflops"] / acc.PEAK_FP8_TFLOPS, 4)
         f8["keys_per_s"] = round(pairs / (t8 * 1e-3), 1)
-        if args.workload == "decode":
+        if name == "decode":
             # bytes as if each request streamed its own prefix; the synthetic
             # batch shares one context, so a key tile serves the workgroup's
             # 12 queries and this figure can exceed what HBM delivers
             fb = acc.indexer_bytes_per_request(pos_np, w.h_idx, w.d_idx, w.d_idx + 4, q_bytes_per_elem=1)
             f8["gbs_per_request_counted"] = round(fb / (t8 * 1e-3) / 1e9, 1)
+    if fp8kv:
+        for k in ("fp8_ds_mla", "fp8_row"):
+            if k in fp8kv:
+                fp8kv[k]["frac_bf16_peak"] = round(fp8kv[k]["tflops"] / acc.PEAK_BF16_TFLOPS, 4)
     dom = max(kern, key=lambda k: kern[k]["ms"])
     roof = {"kernel": dom, "bound": kern[dom]["bound"], "achieved": round(kern[dom]["achieved"], 3),
             "peak": kern[dom]["peak"], "unit": kern[dom]["unit"], "frac": round(kern[dom]["frac"], 4),
@@ -393,13 +479,8 @@ def main():
     parity = None
     if not args.no_cpu:
         import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:
-            threads = os.cpu_count()
-        m = min(args.cpu_rows or {"prefill64k": 4096, "prefill16k": 8192, "pcp": 2048, "decode": 64}[args.workload],
-                n_q)
+        hi = host_info()
+        m = min((args.cpu_rows if headline and args.cpu_rows else CPU_ROWS[name]), n_q)
         sample = np.unique(np.linspace(0, n_q - 1, m).round().astype(np.int64))
         f = oracle.bf16_bits_to_f64
         kk = oracle.keys_f64((host(k_idx, np.uint8), host(k_scale)) if w.fp8 else host(k_idx, np.uint16), w.fp8)
@@ -412,12 +493,14 @@ def main():
         t_c = time.perf_counter()
         sc, ref_idx, ref_out, _ = oracle.prefill(qi_s, w_s, kk, q_s, kvv, p_s, w.top_k, w.sm_scale)
         cpu_s = time.perf_counter() - t_c
-        cpu = {"value": round(sample.size / cpu_s, 3), "unit": "tokens/s", "cores": int(threads),
-               "kind": "oracle",
-               "sample": f"{sample.size} query rows spread evenly over the {n_q} rows of {w.name} "
-                         f"(indexer over each row's causal prefix, top-k, sparse MLA), float64 numpy, "
-                         f"{cpu_s:.1f} s"}
-        _log(f"oracle: {sample.size} rows in {cpu_s:.1f}s")
+        whole = sample.size == n_q
+        cpu = {"value": round(sample.size / cpu_s, 3), "unit": "tokens/s", "cores": hi["cores"], "kind": "oracle",
+               "sample": (f"all {n_q} query rows of {w.name}" if whole else
+                          f"{sample.size} query rows spread evenly over the {n_q} rows of {w.name}")
+               + f" (indexer over each row's causal prefix, top-k, sparse MLA), float64 numpy, {cpu_s:.1f} s",
+               "indexer_keys_per_s": round(acc.causal_pairs(p_s) / cpu_s, 1),
+               "host": {k: v for k, v in hi.items() if k != "cores"}}
+        _log(f"{name}: oracle: {sample.size} rows in {cpu_s:.1f}s")
         # parity of the GPU's rows against the oracle on the same sample
         g_idx = host(idx[s_idx])
         g_out = host(out[s_idx].float()).astype(np.float64)
@@ -425,9 +508,13 @@ def main():
         own_ref, _ = oracle.sparse_mla(q_s, kvv, g_idx, w.sm_scale)
         err = float(np.abs(g_out - own_ref).max() / np.abs(own_ref).max())
         exact_sets = float(np.mean([np.array_equal(g_idx[j], ref_idx[j]) for j in range(sample.size)]))
+        tol = 3e-2 if w.fp8 else 1e-2
         parity = {"rows": int(sample.size), "topk_threshold_rule": bool(rule), "topk_sets_identical": exact_sets,
-                  "mla_max_err_rel_to_max_ref": err, "tolerance": 3e-2 if w.fp8 else 1e-2,
-                  "ok": bool(rule and err <= (3e-2 if w.fp8 else 1e-2))}
+                  "mla_max_err_rel_to_max_ref": err, "tolerance": tol, "ok": bool(rule and err <= tol)}
+        if w.int_indexer:
+            # integer indexer inputs: exact scores, so the lists must be the oracle's
+            parity["topk_exact_required"] = True
+            parity["ok"] = bool(parity["ok"] and exact_sets == 1.0)
         if ab:
             # absorption products on a few sampled rows against the oracle
             sub = sample[:: max(1, sample.size // 32)]
@@ -441,20 +528,24 @@ def main():
             e_o = float(np.abs(got_o - ref_o).max() / np.abs(ref_o).max())
             ab["parity"] = {"rows": int(sub.size), "absorb_q_max_err_rel": e_q, "project_out_max_err_rel": e_o,
                             "ok": bool(e_q <= 1e-2 and e_o <= 1e-2)}
-        if ds:
-            # the 656-byte rows: attention on the GPU's own lists against the
+        if fp8kv:
+            # FP8 latent rows: attention on the GPU's own lists against the
             # oracle over the decoded rows those lists select
             g_all = host(idx[s_idx])
             used = np.unique(g_all[g_all >= 0])
-            dec = oracle.fp8_ds_mla_rows_to_f64(host(ds_rows[torch.from_numpy(used).to(dev)], np.uint8))
+            used_t = torch.from_numpy(used).to(dev)
             remap = np.where(g_all >= 0, np.searchsorted(used, np.maximum(g_all, 0)), -1)
-            ref_ds, _ = oracle.sparse_mla(q_s, dec, remap, w.sm_scale)
-            err_ds = float(np.abs(host(out_ds[s_idx].float()).astype(np.float64) - ref_ds).max() /
-                           np.abs(ref_ds).max())
-            ds["parity"] = {"rows": int(sample.size), "mla_max_err_rel_to_max_ref": err_ds, "tolerance": 3e-2,
-                            "ok": bool(err_ds <= 3e-2)}
-            _log(f"fp8_ds_mla parity: err {err_ds:.2e}")
-        if f8:
+            legs = [("fp8_ds_mla", out_ds, lambda: oracle.fp8_ds_mla_rows_to_f64(host(ds_rows[used_t], np.uint8)))]
+            if rows8 is not None:
+                legs.append(("fp8_row", out_r8,
+                             lambda: oracle.fp8_rows_to_f64(host(rows8[used_t], np.uint8), host(scale8[used_t]))))
+            for k, o_t, dec in legs:
+                ref_k, _ = oracle.sparse_mla(q_s, dec(), remap, w.sm_scale)
+                e_k = float(np.abs(host(o_t[s_idx].float()).astype(np.float64) - ref_k).max() / np.abs(ref_k).max())
+                fp8kv[k]["parity"] = {"rows": int(sample.size), "mla_max_err_rel_to_max_ref": e_k, "tolerance": 3e-2,
+                                      "ok": bool(e_k <= 3e-2)}
+                _log(f"{name}: {k} parity: err {e_k:.2e}")
+        if f8 and "step_ms" in f8:
             # the FP8 path on part of the sample: its selections against the
             # oracle's FP8 scores (same codes), its attention output, and how
             # much of the bf16 indexer's selection it keeps
@@ -476,14 +567,10 @@ def main():
                             "mla_max_err_rel_to_max_ref": err8, "ok": bool(rule8 and err8 <= parity["tolerance"]),
                             "oracle_fp8_indexer_s": round(cpu8_s, 2)}
             f8["bf16_selection_kept"] = round(float(np.mean(keep)), 4)
-            _log(f"fp8 parity: rule {rule8}, mla err {err8:.2e}, kept {np.mean(keep):.4f} of the bf16 selection")
+            _log(f"{name}: fp8 parity: rule {rule8}, mla err {err8:.2e}, kept {np.mean(keep):.4f} of bf16 selection")
 
-    tokens_s = n_q / (ms_step * 1e-3)
-    res = {
-        "metric": "sparse-MLA prefill tokens/s + indexer keys/s at 64K ctx; % of HBM/MFMA roofline",
-        "value": round(tokens_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, generated per run)",
+    rec = {
+        "workload": w.name, "ms_per_step": round(ms_step, 4), "tokens_per_s": round(n_q / (ms_step * 1e-3), 2),
         "config": {"workload": w.name, "n_queries": int(n_q), "n_keys": int(n_k), "top_k": w.top_k,
                    "mla_heads": 64, "d_qk": 576, "d_v": 512, "indexer_heads": w.h_idx, "d_idx": w.d_idx,
                    "kv": "fp8-e4m3+scale" if w.fp8 else "bf16", "score_block_rows": int(nb)},
@@ -491,6 +578,7 @@ def main():
         "indexer_keys_per_s": round(pairs / (t_idx * 1e-3), 1),
         "indexer_plus_topk_keys_per_s": round(pairs / ((t_idx + t_topk) * 1e-3), 1),
         "sparse_mla_tokens_per_s": round(n_q / (t_mla * 1e-3), 1),
+        "prefill_tokens_per_s_kernels": round(n_q / ((t_idx + t_topk + t_mla) * 1e-3), 1),
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kern.items()},
         "roofline": roof,
@@ -498,40 +586,61 @@ def main():
         "parity": parity,
     }
     if pcp:
-        res["pcp_load_balance"] = pcp
+        rec["pcp_load_balance"] = pcp
     if dcp:
-        res["dcp_share"] = dcp
+        rec["dcp_share"] = dcp
     if f8:
-        res["fp8_indexer"] = f8
-    if ds:
-        res["fp8_ds_mla"] = ds
+        rec["fp8_indexer"] = f8
+    if fp8kv:
+        rec["fp8_kv"] = fp8kv
     if ab:
-        res["absorption"] = ab
-    print(json.dumps(res), flush=True)
+        rec["absorption"] = ab
+    return rec
 
 
-def _threshold_rule_ok(oracle, got, ref_scores, top_k, rel=1e-3):
-    """GPU index list vs the oracle's: same length, ascending, and members
-    may differ only where the oracle score is within rel*|threshold| of it."""
-    n = ref_scores.size
-    m = min(top_k, n)
-    v = np.asarray(got[:m])
-    if np.any(np.asarray(got[m:]) != -1) or np.any(v < 0) or np.any(v >= n) or np.any(np.diff(v) <= 0):
-        return False
-    ref = oracle.topk_row(ref_scores, top_k)[:m]
-    t = oracle.topk_threshold(ref_scores, top_k)
-    diff = np.setxor1d(v, ref)
-    return bool(np.all(np.abs(ref_scores[diff] - t) <= rel * abs(t)))
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
+                                   "(the PCP rank share is benchmarked on one GPU in the `pcp` workload)"}))
+        sys.exit(2)
 
-
-def host(t, view=None):
     import torch
-    a = t.detach().cpu()
-    if view is np.uint16:
-        return a.view(torch.int16).numpy().view(np.uint16)
-    if view is np.uint8:
-        return a.view(torch.uint8).numpy()
-    return a.numpy()
+
+    import sparse_mla_attention_index_amd as sma
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    sma.lib()   # fails loudly if the HIP library is missing
+    torch.cuda.set_device(torch.device("cuda:0"))
+
+    t_all = time.time()
+    head = run_workload(args.workload, args, headline=True)
+    torch.cuda.empty_cache()
+    configs = {}
+    if not args.only:
+        for name in ("tiny", "prefill16k", "prefill64k", "pcp", "decode"):
+            if name == args.workload:
+                continue
+            configs[name] = run_workload(name, args, headline=False)
+            torch.cuda.empty_cache()
+
+    cfg = head.pop("config")
+    res = {
+        "metric": "sparse-MLA prefill tokens/s + indexer keys/s at 64K ctx; % of HBM/MFMA roofline",
+        "value": head.pop("tokens_per_s"), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(head.pop("ms_per_step"), 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, generated per run)",
+        "config": cfg,
+    }
+    head.pop("workload")
+    res.update(head)
+    if configs:
+        res["configs"] = configs
+    res["bench_wall_s"] = round(time.time() - t_all, 1)
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

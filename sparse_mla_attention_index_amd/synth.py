@@ -178,6 +178,12 @@ def to_fp8_ds_mla_rows(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def latent_rows_fp8(w: Workload, start: int, stop: int, threads: int = 8) -> tuple[np.ndarray, np.ndarray]:
+    """Rows [start, stop) of the workload's latent KV as per-token FP8 (codes,
+    scale) quantised from the same fp32 draws its bf16 storage rounds."""
+    return to_fp8_rows(_gen_f32_rows(w, "kv", start, stop, threads))
+
+
 def latent_rows_fp8_ds_mla(w: Workload, start: int, stop: int, threads: int = 8) -> np.ndarray:
     """Rows [start, stop) of the workload's latent KV in fp8_ds_mla storage
     (the same fp32 draws the other storage formats quantise)."""
