@@ -299,6 +299,52 @@ def project_out(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
     return np.einsum("nhc,hvc->nhv", np.asarray(o_lat, np.float64), np.asarray(w_uv, np.float64))
 
 
+def dense_mha_prefill(q_mha: np.ndarray, kv: np.ndarray, w_uk: np.ndarray, w_uv: np.ndarray, q_pos,
+                      sm_scale: float):
+    """Dense causal multi-head attention over the latent expanded per head:
+    the prefill path the pages describe for prompts that fit inside top-k
+    (GLM-5.3 part 2, "Essayez-le": without the forced MQA mode, such prefill
+    batches take the dense MHA path; DeepSeek multi-node page, "Travaux
+    futurs": in prefill, project the latent into K/V space first, then run
+    multi-head attention; "Couche MLA": kv_b_proj split into its key and
+    value halves).
+
+    q_mha [n_q, H, 192]: each head's 128 no-rope dims then its 64 rope dims;
+    kv [n_k, 576]: latent c_s (dims 0..511) and the shared rope key (dims
+    512..575); w_uk, w_uv [H, 128, 512] (row d of W_UK[h] maps the latent to
+    no-rope key dim d, row d of W_UV[h] to value dim d).  For query i at
+    position p_i and head h, over s = 0..p_i:
+        k[s,h,:] = [W_UK[h] c_s, rope_s]      v[s,h,:] = W_UV[h] c_s
+        z_s = tau * q_mha[i,h,:] . k[s,h,:]
+        o[i,h,:] = sum_s softmax(z)_s v[s,h,:],  lse[i,h] = log sum_s exp(z_s)
+    Returns (o [n_q, H, 128], lse [n_q, H]); an empty prefix (p_i < 0)
+    gives o = 0 and lse = -inf.
+    """
+    q_mha = np.asarray(q_mha, dtype=np.float64)
+    kv = np.asarray(kv, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    n_q, n_h, _ = q_mha.shape
+    d_nope = w_uk.shape[1]
+    c, rope = kv[:, :D_V], kv[:, D_V:]
+    k_nope = np.einsum("sc,hdc->shd", c, w_uk)     # [n_k, H, 128]: the key half of kv_b_proj
+    v = np.einsum("sc,hdc->shd", c, w_uv)          # [n_k, H, 128]: the value half
+    out = np.zeros((n_q, n_h, w_uv.shape[1]), dtype=np.float64)
+    lse = np.full((n_q, n_h), -np.inf, dtype=np.float64)
+    for i in range(n_q):
+        p = int(q_pos[i])
+        if p < 0:
+            continue
+        qn, qr = q_mha[i, :, :d_nope], q_mha[i, :, d_nope:]
+        z = sm_scale * (np.einsum("hd,shd->hs", qn, k_nope[: p + 1]) + qr @ rope[: p + 1].T)   # [H, p+1]
+        mx = z.max(axis=1, keepdims=True)
+        e = np.exp(z - mx)
+        den = e.sum(axis=1, keepdims=True)
+        out[i] = np.einsum("hs,shd->hd", e, v[: p + 1]) / den
+        lse[i] = mx[:, 0] + np.log(den[:, 0])
+    return out, lse
+
+
 def dcp_shard_rows(rank: int, dcp_size: int, kv: np.ndarray) -> np.ndarray:
     """The latent rows one DCP rank stores: tokens are dealt round-robin over
     the ranks, so rank r holds tokens r, r + P, r + 2P, ... (local row j is
