@@ -386,6 +386,59 @@ def run_workload(name, args, headline):
               "project_out_frac_hbm": round(b_po / (t_po * 1e-3) / 1e9 / acc.PEAK_HBM_GBS, 4)}
         _log(f"absorption: absorb_q {t_aq:.3f} ms, project_out {t_po:.3f} ms")
 
+    # dense MHA vs forced MQA on a prompt that fits inside top-k (the first
+    # 2,048 tokens of the 16K prompt): the dense path expands the latent per
+    # head and runs causal MHA; the MQA path absorbs W_UK into the query, runs
+    # indexer -> top-k (which keeps every causal token) -> sparse MLA, and
+    # applies W_UV to the latent output
+    dmha = None
+    if name == "prefill16k":
+        Ld = w.top_k
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(synth.SEED_BASE + 10)
+        q_nope = (torch.randn((Ld, 64, 128), generator=gen, device=dev) * 0.1).to(torch.bfloat16)
+        w_uk = (torch.randn((64, 128, 512), generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+        w_uv = (torch.randn((64, 128, 512), generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+        q_mha = torch.cat([q_nope.view(torch.int16), q[:Ld, :, 512:]], dim=2).contiguous()
+        kv_d = kv[:Ld].contiguous()
+        pos_d = q_pos[:Ld].contiguous()
+        o_dense = torch.empty((Ld, 64, 128), dtype=torch.bfloat16, device=dev)
+        dws = torch.empty(sma.workspace_bytes(sma._lib.SMA_OP_DENSE_MHA, Ld, Ld, w.top_k), dtype=torch.uint8,
+                          device=dev)
+        q_abs = torch.empty((Ld, 64, 576), dtype=torch.int16, device=dev)
+        q_abs[:, :, 512:] = q[:Ld, :, 512:]
+        o_lat = torch.empty((Ld, 64, 512), dtype=torch.bfloat16, device=dev)
+        o_mqa = torch.empty((Ld, 64, 128), dtype=torch.bfloat16, device=dev)
+        idx_d = torch.empty((Ld, w.top_k), dtype=torch.int32, device=dev)
+        mws = torch.empty(sma.workspace_bytes(sma._lib.SMA_OP_PREFILL, Ld, Ld, w.top_k), dtype=torch.uint8,
+                          device=dev)
+
+        def dense():
+            sma.dense_mha_prefill(q_mha, kv_d, w_uk, w_uv, pos_d, w.sm_scale, out=o_dense, workspace=dws)
+
+        def mqa():
+            sma.absorb_q(q_nope, w_uk, out=q_abs)
+            sma.prefill(q_idx[:Ld], wts[:Ld], k_idx[:Ld], q_abs, kv_d, pos_d, w.top_k, w.sm_scale, out=o_lat,
+                        idx_out=idx_d, workspace=mws)
+            sma.project_out(o_lat, w_uv, out=o_mqa)
+
+        t_dense = timed(dense, reps)
+        t_mqa = timed(mqa, reps)
+        dense()
+        mqa()
+        torch.cuda.synchronize()
+        pairs_d = acc.causal_pairs(pos_np[:Ld])
+        fl_dense = pairs_d * 64 * 2 * (192 + 128) + 2 * 2 * Ld * 512 * 64 * 128
+        fl_mqa = (pairs_d * acc.indexer_flops_per_pair(w.h_idx, w.d_idx) + acc.mla_flops(pos_np[:Ld], w.top_k)
+                  + 2 * 2 * Ld * 64 * 128 * 512)
+        d_err = float((o_dense.float() - o_mqa.float()).abs().max() / o_mqa.float().abs().max())
+        dmha = {"prompt_tokens": Ld, "dense_mha_ms": round(t_dense, 4), "forced_mqa_ms": round(t_mqa, 4),
+                "mqa_over_dense": round(t_mqa / t_dense, 3), "dense_mha_gflop": round(fl_dense / 1e9, 2),
+                "forced_mqa_gflop": round(fl_mqa / 1e9, 2),
+                "dense_mha_tflops": round(fl_dense / (t_dense * 1e-3) / 1e12, 2),
+                "dense_vs_mqa_max_err_rel": d_err}
+        _log(f"dense MHA {t_dense:.3f} ms vs forced MQA {t_mqa:.3f} ms on a {Ld}-token prompt (max diff {d_err:.2e})")
+
     # FP8 indexer leg: q_I (and bf16 keys) quantised per row on the GPU, the
     # e4m3 x e4m3 indexer, and a whole step with it (quantisers included).
     f8 = None
@@ -545,6 +598,17 @@ def run_workload(name, args, headline):
                 fp8kv[k]["parity"] = {"rows": int(sample.size), "mla_max_err_rel_to_max_ref": e_k, "tolerance": 3e-2,
                                       "ok": bool(e_k <= 3e-2)}
                 _log(f"{name}: {k} parity: err {e_k:.2e}")
+        if dmha:
+            # dense MHA on a few rows of the 2,048-token prompt against the oracle
+            sub = np.array([0, 1, 127, 128, 1024, dmha["prompt_tokens"] - 1])
+            sd = torch.from_numpy(sub).to(dev)
+            ref_d, _ = oracle.dense_mha_prefill(f(host(q_mha[sd], np.uint16)), f(host(kv_d, np.uint16)),
+                                                f(host(w_uk, np.uint16)), f(host(w_uv, np.uint16)), pos_np[sub],
+                                                w.sm_scale)
+            e_d = float(np.abs(host(o_dense[sd].float()).astype(np.float64) - ref_d).max() / np.abs(ref_d).max())
+            dmha["parity"] = {"rows": int(sub.size), "max_err_rel_to_max_ref": e_d, "tolerance": 1e-2,
+                              "ok": bool(e_d <= 1e-2)}
+            _log(f"{name}: dense MHA parity: err {e_d:.2e}")
         if f8 and "step_ms" in f8:
             # the FP8 path on part of the sample: its selections against the
             # oracle's FP8 scores (same codes), its attention output, and how
@@ -595,6 +659,8 @@ def run_workload(name, args, headline):
         rec["fp8_kv"] = fp8kv
     if ab:
         rec["absorption"] = ab
+    if dmha:
+        rec["dense_mha_vs_forced_mqa"] = dmha
     return rec
 
 

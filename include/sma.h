@@ -76,7 +76,8 @@ typedef enum {
   SMA_OP_SPARSE_MLA = 2,
   SMA_OP_PREFILL = 3,
   SMA_OP_PCP_SHARE = 4,
-  SMA_OP_DCP_PARTIAL = 5
+  SMA_OP_DCP_PARTIAL = 5,
+  SMA_OP_DENSE_MHA = 6
 } sma_op;
 
 /* Fixed MLA geometry: 64 heads share one 576-wide latent row (512 latent +
@@ -287,6 +288,41 @@ sma_status sma_project_out(const uint16_t* o_lat, const uint16_t* w_uv, int32_t 
                            void* stream);
 
 /*
+ * sma_dense_mha_prefill — dense causal multi-head attention over the latent
+ * expanded per head: the prefill path for prompts that fit inside top-k
+ * (GLM-5.3 part 2, "Essayez-le": without the forced MQA mode, prefill
+ * batches whose prompts fit in the 2,048-token top-k take dense MHA;
+ * DeepSeek multi-node page, "Travaux futurs": in prefill, project the latent
+ * into K/V space first, then run MHA; "Couche MLA": kv_b_proj's key half
+ * W_UK and value half W_UV).  For query i at p_i = clamp(q_pos[i], -1,
+ * n_k-1) and head h, over s = 0..p_i:
+ *
+ *   k[s,h,:] = [W_UK[h] kv[s,0:512], kv[s,512:576]]   v[s,h,:] = W_UV[h] kv[s,0:512]
+ *   out[i,h,:] = sum_s softmax_s(sm_scale * q[i,h,:] . k[s,h,:]) v[s,h,:]
+ *   lse[i,h]   = log sum_s exp(sm_scale * q[i,h,:] . k[s,h,:])   (natural log)
+ *
+ *  q      [n_q, 64, 192] bf16: each head's 128 no-rope dims, then its 64
+ *         rope dims
+ *  kv     [n_k, 576] bf16 latent rows (the sparse path's KV)
+ *  w_uk, w_uv [64, 128, 512] bf16 (row d of W_UK[h] maps the latent to
+ *         no-rope key dim d, row d of W_UV[h] to value dim d; the layout of
+ *         sma_absorb_q / sma_project_out)
+ *  out    [n_q, 64, 128] bf16 or fp32 (out_dtype); lse [n_q, 64] fp32 or NULL.
+ *         A query with an empty prefix (p_i = -1) gets 0 and -inf.
+ *  ws     at least sma_workspace_bytes(SMA_OP_DENSE_MHA, n_q, n_k, ...) =
+ *         n_k * 32,768 bytes, 256-byte aligned: the expanded keys and
+ *         values, bf16 (one rounding each); fp32 accumulation and softmax.
+ *  With every causal token selected (p_i < top_k, the prompts the pages
+ *  route here) the result equals sma_project_out applied to
+ *  sma_sparse_mla_prefill over the absorbed query [W_UK^T q_nope, q_rope],
+ *  up to rounding; sm_scale must be finite and > 0.  Tensors 16-byte
+ *  aligned.  n_q = 0 is a no-op.
+ */
+sma_status sma_dense_mha_prefill(const uint16_t* q, const uint16_t* kv, const uint16_t* w_uk, const uint16_t* w_uv,
+                                 const int32_t* q_pos, int32_t n_q, int64_t n_k, float sm_scale, void* out,
+                                 int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * sma_dcp_shard_partial — one DCP rank's share of sparse MLA (same article,
  * "DCP : sharder aussi le cache KV": tokens are dealt round-robin over the
  * dcp_size ranks, so rank r stores tokens r, r + P, r + 2P, ...; in decode
@@ -360,7 +396,8 @@ sma_status sma_dcp_shard_partial_noalloc(int32_t rank, int32_t dcp_size, const u
 sma_status sma_lse_merge(const float* parts, const float* lses, int32_t n_part, int32_t n_q, void* out,
                          int32_t out_dtype, float* lse_out, void* stream);
 
-/* Minimum workspace in bytes for `op` (an sma_op) at these sizes.  For
+/* Minimum workspace in bytes for `op` (an sma_op) at these sizes
+ * (SMA_OP_DENSE_MHA: n_k * 64 * 256 * 2, whatever n_q and top_k).  For
  * SMA_OP_PREFILL / SMA_OP_PCP_SHARE, n_q is the number of query rows and the
  * figure assumes idx_out == NULL (the index list lives in the workspace).
  * For SMA_OP_SPARSE_MLA the workspace is optional: the figure is what lets a

@@ -327,8 +327,9 @@ def dense_mha_prefill(q_mha: np.ndarray, kv: np.ndarray, w_uk: np.ndarray, w_uv:
     n_q, n_h, _ = q_mha.shape
     d_nope = w_uk.shape[1]
     c, rope = kv[:, :D_V], kv[:, D_V:]
-    k_nope = np.einsum("sc,hdc->shd", c, w_uk)     # [n_k, H, 128]: the key half of kv_b_proj
-    v = np.einsum("sc,hdc->shd", c, w_uv)          # [n_k, H, 128]: the value half
+    # per head h: k_nope[h, s, :] = W_UK[h] c_s and v[h, s, :] = W_UV[h] c_s
+    k_nope = np.matmul(w_uk, c.T).transpose(0, 2, 1)   # [H, n_k, 128]: the key half of kv_b_proj
+    v = np.matmul(w_uv, c.T).transpose(0, 2, 1)        # [H, n_k, 128]: the value half
     out = np.zeros((n_q, n_h, w_uv.shape[1]), dtype=np.float64)
     lse = np.full((n_q, n_h), -np.inf, dtype=np.float64)
     for i in range(n_q):
@@ -336,11 +337,12 @@ def dense_mha_prefill(q_mha: np.ndarray, kv: np.ndarray, w_uk: np.ndarray, w_uv:
         if p < 0:
             continue
         qn, qr = q_mha[i, :, :d_nope], q_mha[i, :, d_nope:]
-        z = sm_scale * (np.einsum("hd,shd->hs", qn, k_nope[: p + 1]) + qr @ rope[: p + 1].T)   # [H, p+1]
+        z_nope = np.matmul(k_nope[:, : p + 1, :], qn[:, :, None])[:, :, 0]      # [H, p+1]
+        z = sm_scale * (z_nope + qr @ rope[: p + 1].T)
         mx = z.max(axis=1, keepdims=True)
         e = np.exp(z - mx)
         den = e.sum(axis=1, keepdims=True)
-        out[i] = np.einsum("hs,shd->hd", e, v[: p + 1]) / den
+        out[i] = np.matmul(e[:, None, :], v[:, : p + 1, :])[:, 0, :] / den     # [H, 128]
         lse[i] = mx[:, 0] + np.log(den[:, 0])
     return out, lse
 

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libsma.so")
 SMA_DT_BF16, SMA_DT_FP8_E4M3, SMA_DT_FP32, SMA_DT_FP8_DS_MLA = 0, 1, 2, 3
 DS_ROW_BYTES = 656   # fp8_ds_mla latent row: 512 e4m3 codes, 4 fp32 scales, 64 bf16 rope dims
 SMA_OP_INDEX_SCORES, SMA_OP_TOPK, SMA_OP_SPARSE_MLA, SMA_OP_PREFILL, SMA_OP_PCP_SHARE = 0, 1, 2, 3, 4
-SMA_OP_DCP_PARTIAL = 5
+SMA_OP_DCP_PARTIAL, SMA_OP_DENSE_MHA = 5, 6
 HEADS, D_QK, D_V = 64, 576, 512
 
 # (name, restype, argtypes) of every entry point declared in include/sma.h
@@ -36,6 +36,7 @@ SIGNATURES = {
     "sma_dcp_shard_partial": (_I32, [_I32, _I32, _P, _P, _P, _I32, _I64, _P, _I32, _I32, _F, _P, _P, _P, _SZ,
                                      _P]),
     "sma_dcp_shard_partial_noalloc": (_I32, [_I32, _I32, _P, _P, _P, _I32, _I64, _P, _I32, _I32, _F, _P, _P, _P]),
+    "sma_dense_mha_prefill": (_I32, [_P, _P, _P, _P, _P, _I32, _I64, _F, _P, _I32, _P, _P, _SZ, _P]),
     "sma_lse_merge": (_I32, [_P, _P, _I32, _I32, _P, _I32, _P, _P]),
     "sma_quantize_fp8_rows": (_I32, [_P, _I64, _I32, _P, _P, _P]),
     "sma_absorb_q": (_I32, [_P, _P, _I32, _I32, _P, _I64, _P]),
@@ -359,6 +360,37 @@ def pcp_rank_share(rank: int, pcp_size: int, q_idx_share, w_share, k_idx, q_shar
                                     _ptr(lse), _ptr(idx_share), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(dev)))
     return out, lse, idx_share
+
+
+def dense_mha_prefill(q, kv, w_uk, w_uv, q_pos, sm_scale: float, *, out=None, out_dtype=torch.bfloat16,
+                      want_lse: bool = False, workspace=None):
+    """Dense causal MHA over the latent expanded per head (the path for
+    prompts within top-k): q bf16 [n_q, 64, 192] (128 no-rope + 64 rope
+    dims), kv bf16 [n_k, 576], w_uk / w_uv bf16 [64, 128, 512], q_pos int32
+    [n_q].  Returns (out [n_q, 64, 128], lse [n_q, 64] or None)."""
+    n_q = q.shape[0]
+    _bf16(q, "q")
+    _bf16(kv, "kv")
+    _bf16(w_uk, "w_uk")
+    _bf16(w_uv, "w_uv")
+    if tuple(q.shape[1:]) != (HEADS, 192) or kv.shape[1] != 576:
+        raise ValueError("q must be [n_q, 64, 192] and kv [n_k, 576]")
+    if tuple(w_uk.shape) != (HEADS, 128, 512) or tuple(w_uv.shape) != (HEADS, 128, 512):
+        raise ValueError("w_uk and w_uv must be [64, 128, 512]")
+    if q_pos.dtype != torch.int32 or not q_pos.is_contiguous():
+        raise ValueError("q_pos must be contiguous int32")
+    dev = q.device
+    if out is None:
+        out = torch.empty((n_q, HEADS, 128), dtype=out_dtype, device=dev)
+    odt = SMA_DT_FP32 if out.dtype == torch.float32 else SMA_DT_BF16
+    lse = torch.empty((n_q, HEADS), dtype=torch.float32, device=dev) if want_lse else None
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(SMA_OP_DENSE_MHA, n_q, kv.shape[0], 1), 1), dtype=torch.uint8,
+                                device=dev)
+    _check(lib().sma_dense_mha_prefill(_ptr(q), _ptr(kv), _ptr(w_uk), _ptr(w_uv), _ptr(q_pos), n_q, kv.shape[0],
+                                       float(sm_scale), _ptr(out), odt, _ptr(lse), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, lse
 
 
 def dcp_shard_partial(rank: int, dcp_size: int, q, kv_local, idx, sm_scale: float, *, kv_scale_local=None,

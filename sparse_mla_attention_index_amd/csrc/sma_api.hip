@@ -421,6 +421,31 @@ sma_status sma_sparse_mla_prefill(const uint16_t* q, const void* kv, const float
   return e == hipSuccess ? SMA_OK : hip_fail(e, "sparse_mla launch");
 }
 
+sma_status sma_dense_mha_prefill(const uint16_t* q, const uint16_t* kv, const uint16_t* w_uk, const uint16_t* w_uv,
+                                 const int32_t* q_pos, int32_t n_q, int64_t n_k, float sm_scale, void* out,
+                                 int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  SMA_CHECK(n_q >= 0, "n_q = %d < 0", n_q);
+  SMA_CHECK(n_k >= 1 && n_k <= kMaxKeys, "n_k = %lld out of [1, 2^31)", (long long)n_k);
+  SMA_CHECK(out_dtype == SMA_DT_BF16 || out_dtype == SMA_DT_FP32, "out_dtype = %d", out_dtype);
+  SMA_CHECK(std::isfinite(sm_scale) && sm_scale > 0.f, "sm_scale = %g (finite and > 0)", (double)sm_scale);
+  SMA_CHECK(kv && w_uk && w_uv, "kv, w_uk and w_uv must be non-NULL");
+  SMA_CHECK(aligned(kv, 16) && aligned(w_uk, 16) && aligned(w_uv, 16), "kv, w_uk and w_uv must be 16-byte aligned");
+  if (n_q == 0) return SMA_OK;
+  SMA_CHECK(q && q_pos && out, "q, q_pos and out must be non-NULL");
+  SMA_CHECK(aligned(q, 16) && aligned(out, 16), "q and out must be 16-byte aligned");
+  SMA_CHECK((int64_t)n_q <= ((int64_t)1 << 31) / SMA_HEADS, "n_q = %d too large", n_q);
+  const size_t need = sma::dense_mha_ws_bytes(n_k);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(SMA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws ? ws_bytes : 0, need);
+  SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
+  sma_status s = check_device();
+  if (s != SMA_OK) return s;
+  sma::DenseMhaArgs a{q, kv, w_uk, w_uv, q_pos, n_q, n_k, sm_scale, out, out_dtype == SMA_DT_FP32, lse, ws};
+  hipError_t e = sma::launch_dense_mha(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMA_OK : hip_fail(e, "dense_mha launch");
+}
+
 sma_status sma_dcp_shard_partial(int32_t rank, int32_t dcp_size, const uint16_t* q, const void* kv_local,
                                  const float* kv_scale_local, int32_t kv_dtype, int64_t n_k_local,
                                  const int32_t* idx, int32_t n_q, int32_t top_k, float sm_scale,
@@ -494,6 +519,8 @@ size_t sma_workspace_bytes(int32_t op, int32_t n_q, int64_t n_k, int32_t top_k, 
     case SMA_OP_DCP_PARTIAL:   // the rank's local index list, then an FP8 batch's row slices
       return align_up((size_t)n_q * (size_t)top_k * 4, 256) +
              align_up(sma::mla_split_bytes(n_q, sma::mla_split_count(n_q, top_k, true)), 256);
+    case SMA_OP_DENSE_MHA:   // the expanded keys and values, bf16
+      return sma::dense_mha_ws_bytes(n_k);
     case SMA_OP_PREFILL:
     case SMA_OP_PCP_SHARE: {
       const int32_t blk = n_q < kMinScoreBlock ? n_q : kMinScoreBlock;

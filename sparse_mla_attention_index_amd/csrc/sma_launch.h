@@ -103,6 +103,26 @@ struct BmmArgs {
 };
 hipError_t launch_bmm_bf16(const BmmArgs& a, hipStream_t s);
 
+// Dense causal MHA prefill over the latent expanded per head: q [n_q, 64,
+// 192] (128 no-rope + 64 rope), kv [n_k, 576] latent rows, w_uk / w_uv [64,
+// 128, 512]; ws holds the expanded keys and values (dense_mha_ws_bytes).
+struct DenseMhaArgs {
+  const uint16_t* q;
+  const uint16_t* kv;
+  const uint16_t* w_uk;
+  const uint16_t* w_uv;
+  const int32_t* q_pos;
+  int32_t n_q;
+  int64_t n_k;
+  float sm_scale;
+  void* out;
+  bool out_f32;
+  float* lse;
+  void* ws;
+};
+size_t dense_mha_ws_bytes(int64_t n_k);
+hipError_t launch_dense_mha(const DenseMhaArgs& a, hipStream_t s);
+
 hipError_t launch_pcp_positions(int32_t* pos, int32_t rank, int32_t pcp_size, int64_t L_total,
                                 hipStream_t s);
 

@@ -186,3 +186,16 @@ def test_dcp_noalloc_limit():
     assert r == -3 and "static scratch" in sma.last_error()
     r = sma.lib().sma_dcp_shard_partial_noalloc(2, 2, FAKE, FAKE, None, 0, 100, FAKE, 1, 8, 0.1, FAKE, FAKE, None)
     assert r == -1 and "rank" in sma.last_error()
+
+
+def test_dense_mha_validation_and_workspace():
+    assert sma.workspace_bytes(_lib.SMA_OP_DENSE_MHA, 10, 2048, 1) == 2048 * 64 * 256 * 2
+    L = sma.lib()
+    args = lambda **k: dict(dict(q=FAKE, kv=FAKE, nq=4, nk=100, scale=0.1, odt=0, ws=FAKE, wsb=100 * 32768), **k)
+    for bad, code, msg in [(dict(odt=3), -1, "out_dtype"), (dict(scale=-1.0), -1, "sm_scale"),
+                           (dict(nk=0), -1, "n_k"), (dict(kv=None), -1, "NULL"),
+                           (dict(wsb=100 * 32768 - 1), -3, "workspace"), (dict(ws=None), -3, "workspace")]:
+        a = args(**bad)
+        r = L.sma_dense_mha_prefill(a["q"], a["kv"], FAKE, FAKE, FAKE, a["nq"], a["nk"], a["scale"], FAKE, a["odt"],
+                                    None, a["ws"], a["wsb"], None)
+        assert r == code and msg in sma.last_error(), (bad, r, sma.last_error())
