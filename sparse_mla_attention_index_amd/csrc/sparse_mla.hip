@@ -424,11 +424,15 @@ __device__ __forceinline__ void dma_load16_at(const void* gaddr, uint32_t lds_ba
 // emits every MFMA builtin of a kernel that also uses AGPRs in the AGPR
 // form; the output accumulators fill the AGPR file, so the QK partial sums
 // are formed through these instead.  Being opaque to the compiler's hazard
-// recognizer, they carry their own wait states: two before each MFMA (a
-// VALU write of an A/B register just before it) and, in drain, 24 after the
-// last one before any VALU or LDS instruction reads the result (an 8-pass
-// XDL op needs 11).  A dependent chain through the same accumulator needs
-// none.
+// recognizer, they carry their own wait states, counted from the MFMA
+// dependency table of AMD's CDNA3/CDNA4 instruction-set reference (the
+// required independent instructions between a VALU write and an XDL read of
+// the same VGPR, and between an XDL write and a VALU / LDS read of its
+// result, by pass count): two before each MFMA (a VALU write of an A/B
+// register just before it) and, in drain, 24 after the last one before any
+// VALU or LDS instruction reads the result (an 8-pass XDL op needs 11).  A
+// dependent chain through the same accumulator (SrcC = the previous
+// result) needs none.
 __device__ __forceinline__ void mfma32_vgpr_first(f32x16v_t& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }

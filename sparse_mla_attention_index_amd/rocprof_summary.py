@@ -15,7 +15,9 @@ writes a kernel-time table (calls, average / min / max ms, share of the total);
 
 averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the named kernel,
 scales each by bytes / counter of the plain copy kernel of N bytes that the
-same run executed (torch's device copy), and records the result with the
+same run executed (the runtime's device copy kernel, __amd_rocclr_copyBuffer,
+which a same-dtype torch copy_ between device tensors launches), and records
+the result with the
 SHA-256 of the kernel's source file, so that a reader can tell whether the
 kernel changed since the counters were taken;
 
