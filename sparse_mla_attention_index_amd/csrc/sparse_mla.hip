@@ -518,12 +518,66 @@ __device__ __forceinline__ int tile_swz(int r) {
 }
 __device__ __forceinline__ constexpr int tile_block(int rg, int cg) { return (4 * cg + rg) * 1024; }
 
-template <bool OUT_F32>
+// Widen 16-code pieces P0 .. P0 + 2 NI - 1 of every row of an FP8 tile
+// (dims 16 P0 .. 16 (P0 + 2 NI) - 1) from its staging slot into the bf16
+// tile.  The staging slot holds piece c of row r at byte 1024 (c >> 1) +
+// 512 (c & 1) + 16 r (the gather's load k = c >> 1, lane 32 (c & 1) + r), so
+// lane l (row l & 31, pieces P0 + (l >> 5) + 2i) reads 16 bytes at
+// 1024 (P0 / 2 + i) + 16 l; bf16 chunk cc = 2c + hh of row r goes to its
+// block (r >> 3, cc >> 3) = (r >> 3, P0 / 4 + i / 2) at slot (cc & 7) ^
+// swz(r), cc & 7 = 4 (i & 1) + 2 (l >> 5) + hh.  The convert is
+// v_cvt_scalef32_pk_bf16_fp8 at scale 1: exact.
+template <int P0, int NI>
+__device__ __forceinline__ void widen_fp8_dims(const uint8_t* stage, uint8_t* tile, int lane) {
+  static_assert(P0 % 4 == 0, "pieces start at a chunk group");
+  const int r = lane & 31, g = lane >> 5, sw = tile_swz(r);
+  uint8_t* rowp = tile + tile_block(r >> 3, 0) + 128 * (r & 7);
+  int off[2][2];
+#pragma unroll
+  for (int ip = 0; ip < 2; ++ip)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) off[ip][hh] = 16 * ((4 * ip + 2 * g + hh) ^ sw);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 1024 * (P0 / 2 + i) + 16 * lane);
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[e], 1.f, false));
+      w[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[e], 1.f, true));
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      *reinterpret_cast<u32x4*>(rowp + 4096 * (P0 / 4 + i / 2) + off[i & 1][hh]) =
+          u32x4{w[4 * hh], w[4 * hh + 1], w[4 * hh + 2], w[4 * hh + 3]};
+  }
+}
+
+// FP8 = true: per-token FP8 latent rows (576 e4m3 codes + an fp32 scale per
+// row).  A tile's 32 rows x 576 codes (18 KiB) are gathered by the same
+// direct global->LDS loads into one of two staging slots (half the bytes of
+// a bf16 tile), the row scales beside them; once a tile has landed the
+// workgroup widens its codes to bf16 (v_cvt_scalef32_pk_bf16_fp8 at scale
+// 1: exact, every e4m3 value is a bf16 value) into the one bf16 tile, laid
+// out and swizzled as below, and QK / softmax / PV run unchanged on it; each
+// wave widens the dims it reads (wave 0: 0..287 for QK and PV, wave 1:
+// 256..575; 256..287 are written by both, with the same values), so the
+// widened tile needs no barrier of its own.  The
+// row's scale stays out of the operands: it multiplies the row's summed
+// logit and its softmax weight before PV (the sum of the weights, the
+// softmax denominator, is taken unscaled).  LDS: the bf16 tile and the two
+// staging slots fill the same 72 KiB the bf16 kernel's two tiles take.
+constexpr int kF8TileB = kMlaRows * kDqk;   // 18432: one tile of codes
+
+template <bool OUT_F32, bool FP8>
 __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int n_k,
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, const float* __restrict__ kv_scale, int n_k,
     const int32_t* __restrict__ idx, int n_q, int K, float scale_log2, void* __restrict__ out,
     float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_kv[2][kDmaTileB];
+  // bf16: tiles 0 and 1; FP8: the bf16 tile, then staging slots 0 and 1
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * kDmaTileB];
+  static_assert(kDmaTileB + 2 * kF8TileB <= 2 * kDmaTileB, "FP8 staging fits the ring");
+  __shared__ __attribute__((aligned(16))) float s_sc[2][64];
   __shared__ __attribute__((aligned(1024))) uint8_t s_x[4096];
   __shared__ __attribute__((aligned(1024))) int s_idx[2][kIdxChunk];
   __shared__ float s_l[kHeads];
@@ -589,15 +643,33 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
   };
   auto entry_raw = [&](int e) -> int { return s_idx[(e / kIdxChunk) & 1][e % kIdxChunk]; };
   auto entry_ok = [&](int e, int x) -> bool { return e < n_ext && x >= 0 && x < n_k; };
-  const uint8_t* kv_bytes = reinterpret_cast<const uint8_t*>(kv);
   const int r_lo = 16 * d + rg_row, r_hi = r_lo + 8;   // rows of row groups 2d and 2d+1
   const int c_lo = 16 * ((lane & 7) ^ tile_swz(r_lo)), c_hi = 16 * ((lane & 7) ^ tile_swz(r_hi));
+  // FP8 staging: load k (0..17) of a tile brings 16 bytes to each lane,
+  // lane l: row l & 31, 16-byte chunk 2k + (l >> 5) of its 576 codes, at
+  // staging byte 1024k + 16l; wave d issues loads 9d .. 9d + 8, so a lane
+  // reads one index per tile and its nine chunks are 32 bytes apart.
+  auto issue_f8 = [&](int t, int b) -> uint32_t {   // returns the tile's row mask
+    const int e = t * kMlaRows + (lane & 31);
+    const int raw = entry_raw(e);
+    const bool ok = entry_ok(e, raw);
+    const int row = ok ? raw : 0;
+    const uint8_t* src = kv + (int64_t)row * kDqk + 16 * (18 * d + (lane >> 5));
+    const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)(s_ring + kDmaTileB + b * kF8TileB + 1024 * 9 * d);
+#define SMA_F8_LOAD(k) dma_load16_at<32 * (k)>(src, dst + 1024 * (k));
+    SMA_F8_LOAD(0) SMA_F8_LOAD(1) SMA_F8_LOAD(2) SMA_F8_LOAD(3) SMA_F8_LOAD(4)
+    SMA_F8_LOAD(5) SMA_F8_LOAD(6) SMA_F8_LOAD(7) SMA_F8_LOAD(8)
+#undef SMA_F8_LOAD
+    if (d == 0) dma_load4(kv_scale + row, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&s_sc[b][0]);
+    return (uint32_t)__ballot(ok);
+  };
   auto issue_tile = [&](int t, int b) -> uint32_t {   // returns the tile's row mask
+    if constexpr (FP8) return issue_f8(t, b);
     const int raw_lo = entry_raw(t * kMlaRows + r_lo), raw_hi = entry_raw(t * kMlaRows + r_hi);
     const bool ok_lo = entry_ok(t * kMlaRows + r_lo, raw_lo), ok_hi = entry_ok(t * kMlaRows + r_hi, raw_hi);
-    const uint8_t* src_lo = kv_bytes + (int64_t)(ok_lo ? raw_lo : 0) * kDmaRowB + c_lo;
-    const uint8_t* src_hi = kv_bytes + (int64_t)(ok_hi ? raw_hi : 0) * kDmaRowB + c_hi;
-    const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)&s_kv[b][tile_block(2 * d, 0)];
+    const uint8_t* src_lo = kv + (int64_t)(ok_lo ? raw_lo : 0) * kDmaRowB + c_lo;
+    const uint8_t* src_hi = kv + (int64_t)(ok_hi ? raw_hi : 0) * kDmaRowB + c_hi;
+    const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)(s_ring + b * kDmaTileB + tile_block(2 * d, 0));
     // chunk group cg of both rows: global offset 128 cg, LDS block (rg, cg)
 #define SMA_TILE_CG(cg)                                           \
   dma_load16_at<128 * (cg)>(src_lo, dst + 4096 * (cg));           \
@@ -661,7 +733,14 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
         stage_chunk(t / (kIdxChunk / kMlaRows) + 1);
       uint32_t mask_next = 0;
       if (t + 1 < ntiles) mask_next = issue_tile(t + 1, (t + 1) & 1);
-      uint8_t* tile = s_kv[t & 1];
+      uint8_t* tile = FP8 ? s_ring : s_ring + (t & 1) * kDmaTileB;
+      if constexpr (FP8) {
+        // the bf16 tile is free (every wave is past tile t-1, barrier above);
+        // each wave widens the dims it reads itself, so no barrier follows
+        const uint8_t* stage = s_ring + kDmaTileB + (t & 1) * kF8TileB;
+        if (d == 0) widen_fp8_dims<0, 9>(stage, tile, lane);
+        else widen_fp8_dims<16, 10>(stage, tile, lane);
+      }
 
       // ---- partial S^T over this wave's dims, both head blocks ----
       constexpr int kPf = 3;
@@ -707,6 +786,14 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
       for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int r = 0; r < 4; ++r) s_own[4 * p + r] += y[p][r];
+      if constexpr (FP8) {   // the rows' scales on their summed logits (rows 8p + 4h + r)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const f32x4 rs = *reinterpret_cast<const f32x4*>(&s_sc[t & 1][8 * p + 4 * h]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s_own[4 * p + r] *= rs[r];
+        }
+      }
 
       // ---- softmax weights of the own heads: element j is row 8(j>>2) + 4h + (j&3) ----
       // A full tile (every row valid; the mask is the same in every lane)
@@ -736,7 +823,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
         float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s_own[j], scale_log2, neg_ref));
         if (!full) pe = row_ok(j) ? pe : 0.f;
         ps += pe;
-        pb[j >> 3][j & 7] = (__bf16)pe;
+        if constexpr (FP8)   // PV takes the codes: the row's scale goes on its weight
+          pb[j >> 3][j & 7] = (__bf16)(pe * s_sc[t & 1][8 * (j >> 2) + 4 * h + (j & 3)]);
+        else
+          pb[j >> 3][j & 7] = (__bf16)pe;
       }
       l_run += ps;
 
@@ -814,7 +904,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     // 16-byte chunk c sits at slot c ^ (head & 63), then write it with
     // 16-byte stores by consecutive lanes.  Lanes of one accumulator store
     // hold 32 heads, which the slot rotation spreads over the banks.
-    uint8_t* obuf = &s_kv[0][0];
+    uint8_t* obuf = s_ring;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int head = 32 * (d ^ hb) + c32;
@@ -858,6 +948,8 @@ hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
   if (A.n_q <= 0) return hipSuccess;
   const float scale_log2 = A.sm_scale * 1.4426950408889634f;
   const dim3 grid((unsigned)A.n_q), block(kMlaThreads);
+  const dim3 block2(kPairThreads);
+  const uint8_t* kv8 = static_cast<const uint8_t*>(A.kv);
   if (A.fp8) {
     // small batches split each query's rows across workgroups, into as many
     // slices as the workspace holds partials for (up to the preferred count)
@@ -867,6 +959,17 @@ hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
       const size_t fit = A.ws ? A.ws_bytes / per_slice : 0;
       if ((size_t)n_split > fit) n_split = (int)fit;
       if (n_split < 2) n_split = 1;
+    }
+    if (!A.ds_mla && n_split == 1) {
+      // per-token FP8 rows, one workgroup per query: the bf16 kernel's
+      // design with the rows widened in LDS
+      if (A.out_f32)
+        hipLaunchKernelGGL((sparse_mla_bf16_kernel<true, true>), grid, block2, 0, st, A.q, kv8, A.kv_scale,
+                           (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
+      else
+        hipLaunchKernelGGL((sparse_mla_bf16_kernel<false, true>), grid, block2, 0, st, A.q, kv8, A.kv_scale,
+                           (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
+      return hipGetLastError();
     }
     float* part = n_split > 1 ? static_cast<float*>(A.ws) : nullptr;
     const dim3 grid_s((unsigned)(A.n_q * n_split));
@@ -890,14 +993,12 @@ hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
         hipLaunchKernelGGL((mla_merge_kernel<false>), grid, dim3(256), 0, st, part, n_split, A.out, A.lse);
     }
   } else {
-    const uint16_t* kv = static_cast<const uint16_t*>(A.kv);
-    const dim3 block2(kPairThreads);
     if (A.out_f32)
-      hipLaunchKernelGGL((sparse_mla_bf16_kernel<true>), grid, block2, 0, st, A.q, kv, (int)A.n_k, A.idx, A.n_q,
-                         A.top_k, scale_log2, A.out, A.lse);
+      hipLaunchKernelGGL((sparse_mla_bf16_kernel<true, false>), grid, block2, 0, st, A.q, kv8, nullptr, (int)A.n_k,
+                         A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
     else
-      hipLaunchKernelGGL((sparse_mla_bf16_kernel<false>), grid, block2, 0, st, A.q, kv, (int)A.n_k, A.idx,
-                         A.n_q, A.top_k, scale_log2, A.out, A.lse);
+      hipLaunchKernelGGL((sparse_mla_bf16_kernel<false, false>), grid, block2, 0, st, A.q, kv8, nullptr,
+                         (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
   }
   return hipGetLastError();
 }
