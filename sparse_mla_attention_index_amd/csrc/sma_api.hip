@@ -569,8 +569,10 @@ sma_status sma_pcp_rank_share(int32_t rank, int32_t pcp_size, int64_t L_total, c
   g_err.clear();
   SMA_CHECK(pcp_size >= 1, "pcp_size = %d < 1", pcp_size);
   SMA_CHECK(rank >= 0 && rank < pcp_size, "rank = %d not in [0, %d)", rank, pcp_size);
-  SMA_CHECK(L_total >= 2 * pcp_size && L_total % (2 * pcp_size) == 0,
-            "L_total = %lld is not a positive multiple of 2*pcp_size = %d", (long long)L_total, 2 * pcp_size);
+  const int64_t n_chunks = 2 * (int64_t)pcp_size;   // 64-bit: no overflow for any pcp_size
+  SMA_CHECK(L_total >= n_chunks && L_total % n_chunks == 0,
+            "L_total = %lld is not a positive multiple of 2*pcp_size = %lld", (long long)L_total,
+            (long long)n_chunks);
   SMA_CHECK(L_total <= kMaxKeys, "L_total too large");
   const int64_t n_q64 = L_total / pcp_size;   // two chunks of L_total / (2 pcp_size)
   SMA_CHECK(n_q64 <= 0x7FFFFFFF, "share too large");
