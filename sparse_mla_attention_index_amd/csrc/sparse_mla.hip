@@ -352,13 +352,18 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
 
 // Log-sum-exp merge of the n_split partials of each query: with
 // M = max_s m_s, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s and
-// lse = (M + log2 of that sum) * ln 2.  One 256-thread workgroup per query;
-// thread t handles head t/4, dims 128(t%4) .. +127.
+// lse = (M + log2 of that sum) * ln 2.  A 256-thread workgroup merges 4
+// heads of one query (16 workgroups per query, so a 64-query batch keeps
+// 1,024 workgroups busy): thread t takes head 4 blockIdx.y + (t >> 6) and
+// dims 8 (t & 63) .. + 7, so consecutive threads read consecutive 32 bytes
+// of each partial.
+constexpr int kMergeHeads = 4;
+
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void mla_merge_kernel(const float* __restrict__ part, int n_split,
                                                         void* __restrict__ out, float* __restrict__ lse) {
   constexpr int kMaxSplit = 16;
-  const int qi = blockIdx.x, h = threadIdx.x >> 2, q4 = threadIdx.x & 3;
+  const int qi = blockIdx.x, h = kMergeHeads * blockIdx.y + (threadIdx.x >> 6), c8 = threadIdx.x & 63;
   const float* base = part + (int64_t)qi * n_split * kMlaPartFloats;
   float m[kMaxSplit], wgt[kMaxSplit];
   float M = -INFINITY;
@@ -372,20 +377,24 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(const float* __restrict_
     L += wgt[s] * base[s * kMlaPartFloats + kHeads * kDv + kHeads + h];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  const int64_t o_row = ((int64_t)qi * kHeads + h) * kDv + 128 * q4;
-  for (int c = 0; c < 32; ++c) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n_split; ++s)
-      acc += wgt[s] * *reinterpret_cast<const f32x4*>(base + s * kMlaPartFloats + h * kDv + 128 * q4 + 4 * c);
-    acc *= inv;
-    if constexpr (OUT_F32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o_row + 4 * c) = acc;
-    } else {
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o_row + 4 * c) =
-          u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-    }
+  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  for (int s = 0; s < n_split; ++s) {
+    const float* src = base + s * kMlaPartFloats + h * kDv + 8 * c8;
+    acc0 += wgt[s] * *reinterpret_cast<const f32x4*>(src);
+    acc1 += wgt[s] * *reinterpret_cast<const f32x4*>(src + 4);
   }
-  if (lse && q4 == 0)
+  acc0 *= inv;
+  acc1 *= inv;
+  const int64_t o_off = ((int64_t)qi * kHeads + h) * kDv + 8 * c8;
+  if constexpr (OUT_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o_off) = acc0;
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o_off + 4) = acc1;
+  } else {
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + o_off) =
+        u32x4{pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]), pack_bf16x2(acc1[0], acc1[1]),
+              pack_bf16x2(acc1[2], acc1[3])};
+  }
+  if (lse && c8 == 0)
     lse[(int64_t)qi * kHeads + h] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
@@ -569,7 +578,15 @@ __device__ __forceinline__ void widen_fp8_dims(const uint8_t* stage, uint8_t* ti
 // staging slots fill the same 72 KiB the bf16 kernel's two tiles take.
 constexpr int kF8TileB = kMlaRows * kDqk;   // 18432: one tile of codes
 
-template <bool OUT_F32, bool FP8>
+// HS = true (bf16 rows): the two waves split the heads instead of the dims.
+// Wave d owns heads 32d..32d+31 over all 576 dims: it holds their Q (dims
+// 288hb + 16ks + 8h in block hb, 144 VGPRs as before), forms their full S^T
+// in two accumulator chains (one per 288-dim half, each with its own K
+// operand), takes their softmax and accumulates O^T[512 dims x 32 heads]
+// (16 M-tiles, 256 AGPRs as before).  No S or P crosses between the waves,
+// so a tile needs one barrier (the ring's) instead of three; each wave reads
+// the whole tile from LDS, twice the LDS reads of the dims split.
+template <bool OUT_F32, bool FP8, bool HS = false>
 __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, const float* __restrict__ kv_scale, int n_k,
     const int32_t* __restrict__ idx, int n_q, int K, float scale_log2, void* __restrict__ out,
@@ -588,6 +605,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
   const int qi = blockIdx.x;
   const int h = lane >> 5, c32 = lane & 31;
   const int32_t* irow = idx + (int64_t)qi * K;
+  static_assert(!(HS && FP8), "the head split serves bf16 rows");
 
   // ---- extent of the selection: entries [0, n_ext) hold every valid index ----
   int last = -1;
@@ -618,10 +636,12 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
   const int ntiles = (n_ext + kMlaRows - 1) / kMlaRows;
 
   // ---- Q: block 0 = own heads 32d+c32, block 1 = partner heads; dims 288d + 16ks + 8h .. +7 ----
+  // (HS: both blocks hold the own heads, block hb dims 288hb + 16ks + 8h)
   bf16x8 qf[2][kPairKs];
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    const uint16_t* src = q + ((int64_t)qi * kHeads + 32 * (d ^ hb) + c32) * kDqk + 16 * kPairKs * d + 8 * h;
+    const uint16_t* src = HS ? q + ((int64_t)qi * kHeads + 32 * d + c32) * kDqk + 16 * kPairKs * hb + 8 * h
+                             : q + ((int64_t)qi * kHeads + 32 * (d ^ hb) + c32) * kDqk + 16 * kPairKs * d + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < kPairKs; ++ks) qf[hb][ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
   }
@@ -695,6 +715,15 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     const int c = 36 * d + 2 * p + h;
     kb[p] = tile_block(c32 >> 3, c >> 3) + 128 * (c32 & 7) + 16 * ((c & 7) ^ tile_swz(c32));
   }
+  // HS: the same for each 288-dim half hb (chunks 36hb + 2ks + h)
+  int kbh[2][4];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int c = 36 * hb + 2 * p + h;
+      kbh[hb][p] = tile_block(c32 >> 3, c >> 3) + 128 * (c32 & 7) + 16 * ((c & 7) ^ tile_swz(c32));
+    }
   // V^T operand of M-tile m (dims 256d+32m..), k-step kk, half e: 16-lane group b = lane>>4
   // reads row 16kk + 8e + 4h + (L>>2) at dims 256d + 32m + 16(b&1) + 4(L&3), L = lane&15;
   // chunk group 4d + (m>>1), slot from 4(m&1) + 2(b&1) + ((L&3)>>1): four bases
@@ -707,7 +736,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     for (int m1 = 0; m1 < 2; ++m1) {
       const int r = 8 * e + 4 * h + (L >> 2);
       const int c7 = 4 * m1 + 2 * ((lane >> 4) & 1) + ((L & 3) >> 1);
-      vb[e][m1] = tile_block(e, 4 * d) + 128 * (r & 7) + 16 * (c7 ^ tile_swz(r)) + 8 * (L & 1);
+      vb[e][m1] = tile_block(e, HS ? 0 : 4 * d) + 128 * (r & 7) + 16 * (c7 ^ tile_swz(r)) + 8 * (L & 1);
     }
 
   f32x16v o[kPairMt][2];
@@ -742,10 +771,41 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
         else widen_fp8_dims<16, 10>(stage, tile, lane);
       }
 
+      f32x16v s_own, s_oth;
+      if constexpr (HS) {
+        // ---- full S^T of the own heads: two chains, one per 288-dim half ----
+        auto kread2 = [&](int hb, int ks) {
+          return *reinterpret_cast<const bf16x8*>(tile + kbh[hb][ks & 3] + (ks >> 2) * 4096);
+        };
+        constexpr int kPf = 2;
+        bf16x8 kop[kPf][2];
+#pragma unroll
+        for (int ks = 0; ks < kPf; ++ks) {
+          kop[ks][0] = kread2(0, ks);
+          kop[ks][1] = kread2(1, ks);
+        }
+#pragma unroll
+        for (int ks = 0; ks < kPairKs; ++ks) {
+          const bf16x8 a0 = kop[ks % kPf][0], a1 = kop[ks % kPf][1];
+          if (ks + kPf < kPairKs) {
+            kop[ks % kPf][0] = kread2(0, ks + kPf);
+            kop[ks % kPf][1] = kread2(1, ks + kPf);
+          }
+          if (ks == 0) {
+            mfma32_vgpr_first(s_own, a0, qf[0][0]);
+            mfma32_vgpr_first(s_oth, a1, qf[1][0]);
+          } else {
+            mfma32_vgpr(s_own, a0, qf[0][ks]);
+            mfma32_vgpr(s_oth, a1, qf[1][ks]);
+          }
+        }
+        mfma32_vgpr_drain(s_own, s_oth);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s_own[j] += s_oth[j];
+      } else {
       // ---- partial S^T over this wave's dims, both head blocks ----
       constexpr int kPf = 3;
       auto kread = [&](int ks) { return *reinterpret_cast<const bf16x8*>(tile + kb[ks & 3] + (ks >> 2) * 4096); };
-      f32x16v s_own, s_oth;
       bf16x8 kop[kPf];
 #pragma unroll
       for (int ks = 0; ks < kPf; ++ks) kop[ks] = kread(ks);
@@ -786,6 +846,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
       for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int r = 0; r < 4; ++r) s_own[4 * p + r] += y[p][r];
+      }
       if constexpr (FP8) {   // the rows' scales on their summed logits (rows 8p + 4h + r)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -831,12 +892,16 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
       l_run += ps;
 
       // ---- P to the partner (into the buffer just read), P of the partner's heads back ----
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(xr + 1024 * kk + 16 * lane) = pb[kk];
-      block_sync_lds();
       bf16x8 pq[2];
+      if constexpr (!HS) {
+        uint8_t* xw = d ? tile + kRopeOff : s_x;   // written by this wave
+        uint8_t* xr = d ? s_x : tile + kRopeOff;   // written by the partner
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) pq[kk] = *reinterpret_cast<const bf16x8*>(xw + 1024 * kk + 16 * lane);
+        for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(xr + 1024 * kk + 16 * lane) = pb[kk];
+        block_sync_lds();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) pq[kk] = *reinterpret_cast<const bf16x8*>(xw + 1024 * kk + 16 * lane);
+      }
 
       // ---- O^T += V^T . P^T over this wave's dims, both head blocks ----
       auto vread = [&](int m, int kk) {
@@ -854,10 +919,24 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
           vop[(m + 1) & 1][0] = vread(m + 1, 0);
           vop[(m + 1) & 1][1] = vread(m + 1, 1);
         }
+        if constexpr (HS) {
+          // o[m][hb]: dims 256hb + 32m .., the own heads; the second half's
+          // V^T is read right here
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          o[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m & 1][kk], pb[kk], o[m][0], 0, 0, 0);
-          o[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m & 1][kk], pq[kk], o[m][1], 0, 0, 0);
+          for (int kk = 0; kk < 2; ++kk) {
+            const int off = 4096 * (4 + (m >> 1)) + 2048 * kk;
+            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb[0][m & 1] + off));
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb[1][m & 1] + off));
+            const bf16x8 vh = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m & 1][kk], pb[kk], o[m][0], 0, 0, 0);
+            o[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pb[kk], o[m][1], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            o[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m & 1][kk], pb[kk], o[m][0], 0, 0, 0);
+            o[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m & 1][kk], pq[kk], o[m][1], 0, 0, 0);
+          }
         }
       }
       mask = mask_next;
@@ -884,11 +963,14 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (h == 0) s_l[32 * d + c32] = l_tot;
   block_sync_lds();
-  const float inv[2] = {1.f / l_tot, 1.f / s_l[32 * (d ^ 1) + c32]};
+  const float inv[2] = {1.f / l_tot, HS ? 1.f / l_tot : 1.f / s_l[32 * (d ^ 1) + c32]};
+  // head of o[.][hb] and the first dim of its M-tiles
+  auto o_head = [&](int hb) { return HS ? 32 * d + c32 : 32 * (d ^ hb) + c32; };
+  auto o_dim0 = [&](int hb) { return HS ? 256 * hb : 256 * d; };
   if constexpr (OUT_F32) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const int64_t row_off = ((int64_t)qi * kHeads + 32 * (d ^ hb) + c32) * kDv + 256 * d + 4 * h;
+      const int64_t row_off = ((int64_t)qi * kHeads + o_head(hb)) * kDv + o_dim0(hb) + 4 * h;
 #pragma unroll
       for (int m = 0; m < kPairMt; ++m)
 #pragma unroll
@@ -907,7 +989,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     uint8_t* obuf = s_ring;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const int head = 32 * (d ^ hb) + c32;
+      const int head = o_head(hb);
       uint8_t* orow = obuf + head * 1024 + 8 * h;
 #pragma unroll
       for (int m = 0; m < kPairMt; ++m)
@@ -915,7 +997,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
         for (int jj = 0; jj < 4; ++jj) {
           const f32x4 r = f32x4{o[m][hb][4 * jj], o[m][hb][4 * jj + 1], o[m][hb][4 * jj + 2], o[m][hb][4 * jj + 3]} *
                           inv[hb];
-          const int chunk = 32 * d + 4 * m + jj;   // dims 8 chunk .. 8 chunk + 7
+          const int chunk = o_dim0(hb) / 8 + 4 * m + jj;   // dims 8 chunk .. 8 chunk + 7
           *reinterpret_cast<u32x2*>(orow + 16 * (chunk ^ (head & 63))) =
               u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
         }
@@ -987,10 +1069,11 @@ hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
     if (n_split > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
+      const dim3 grid_m((unsigned)A.n_q, kHeads / kMergeHeads);
       if (A.out_f32)
-        hipLaunchKernelGGL((mla_merge_kernel<true>), grid, dim3(256), 0, st, part, n_split, A.out, A.lse);
+        hipLaunchKernelGGL((mla_merge_kernel<true>), grid_m, dim3(256), 0, st, part, n_split, A.out, A.lse);
       else
-        hipLaunchKernelGGL((mla_merge_kernel<false>), grid, dim3(256), 0, st, part, n_split, A.out, A.lse);
+        hipLaunchKernelGGL((mla_merge_kernel<false>), grid_m, dim3(256), 0, st, part, n_split, A.out, A.lse);
     }
   } else {
     if (A.out_f32)
