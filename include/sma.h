@@ -198,8 +198,9 @@ sma_status sma_topk_select(const float* scores, int64_t ld_scores, const int32_t
  *  times the block's scale).
  *  sm_scale must be finite and > 0 (SMA_ERR_INVALID_ARG otherwise).
  *  Supported: 1 <= top_k <= 2048.  ws may be NULL (ws_bytes 0).  With a
- *  workspace (256-byte aligned), a small FP8 batch splits each query's rows
- *  into slices whose partial results are merged by log-sum-exp: with
+ *  workspace (256-byte aligned), a batch of fewer queries than the device
+ *  has compute units splits each query's rows into slices whose partial
+ *  results are merged by log-sum-exp: with
  *  sma_workspace_bytes(SMA_OP_SPARSE_MLA, ...) bytes into the preferred
  *  number of slices, with less into as many as the workspace holds
  *  partials for.  Slices change the result only by rounding: fp32
@@ -341,7 +342,7 @@ sma_status sma_dense_mha_prefill(const uint16_t* q, const uint16_t* kv, const ui
  *            0 and -inf
  *  ws        at least sma_workspace_bytes(SMA_OP_DCP_PARTIAL, n_q, n_k_local,
  *            top_k, 0, 0) bytes, 256-byte aligned (the rank's local index
- *            list, and an FP8 batch's row slices)
+ *            list, and a small batch's row slices)
  *  Requires 0 <= rank < dcp_size.
  */
 sma_status sma_dcp_shard_partial(int32_t rank, int32_t dcp_size, const uint16_t* q, const void* kv_local,
@@ -360,7 +361,7 @@ sma_status sma_dcp_shard_partial(int32_t rank, int32_t dcp_size, const uint16_t*
  *  device, part of the library's code object, so each device that runs the
  *  library holds it until the process ends.  It holds the rank's local
  *  index list (n_q*top_k*4 bytes, 256-byte aligned) and, in what remains,
- *  the partials of an FP8 batch's row slices (as many slices as fit, up to
+ *  the partials of a small batch's row slices (as many slices as fit, up to
  *  the count sma_dcp_shard_partial uses with a full workspace).  With the
  *  same slice count the two entries give identical results; with fewer
  *  slices they differ by the bf16 rounding of the softmax weights, which
@@ -401,7 +402,7 @@ sma_status sma_lse_merge(const float* parts, const float* lses, int32_t n_part, 
  * SMA_OP_PREFILL / SMA_OP_PCP_SHARE, n_q is the number of query rows and the
  * figure assumes idx_out == NULL (the index list lives in the workspace).
  * For SMA_OP_SPARSE_MLA the workspace is optional: the figure is what lets a
- * small FP8 batch split its queries' rows (0 when no split is used). */
+ * small batch split its queries' rows (0 when no split is used). */
 size_t sma_workspace_bytes(int32_t op, int32_t n_q, int64_t n_k, int32_t top_k,
                            int32_t h_idx, int32_t d_idx);
 

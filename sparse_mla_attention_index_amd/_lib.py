@@ -230,7 +230,7 @@ def sparse_mla_prefill(q, kv, idx, sm_scale: float, *, kv_scale=None, out=None, 
     """Sparse MLA over idx: returns (out [n_q, 64, 512], lse [n_q, 64] or None).
 
     `workspace` (uint8 device tensor, optional): with at least
-    workspace_bytes(SMA_OP_SPARSE_MLA, n_q, n_k, top_k) bytes, small FP8
+    workspace_bytes(SMA_OP_SPARSE_MLA, n_q, n_k, top_k) bytes, small
     batches split each query's rows across workgroups."""
     n_q = q.shape[0]
     _bf16(q, "q")

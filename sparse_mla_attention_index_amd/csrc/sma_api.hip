@@ -15,7 +15,7 @@
 #include "sma_launch.h"
 
 // Scratch of sma_dcp_shard_partial_noalloc (its callers cannot allocate):
-// the rank's local index list and the FP8 row slices' partials.
+// the rank's local index list and the row slices' partials.
 constexpr size_t kStaticScratchBytes = SMA_STATIC_SCRATCH_BYTES;
 static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
@@ -253,7 +253,7 @@ sma_status validate_dcp(int32_t rank, int32_t dcp_size, const uint16_t* q, const
 }
 
 // One DCP rank's partial after validation: the rank's local index list at the
-// start of `ws`, the FP8 row slices' partials in the rest.
+// start of `ws`, the row slices' partials in the rest.
 sma_status run_dcp_partial(int32_t rank, int32_t dcp_size, const uint16_t* q, const void* kv_local,
                            const float* kv_scale_local, int32_t kv_dtype, int64_t n_k_local, const int32_t* idx,
                            int32_t n_q, int32_t top_k, float sm_scale, float* out_partial, float* lse_partial,

@@ -53,7 +53,7 @@ struct MlaArgs {
   void* out;
   bool out_f32;
   float* lse;
-  // Workspace for the split partials of small FP8 batches (may be null).
+  // Workspace for the split partials of small batches (may be null).
   void* ws = nullptr;
   size_t ws_bytes = 0;
   // fp8 && ds_mla: 656-byte fp8_ds_mla rows (scales inside the row, kv_scale unused)

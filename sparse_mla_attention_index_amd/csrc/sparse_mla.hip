@@ -578,19 +578,15 @@ __device__ __forceinline__ void widen_fp8_dims(const uint8_t* stage, uint8_t* ti
 // staging slots fill the same 72 KiB the bf16 kernel's two tiles take.
 constexpr int kF8TileB = kMlaRows * kDqk;   // 18432: one tile of codes
 
-// HS = true (bf16 rows): the two waves split the heads instead of the dims.
-// Wave d owns heads 32d..32d+31 over all 576 dims: it holds their Q (dims
-// 288hb + 16ks + 8h in block hb, 144 VGPRs as before), forms their full S^T
-// in two accumulator chains (one per 288-dim half, each with its own K
-// operand), takes their softmax and accumulates O^T[512 dims x 32 heads]
-// (16 M-tiles, 256 AGPRs as before).  No S or P crosses between the waves,
-// so a tile needs one barrier (the ring's) instead of three; each wave reads
-// the whole tile from LDS, twice the LDS reads of the dims split.
-template <bool OUT_F32, bool FP8, bool HS = false>
+// With n_split > 1, workgroup (query, slice) covers one slice of the query's
+// tiles (a contiguous range of 32-entry tiles) and leaves its unnormalised
+// partial in `part` (O, the fixed exponent reference and the weight sum per
+// head, the layout mla_merge_kernel reads); an empty slice leaves 0, -inf, 0.
+template <bool OUT_F32, bool FP8>
 __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, const float* __restrict__ kv_scale, int n_k,
     const int32_t* __restrict__ idx, int n_q, int K, float scale_log2, void* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, int n_split, float* __restrict__ part) {
   // bf16: tiles 0 and 1; FP8: the bf16 tile, then staging slots 0 and 1
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * kDmaTileB];
   static_assert(kDmaTileB + 2 * kF8TileB <= 2 * kDmaTileB, "FP8 staging fits the ring");
@@ -602,10 +598,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int d = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qi = blockIdx.x;
+  const int qi = blockIdx.x / n_split, split = blockIdx.x % n_split;
+  float* mypart = part ? part + (int64_t)blockIdx.x * kMlaPartFloats : nullptr;
   const int h = lane >> 5, c32 = lane & 31;
   const int32_t* irow = idx + (int64_t)qi * K;
-  static_assert(!(HS && FP8), "the head split serves bf16 rows");
 
   // ---- extent of the selection: entries [0, n_ext) hold every valid index ----
   int last = -1;
@@ -622,6 +618,19 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
   if (lane == 0) s_red[d] = last;
   __syncthreads();
   const int n_ext = max(s_red[0], s_red[1]) + 1;
+  // this workgroup's tiles [t_beg, t_end)
+  const int n_tiles_all = (n_ext + kMlaRows - 1) / kMlaRows;
+  const int tps = (n_tiles_all + n_split - 1) / n_split;
+  const int t_beg = min(n_tiles_all, split * tps), t_end = min(n_tiles_all, t_beg + tps);
+  if (mypart && t_beg == t_end) {   // empty slice: zero partial, reference -inf
+    for (int i = tid; i < kHeads * kDv / 4; i += kPairThreads)
+      reinterpret_cast<f32x4*>(mypart)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (tid < kHeads) {
+      mypart[kHeads * kDv + tid] = -INFINITY;
+      mypart[kHeads * kDv + kHeads + tid] = 0.f;
+    }
+    return;
+  }
   if (n_ext == 0) {
     for (int i = tid; i < kHeads * kDv / 4; i += kPairThreads) {
       if constexpr (OUT_F32) {
@@ -633,15 +642,12 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     if (lse && tid < kHeads) lse[(int64_t)qi * kHeads + tid] = -INFINITY;
     return;
   }
-  const int ntiles = (n_ext + kMlaRows - 1) / kMlaRows;
 
   // ---- Q: block 0 = own heads 32d+c32, block 1 = partner heads; dims 288d + 16ks + 8h .. +7 ----
-  // (HS: both blocks hold the own heads, block hb dims 288hb + 16ks + 8h)
   bf16x8 qf[2][kPairKs];
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    const uint16_t* src = HS ? q + ((int64_t)qi * kHeads + 32 * d + c32) * kDqk + 16 * kPairKs * hb + 8 * h
-                             : q + ((int64_t)qi * kHeads + 32 * (d ^ hb) + c32) * kDqk + 16 * kPairKs * d + 8 * h;
+    const uint16_t* src = q + ((int64_t)qi * kHeads + 32 * (d ^ hb) + c32) * kDqk + 16 * kPairKs * d + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < kPairKs; ++ks) qf[hb][ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
   }
@@ -715,15 +721,6 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     const int c = 36 * d + 2 * p + h;
     kb[p] = tile_block(c32 >> 3, c >> 3) + 128 * (c32 & 7) + 16 * ((c & 7) ^ tile_swz(c32));
   }
-  // HS: the same for each 288-dim half hb (chunks 36hb + 2ks + h)
-  int kbh[2][4];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int c = 36 * hb + 2 * p + h;
-      kbh[hb][p] = tile_block(c32 >> 3, c >> 3) + 128 * (c32 & 7) + 16 * ((c & 7) ^ tile_swz(c32));
-    }
   // V^T operand of M-tile m (dims 256d+32m..), k-step kk, half e: 16-lane group b = lane>>4
   // reads row 16kk + 8e + 4h + (L>>2) at dims 256d + 32m + 16(b&1) + 4(L&3), L = lane&15;
   // chunk group 4d + (m>>1), slot from 4(m&1) + 2(b&1) + ((L&3)>>1): four bases
@@ -736,7 +733,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     for (int m1 = 0; m1 < 2; ++m1) {
       const int r = 8 * e + 4 * h + (L >> 2);
       const int c7 = 4 * m1 + 2 * ((lane >> 4) & 1) + ((L & 3) >> 1);
-      vb[e][m1] = tile_block(e, HS ? 0 : 4 * d) + 128 * (r & 7) + 16 * (c7 ^ tile_swz(r)) + 8 * (L & 1);
+      vb[e][m1] = tile_block(e, 4 * d) + 128 * (r & 7) + 16 * (c7 ^ tile_swz(r)) + 8 * (L & 1);
     }
 
   f32x16v o[kPairMt][2];
@@ -751,17 +748,23 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     l_run = 0.f;
     bool far = false;
     // Vector-memory operations of iteration t: [index chunk], gather(t+1).
-    stage_chunk(0);
+    // Chunk c (entries 256c ..) sits in slot c & 1.  The slice's first chunk
+    // and the one after it are staged before the loop; later, chunk k + 1 is
+    // staged at tile 8k, seven tiles before its first entries are read (the
+    // issue of tile 8k + 8 at iteration 8k + 7), when chunk k - 1 is dead.
+    constexpr int kTpc = kIdxChunk / kMlaRows;   // tiles per index chunk
+    const int c_beg = t_beg / kTpc;
+    stage_chunk(c_beg);
+    if ((c_beg + 1) * kTpc < t_end) stage_chunk(c_beg + 1);
     wait_vmcnt<0>();
     block_sync_lds();
-    uint32_t mask = issue_tile(0, 0);
-    for (int t = 0; t < ntiles; ++t) {
+    uint32_t mask = issue_tile(t_beg, t_beg & 1);
+    for (int t = t_beg; t < t_end; ++t) {
       wait_vmcnt<0>();     // tile t (and any index chunk) has landed
       block_sync_lds();    // for both waves; tile t-1's slot and the exchange buffers are free
-      if (t % (kIdxChunk / kMlaRows) == 0 && (t / (kIdxChunk / kMlaRows) + 1) * (kIdxChunk / kMlaRows) < ntiles)
-        stage_chunk(t / (kIdxChunk / kMlaRows) + 1);
+      if (t > t_beg && t % kTpc == 0 && (t / kTpc + 1) * kTpc < t_end) stage_chunk(t / kTpc + 1);
       uint32_t mask_next = 0;
-      if (t + 1 < ntiles) mask_next = issue_tile(t + 1, (t + 1) & 1);
+      if (t + 1 < t_end) mask_next = issue_tile(t + 1, (t + 1) & 1);
       uint8_t* tile = FP8 ? s_ring : s_ring + (t & 1) * kDmaTileB;
       if constexpr (FP8) {
         // the bf16 tile is free (every wave is past tile t-1, barrier above);
@@ -771,41 +774,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
         else widen_fp8_dims<16, 10>(stage, tile, lane);
       }
 
-      f32x16v s_own, s_oth;
-      if constexpr (HS) {
-        // ---- full S^T of the own heads: two chains, one per 288-dim half ----
-        auto kread2 = [&](int hb, int ks) {
-          return *reinterpret_cast<const bf16x8*>(tile + kbh[hb][ks & 3] + (ks >> 2) * 4096);
-        };
-        constexpr int kPf = 2;
-        bf16x8 kop[kPf][2];
-#pragma unroll
-        for (int ks = 0; ks < kPf; ++ks) {
-          kop[ks][0] = kread2(0, ks);
-          kop[ks][1] = kread2(1, ks);
-        }
-#pragma unroll
-        for (int ks = 0; ks < kPairKs; ++ks) {
-          const bf16x8 a0 = kop[ks % kPf][0], a1 = kop[ks % kPf][1];
-          if (ks + kPf < kPairKs) {
-            kop[ks % kPf][0] = kread2(0, ks + kPf);
-            kop[ks % kPf][1] = kread2(1, ks + kPf);
-          }
-          if (ks == 0) {
-            mfma32_vgpr_first(s_own, a0, qf[0][0]);
-            mfma32_vgpr_first(s_oth, a1, qf[1][0]);
-          } else {
-            mfma32_vgpr(s_own, a0, qf[0][ks]);
-            mfma32_vgpr(s_oth, a1, qf[1][ks]);
-          }
-        }
-        mfma32_vgpr_drain(s_own, s_oth);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) s_own[j] += s_oth[j];
-      } else {
       // ---- partial S^T over this wave's dims, both head blocks ----
       constexpr int kPf = 3;
       auto kread = [&](int ks) { return *reinterpret_cast<const bf16x8*>(tile + kb[ks & 3] + (ks >> 2) * 4096); };
+      f32x16v s_own, s_oth;
       bf16x8 kop[kPf];
 #pragma unroll
       for (int ks = 0; ks < kPf; ++ks) kop[ks] = kread(ks);
@@ -846,7 +818,6 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
       for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int r = 0; r < 4; ++r) s_own[4 * p + r] += y[p][r];
-      }
       if constexpr (FP8) {   // the rows' scales on their summed logits (rows 8p + 4h + r)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -892,16 +863,12 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
       l_run += ps;
 
       // ---- P to the partner (into the buffer just read), P of the partner's heads back ----
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(xr + 1024 * kk + 16 * lane) = pb[kk];
+      block_sync_lds();
       bf16x8 pq[2];
-      if constexpr (!HS) {
-        uint8_t* xw = d ? tile + kRopeOff : s_x;   // written by this wave
-        uint8_t* xr = d ? s_x : tile + kRopeOff;   // written by the partner
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<bf16x8*>(xr + 1024 * kk + 16 * lane) = pb[kk];
-        block_sync_lds();
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) pq[kk] = *reinterpret_cast<const bf16x8*>(xw + 1024 * kk + 16 * lane);
-      }
+      for (int kk = 0; kk < 2; ++kk) pq[kk] = *reinterpret_cast<const bf16x8*>(xw + 1024 * kk + 16 * lane);
 
       // ---- O^T += V^T . P^T over this wave's dims, both head blocks ----
       auto vread = [&](int m, int kk) {
@@ -919,24 +886,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
           vop[(m + 1) & 1][0] = vread(m + 1, 0);
           vop[(m + 1) & 1][1] = vread(m + 1, 1);
         }
-        if constexpr (HS) {
-          // o[m][hb]: dims 256hb + 32m .., the own heads; the second half's
-          // V^T is read right here
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const int off = 4096 * (4 + (m >> 1)) + 2048 * kk;
-            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb[0][m & 1] + off));
-            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb[1][m & 1] + off));
-            const bf16x8 vh = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m & 1][kk], pb[kk], o[m][0], 0, 0, 0);
-            o[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pb[kk], o[m][1], 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            o[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m & 1][kk], pb[kk], o[m][0], 0, 0, 0);
-            o[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m & 1][kk], pq[kk], o[m][1], 0, 0, 0);
-          }
+        for (int kk = 0; kk < 2; ++kk) {
+          o[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m & 1][kk], pb[kk], o[m][0], 0, 0, 0);
+          o[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m & 1][kk], pq[kk], o[m][1], 0, 0, 0);
         }
       }
       mask = mask_next;
@@ -961,16 +914,30 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
 
   // ---- normalise and write: o[m][hb] holds head 32(d^hb)+c32, dims 256d + 32m + 8jj + 4h + r ----
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (mypart) {   // the slice's partial: unnormalised O, reference (log2 units), weight sum
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float* prow = mypart + (32 * (d ^ hb) + c32) * kDv + 256 * d + 4 * h;
+#pragma unroll
+      for (int m = 0; m < kPairMt; ++m)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<f32x4*>(prow + 32 * m + 8 * jj) =
+              f32x4{o[m][hb][4 * jj], o[m][hb][4 * jj + 1], o[m][hb][4 * jj + 2], o[m][hb][4 * jj + 3]};
+    }
+    if (h == 0) {
+      mypart[kHeads * kDv + 32 * d + c32] = m_ref;
+      mypart[kHeads * kDv + kHeads + 32 * d + c32] = l_tot;
+    }
+    return;
+  }
   if (h == 0) s_l[32 * d + c32] = l_tot;
   block_sync_lds();
-  const float inv[2] = {1.f / l_tot, HS ? 1.f / l_tot : 1.f / s_l[32 * (d ^ 1) + c32]};
-  // head of o[.][hb] and the first dim of its M-tiles
-  auto o_head = [&](int hb) { return HS ? 32 * d + c32 : 32 * (d ^ hb) + c32; };
-  auto o_dim0 = [&](int hb) { return HS ? 256 * hb : 256 * d; };
+  const float inv[2] = {1.f / l_tot, 1.f / s_l[32 * (d ^ 1) + c32]};
   if constexpr (OUT_F32) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const int64_t row_off = ((int64_t)qi * kHeads + o_head(hb)) * kDv + o_dim0(hb) + 4 * h;
+      const int64_t row_off = ((int64_t)qi * kHeads + 32 * (d ^ hb) + c32) * kDv + 256 * d + 4 * h;
 #pragma unroll
       for (int m = 0; m < kPairMt; ++m)
 #pragma unroll
@@ -989,7 +956,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     uint8_t* obuf = s_ring;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const int head = o_head(hb);
+      const int head = 32 * (d ^ hb) + c32;
       uint8_t* orow = obuf + head * 1024 + 8 * h;
 #pragma unroll
       for (int m = 0; m < kPairMt; ++m)
@@ -997,7 +964,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
         for (int jj = 0; jj < 4; ++jj) {
           const f32x4 r = f32x4{o[m][hb][4 * jj], o[m][hb][4 * jj + 1], o[m][hb][4 * jj + 2], o[m][hb][4 * jj + 3]} *
                           inv[hb];
-          const int chunk = o_dim0(hb) / 8 + 4 * m + jj;   // dims 8 chunk .. 8 chunk + 7
+          const int chunk = 32 * d + 4 * m + jj;   // dims 8 chunk .. 8 chunk + 7
           *reinterpret_cast<u32x2*>(orow + 16 * (chunk ^ (head & 63))) =
               u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
         }
@@ -1014,7 +981,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
 }
 
 int mla_split_count(int n_q, int top_k, bool fp8) {
-  if (!fp8 || n_q <= 0) return 1;
+  (void)fp8;   // every KV format splits small batches
+  if (n_q <= 0) return 1;
   const int cus = device_cu_count();
   if (n_q >= cus) return 1;
   int s = (2 * cus + n_q - 1) / n_q;            // about two workgroups per CU
@@ -1032,56 +1000,47 @@ hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
   const dim3 grid((unsigned)A.n_q), block(kMlaThreads);
   const dim3 block2(kPairThreads);
   const uint8_t* kv8 = static_cast<const uint8_t*>(A.kv);
-  if (A.fp8) {
-    // small batches split each query's rows across workgroups, into as many
-    // slices as the workspace holds partials for (up to the preferred count)
-    int n_split = mla_split_count(A.n_q, A.top_k, true);
-    if (n_split > 1) {
-      const size_t per_slice = mla_split_bytes(A.n_q, 2) / 2;
-      const size_t fit = A.ws ? A.ws_bytes / per_slice : 0;
-      if ((size_t)n_split > fit) n_split = (int)fit;
-      if (n_split < 2) n_split = 1;
-    }
-    if (!A.ds_mla && n_split == 1) {
-      // per-token FP8 rows, one workgroup per query: the bf16 kernel's
-      // design with the rows widened in LDS
-      if (A.out_f32)
-        hipLaunchKernelGGL((sparse_mla_bf16_kernel<true, true>), grid, block2, 0, st, A.q, kv8, A.kv_scale,
-                           (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
-      else
-        hipLaunchKernelGGL((sparse_mla_bf16_kernel<false, true>), grid, block2, 0, st, A.q, kv8, A.kv_scale,
-                           (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
-      return hipGetLastError();
-    }
-    float* part = n_split > 1 ? static_cast<float*>(A.ws) : nullptr;
-    const dim3 grid_s((unsigned)(A.n_q * n_split));
-#define SMA_MLA_F8(KVF, F32)                                                                          \
-  hipLaunchKernelGGL((sparse_mla_kernel<KVF, F32>), grid_s, block, 0, st, A.q, A.kv, A.kv_scale, (int)A.n_k, \
-                     A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part)
-    if (A.ds_mla) {
-      if (A.out_f32) SMA_MLA_F8(kKvFp8Ds, true);
-      else SMA_MLA_F8(kKvFp8Ds, false);
-    } else {
-      if (A.out_f32) SMA_MLA_F8(kKvFp8Row, true);
-      else SMA_MLA_F8(kKvFp8Row, false);
-    }
-#undef SMA_MLA_F8
-    if (n_split > 1) {
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      const dim3 grid_m((unsigned)A.n_q, kHeads / kMergeHeads);
-      if (A.out_f32)
-        hipLaunchKernelGGL((mla_merge_kernel<true>), grid_m, dim3(256), 0, st, part, n_split, A.out, A.lse);
-      else
-        hipLaunchKernelGGL((mla_merge_kernel<false>), grid_m, dim3(256), 0, st, part, n_split, A.out, A.lse);
-    }
-  } else {
+  // small batches split each query's rows across workgroups, into as many
+  // slices as the workspace holds partials for (up to the preferred count)
+  int n_split = mla_split_count(A.n_q, A.top_k, true);
+  if (n_split > 1) {
+    const size_t per_slice = mla_split_bytes(A.n_q, 2) / 2;
+    const size_t fit = A.ws ? A.ws_bytes / per_slice : 0;
+    if ((size_t)n_split > fit) n_split = (int)fit;
+    if (n_split < 2) n_split = 1;
+  }
+  float* part = n_split > 1 ? static_cast<float*>(A.ws) : nullptr;
+  const dim3 grid_s((unsigned)(A.n_q * n_split));
+  if (A.fp8 && A.ds_mla) {
+    // 656-byte fp8_ds_mla rows: the 4-wave kernel
     if (A.out_f32)
-      hipLaunchKernelGGL((sparse_mla_bf16_kernel<true, false>), grid, block2, 0, st, A.q, kv8, nullptr, (int)A.n_k,
-                         A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
+      hipLaunchKernelGGL((sparse_mla_kernel<kKvFp8Ds, true>), grid_s, block, 0, st, A.q, A.kv, A.kv_scale,
+                         (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part);
     else
-      hipLaunchKernelGGL((sparse_mla_bf16_kernel<false, false>), grid, block2, 0, st, A.q, kv8, nullptr,
-                         (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse);
+      hipLaunchKernelGGL((sparse_mla_kernel<kKvFp8Ds, false>), grid_s, block, 0, st, A.q, A.kv, A.kv_scale,
+                         (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part);
+  } else {
+    // bf16 rows, or per-token FP8 rows widened in LDS: the 2-wave kernel
+#define SMA_MLA_PAIR(F32, F8)                                                                                     \
+  hipLaunchKernelGGL((sparse_mla_bf16_kernel<F32, F8>), grid_s, block2, 0, st, A.q, kv8, A.kv_scale, (int)A.n_k, \
+                     A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part)
+    if (A.fp8) {
+      if (A.out_f32) SMA_MLA_PAIR(true, true);
+      else SMA_MLA_PAIR(false, true);
+    } else {
+      if (A.out_f32) SMA_MLA_PAIR(true, false);
+      else SMA_MLA_PAIR(false, false);
+    }
+#undef SMA_MLA_PAIR
+  }
+  if (n_split > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 grid_m((unsigned)A.n_q, kHeads / kMergeHeads);
+    if (A.out_f32)
+      hipLaunchKernelGGL((mla_merge_kernel<true>), grid_m, dim3(256), 0, st, part, n_split, A.out, A.lse);
+    else
+      hipLaunchKernelGGL((mla_merge_kernel<false>), grid_m, dim3(256), 0, st, part, n_split, A.out, A.lse);
   }
   return hipGetLastError();
 }
