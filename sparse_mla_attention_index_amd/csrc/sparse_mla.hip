@@ -6,23 +6,18 @@
 // têtes" and footnote 1: one KV row read serves every head; QK over 576, PV
 // over 512).
 //
-// Two kernels share that computation:
-//  * sparse_mla_kernel (FP8-e4m3 KV, two storage formats): one 4-wave
-//    workgroup per query, wave w owns heads
-//    16w..16w+15, rows staged through registers into a padded row-major
-//    LDS tile, the codes widened to bf16 exactly on the way;
-//    v_mfma_f32_16x16x32_bf16 for S^T = K.Q^T and O^T += V^T.P^T with an
-//    online softmax.  Formats: 576 codes with one fp32 scale per row (a
-//    separate array), whose scale stays out of the bf16 operands (it
-//    multiplies the row's logit and softmax weight, so the codes widen to
-//    bf16 exactly); or FlashMLA's 656-byte fp8_ds_mla row (512 codes, four
-//    fp32 scales of 128 dims each, 64 bf16 rope dims; GLM-5.3 part 2,
-//    footnote 1, names it), whose codes are staged as bf16(code x block
-//    scale), one rounding per element, so QK and PV run as for bf16 rows.
-//  * sparse_mla_bf16_kernel (bf16 KV): one 2-wave workgroup per query that
-//    splits both contractions by dims, gathers with direct global->LDS
-//    loads and uses v_mfma_f32_32x32x16_bf16 (twice the rate of the 16x16
-//    form on gfx950); its design is described where it is defined.
+// One kernel (sparse_mla_kernel) computes it for three KV row formats:
+// bf16 rows (576 x 2 bytes); per-token FP8 rows (576 e4m3 codes, one fp32
+// scale per row in a separate array), whose scale stays out of the bf16
+// operands (it multiplies the row's logit and softmax weight, so the codes
+// widen to bf16 exactly); and FlashMLA's 656-byte fp8_ds_mla row (512 codes,
+// four fp32 scales of 128 dims each, 64 bf16 rope dims; GLM-5.3 part 2,
+// footnote 1, names it), whose codes are widened as bf16(code x block
+// scale), one rounding per element, so QK and PV run as for bf16 rows.  One
+// 2-wave workgroup per query (or per slice of a query's rows on small
+// batches, merged by mla_merge_kernel) splits both contractions by dims,
+// gathers with direct global->LDS loads and uses v_mfma_f32_32x32x16_bf16;
+// its design is described where it is defined.
 // Writing the products transposed puts one head per lane column in both
 // accumulators, so the softmax statistics of a head and the output rows
 // they scale live in the same lanes.
@@ -34,321 +29,11 @@
 namespace sma {
 
 constexpr int kMlaRows = 32;                // gathered rows per tile
-constexpr int kMlaRowB = kDqk * 2 + 16;     // padded LDS row, bytes (1168)
-constexpr int kMlaThreads = 256;
 // Split partial of one (query, slice): O [64][512] unnormalised, then the
 // per-head exponent reference m (log2 domain) and sum l.
 constexpr int kMlaPartFloats = kHeads * kDv + 2 * kHeads;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// KV formats of sparse_mla_kernel
-constexpr int kKvBf16 = 0;      // bf16 rows (576 x 2 bytes)
-constexpr int kKvFp8Row = 1;    // 576 e4m3 codes, one fp32 scale per row in a separate array
-constexpr int kKvFp8Ds = 2;     // 656-byte fp8_ds_mla rows
-constexpr int kDsRowB = 656;    // 512 codes + 4 fp32 scales + 64 bf16
-constexpr int kDsChunks = kDsRowB / 16;   // 41 16-byte chunks: 32 of codes, 1 of scales, 8 of rope
-
-template <int KVF, bool OUT_F32>
-__global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
-    const uint16_t* __restrict__ q, const void* __restrict__ kv, const float* __restrict__ kv_scale,
-    int n_k, const int32_t* __restrict__ idx, int n_q, int K, float scale_log2,
-    void* __restrict__ out, float* __restrict__ lse, int n_split, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][kMlaRows * kMlaRowB];
-  __shared__ int s_list[SMA_MAX_TOPK_DEV];
-  constexpr bool FP8 = KVF != kKvBf16, DS = KVF == kKvFp8Ds;
-  __shared__ __attribute__((aligned(16))) float s_scale[2][DS ? 4 * kMlaRows : kMlaRows];
-  __shared__ uint32_t s_cnt[kMlaThreads / 64];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // With n_split > 1 workgroup (qi, split) covers one slice of the query's
-  // compacted rows and leaves an unnormalised partial in `part` (merged by
-  // mla_merge_kernel); otherwise it covers all of them.
-  const int qi = blockIdx.x / n_split, split = blockIdx.x % n_split;
-  const int g = lane >> 4, i = lane & 15;   // lane group (k slot) and column (head)
-
-  // ---- compact the valid indices, keeping their order ----
-  constexpr int PER = SMA_MAX_TOPK_DEV / kMlaThreads;   // 8
-  int v[PER];
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int j = tid * PER + e;
-    int x = j < K ? idx[(int64_t)qi * K + j] : -1;
-    if (x < 0 || x >= n_k) x = -1;
-    v[e] = x;
-    cnt += x >= 0;
-  }
-  uint32_t incl = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) s_cnt[wave] = incl;
-  __syncthreads();
-  uint32_t before = incl - cnt, total = 0;
-#pragma unroll
-  for (int w = 0; w < kMlaThreads / 64; ++w) {
-    if (w < wave) before += s_cnt[w];
-    total += s_cnt[w];
-  }
-#pragma unroll
-  for (int e = 0; e < PER; ++e)
-    if (v[e] >= 0) s_list[before++] = v[e];
-  __syncthreads();
-  const int n_valid = (int)total;
-  // this workgroup's slice [lb, le) of the compacted list (whole tiles)
-  const int per = ((n_valid + n_split - 1) / n_split + kMlaRows - 1) / kMlaRows * kMlaRows;
-  const int lb = min(n_valid, split * per), le = min(n_valid, lb + per);
-
-  const int head = 16 * wave + i;
-  float* mypart = part ? part + (int64_t)blockIdx.x * kMlaPartFloats : nullptr;
-  if (mypart && le == lb) {   // empty slice: zero partial, reference -inf
-    for (int mt = 0; mt < kDv / 16; ++mt)
-      *reinterpret_cast<f32x4*>(mypart + head * kDv + 16 * mt + 4 * g) = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (g == 0) {
-      mypart[kHeads * kDv + head] = -INFINITY;
-      mypart[kHeads * kDv + kHeads + head] = 0.f;
-    }
-    return;
-  }
-  if (n_valid == 0) {
-    for (int mt = 0; mt < kDv / 16; ++mt) {
-      const int64_t o_off = ((int64_t)qi * kHeads + head) * kDv + 16 * mt + 4 * g;
-      if constexpr (OUT_F32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o_off) = f32x4{0.f, 0.f, 0.f, 0.f};
-      } else {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o_off) = u32x2{0u, 0u};
-      }
-    }
-    if (lse && g == 0) lse[(int64_t)qi * kHeads + head] = -INFINITY;
-    return;
-  }
-
-  // ---- the wave's Q fragment: head 16w+i, dims 32ks + 8g .. +7 ----
-  bf16x8 qf[kDqk / 32];
-  {
-    const uint16_t* src = q + ((int64_t)qi * kHeads + head) * kDqk + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + 32 * ks);
-  }
-
-  // ---- gather staging ----
-  constexpr int NCH = DS    ? (kMlaRows * kDsChunks + kMlaThreads - 1) / kMlaThreads
-                      : FP8 ? (kMlaRows * kDqk / 16 + kMlaThreads - 1) / kMlaThreads
-                            : kMlaRows * kDqk / 8 / kMlaThreads;   // 16-byte loads per thread
-  u32x4 stage[NCH];
-  float stage_sc = 0.f;
-  auto load_tile = [&](int t) {
-    const int r0 = lb + t * kMlaRows;
-#pragma unroll
-    for (int r = 0; r < NCH; ++r) {
-      const int c = tid + kMlaThreads * r;
-      if constexpr (DS) {
-        if (c < kMlaRows * kDsChunks) {
-          const int row = c / kDsChunks, col = c % kDsChunks;
-          const int li = r0 + row < le ? r0 + row : lb;
-          stage[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(kv) +
-                                                     (int64_t)s_list[li] * kDsRowB + col * 16);
-        }
-      } else if constexpr (FP8) {
-        if (c < kMlaRows * kDqk / 16) {
-          const int row = c / (kDqk / 16), col = c % (kDqk / 16);
-          const int li = r0 + row < le ? r0 + row : lb;
-          stage[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(kv) +
-                                                     (int64_t)s_list[li] * kDqk + col * 16);
-        }
-      } else {
-        const int row = c / (kDqk / 8), col = c % (kDqk / 8);
-        const int li = r0 + row < le ? r0 + row : lb;
-        stage[r] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(kv) +
-                                                   (int64_t)s_list[li] * kDqk + col * 8);
-      }
-    }
-    if constexpr (KVF == kKvFp8Row) {
-      if (tid < kMlaRows) {
-        const int li = r0 + tid < le ? r0 + tid : lb;
-        stage_sc = kv_scale[s_list[li]];
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < NCH; ++r) {
-      const int c = tid + kMlaThreads * r;
-      if constexpr (DS) {
-        // the row's four block scales and its rope dims (bf16 as stored);
-        // the codes follow once every scale of the tile is in LDS
-        if (c < kMlaRows * kDsChunks) {
-          const int row = c / kDsChunks, col = c % kDsChunks;
-          if (col == 32) *reinterpret_cast<u32x4*>(&s_scale[buf][4 * row]) = stage[r];
-          else if (col > 32) *reinterpret_cast<u32x4*>(&s_kv[buf][row * kMlaRowB + 1024 + 16 * (col - 33)]) = stage[r];
-        }
-      } else if constexpr (FP8) {
-        // codes widened by the hardware convert: every e4m3 value is exact
-        // in fp32 and in bf16
-        if (c < kMlaRows * kDqk / 16) {
-          const int row = c / (kDqk / 16), col = c % (kDqk / 16);
-          uint8_t* dst = &s_kv[buf][row * kMlaRowB + col * 32];
-          uint32_t packed[8];
-#pragma unroll
-          for (int wd = 0; wd < 4; ++wd) {
-            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[r][wd], false);
-            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[r][wd], true);
-            packed[2 * wd] = pack_bf16x2(lo[0], lo[1]);
-            packed[2 * wd + 1] = pack_bf16x2(hi[0], hi[1]);
-          }
-          *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-          *reinterpret_cast<u32x4*>(dst + 16) = u32x4{packed[4], packed[5], packed[6], packed[7]};
-        }
-      } else {
-        const int row = c / (kDqk / 8), col = c % (kDqk / 8);
-        *reinterpret_cast<u32x4*>(&s_kv[buf][row * kMlaRowB + col * 16]) = stage[r];
-      }
-    }
-    if constexpr (KVF == kKvFp8Row) {
-      if (tid < kMlaRows) s_scale[buf][tid] = stage_sc;
-    }
-    if constexpr (DS) {
-      // codes of dims 16col .. 16col + 15 times the row's scale of block
-      // col / 8, rounded once to bf16 (e4m3 -> fp32 is exact)
-      __syncthreads();
-#pragma unroll
-      for (int r = 0; r < NCH; ++r) {
-        const int c = tid + kMlaThreads * r;
-        if (c < kMlaRows * kDsChunks) {
-          const int row = c / kDsChunks, col = c % kDsChunks;
-          if (col < 32) {
-            const float sc = s_scale[buf][4 * row + (col >> 3)];
-            uint32_t packed[8];
-#pragma unroll
-            for (int wd = 0; wd < 4; ++wd) {
-              const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[r][wd], false);
-              const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[r][wd], true);
-              packed[2 * wd] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
-              packed[2 * wd + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
-            }
-            uint8_t* dst = &s_kv[buf][row * kMlaRowB + col * 32];
-            *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-            *reinterpret_cast<u32x4*>(dst + 16) = u32x4{packed[4], packed[5], packed[6], packed[7]};
-          }
-        }
-      }
-    }
-  };
-
-  // ---- running state: O^T[dim 16mt+4g+r][head i] in o[mt][r] ----
-  f32x4 o[kDv / 16];
-#pragma unroll
-  for (int mt = 0; mt < kDv / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // running max of the head's logits (log2 domain)
-  float l_run = 0.f;         // this lane's share of the softmax denominator
-
-  const int ntiles = (le - lb + kMlaRows - 1) / kMlaRows;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) load_tile(t + 1);
-    const uint8_t* tile = s_kv[buf];
-
-    // S^T = K . Q^T : rows 16mt + 4g + r, head i
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(tile + (16 * mt + i) * kMlaRowB + (32 * ks + 8 * g) * 2);
-        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
-      }
-    }
-
-    // online softmax (log2 domain)
-    const int valid_rows = le - lb - t * kMlaRows;
-    float s2[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mt + 4 * g + r;
-        float x = sacc[mt][r] * scale_log2;
-        if constexpr (KVF == kKvFp8Row) x *= s_scale[buf][row];
-        x = row < valid_rows ? x : -INFINITY;
-        s2[4 * mt + r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    float psum = 0.f;
-    float pv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = exp2f(s2[e] - m_new);
-      psum += pe;
-      pv[e] = pe;
-      if constexpr (KVF == kKvFp8Row) pv[e] = pe * s_scale[buf][16 * (e / 4) + 4 * g + (e % 4)];
-    }
-    l_run = l_run * alpha + psum;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int mt = 0; mt < kDv / 16; ++mt) o[mt] *= alpha;
-    }
-    m_run = m_new;
-    bf16x8 pb;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pv[e];
-
-    // O^T += V^T . P^T ; V^T columns read transposed from the row-major tile
-    const uint8_t* va_base = tile + (4 * g + (i >> 2)) * kMlaRowB + 8 * (i & 3);
-    const uint8_t* vb_base = va_base + 16 * kMlaRowB;
-#pragma unroll
-    for (int mt = 0; mt < kDv / 16; ++mt) {
-      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(va_base + 32 * mt));
-      const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_base + 32 * mt));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mt], 0, 0, 0);
-    }
-
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- normalise and write (or leave the partial) ----
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (mypart) {
-#pragma unroll
-    for (int mt = 0; mt < kDv / 16; ++mt)
-      *reinterpret_cast<f32x4*>(mypart + head * kDv + 16 * mt + 4 * g) = o[mt];
-    if (g == 0) {
-      mypart[kHeads * kDv + head] = m_run;
-      mypart[kHeads * kDv + kHeads + head] = l_tot;
-    }
-    return;
-  }
-  const float inv = 1.f / l_tot;
-#pragma unroll
-  for (int mt = 0; mt < kDv / 16; ++mt) {
-    const int64_t o_off = ((int64_t)qi * kHeads + head) * kDv + 16 * mt + 4 * g;
-    const f32x4 r = o[mt] * inv;
-    if constexpr (OUT_F32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o_off) = r;
-    } else {
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o_off) =
-          u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
-    }
-  }
-  if (lse && g == 0)
-    lse[(int64_t)qi * kHeads + head] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
-}
 
 // Log-sum-exp merge of the n_split partials of each query: with
 // M = max_s m_s, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s and
@@ -536,8 +221,14 @@ __device__ __forceinline__ constexpr int tile_block(int rg, int cg) { return (4 
 // block (r >> 3, cc >> 3) = (r >> 3, P0 / 4 + i / 2) at slot (cc & 7) ^
 // swz(r), cc & 7 = 4 (i & 1) + 2 (l >> 5) + hh.  The convert is
 // v_cvt_scalef32_pk_bf16_fp8 at scale 1: exact.
-template <int P0, int NI>
-__device__ __forceinline__ void widen_fp8_dims(const uint8_t* stage, uint8_t* tile, int lane) {
+//
+// With block scales (fp8_ds_mla rows, BS = true) piece c belongs to the
+// 128-dim block c >> 3, which for the pieces a lane widens is (P0 + 2 i) >> 3
+// (P0 + 2 i is even, so adding l >> 5 stays in the block); each code is
+// widened exactly to fp32, multiplied by the row's scale of that block
+// (bsc = the row's four scales) and rounded once to bf16.
+template <int P0, int NI, bool BS = false>
+__device__ __forceinline__ void widen_fp8_dims(const uint8_t* stage, uint8_t* tile, int lane, f32x4 bsc = {}) {
   static_assert(P0 % 4 == 0, "pieces start at a chunk group");
   const int r = lane & 31, g = lane >> 5, sw = tile_swz(r);
   uint8_t* rowp = tile + tile_block(r >> 3, 0) + 128 * (r & 7);
@@ -552,8 +243,16 @@ __device__ __forceinline__ void widen_fp8_dims(const uint8_t* stage, uint8_t* ti
     uint32_t w[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      w[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[e], 1.f, false));
-      w[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[e], 1.f, true));
+      if constexpr (BS) {
+        const float sc = bsc[((P0 + 2 * i) >> 3) & 3];
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], true);
+        w[2 * e] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+        w[2 * e + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
+      } else {
+        w[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[e], 1.f, false));
+        w[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[e], 1.f, true));
+      }
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
@@ -562,35 +261,57 @@ __device__ __forceinline__ void widen_fp8_dims(const uint8_t* stage, uint8_t* ti
   }
 }
 
-// FP8 = true: per-token FP8 latent rows (576 e4m3 codes + an fp32 scale per
-// row).  A tile's 32 rows x 576 codes (18 KiB) are gathered by the same
+// KV row formats.
+constexpr int kKvBf16 = 0;     // 576 bf16 dims (1,152 bytes)
+constexpr int kKvFp8Row = 1;   // 576 e4m3 codes; one fp32 scale per row in a separate array
+constexpr int kKvFp8Ds = 2;    // fp8_ds_mla: 512 codes, 4 fp32 block scales, 64 bf16 rope dims
+constexpr int kDsRowB = 656;
+constexpr int kDsScaleOff = 512, kDsRopeOff = 528;   // byte offsets inside a 656-byte row
+
+// FP8 rows (kKvFp8Row, kKvFp8Ds).  A tile's codes are gathered by the same
 // direct global->LDS loads into one of two staging slots (half the bytes of
-// a bf16 tile), the row scales beside them; once a tile has landed the
-// workgroup widens its codes to bf16 (v_cvt_scalef32_pk_bf16_fp8 at scale
-// 1: exact, every e4m3 value is a bf16 value) into the one bf16 tile, laid
-// out and swizzled as below, and QK / softmax / PV run unchanged on it; each
-// wave widens the dims it reads (wave 0: 0..287 for QK and PV, wave 1:
-// 256..575; 256..287 are written by both, with the same values), so the
-// widened tile needs no barrier of its own.  The
-// row's scale stays out of the operands: it multiplies the row's summed
-// logit and its softmax weight before PV (the sum of the weights, the
-// softmax denominator, is taken unscaled).  LDS: the bf16 tile and the two
-// staging slots fill the same 72 KiB the bf16 kernel's two tiles take.
-constexpr int kF8TileB = kMlaRows * kDqk;   // 18432: one tile of codes
+// a bf16 tile), the row scales beside them; once a tile has landed each
+// wave widens the codes of the dims it reads into the one bf16 tile, laid
+// out and swizzled as below, and QK / softmax / PV run on it unchanged
+// (wave 0 widens dims 0..287, wave 1 256..575 or 256..511; 256..287 are
+// written by both, with the same values, so the widened tile needs no
+// barrier of its own).
+//  * kKvFp8Row: 32 rows x 576 codes (18 KiB) per slot, widened by
+//    v_cvt_scalef32_pk_bf16_fp8 at scale 1 (exact: every e4m3 value is a
+//    bf16 value).  The row's scale stays out of the operands: it multiplies
+//    the row's summed logit and its softmax weight before PV (the sum of the
+//    weights, the softmax denominator, is taken unscaled).
+//  * kKvFp8Ds: 32 rows x 512 codes (16 KiB) per slot and the rows' four
+//    block scales; each code widened as bf16(code x its block's scale), one
+//    rounding.  The 64 rope dims are stored in bf16 already: they are
+//    gathered straight into a rope buffer laid out as the bf16 tile's chunk
+//    group 8, one per ring parity (the tile being computed keeps its rope
+//    while the next tile's arrives), and wave 1's last four QK k-steps read
+//    them there.
+// LDS: bf16 tile + two staging slots fill the 72 KiB the bf16 format's two
+// tiles take (kKvFp8Ds: the codes part of the tile, 32 KiB, two 4-KiB rope
+// buffers, two 16-KiB slots).
+constexpr int kF8TileB = kMlaRows * kDqk;   // 18432: one tile of per-token codes
+constexpr int kDsTileB = kMlaRows * kDv;    // 16384: one tile of fp8_ds_mla codes
+constexpr int kDsStageOff = kRopeOff + 2 * 4096;   // first staging slot (after the two rope buffers)
+static_assert(kDmaTileB + 2 * kF8TileB <= 2 * kDmaTileB, "FP8 staging fits the ring");
+static_assert(kDsStageOff + 2 * kDsTileB <= 2 * kDmaTileB, "fp8_ds_mla staging fits the ring");
 
 // With n_split > 1, workgroup (query, slice) covers one slice of the query's
 // tiles (a contiguous range of 32-entry tiles) and leaves its unnormalised
 // partial in `part` (O, the fixed exponent reference and the weight sum per
 // head, the layout mla_merge_kernel reads); an empty slice leaves 0, -inf, 0.
-template <bool OUT_F32, bool FP8>
-__global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
+template <bool OUT_F32, int KVF>
+__global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, const float* __restrict__ kv_scale, int n_k,
     const int32_t* __restrict__ idx, int n_q, int K, float scale_log2, void* __restrict__ out,
     float* __restrict__ lse, int n_split, float* __restrict__ part) {
-  // bf16: tiles 0 and 1; FP8: the bf16 tile, then staging slots 0 and 1
+  constexpr bool FP8 = KVF != kKvBf16, ROW = KVF == kKvFp8Row, DS = KVF == kKvFp8Ds;
+  // bf16: tiles 0 and 1; FP8: the bf16 tile (and rope buffers), then staging slots 0 and 1
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * kDmaTileB];
-  static_assert(kDmaTileB + 2 * kF8TileB <= 2 * kDmaTileB, "FP8 staging fits the ring");
-  __shared__ __attribute__((aligned(16))) float s_sc[2][64];
+  // per-row scales of the two staging slots: kKvFp8Row lane l's word (rows
+  // l & 31), kKvFp8Ds four per row
+  __shared__ __attribute__((aligned(16))) float s_sc[2][DS ? 4 * kMlaRows : 64];
   __shared__ __attribute__((aligned(1024))) uint8_t s_x[4096];
   __shared__ __attribute__((aligned(1024))) int s_idx[2][kIdxChunk];
   __shared__ float s_l[kHeads];
@@ -689,8 +410,33 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
     if (d == 0) dma_load4(kv_scale + row, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&s_sc[b][0]);
     return (uint32_t)__ballot(ok);
   };
+  // fp8_ds_mla: codes as issue_f8 with 512-code rows (loads k = 0..15, wave
+  // d issues 8d .. 8d + 7), the 32 rows' scale chunks by wave 0's lanes 0..31
+  // into s_sc, and the rope chunks of row groups 2d, 2d + 1 into the rope
+  // buffer of parity b as the bf16 layout's blocks (rg, 8).
+  auto issue_ds = [&](int t, int b) -> uint32_t {
+    const int e = t * kMlaRows + (lane & 31);
+    const int raw = entry_raw(e);
+    const bool ok = entry_ok(e, raw);
+    const uint8_t* rowp = kv + (int64_t)(ok ? raw : 0) * kDsRowB;
+    const uint8_t* src = rowp + 256 * d + 16 * (lane >> 5);
+    const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)(s_ring + kDsStageOff + b * kDsTileB + 8192 * d);
+#define SMA_DS_LOAD(k) dma_load16_at<32 * (k)>(src, dst + 1024 * (k));
+    SMA_DS_LOAD(0) SMA_DS_LOAD(1) SMA_DS_LOAD(2) SMA_DS_LOAD(3)
+    SMA_DS_LOAD(4) SMA_DS_LOAD(5) SMA_DS_LOAD(6) SMA_DS_LOAD(7)
+#undef SMA_DS_LOAD
+    if (d == 0 && lane < 32)
+      dma_load16(rowp + kDsScaleOff, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&s_sc[b][0]);
+    const int raw_lo = entry_raw(t * kMlaRows + r_lo), raw_hi = entry_raw(t * kMlaRows + r_hi);
+    const bool ok_lo = entry_ok(t * kMlaRows + r_lo, raw_lo), ok_hi = entry_ok(t * kMlaRows + r_hi, raw_hi);
+    const uint32_t rdst = (uint32_t)(uintptr_t)(lds_u8*)(s_ring + kRopeOff + 4096 * b + 1024 * 2 * d);
+    dma_load16(kv + (int64_t)(ok_lo ? raw_lo : 0) * kDsRowB + kDsRopeOff + c_lo, rdst);
+    dma_load16(kv + (int64_t)(ok_hi ? raw_hi : 0) * kDsRowB + kDsRopeOff + c_hi, rdst + 1024);
+    return (uint32_t)__ballot(ok);
+  };
   auto issue_tile = [&](int t, int b) -> uint32_t {   // returns the tile's row mask
-    if constexpr (FP8) return issue_f8(t, b);
+    if constexpr (DS) return issue_ds(t, b);
+    if constexpr (ROW) return issue_f8(t, b);
     const int raw_lo = entry_raw(t * kMlaRows + r_lo), raw_hi = entry_raw(t * kMlaRows + r_hi);
     const bool ok_lo = entry_ok(t * kMlaRows + r_lo, raw_lo), ok_hi = entry_ok(t * kMlaRows + r_hi, raw_hi);
     const uint8_t* src_lo = kv + (int64_t)(ok_lo ? raw_lo : 0) * kDmaRowB + c_lo;
@@ -766,17 +512,30 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
       uint32_t mask_next = 0;
       if (t + 1 < t_end) mask_next = issue_tile(t + 1, (t + 1) & 1);
       uint8_t* tile = FP8 ? s_ring : s_ring + (t & 1) * kDmaTileB;
-      if constexpr (FP8) {
+      // fp8_ds_mla: tile t's rope dims sit in the rope buffer of its parity
+      const int rope_add = DS ? 4096 * (t & 1) : 0;
+      if constexpr (ROW) {
         // the bf16 tile is free (every wave is past tile t-1, barrier above);
         // each wave widens the dims it reads itself, so no barrier follows
         const uint8_t* stage = s_ring + kDmaTileB + (t & 1) * kF8TileB;
         if (d == 0) widen_fp8_dims<0, 9>(stage, tile, lane);
         else widen_fp8_dims<16, 10>(stage, tile, lane);
+      } else if constexpr (DS) {
+        const uint8_t* stage = s_ring + kDsStageOff + (t & 1) * kDsTileB;
+        const f32x4 bsc = *reinterpret_cast<const f32x4*>(&s_sc[t & 1][4 * (lane & 31)]);
+        if (d == 0) widen_fp8_dims<0, 9, true>(stage, tile, lane, bsc);
+        else widen_fp8_dims<16, 8, true>(stage, tile, lane, bsc);
       }
 
       // ---- partial S^T over this wave's dims, both head blocks ----
       constexpr int kPf = 3;
-      auto kread = [&](int ks) { return *reinterpret_cast<const bf16x8*>(tile + kb[ks & 3] + (ks >> 2) * 4096); };
+      // (wave 1's k-steps 14..17 are the rope dims, chunk group 8; wave 0's
+      // are code dims)
+      const int rope_k = d ? rope_add : 0;
+      auto kread = [&](int ks) {
+        const int ra = ks >= kPairKs - 4 ? rope_k : 0;
+        return *reinterpret_cast<const bf16x8*>(tile + kb[ks & 3] + (ks >> 2) * 4096 + ra);
+      };
       f32x16v s_own, s_oth;
       bf16x8 kop[kPf];
 #pragma unroll
@@ -802,8 +561,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
       mfma32_vgpr_drain1(s_oth);
 
       // ---- exchange half-sums: wave 1 writes into the (now dead) rope blocks, wave 0 into s_x ----
-      uint8_t* xw = d ? tile + kRopeOff : s_x;   // written by this wave
-      uint8_t* xr = d ? s_x : tile + kRopeOff;   // written by the partner
+      uint8_t* xw = d ? tile + kRopeOff + rope_add : s_x;   // written by this wave
+      uint8_t* xr = d ? s_x : tile + kRopeOff + rope_add;   // written by the partner
 #pragma unroll
       for (int p = 0; p < 4; ++p)
         *reinterpret_cast<f32x4*>(xw + 1024 * p + 16 * lane) =
@@ -818,7 +577,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
       for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int r = 0; r < 4; ++r) s_own[4 * p + r] += y[p][r];
-      if constexpr (FP8) {   // the rows' scales on their summed logits (rows 8p + 4h + r)
+      if constexpr (ROW) {   // the rows' scales on their summed logits (rows 8p + 4h + r)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const f32x4 rs = *reinterpret_cast<const f32x4*>(&s_sc[t & 1][8 * p + 4 * h]);
@@ -855,7 +614,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_bf16_kernel(
         float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s_own[j], scale_log2, neg_ref));
         if (!full) pe = row_ok(j) ? pe : 0.f;
         ps += pe;
-        if constexpr (FP8)   // PV takes the codes: the row's scale goes on its weight
+        if constexpr (ROW)   // PV takes the codes: the row's scale goes on its weight
           pb[j >> 3][j & 7] = (__bf16)(pe * s_sc[t & 1][8 * (j >> 2) + 4 * h + (j & 3)]);
         else
           pb[j >> 3][j & 7] = (__bf16)pe;
@@ -997,8 +756,7 @@ size_t mla_split_bytes(int n_q, int n_split) {
 hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
   if (A.n_q <= 0) return hipSuccess;
   const float scale_log2 = A.sm_scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)A.n_q), block(kMlaThreads);
-  const dim3 block2(kPairThreads);
+  const dim3 block(kPairThreads);
   const uint8_t* kv8 = static_cast<const uint8_t*>(A.kv);
   // small batches split each query's rows across workgroups, into as many
   // slices as the workspace holds partials for (up to the preferred count)
@@ -1011,28 +769,20 @@ hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
   }
   float* part = n_split > 1 ? static_cast<float*>(A.ws) : nullptr;
   const dim3 grid_s((unsigned)(A.n_q * n_split));
+#define SMA_MLA_LAUNCH(F32, KVF)                                                                              \
+  hipLaunchKernelGGL((sparse_mla_kernel<F32, KVF>), grid_s, block, 0, st, A.q, kv8, A.kv_scale, (int)A.n_k, A.idx, \
+                     A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part)
   if (A.fp8 && A.ds_mla) {
-    // 656-byte fp8_ds_mla rows: the 4-wave kernel
-    if (A.out_f32)
-      hipLaunchKernelGGL((sparse_mla_kernel<kKvFp8Ds, true>), grid_s, block, 0, st, A.q, A.kv, A.kv_scale,
-                         (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part);
-    else
-      hipLaunchKernelGGL((sparse_mla_kernel<kKvFp8Ds, false>), grid_s, block, 0, st, A.q, A.kv, A.kv_scale,
-                         (int)A.n_k, A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part);
+    if (A.out_f32) SMA_MLA_LAUNCH(true, kKvFp8Ds);
+    else SMA_MLA_LAUNCH(false, kKvFp8Ds);
+  } else if (A.fp8) {
+    if (A.out_f32) SMA_MLA_LAUNCH(true, kKvFp8Row);
+    else SMA_MLA_LAUNCH(false, kKvFp8Row);
   } else {
-    // bf16 rows, or per-token FP8 rows widened in LDS: the 2-wave kernel
-#define SMA_MLA_PAIR(F32, F8)                                                                                     \
-  hipLaunchKernelGGL((sparse_mla_bf16_kernel<F32, F8>), grid_s, block2, 0, st, A.q, kv8, A.kv_scale, (int)A.n_k, \
-                     A.idx, A.n_q, A.top_k, scale_log2, A.out, A.lse, n_split, part)
-    if (A.fp8) {
-      if (A.out_f32) SMA_MLA_PAIR(true, true);
-      else SMA_MLA_PAIR(false, true);
-    } else {
-      if (A.out_f32) SMA_MLA_PAIR(true, false);
-      else SMA_MLA_PAIR(false, false);
-    }
-#undef SMA_MLA_PAIR
+    if (A.out_f32) SMA_MLA_LAUNCH(true, kKvBf16);
+    else SMA_MLA_LAUNCH(false, kKvBf16);
   }
+#undef SMA_MLA_LAUNCH
   if (n_split > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -37,6 +37,8 @@ def _idx_lists(n_q, n_k, top_k, seed):
     idx[1, 0] = n_k + 9      # out of range: skipped
     idx[2, :] = -1           # empty set
     idx[3, ::3] = -1         # padding in the middle
+    if n_q > 4:
+        idx[4, : min(top_k, 96)] = -1   # the first tiles hold no valid row
     return idx
 
 
@@ -144,3 +146,29 @@ def test_prefill_and_dcp_with_fp8_ds_mla_rows():
     merged, _ = sma.lse_merge(parts, lses, out_dtype=torch.float32)
     full, _ = sma.sparse_mla_prefill(dev(q), dev(rows), idx, TAU, out_dtype=torch.float32)
     assert float((merged - full).abs().max()) <= 1e-2 * float(full.abs().max())
+
+
+def test_fp8_ds_mla_logits_rising_far_above_first_tile():
+    """Rows whose logits pass the first valid tile's maximum by far more than
+    the fixed-reference range (the query is swept again), with the rope part
+    carrying its share of the logit; both output types."""
+    rng = np.random.default_rng(23)
+    n_q, n_k, top_k = 260, 400, 256
+    q = synth.to_bf16_bits(np.abs(rng.standard_normal((n_q, 64, 576)).astype(np.float32)) * np.float32(0.1)
+                           + np.float32(0.05))
+    x = np.abs(rng.standard_normal((n_k, 576)).astype(np.float32)) * np.float32(0.01)
+    x[300:] += np.float32(12.0)                   # these rows: logits far above the rest
+    rows = synth.to_fp8_ds_mla_rows(x)
+    idx = np.stack([np.sort(rng.choice(n_k, top_k, replace=False)) for _ in range(n_q)]).astype(np.int32)
+    idx[:, :40] = np.arange(40)
+    idx = np.sort(idx, axis=1)
+    ref, ref_lse = _ref(q, rows, idx)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out, lse = sma.sparse_mla_prefill(dev(q), dev(rows), dev(idx), TAU, out_dtype=out_dtype, want_lse=True)
+        got = out_f64(out)
+        assert np.all(np.isfinite(got))
+        assert np.abs(got - ref).max() <= 3e-2 * np.abs(ref).max()
+        # every code x block scale is rounded once to bf16 (2^-9 relative);
+        # these rows' products all have one sign, so the logits (~70) carry
+        # that relative error without cancellation: LSE within 2.5e-3 of it
+        assert np.abs(host(lse) - ref_lse).max() <= 2.5e-3 * np.abs(ref_lse).max()
