@@ -38,6 +38,15 @@
  *    kernels: a query position p is clamped to [-1, n_k-1] (p = -1 means an
  *    empty causal prefix); an index outside [0, n_k) in an index list is
  *    skipped like the -1 padding.
+ *  - Debug build (libsma_debug.so; sma_build_flags() has
+ *    SMA_BUILD_DEBUG_CHECKS): the same entry points, which also scan each
+ *    device-resident index list and position array before the launch that
+ *    reads it and return SMA_ERR_INVALID_ARG, with nothing else launched,
+ *    for a value the release build would skip or clamp (a position outside
+ *    [-1, n_k-1]; an index list entry below -1 or, except in a DCP shard's
+ *    global list, at or past n_k); and fill the workspace (or the static
+ *    scratch) with 0xFF bytes, fp32 NaN, before using it.  These checks
+ *    synchronise the stream and are meant for testing, not for capture.
  *  - Results are deterministic: the same inputs give bit-identical outputs,
  *    whatever the launch split (a PCP share equals the matching rows of the
  *    unsharded call).
@@ -192,10 +201,10 @@ sma_status sma_topk_select(const float* scores, int64_t ld_scores, const int32_t
  *  lse      [n_q, 64] fp32, or NULL.  A query with no valid index gets
  *           out = 0 and lse = -inf.
  *  Softmax and accumulation are fp32; QK and PV run on bf16 MFMA (an FP8
- *  row is widened to bf16 exactly; its scale multiplies the logit and the
- *  softmax weight; an fp8_ds_mla row's QK is summed per 128-dim block and
- *  each block's scale applied to its part, its PV takes the softmax weight
- *  times the block's scale).
+ *  row is widened to bf16 exactly and its scale multiplies the logit and
+ *  the softmax weight; an fp8_ds_mla row's codes are widened as bf16(code x
+ *  the scale of their 128-dim block), one rounding each, its rope dims
+ *  taken as stored).
  *  sm_scale must be finite and > 0 (SMA_ERR_INVALID_ARG otherwise).
  *  Supported: 1 <= top_k <= 2048.  ws may be NULL (ws_bytes 0).  With a
  *  workspace (256-byte aligned), a batch of fewer queries than the device
@@ -412,6 +421,12 @@ const char* sma_last_error(void);
 
 /* ABI version: (major << 16) | minor. */
 int32_t sma_version(void);
+
+/* Build flags of the loaded library: SMA_BUILD_DEBUG_CHECKS in the debug
+ * build (the device-resident range checks and workspace fill described at
+ * the top of this file), 0 in the release build. */
+#define SMA_BUILD_DEBUG_CHECKS 1
+int32_t sma_build_flags(void);
 
 #ifdef __cplusplus
 }

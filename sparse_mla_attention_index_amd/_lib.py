@@ -16,6 +16,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsma.so")
+# the debug build (device-resident range checks, workspace fill; include/sma.h)
+DEBUG_LIB_PATH = os.path.join(_HERE, "libsma_debug.so")
+SMA_BUILD_DEBUG_CHECKS = 1
 
 SMA_DT_BF16, SMA_DT_FP8_E4M3, SMA_DT_FP32, SMA_DT_FP8_DS_MLA = 0, 1, 2, 3
 DS_ROW_BYTES = 656   # fp8_ds_mla latent row: 512 e4m3 codes, 4 fp32 scales, 64 bf16 rope dims
@@ -47,6 +50,7 @@ SIGNATURES = {
     "sma_workspace_bytes": (_SZ, [_I32, _I32, _I64, _I32, _I32, _I32]),
     "sma_last_error": (ctypes.c_char_p, []),
     "sma_version": (_I32, []),
+    "sma_build_flags": (_I32, []),
 }
 
 _lib = None
@@ -58,20 +62,46 @@ class SmaError(RuntimeError):
         self.status = status
 
 
+def load(path: str):
+    """Open one build of the library with every entry point's signature set
+    (raises if it was not built: there is no fallback)."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing; build it with `python -m sparse_mla_attention_index_amd.build`")
+    L = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
 def lib():
-    """Load libsma.so (raises if it was not built: there is no fallback)."""
+    """The library every wrapper below calls: libsma.so, or the debug build
+    when SMA_DEBUG_LIBRARY=1 is set before the first call."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing; build it with "
-                              "`python -m sparse_mla_attention_index_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = L
+        _lib = load(DEBUG_LIB_PATH if os.environ.get("SMA_DEBUG_LIBRARY") == "1" else LIB_PATH)
     return _lib
+
+
+class debug_library:
+    """Context manager: the wrappers call the debug build inside the block
+    and the library they called before it afterwards."""
+
+    def __enter__(self):
+        global _lib
+        self._prev = lib()
+        _lib = load(DEBUG_LIB_PATH)
+        return _lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self._prev
+        return False
+
+
+def build_flags() -> int:
+    return int(lib().sma_build_flags())
 
 
 def last_error() -> str:

@@ -19,6 +19,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsma.so")
+# The debug build: the same kernels, the C ABI compiled with SMA_DEBUG_CHECKS
+# (device-resident range checks and workspace fill, include/sma.h).
+DEBUG_LIB = os.path.join(PKG, "libsma_debug.so")
+DEBUG_SRC = "sma_api.hip"
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
@@ -44,22 +48,29 @@ def _run(cmd):
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every source and link libsma.so and libsma_debug.so; returns
+    the release library's path."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    dbg_src = os.path.join(CSRC, DEBUG_SRC)
+    dbg_obj = os.path.join(BUILD, DEBUG_SRC[:-4] + "_debug.o")
+    jobs = [(s, o, []) for s, o in zip(srcs, objs)] + [(dbg_src, dbg_obj, ["-DSMA_DEBUG_CHECKS=1"])]
 
-    def compile_one(so):
-        s, o = so
-        out = _run([cc, *HIPFLAGS, "-c", s, "-o", o])
+    def compile_one(job):
+        s, o, extra = job
+        out = _run([cc, *HIPFLAGS, *extra, "-c", s, "-o", o])
         if verbose and out.strip():
             print(out)
 
-    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        list(ex.map(compile_one, zip(srcs, objs)))
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(min(8, len(jobs))) as ex:
+        list(ex.map(compile_one, jobs))
+    dbg_objs = [dbg_obj if os.path.basename(s) == DEBUG_SRC else o for s, o in zip(srcs, objs)]
+    for lib, lib_objs in ((LIB, objs), (DEBUG_LIB, dbg_objs)):
+        tmp = lib + ".tmp"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs])
+        os.replace(tmp, lib)
     return LIB
 
 

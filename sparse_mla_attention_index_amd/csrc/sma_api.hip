@@ -3,7 +3,9 @@
 // contract of every entry point are in include/sma.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -18,6 +20,18 @@
 // the rank's local index list and the row slices' partials.
 constexpr size_t kStaticScratchBytes = SMA_STATIC_SCRATCH_BYTES;
 static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+// Debug builds (SMA_DEBUG_CHECKS=1, libsma_debug.so): index lists and query
+// positions held in device memory are scanned before the launch that reads
+// them, and a value a release build would skip or clamp is reported as an
+// error; workspace is filled with 0xFF bytes (fp32 NaN) before use.
+#ifndef SMA_DEBUG_CHECKS
+#define SMA_DEBUG_CHECKS 0
+#endif
+#if SMA_DEBUG_CHECKS
+// index of the first out-of-range element the last check on this device found
+static __device__ unsigned long long dbg_first_bad;
+#endif
 
 namespace {
 
@@ -72,6 +86,67 @@ constexpr int32_t kMinScoreBlock = 64;   // query rows of scores the prefill wor
   do {                       \
     if (!(cond)) return fail(SMA_ERR_INVALID_ARG, __VA_ARGS__); \
   } while (0)
+
+#if SMA_DEBUG_CHECKS
+__global__ void dbg_reset_kernel(unsigned long long* first_bad) { *first_bad = ~0ull; }
+
+__global__ void dbg_range_kernel(const int32_t* v, int64_t n, int32_t lo, int32_t hi,
+                                 unsigned long long* first_bad) {
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step) {
+    const int32_t x = v[i];
+    if (x < lo || x > hi) atomicMin(first_bad, (unsigned long long)i);
+  }
+}
+
+// Reports the first of v[0 .. n) outside [lo, hi] as SMA_ERR_INVALID_ARG.
+// Synchronises `st` (debug builds only).
+sma_status dbg_range(const int32_t* v, int64_t n, int32_t lo, int32_t hi, const char* what, hipStream_t st) {
+  if (n <= 0) return SMA_OK;
+  void* addr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(dbg_first_bad));
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(dbg_first_bad)");
+  auto* first_bad = static_cast<unsigned long long*>(addr);
+  hipLaunchKernelGGL(dbg_reset_kernel, dim3(1), dim3(1), 0, st, first_bad);
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(dbg_range_kernel, dim3((unsigned)blocks), dim3(256), 0, st, v, n, lo, hi, first_bad);
+  unsigned long long first = 0;
+  e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpyAsync(&first, first_bad, sizeof first, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "debug range check");
+  if (first == ~0ull) return SMA_OK;
+  int32_t val = 0;
+  e = hipMemcpy(&val, v + first, sizeof val, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "debug range check");
+  return fail(SMA_ERR_INVALID_ARG, "debug check: %s[%llu] = %d outside [%d, %d]", what, first, (int)val, (int)lo,
+              (int)hi);
+}
+
+sma_status dbg_poison(void* ws, size_t bytes, hipStream_t st) {
+  if (ws == nullptr || bytes == 0) return SMA_OK;
+  hipError_t e = hipMemsetAsync(ws, 0xFF, bytes, st);
+  return e == hipSuccess ? SMA_OK : hip_fail(e, "debug workspace fill");
+}
+
+#define SMA_DEBUG_RANGE(v, n, lo, hi, what, st)                       \
+  do {                                                                \
+    const sma_status dbg_s = dbg_range(v, n, lo, hi, what, st);       \
+    if (dbg_s != SMA_OK) return dbg_s;                                \
+  } while (0)
+#define SMA_DEBUG_POISON(ws, bytes, st)                               \
+  do {                                                                \
+    const sma_status dbg_s = dbg_poison(ws, bytes, st);               \
+    if (dbg_s != SMA_OK) return dbg_s;                                \
+  } while (0)
+#else
+#define SMA_DEBUG_RANGE(v, n, lo, hi, what, st) \
+  do {                                          \
+  } while (0)
+#define SMA_DEBUG_POISON(ws, bytes, st) \
+  do {                                  \
+  } while (0)
+#endif
 
 sma_status validate_indexer(const void* q_idx, const float* w, int64_t w_stride, const void* k_idx,
                             const float* k_scale, int32_t k_dtype, const int32_t* q_pos, int32_t n_q,
@@ -229,6 +304,8 @@ sma_status prefill_entry(const void* q_idx, const float* q_scale, const float* w
     return fail(SMA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
   SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
   if ((s = check_device()) != SMA_OK) return s;
+  SMA_DEBUG_RANGE(q_pos, n_q, -1, (int32_t)(n_k - 1), "q_pos", (hipStream_t)stream);
+  SMA_DEBUG_POISON(ws, ws_bytes, (hipStream_t)stream);
   uint8_t* p = static_cast<uint8_t*>(ws);
   int32_t* idx = idx_out;
   if (!idx) {
@@ -314,6 +391,7 @@ sma_status sma_index_scores(const uint16_t* q_idx, const float* w, int64_t w_str
   if (n_q > 0) SMA_CHECK(scores != nullptr, "scores is NULL");
   if (n_q == 0) return SMA_OK;
   if ((s = check_device()) != SMA_OK) return s;
+  SMA_DEBUG_RANGE(q_pos, n_q, -1, (int32_t)(n_k - 1), "q_pos", (hipStream_t)stream);
   hipError_t e = sma::launch_index_scores(
       idx_args(q_idx, nullptr, w, w_stride, k_idx, k_scale, k_dtype, q_pos, n_q, n_k, h_idx, d_idx, scores,
                ld_scores),
@@ -332,6 +410,7 @@ sma_status sma_index_scores_fp8(const uint8_t* q_idx, const float* q_scale, cons
   if (n_q > 0) SMA_CHECK(scores != nullptr, "scores is NULL");
   if (n_q == 0) return SMA_OK;
   if ((s = check_device()) != SMA_OK) return s;
+  SMA_DEBUG_RANGE(q_pos, n_q, -1, (int32_t)(n_k - 1), "q_pos", (hipStream_t)stream);
   hipError_t e = sma::launch_index_scores(idx_args(q_idx, q_scale, w, w_stride, k_idx, k_scale, SMA_DT_FP8_E4M3,
                                                    q_pos, n_q, n_k, h_idx, d_idx, scores, ld_scores),
                                           (hipStream_t)stream);
@@ -398,6 +477,8 @@ sma_status sma_topk_select(const float* scores, int64_t ld_scores, const int32_t
   if (n_q == 0) return SMA_OK;
   if (ws) SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
   if ((s = check_device()) != SMA_OK) return s;
+  SMA_DEBUG_RANGE(q_pos, n_q, -1, (int32_t)(n_k - 1), "q_pos", (hipStream_t)stream);
+  SMA_DEBUG_POISON(ws, ws_bytes, (hipStream_t)stream);
   sma::TopkArgs a{scores, ld_scores, q_pos, n_q, n_k, top_k, idx, ws, ws ? ws_bytes : 0};
   hipError_t e = sma::launch_topk(a, (hipStream_t)stream);
   return e == hipSuccess ? SMA_OK : hip_fail(e, "topk launch");
@@ -414,6 +495,8 @@ sma_status sma_sparse_mla_prefill(const uint16_t* q, const void* kv, const float
   if (n_q == 0) return SMA_OK;
   if ((s = check_device()) != SMA_OK) return s;
   if (ws && !aligned(ws, 256)) return fail(SMA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  SMA_DEBUG_RANGE(idx, (int64_t)n_q * top_k, -1, (int32_t)(n_k - 1), "idx", (hipStream_t)stream);
+  SMA_DEBUG_POISON(ws, ws_bytes, (hipStream_t)stream);
   sma::MlaArgs a{q, kv, kv_scale, kv_dtype != SMA_DT_BF16, n_k, idx, n_q, top_k, sm_scale,
                  out, out_dtype == SMA_DT_FP32, lse, ws, ws ? ws_bytes : 0};
   a.ds_mla = kv_dtype == SMA_DT_FP8_DS_MLA;
@@ -441,6 +524,8 @@ sma_status sma_dense_mha_prefill(const uint16_t* q, const uint16_t* kv, const ui
   SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
   sma_status s = check_device();
   if (s != SMA_OK) return s;
+  SMA_DEBUG_RANGE(q_pos, n_q, -1, (int32_t)(n_k - 1), "q_pos", (hipStream_t)stream);
+  SMA_DEBUG_POISON(ws, ws_bytes, (hipStream_t)stream);
   sma::DenseMhaArgs a{q, kv, w_uk, w_uv, q_pos, n_q, n_k, sm_scale, out, out_dtype == SMA_DT_FP32, lse, ws};
   hipError_t e = sma::launch_dense_mha(a, (hipStream_t)stream);
   return e == hipSuccess ? SMA_OK : hip_fail(e, "dense_mha launch");
@@ -460,6 +545,8 @@ sma_status sma_dcp_shard_partial(int32_t rank, int32_t dcp_size, const uint16_t*
     return fail(SMA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws ? ws_bytes : 0, idx_bytes);
   SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
   if ((s = check_device()) != SMA_OK) return s;
+  SMA_DEBUG_RANGE(idx, (int64_t)n_q * top_k, -1, INT32_MAX, "idx", (hipStream_t)stream);
+  SMA_DEBUG_POISON(ws, ws_bytes, (hipStream_t)stream);
   return run_dcp_partial(rank, dcp_size, q, kv_local, kv_scale_local, kv_dtype, n_k_local, idx, n_q, top_k,
                          sm_scale, out_partial, lse_partial, static_cast<uint8_t*>(ws), ws_bytes,
                          (hipStream_t)stream);
@@ -482,6 +569,8 @@ sma_status sma_dcp_shard_partial_noalloc(int32_t rank, int32_t dcp_size, const u
   if ((s = check_device()) != SMA_OK) return s;
   uint8_t* ws = nullptr;
   if ((s = static_scratch(&ws)) != SMA_OK) return s;
+  SMA_DEBUG_RANGE(idx, (int64_t)n_q * top_k, -1, INT32_MAX, "idx", (hipStream_t)stream);
+  SMA_DEBUG_POISON(ws, kStaticScratchBytes, (hipStream_t)stream);
   return run_dcp_partial(rank, dcp_size, q, kv_local, kv_scale_local, kv_dtype, n_k_local, idx, n_q, top_k,
                          sm_scale, out_partial, lse_partial, ws, kStaticScratchBytes, (hipStream_t)stream);
 }
@@ -591,6 +680,7 @@ sma_status sma_pcp_rank_share(int32_t rank, int32_t pcp_size, int64_t L_total, c
   SMA_CHECK(aligned(ws, 256), "workspace not 256-byte aligned");
   if ((s = check_device()) != SMA_OK) return s;
   hipStream_t st = (hipStream_t)stream;
+  SMA_DEBUG_POISON(ws, ws_bytes, st);
   uint8_t* p = static_cast<uint8_t*>(ws);
   int32_t* pos = reinterpret_cast<int32_t*>(p);
   p += align_up((size_t)n_q * 4, 256);
@@ -609,6 +699,8 @@ sma_status sma_pcp_rank_share(int32_t rank, int32_t pcp_size, int64_t L_total, c
 const char* sma_last_error(void) { return g_err.c_str(); }
 
 int32_t sma_version(void) { return (1 << 16) | 0; }
+
+int32_t sma_build_flags(void) { return SMA_DEBUG_CHECKS ? SMA_BUILD_DEBUG_CHECKS : 0; }
 
 }  // extern "C"
 

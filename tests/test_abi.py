@@ -27,6 +27,23 @@ def test_library_exports_every_symbol():
     for name in _declared():
         assert getattr(L, name) is not None
     assert sma.version() >> 16 == 1
+    assert L.sma_build_flags() == 0
+
+
+def test_debug_library_exports_every_symbol_and_says_so():
+    """The debug build has the same entry points (same ABI version) and
+    reports its range checks in sma_build_flags; its host-side validation is
+    the release build's."""
+    D = _lib.load(_lib.DEBUG_LIB_PATH)
+    for name in _declared():
+        assert getattr(D, name) is not None
+    assert D.sma_version() == sma.lib().sma_version()
+    assert D.sma_build_flags() == _lib.SMA_BUILD_DEBUG_CHECKS
+    with _lib.debug_library():
+        assert _lib.build_flags() == _lib.SMA_BUILD_DEBUG_CHECKS
+        assert D.sma_topk_select(None, 10, None, 4, 10, 0, None, None, 0, None) == -1
+        assert "top_k" in _lib.last_error()
+    assert _lib.build_flags() == 0
 
 
 def test_workspace_sizes():
