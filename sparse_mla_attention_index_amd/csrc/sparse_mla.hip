@@ -22,6 +22,7 @@
 // accumulators, so the softmax statistics of a head and the output rows
 // they scale live in the same lanes.
 #include <algorithm>
+#include <type_traits>
 
 #include "sma_device.h"
 #include "sma_launch.h"
@@ -593,32 +594,39 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
       // weight can only exceed 2^kRefGap when `far` is set, and then the
       // sweep's results are discarded.
       const bool full = mask == 0xFFFFFFFFu;
-      const uint32_t mh = mask >> (4 * h);
-      auto row_ok = [&](int j) { return full || ((mh >> (8 * (j >> 2) + (j & 3))) & 1u); };
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, row_ok(j) ? s_own[j] : -INFINITY);
-      mx *= scale_log2;
-      {   // lanes l and l ^ 32 hold the same head: v_permlane32_swap hands each the other's value
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      if (m_ref == -INFINITY) m_ref = mx;   // first tile holding a valid row
-      m_max = fmaxf(m_max, mx);
-      far |= mx > m_ref + kRefGap;
       bf16x8 pb[2];
       float ps = 0.f;
-      const float neg_ref = -m_ref;
+      auto softmax = [&](auto masked) {
+        constexpr bool M = decltype(masked)::value;
+        const uint32_t mh = mask >> (4 * h);
+        auto row_ok = [&](int j) { return ((mh >> (8 * (j >> 2) + (j & 3))) & 1u) != 0u; };
+        float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s_own[j], scale_log2, neg_ref));
-        if (!full) pe = row_ok(j) ? pe : 0.f;
-        ps += pe;
-        if constexpr (ROW)   // PV takes the codes: the row's scale goes on its weight
-          pb[j >> 3][j & 7] = (__bf16)(pe * s_sc[t & 1][8 * (j >> 2) + 4 * h + (j & 3)]);
-        else
-          pb[j >> 3][j & 7] = (__bf16)pe;
-      }
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, !M || row_ok(j) ? s_own[j] : -INFINITY);
+        mx *= scale_log2;
+        {   // lanes l and l ^ 32 hold the same head: v_permlane32_swap hands each the other's value
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        if (m_ref == -INFINITY) m_ref = mx;   // first tile holding a valid row
+        m_max = fmaxf(m_max, mx);
+        far |= mx > m_ref + kRefGap;
+        const float neg_ref = -m_ref;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s_own[j], scale_log2, neg_ref));
+          if constexpr (M) pe = row_ok(j) ? pe : 0.f;
+          ps += pe;
+          if constexpr (ROW)   // PV takes the codes: the row's scale goes on its weight
+            pb[j >> 3][j & 7] = (__bf16)(pe * s_sc[t & 1][8 * (j >> 2) + 4 * h + (j & 3)]);
+          else
+            pb[j >> 3][j & 7] = (__bf16)pe;
+        }
+      };
+      // `full` is the same in every lane: one uniform branch keeps the row
+      // masking out of the (common) full tiles' code
+      if (full) softmax(std::false_type{});
+      else softmax(std::true_type{});
       l_run += ps;
 
       // ---- P to the partner (into the buffer just read), P of the partner's heads back ----
