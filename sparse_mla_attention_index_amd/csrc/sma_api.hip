@@ -603,11 +603,11 @@ size_t sma_workspace_bytes(int32_t op, int32_t n_q, int64_t n_k, int32_t top_k, 
       return 0;
     case SMA_OP_TOPK:   // optional: lets rows longer than 65,536 scores split across workgroups
       return sma::topk_multi_wanted(n_k) ? align_up(sma::topk_multi_bytes(n_q, n_k, top_k), 256) : 0;
-    case SMA_OP_SPARSE_MLA:   // optional: lets small FP8 batches split each query's rows
-      return align_up(sma::mla_split_bytes(n_q, sma::mla_split_count(n_q, top_k, true)), 256);
-    case SMA_OP_DCP_PARTIAL:   // the rank's local index list, then an FP8 batch's row slices
+    case SMA_OP_SPARSE_MLA:   // optional: lets small batches split each query's rows
+      return align_up(sma::mla_split_bytes(n_q, sma::mla_split_count(n_q, top_k)), 256);
+    case SMA_OP_DCP_PARTIAL:   // the rank's local index list, then a small batch's row slices
       return align_up((size_t)n_q * (size_t)top_k * 4, 256) +
-             align_up(sma::mla_split_bytes(n_q, sma::mla_split_count(n_q, top_k, true)), 256);
+             align_up(sma::mla_split_bytes(n_q, sma::mla_split_count(n_q, top_k)), 256);
     case SMA_OP_DENSE_MHA:   // the expanded keys and values, bf16
       return sma::dense_mha_ws_bytes(n_k);
     case SMA_OP_PREFILL:

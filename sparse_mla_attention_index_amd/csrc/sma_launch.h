@@ -60,9 +60,9 @@ struct MlaArgs {
   bool ds_mla = false;
 };
 
-// Number of row slices per query the FP8 attention kernel uses for n_q
+// Number of row slices per query the attention kernel uses for n_q
 // queries (1: no split), and the workspace bytes their partials take.
-int mla_split_count(int n_q, int top_k, bool fp8);
+int mla_split_count(int n_q, int top_k);
 size_t mla_split_bytes(int n_q, int n_split);
 
 hipError_t launch_index_scores(const IdxArgs& a, hipStream_t s);

@@ -747,8 +747,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
   if (lse && h == 0) lse[(int64_t)qi * kHeads + 32 * d + c32] = (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
-int mla_split_count(int n_q, int top_k, bool fp8) {
-  (void)fp8;   // every KV format splits small batches
+int mla_split_count(int n_q, int top_k) {
   if (n_q <= 0) return 1;
   const int cus = device_cu_count();
   if (n_q >= cus) return 1;
@@ -768,7 +767,7 @@ hipError_t launch_sparse_mla(const MlaArgs& A, hipStream_t st) {
   const uint8_t* kv8 = static_cast<const uint8_t*>(A.kv);
   // small batches split each query's rows across workgroups, into as many
   // slices as the workspace holds partials for (up to the preferred count)
-  int n_split = mla_split_count(A.n_q, A.top_k, true);
+  int n_split = mla_split_count(A.n_q, A.top_k);
   if (n_split > 1) {
     const size_t per_slice = mla_split_bytes(A.n_q, 2) / 2;
     const size_t fit = A.ws ? A.ws_bytes / per_slice : 0;
