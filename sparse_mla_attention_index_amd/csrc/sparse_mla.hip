@@ -35,6 +35,8 @@ constexpr int kMlaRows = 32;                // gathered rows per tile
 constexpr int kMlaPartFloats = kHeads * kDv + 2 * kHeads;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2v lds_i32x2;
 
 // Log-sum-exp merge of the n_split partials of each query: with
 // M = max_s m_s, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s and
@@ -213,23 +215,31 @@ __device__ __forceinline__ int tile_swz(int r) {
 }
 __device__ __forceinline__ constexpr int tile_block(int rg, int cg) { return (4 * cg + rg) * 1024; }
 
-// Widen 16-code pieces P0 .. P0 + 2 NI - 1 of every row of an FP8 tile
-// (dims 16 P0 .. 16 (P0 + 2 NI) - 1) from its staging slot into the bf16
-// tile.  The staging slot holds piece c of row r at byte 1024 (c >> 1) +
-// 512 (c & 1) + 16 r (the gather's load k = c >> 1, lane 32 (c & 1) + r), so
-// lane l (row l & 31, pieces P0 + (l >> 5) + 2i) reads 16 bytes at
-// 1024 (P0 / 2 + i) + 16 l; bf16 chunk cc = 2c + hh of row r goes to its
+// Eight e4m3 codes (bytes 0..7 of lo, hi) -> eight bf16 in byte order,
+// exactly (v_cvt_scalef32_pk_bf16_fp8 at scale 1: every e4m3 value is a bf16
+// value; at other scales the instruction does not round to nearest).
+__device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) {
+  u32x4 w;
+  w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false));
+  w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true));
+  w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false));
+  w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true));
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Widen the 16-code pieces P0 .. P0 + 2 NI - 1 of every row of an
+// fp8_ds_mla tile (dims 16 P0 .. 16 (P0 + 2 NI) - 1) from its staging slot
+// into the bf16 tile, each code times its row's scale of its 128-dim block
+// (bsc = the row's four scales), rounded once to bf16.  The staging slot
+// holds piece c of row r at byte 1024 (c >> 1) + 512 (c & 1) + 16 r (the
+// gather's load k = c >> 1, lane 32 (c & 1) + r), so lane l (row l & 31,
+// pieces P0 + (l >> 5) + 2i) reads 16 bytes at 1024 (P0 / 2 + i) + 16 l;
+// those pieces lie in block (P0 + 2i) >> 3 (P0 + 2i is even, so adding
+// l >> 5 stays in the block); bf16 chunk cc = 2c + hh of row r goes to its
 // block (r >> 3, cc >> 3) = (r >> 3, P0 / 4 + i / 2) at slot (cc & 7) ^
-// swz(r), cc & 7 = 4 (i & 1) + 2 (l >> 5) + hh.  The convert is
-// v_cvt_scalef32_pk_bf16_fp8 at scale 1: exact.
-//
-// With block scales (fp8_ds_mla rows, BS = true) piece c belongs to the
-// 128-dim block c >> 3, which for the pieces a lane widens is (P0 + 2 i) >> 3
-// (P0 + 2 i is even, so adding l >> 5 stays in the block); each code is
-// widened exactly to fp32, multiplied by the row's scale of that block
-// (bsc = the row's four scales) and rounded once to bf16.
-template <int P0, int NI, bool BS = false>
-__device__ __forceinline__ void widen_fp8_dims(const uint8_t* stage, uint8_t* tile, int lane, f32x4 bsc = {}) {
+// swz(r), cc & 7 = 4 (i & 1) + 2 (l >> 5) + hh.
+template <int P0, int NI>
+__device__ __forceinline__ void widen_ds_dims(const uint8_t* stage, uint8_t* tile, int lane, f32x4 bsc) {
   static_assert(P0 % 4 == 0, "pieces start at a chunk group");
   const int r = lane & 31, g = lane >> 5, sw = tile_swz(r);
   uint8_t* rowp = tile + tile_block(r >> 3, 0) + 128 * (r & 7);
@@ -241,19 +251,14 @@ __device__ __forceinline__ void widen_fp8_dims(const uint8_t* stage, uint8_t* ti
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 1024 * (P0 / 2 + i) + 16 * lane);
+    const float sc = bsc[((P0 + 2 * i) >> 3) & 3];
     uint32_t w[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if constexpr (BS) {
-        const float sc = bsc[((P0 + 2 * i) >> 3) & 3];
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], true);
-        w[2 * e] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
-        w[2 * e + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
-      } else {
-        w[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[e], 1.f, false));
-        w[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[e], 1.f, true));
-      }
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], true);
+      w[2 * e] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+      w[2 * e + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
@@ -271,31 +276,33 @@ constexpr int kDsScaleOff = 512, kDsRopeOff = 528;   // byte offsets inside a 65
 
 // FP8 rows (kKvFp8Row, kKvFp8Ds).  A tile's codes are gathered by the same
 // direct global->LDS loads into one of two staging slots (half the bytes of
-// a bf16 tile), the row scales beside them; once a tile has landed each
-// wave widens the codes of the dims it reads into the one bf16 tile, laid
-// out and swizzled as below, and QK / softmax / PV run on it unchanged
-// (wave 0 widens dims 0..287, wave 1 256..575 or 256..511; 256..287 are
-// written by both, with the same values, so the widened tile needs no
-// barrier of its own).
-//  * kKvFp8Row: 32 rows x 576 codes (18 KiB) per slot, widened by
-//    v_cvt_scalef32_pk_bf16_fp8 at scale 1 (exact: every e4m3 value is a
-//    bf16 value).  The row's scale stays out of the operands: it multiplies
-//    the row's summed logit and its softmax weight before PV (the sum of the
-//    weights, the softmax denominator, is taken unscaled).
+// a bf16 tile), the row scales beside them.
+//  * kKvFp8Row: 32 rows x 576 codes (18 KiB) per slot.  No widened copy of
+//    the tile is made: every MFMA operand is read from the staging slot as
+//    eight codes per lane and widened in registers (widen8, exact), QK's K
+//    rows by plain 8-byte reads, PV's V^T by ds_read_b64_tr_b8 (below), so
+//    the conversions overlap the matrix core instead of preceding it and
+//    the LDS carries half the bytes.  The row's scale stays out of the
+//    operands: it multiplies the row's summed logit and its softmax weight
+//    before PV (the sum of the weights, the softmax denominator, is taken
+//    unscaled).  LDS: the two slots and the S/P exchange buffer.
 //  * kKvFp8Ds: 32 rows x 512 codes (16 KiB) per slot and the rows' four
-//    block scales; each code widened as bf16(code x its block's scale), one
-//    rounding.  The 64 rope dims are stored in bf16 already: they are
-//    gathered straight into a rope buffer laid out as the bf16 tile's chunk
-//    group 8, one per ring parity (the tile being computed keeps its rope
-//    while the next tile's arrives), and wave 1's last four QK k-steps read
-//    them there.
-// LDS: bf16 tile + two staging slots fill the 72 KiB the bf16 format's two
-// tiles take (kKvFp8Ds: the codes part of the tile, 32 KiB, two 4-KiB rope
-// buffers, two 16-KiB slots).
+//    block scales.  Once a tile has landed each wave widens the codes of
+//    the dims it reads into one bf16 tile, laid out and swizzled as the
+//    bf16 format's (wave 0 dims 0..287, wave 1 256..511; 256..287 are
+//    written by both, with the same values, so the widened tile needs no
+//    barrier of its own), each code as bf16(code x its block's scale), one
+//    rounding, and QK / softmax / PV run on it as for bf16 rows.  The 64
+//    rope dims are stored in bf16 already: they are gathered straight into
+//    a rope buffer laid out as the bf16 tile's chunk group 8, one per ring
+//    parity (the tile being computed keeps its rope while the next tile's
+//    arrives), and wave 1's last four QK k-steps read them there.  LDS: the
+//    codes part of the tile, 32 KiB, two 4-KiB rope buffers, two 16-KiB
+//    slots.
 constexpr int kF8TileB = kMlaRows * kDqk;   // 18432: one tile of per-token codes
 constexpr int kDsTileB = kMlaRows * kDv;    // 16384: one tile of fp8_ds_mla codes
 constexpr int kDsStageOff = kRopeOff + 2 * 4096;   // first staging slot (after the two rope buffers)
-static_assert(kDmaTileB + 2 * kF8TileB <= 2 * kDmaTileB, "FP8 staging fits the ring");
+static_assert(2 * kF8TileB + 4096 <= 2 * kDmaTileB, "FP8 staging and exchange buffer fit the ring");
 static_assert(kDsStageOff + 2 * kDsTileB <= 2 * kDmaTileB, "fp8_ds_mla staging fits the ring");
 
 // With n_split > 1, workgroup (query, slice) covers one slice of the query's
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
     const bool ok = entry_ok(e, raw);
     const int row = ok ? raw : 0;
     const uint8_t* src = kv + (int64_t)row * kDqk + 16 * (18 * d + (lane >> 5));
-    const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)(s_ring + kDmaTileB + b * kF8TileB + 1024 * 9 * d);
+    const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)(s_ring + b * kF8TileB + 1024 * 9 * d);
 #define SMA_F8_LOAD(k) dma_load16_at<32 * (k)>(src, dst + 1024 * (k));
     SMA_F8_LOAD(0) SMA_F8_LOAD(1) SMA_F8_LOAD(2) SMA_F8_LOAD(3) SMA_F8_LOAD(4)
     SMA_F8_LOAD(5) SMA_F8_LOAD(6) SMA_F8_LOAD(7) SMA_F8_LOAD(8)
@@ -483,6 +490,23 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
       vb[e][m1] = tile_block(e, 4 * d) + 128 * (r & 7) + 16 * (c7 ^ tile_swz(r)) + 8 * (L & 1);
     }
 
+  // Per-token FP8 rows are read from their staging slot and widened operand
+  // by operand in registers.  QK's A operand (row c32, dims 288d + 16ks +
+  // 8h .. +7) is eight bytes of piece 18d + ks of the row: staging byte
+  // 9216d + 16 c32 + 8h plus 1024 (ks >> 1) + 512 (ks & 1).  PV's V^T
+  // operand comes from ds_read_b64_tr_b8: in a 16-lane group G, output lane
+  // 16G + 8p + i takes byte i of the eight-byte reads of lanes 16G + 2e + p,
+  // e = 0..7, as its elements e.  So lane s = 16G + 2e + p reads row
+  // 16kk + 8(e >> 2) + 4(G >> 1) + (e & 3) (the key order of P's registers,
+  // as the bf16 reads) at dims 256d + 32m + 16(G & 1) + 8p .. +7: staging
+  // byte 8192d + 512(G & 1) + 16 row + 8p plus 1024m + 256kk.
+  const int kb8 = 9216 * d + 16 * c32 + 8 * h;
+  int vb8;
+  {
+    const int G = lane >> 4, e = (lane & 15) >> 1, p = lane & 1;
+    vb8 = 8192 * d + 512 * (G & 1) + 16 * (8 * (e >> 2) + 4 * (G >> 1) + (e & 3)) + 8 * p;
+  }
+
   f32x16v o[kPairMt][2];
   float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.f;
 
@@ -512,20 +536,16 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
       if (t > t_beg && t % kTpc == 0 && (t / kTpc + 1) * kTpc < t_end) stage_chunk(t / kTpc + 1);
       uint32_t mask_next = 0;
       if (t + 1 < t_end) mask_next = issue_tile(t + 1, (t + 1) & 1);
-      uint8_t* tile = FP8 ? s_ring : s_ring + (t & 1) * kDmaTileB;
+      // bf16: tile t's ring slot; per-token FP8: its staging slot;
+      // fp8_ds_mla: the widened tile
+      uint8_t* tile = ROW ? s_ring + (t & 1) * kF8TileB : DS ? s_ring : s_ring + (t & 1) * kDmaTileB;
       // fp8_ds_mla: tile t's rope dims sit in the rope buffer of its parity
       const int rope_add = DS ? 4096 * (t & 1) : 0;
-      if constexpr (ROW) {
-        // the bf16 tile is free (every wave is past tile t-1, barrier above);
-        // each wave widens the dims it reads itself, so no barrier follows
-        const uint8_t* stage = s_ring + kDmaTileB + (t & 1) * kF8TileB;
-        if (d == 0) widen_fp8_dims<0, 9>(stage, tile, lane);
-        else widen_fp8_dims<16, 10>(stage, tile, lane);
-      } else if constexpr (DS) {
+      if constexpr (DS) {
         const uint8_t* stage = s_ring + kDsStageOff + (t & 1) * kDsTileB;
         const f32x4 bsc = *reinterpret_cast<const f32x4*>(&s_sc[t & 1][4 * (lane & 31)]);
-        if (d == 0) widen_fp8_dims<0, 9, true>(stage, tile, lane, bsc);
-        else widen_fp8_dims<16, 8, true>(stage, tile, lane, bsc);
+        if (d == 0) widen_ds_dims<0, 9>(stage, tile, lane, bsc);
+        else widen_ds_dims<16, 8>(stage, tile, lane, bsc);
       }
 
       // ---- partial S^T over this wave's dims, both head blocks ----
@@ -533,9 +553,14 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
       // (wave 1's k-steps 14..17 are the rope dims, chunk group 8; wave 0's
       // are code dims)
       const int rope_k = d ? rope_add : 0;
-      auto kread = [&](int ks) {
-        const int ra = ks >= kPairKs - 4 ? rope_k : 0;
-        return *reinterpret_cast<const bf16x8*>(tile + kb[ks & 3] + (ks >> 2) * 4096 + ra);
+      auto kread = [&](int ks) -> bf16x8 {
+        if constexpr (ROW) {
+          const u32x2 c = *reinterpret_cast<const u32x2*>(tile + kb8 + 1024 * (ks >> 1) + 512 * (ks & 1));
+          return widen8(c[0], c[1]);
+        } else {
+          const int ra = ks >= kPairKs - 4 ? rope_k : 0;
+          return *reinterpret_cast<const bf16x8*>(tile + kb[ks & 3] + (ks >> 2) * 4096 + ra);
+        }
       };
       f32x16v s_own, s_oth;
       bf16x8 kop[kPf];
@@ -562,8 +587,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
       mfma32_vgpr_drain1(s_oth);
 
       // ---- exchange half-sums: wave 1 writes into the (now dead) rope blocks, wave 0 into s_x ----
-      uint8_t* xw = d ? tile + kRopeOff + rope_add : s_x;   // written by this wave
-      uint8_t* xr = d ? s_x : tile + kRopeOff + rope_add;   // written by the partner
+      // (per-token FP8: a buffer of its own past the two staging slots)
+      uint8_t* xa = ROW ? s_ring + 2 * kF8TileB : tile + kRopeOff + rope_add;
+      uint8_t* xw = d ? xa : s_x;   // written by this wave
+      uint8_t* xr = d ? s_x : xa;   // written by the partner
 #pragma unroll
       for (int p = 0; p < 4; ++p)
         *reinterpret_cast<f32x4*>(xw + 1024 * p + 16 * lane) =
@@ -638,7 +665,11 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
       for (int kk = 0; kk < 2; ++kk) pq[kk] = *reinterpret_cast<const bf16x8*>(xw + 1024 * kk + 16 * lane);
 
       // ---- O^T += V^T . P^T over this wave's dims, both head blocks ----
-      auto vread = [&](int m, int kk) {
+      auto vread = [&](int m, int kk) -> bf16x8 {
+        if constexpr (ROW) {
+          const i32x2v c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tile + vb8 + 1024 * m + 256 * kk));
+          return widen8((uint32_t)c[0], (uint32_t)c[1]);
+        }
         const int off = 4096 * (m >> 1) + 2048 * kk;
         const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb[0][m & 1] + off));
         const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + vb[1][m & 1] + off));

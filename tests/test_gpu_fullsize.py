@@ -1,6 +1,7 @@
 """GPU parity at the full sizes the bench times, in its launch configuration
-(all query rows in one call): the 65,536-token prefill and the 64-query
-decode batch over a 1,048,576-token FP8 context, checked on sampled rows
+(all query rows in one call): the 16,384- and 65,536-token prefills, the
+64-query decode batch over a 1,048,576-token FP8 context and the
+131,072-token PCP8 share at ranks 0 and 7, checked on sampled rows
 against the oracle (threshold rule for the selections, attention on the
 GPU's own lists within the bf16 / FP8 tolerance)."""
 import numpy as np
@@ -37,8 +38,15 @@ def _upload(w, tensor, n, chunk, start=0):
     return out
 
 
-def test_prefill_64k_sampled_rows():
-    w = synth.workload(3)
+@pytest.mark.parametrize("cfg,rows", [
+    (2, [0, 1, 2047, 2048, 2049, 9999, 16382, 16383]),
+    (3, [0, 2046, 2047, 2048, 31337, 65534, 65535]),
+])
+def test_prefill_full_size_sampled_rows(cfg, rows):
+    """The 16K and 64K prompts: rows at both ends, and on both sides of the
+    point where the causal prefix outgrows top_k (from 2,048 keys on, the
+    selection is a strict subset)."""
+    w = synth.workload(cfg)
     n = w.n_keys
     k_idx = _upload(w, "k_idx", n, 65536)
     kv = _upload(w, "kv", n, 16384)
@@ -53,7 +61,7 @@ def test_prefill_64k_sampled_rows():
                               workspace=ws)
     del ws
     torch.cuda.synchronize()
-    rows = np.array([0, 2046, 2047, 2048, 31337, 65534, 65535])
+    rows = np.array(rows)
     sel = torch.from_numpy(rows).to("cuda:0")
     f = oracle.bf16_bits_to_f64
     kk = f(host(k_idx).view(np.uint16))
