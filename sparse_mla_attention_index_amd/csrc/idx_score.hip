@@ -402,6 +402,10 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_kernel(
 // tile has landed, the workgroup widens its codes to bf16 (the hardware
 // convert, exact) into one of two bf16 tiles laid out and swizzled as above,
 // so the MFMA loop is unchanged; the key's scale multiplies the head sum.
+// The convert is v_cvt_scalef32_pk_bf16_fp8 at scale 1 (exact), and the
+// barrier that orders a tile's widening before its B-operand reads sits
+// between the previous tile's two N-tiles, so the widening overlaps the
+// first N-tile's MFMAs instead of stalling every wave before them.
 // ---------------------------------------------------------------------------
 constexpr int kF8kTileB = kIdxKT * 128;   // 8 KiB of codes per 64-key tile
 
@@ -469,10 +473,8 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_f8k_kernel(
     uint32_t packed[8];
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[wd], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[wd], true);
-      packed[2 * wd] = pack_bf16x2(lo[0], lo[1]);
-      packed[2 * wd + 1] = pack_bf16x2(hi[0], hi[1]);
+      packed[2 * wd] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[wd], 1.f, false));
+      packed[2 * wd + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[wd], 1.f, true));
     }
     uint8_t* row = &s_k[i & 1][key * 256];
     *reinterpret_cast<u32x4*>(row + 16 * ((2 * c) ^ (key & 15))) = u32x4{packed[0], packed[1], packed[2], packed[3]};
@@ -517,7 +519,6 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_f8k_kernel(
     idx_wait_vmcnt<(kIdxStages - 3) * kLoads>();
     idx_sync_lds();             // tile i + 1 landed; bf16 tile (i + 1) & 1 is no longer read
     widen(i + 1);               // past the range this widens clamped keys, never stored
-    idx_sync_lds();
     issue(i + kIdxStages - 1);  // into slot (i - 1) % kIdxStages, whose codes were widened at i - 2
     const uint8_t* tile = s_k[i & 1];
     const int slot = i % kIdxStages;
@@ -551,6 +552,7 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_f8k_kernel(
         __builtin_amdgcn_sched_group_barrier(0x0002, 4, 0);   // VALU
         __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
       }
+      if (u == 0) idx_sync_lds();   // tile i + 1 widened before the last N-tile reads it
     }
   }
   epilogue(acc[(kIdxKT / 32 - 1) & 1][0], acc[(kIdxKT / 32 - 1) & 1][1], prev_key, prev_sc);
