@@ -228,7 +228,7 @@ sma::IdxArgs idx_args(const void* q_idx, const float* q_scale, const float* w, i
 // buffers.
 size_t score_block_bytes(int64_t qb, int64_t n_k, int32_t top_k) {
   size_t b = align_up((size_t)qb * (size_t)n_k * 4, 256);
-  if (sma::topk_multi_wanted(n_k)) b += align_up(sma::topk_multi_bytes((int32_t)qb, n_k, top_k), 256);
+  if (sma::topk_long_wanted(n_k)) b += align_up(sma::topk_long_bytes((int32_t)qb, n_k, top_k), 256);
   return b;
 }
 
@@ -602,7 +602,7 @@ size_t sma_workspace_bytes(int32_t op, int32_t n_q, int64_t n_k, int32_t top_k, 
     case SMA_OP_INDEX_SCORES:
       return 0;
     case SMA_OP_TOPK:   // optional: lets rows longer than 65,536 scores split across workgroups
-      return sma::topk_multi_wanted(n_k) ? align_up(sma::topk_multi_bytes(n_q, n_k, top_k), 256) : 0;
+      return sma::topk_long_wanted(n_k) ? align_up(sma::topk_long_bytes(n_q, n_k, top_k), 256) : 0;
     case SMA_OP_SPARSE_MLA:   // optional: lets small batches split each query's rows
       return align_up(sma::mla_split_bytes(n_q, sma::mla_split_count(n_q, top_k)), 256);
     case SMA_OP_DCP_PARTIAL:   // the rank's local index list, then a small batch's row slices

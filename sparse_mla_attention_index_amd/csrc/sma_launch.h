@@ -70,11 +70,11 @@ hipError_t launch_index_scores(const IdxArgs& a, hipStream_t s);
 hipError_t launch_quantize_fp8_rows(const uint16_t* x, int64_t n_rows, int d, uint8_t* codes, float* scale,
                                     hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
-// Rows longer than the on-chip top-k holds (n_k > 65,536) are split across
-// workgroups when the workspace holds topk_multi_bytes(n_q, n_k, top_k).
-bool topk_multi_wanted(int64_t n_k);
-size_t topk_multi_bytes(int32_t n_q, int64_t n_k, int32_t top_k);
-hipError_t launch_topk_multi(const TopkArgs& a, void* ws, hipStream_t s);
+// Rows longer than 65,536 scores, when too few to fill the device one per
+// workgroup, are split across workgroups if the workspace holds
+// topk_long_bytes(n_q, n_k, top_k).
+bool topk_long_wanted(int64_t n_k);
+size_t topk_long_bytes(int32_t n_q, int64_t n_k, int32_t top_k);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t s);
 
 // DCP share: the tokens of a query's selection that rank `rank` of P stores

@@ -24,8 +24,9 @@
 //     a block-wide prefix count, so the output is ascending by position.
 // Aligned rows of at most 65,536 scores first keep only the positions at or
 // above a threshold sampled from the row, in one pass, and run steps 2-3 on
-// those (topk_filter_kernel below); rows longer than 65,536 scores are split
-// across workgroups when a workspace is given (topk_multi.hip).
+// those (topk_filter_kernel below); rows longer than 65,536 scores, too few
+// to fill the device one per workgroup, are split across workgroups when a
+// workspace is given (topk_long_* below).
 #include "sma_device.h"
 #include "sma_launch.h"
 
@@ -399,6 +400,84 @@ __device__ uint32_t ft_round(const uint32_t (&key)[M], uint32_t& lo, uint32_t& h
   return in_bin;
 }
 
+// Steps 3-4 of the filtered top-k: the K largest of C kept entries (K <= C
+// <= KEEP * kFtThreads; raw score bits ckey[i] of ascending positions
+// cpos[i], no NaN among them), written to out in ascending position order.
+// Called by the whole kFtThreads-thread workgroup.
+template <typename PosT, int KEEP>
+__device__ void ft_select_kept(const uint32_t* ckey, const PosT* cpos, int C, int K, int32_t* __restrict__ out,
+                               TopkShared<kFtThreads>& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // ---- 3. exact threshold key T among the kept keys ----
+  uint32_t kk[KEEP];
+#pragma unroll
+  for (int j = 0; j < KEEP; ++j) {
+    const int i = tid + kFtThreads * j;
+    kk[j] = i < C ? score_key(__uint_as_float(ckey[i])) : 0u;
+  }
+  uint32_t lo, hi, need_ties = (uint32_t)K;
+  ft_range<KEEP>(kk, lo, hi, sh);
+  for (int round = 0; round < 3 && hi != lo; ++round) {
+    const uint32_t in_bin = ft_round<KEEP>(kk, lo, hi, need_ties, sh);
+    if (hi != lo && in_bin <= 64) {
+      // one wave ranks the bin's keys: T has fewer than need_ties of them
+      // above it and at least need_ties at or above it
+      uint32_t* list = sh.hist;
+      if (tid == 0) sh.bcast[3] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < KEEP; ++j)
+        if (kk[j] >= lo && kk[j] <= hi) list[atomicAdd(&sh.bcast[3], 1u)] = kk[j];
+      __syncthreads();
+      if (wave == 0) {
+        const int nb = (int)in_bin;
+        const uint32_t x = lane < nb ? list[lane] : 0u;
+        uint32_t gt = 0, ge = 0;
+        for (int j = 0; j < nb; ++j) {
+          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
+          gt += y > x;
+          ge += y >= x;
+        }
+        if (lane < nb && gt < need_ties && need_ties <= ge) {   // every such lane holds T
+          sh.bcast[0] = x;
+          sh.bcast[1] = need_ties - gt;
+        }
+      }
+      __syncthreads();
+      lo = hi = sh.bcast[0];
+      need_ties = sh.bcast[1];
+      __syncthreads();
+    }
+  }
+  const uint32_t T = lo;
+
+  // ---- 4. ordered compaction: thread t owns kept entries [t*M, t*M + M) ----
+  // (kept scores are never NaN, so comparing them as floats with T's score
+  // orders them as their keys do, -0.0 == +0.0 included)
+  const float Tf = key_score(T);
+  const int M = (C + kFtThreads - 1) / kFtThreads;
+  const int i0 = min(C, tid * M), i1 = min(C, i0 + M);
+  uint32_t cg = 0, ce = 0;
+  for (int i = i0; i < i1; ++i) {
+    const float v = __uint_as_float(ckey[i]);
+    cg += v > Tf;
+    ce += v == Tf;
+  }
+  uint32_t g_before, e_before, tg, te;
+  block_excl_scan2<kFtThreads>(cg, ce, g_before, e_before, tg, te, sh);
+  for (int i = i0; i < i1; ++i) {
+    const float v = __uint_as_float(ckey[i]);
+    if (v > Tf) {
+      const uint32_t slot = g_before + min(e_before, need_ties);
+      if (slot < (uint32_t)K) out[slot] = cpos[i];
+      ++g_before;
+    } else if (v == Tf) {
+      if (e_before < need_ties && g_before + e_before < (uint32_t)K) out[g_before + e_before] = cpos[i];
+      ++e_before;
+    }
+  }
+}
+
 // PosT holds a position (uint16_t for rows of at most 65,536 scores); SPT
 // samples per thread (SPT * 256 in all).
 template <typename PosT, int SPT, int OCC>
@@ -531,78 +610,258 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
     return;
   }
 
-  // ---- 3. exact threshold key T among the kept keys ----
-  const int C = (int)kept;
-  uint32_t kk[kFtKeep];
-#pragma unroll
-  for (int j = 0; j < kFtKeep; ++j) {
-    const int i = tid + kFtThreads * j;
-    kk[j] = i < C ? score_key(__uint_as_float(ckey[i])) : 0u;
-  }
-  uint32_t lo, hi, need_ties = (uint32_t)K;
-  ft_range<kFtKeep>(kk, lo, hi, sh);
-  for (int round = 0; round < 3 && hi != lo; ++round) {
-    const uint32_t in_bin = ft_round<kFtKeep>(kk, lo, hi, need_ties, sh);
-    if (hi != lo && in_bin <= 64) {
-      // one wave ranks the bin's keys: T has fewer than need_ties of them
-      // above it and at least need_ties at or above it
-      uint32_t* list = sh.hist;
-      if (tid == 0) sh.bcast[3] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kFtKeep; ++j)
-        if (kk[j] >= lo && kk[j] <= hi) list[atomicAdd(&sh.bcast[3], 1u)] = kk[j];
-      __syncthreads();
-      if (wave == 0) {
-        const int nb = (int)in_bin;
-        const uint32_t x = lane < nb ? list[lane] : 0u;
-        uint32_t gt = 0, ge = 0;
-        for (int j = 0; j < nb; ++j) {
-          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
-          gt += y > x;
-          ge += y >= x;
-        }
-        if (lane < nb && gt < need_ties && need_ties <= ge) {   // every such lane holds T
-          sh.bcast[0] = x;
-          sh.bcast[1] = need_ties - gt;
-        }
-      }
-      __syncthreads();
-      lo = hi = sh.bcast[0];
-      need_ties = sh.bcast[1];
-      __syncthreads();
-    }
-  }
-  const uint32_t T = lo;
-
-  // ---- 4. ordered compaction: thread t owns kept entries [t*M, t*M + M) ----
-  // (kept scores are never NaN, so comparing them as floats with T's score
-  // orders them as their keys do, -0.0 == +0.0 included)
-  const float Tf = key_score(T);
-  const int M = (C + kFtThreads - 1) / kFtThreads;
-  const int i0 = min(C, tid * M), i1 = min(C, i0 + M);
-  uint32_t cg = 0, ce = 0;
-  for (int i = i0; i < i1; ++i) {
-    const float v = __uint_as_float(ckey[i]);
-    cg += v > Tf;
-    ce += v == Tf;
-  }
-  uint32_t g_before, e_before, tg, te;
-  block_excl_scan2<kFtThreads>(cg, ce, g_before, e_before, tg, te, sh);
-  for (int i = i0; i < i1; ++i) {
-    const float v = __uint_as_float(ckey[i]);
-    if (v > Tf) {
-      const uint32_t slot = g_before + min(e_before, need_ties);
-      if (slot < (uint32_t)K) out[slot] = cpos[i];
-      ++g_before;
-    } else if (v == Tf) {
-      if (e_before < need_ties && g_before + e_before < (uint32_t)K) out[g_before + e_before] = cpos[i];
-      ++e_before;
-    }
-  }
+  ft_select_kept<PosT, kFtKeep>(ckey, cpos, (int)kept, K, out, sh);
 }
 
-bool topk_multi_wanted(int64_t n_k) { return n_k > 4 * 1024 * 16; }
+// ---------------------------------------------------------------------------
+// Long rows split across workgroups: rows of more than 65,536 scores when
+// there are too few of them to fill the device with one workgroup per row
+// (a decode batch of 64 rows of ~1M scores).  One pass over each row:
+//  1. topk_long_sample: one workgroup per row takes the filtered kernel's
+//     threshold (step 1 above) from kLgSamples samples, 1,024 clusters of 16
+//     consecutive scores spread evenly over the row, and stores it;
+//  2. topk_long_filter: one workgroup per kLgChunk-score chunk of a row keeps,
+//     as step 2 does, every position whose score is at or above the row's
+//     threshold, in ascending order, into the chunk's list in the workspace
+//     ((position, score bits); the first kLgChunkCap) with its count;
+//  3. topk_long_final: one workgroup per row concatenates its chunks' lists
+//     in chunk order and runs steps 3-4 on them.  A row that kept fewer than
+//     K or more than kLgCap, or a chunk more than kLgChunkCap, is redone by
+//     the streaming selection in that workgroup, so the result is exact.
+// With 16,384 samples a row of 1M scores keeps about 4,000 +- 500 (K =
+// 2,048); a row of at most kLgCap scores keeps all of them.
+// ---------------------------------------------------------------------------
+constexpr int kLgChunk = 2 * kFtChunk;                 // 16,384 positions per chunk workgroup
+constexpr int kLgClusters = 1024;
+constexpr int kLgSamples = kLgClusters * kFtClusterLen;   // 16,384
+constexpr int kLgSPT = kLgSamples / kFtThreads;          // 64: four clusters per thread
+constexpr int kLgCap = 8192;                           // kept entries a row's final workgroup holds
+constexpr int kLgKeep = kLgCap / kFtThreads;            // 32 per thread
+constexpr int kLgChunkCap = 4096;                      // kept entries a chunk's list holds
+
+__device__ __forceinline__ int lg_row_len(const int32_t* q_pos, int row, int n_k) {
+  int p = q_pos[row];
+  p = p < -1 ? -1 : (p > n_k - 1 ? n_k - 1 : p);
+  return p + 1;
+}
+
+template <bool ALIGNED>
+__global__ __launch_bounds__(kFtThreads) void topk_long_sample(const float* __restrict__ scores, int64_t ld,
+                                                               const int32_t* __restrict__ q_pos, int n_k, int K,
+                                                               float* __restrict__ thr) {
+  __shared__ TopkShared<kFtThreads> sh;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int n = lg_row_len(q_pos, row, n_k);
+  if (n <= kLgCap) {   // keeps every score (a row of at most K scores takes them all in step 3)
+    if (tid == 0) thr[row] = -INFINITY;
+    return;
+  }
+  const float* src = scores + (int64_t)row * ld;
+  uint32_t sk[kLgSPT];
+#pragma unroll
+  for (int q = 0; q < kLgSPT / kFtClusterLen; ++q) {
+    const int c = tid * (kLgSPT / kFtClusterLen) + q;
+    const int start = (int)(((int64_t)c * (n - kFtClusterLen)) / (kLgClusters - 1)) & ~3;
+#pragma unroll
+    for (int v = 0; v < kFtClusterLen / 4; ++v) {
+      f32x4 x;
+      if constexpr (ALIGNED) {
+        x = *reinterpret_cast<const f32x4*>(src + start + 4 * v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = src[start + 4 * v + e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sk[kFtClusterLen * q + 4 * v + e] = score_key(x[e]);
+    }
+  }
+  const float mu = (float)K * (float)kLgSamples / (float)n;
+  const uint32_t r0 = (uint32_t)fminf(ceilf(1.3f * mu + 3.f * sqrtf(mu) + 4.f), (float)kLgSamples);
+  uint32_t lo, hi, rem = r0;
+  ft_range<kLgSPT>(sk, lo, hi, sh);
+  if (hi != lo) ft_round<kLgSPT>(sk, lo, hi, rem, sh);
+  if (tid == 0) thr[row] = key_score(lo);   // at least r0 samples lie at or above it
+}
+
+template <bool ALIGNED>
+__global__ __launch_bounds__(kFtThreads) void topk_long_filter(const float* __restrict__ scores, int64_t ld,
+                                                               const int32_t* __restrict__ q_pos, int n_k, int K,
+                                                               const float* __restrict__ thr, int nch,
+                                                               uint2* __restrict__ list, uint32_t* __restrict__ cnt) {
+  __shared__ uint32_t tab[2][kFtWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.y, chunk = blockIdx.x;
+  const int n = lg_row_len(q_pos, row, n_k);
+  const int64_t slot0 = (int64_t)row * nch + chunk;
+  const int cbeg = chunk * kLgChunk;
+  if (n <= K || cbeg >= n) {
+    if (tid == 0) cnt[slot0] = 0u;
+    return;
+  }
+  const float t = thr[row];
+  const float* src = scores + (int64_t)row * ld;
+  uint2* my = list + slot0 * kLgChunkCap;
+  // Wave w's step u of the 8,192-position half at c0 covers c0 + 2048w +
+  // 256u .. + 255, lane l the four at + 4l; positions at or past n read as
+  // NaN, which no threshold keeps.
+  auto load = [&](int c0, f32x4 (&x)[kFtU]) {
+    const int pw = c0 + kFtWaveSpan * wave + 4 * lane;
+#pragma unroll
+    for (int u = 0; u < kFtU; ++u) {
+      const int p0 = pw + 256 * u;
+      if (ALIGNED && p0 + 3 < n) {
+        x[u] = *reinterpret_cast<const f32x4*>(src + p0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[u][e] = p0 + e < n ? src[p0 + e] : __builtin_nanf("");
+      }
+    }
+  };
+  f32x4 xa[kFtU], xb[kFtU];
+  load(cbeg, xa);
+  if (cbeg + kFtChunk < n) load(cbeg + kFtChunk, xb);
+  uint32_t kept = 0;
+  auto step = [&](int c0, int ci, f32x4 (&x)[kFtU]) {
+    uint32_t off[kFtU];
+    uint32_t wcnt = 0;
+#pragma unroll
+    for (int u = 0; u < kFtU; ++u) {
+      uint32_t o = wcnt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint64_t m = __ballot(x[u][e] >= t);
+        o = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, o));
+        wcnt += (uint32_t)__popcll(m);
+      }
+      off[u] = o;
+    }
+    if (lane == 0) tab[ci][wave] = wcnt;
+    __syncthreads();
+    uint32_t base = kept, all = 0;
+#pragma unroll
+    for (int w = 0; w < kFtWaves; ++w) {
+      const uint32_t v = tab[ci][w];
+      base += w < wave ? v : 0u;
+      all += v;
+    }
+    const int pw = c0 + kFtWaveSpan * wave + 4 * lane;
+#pragma unroll
+    for (int u = 0; u < kFtU; ++u) {
+      uint32_t slot = base + off[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (x[u][e] >= t) {
+          if (slot < (uint32_t)kLgChunkCap) my[slot] = make_uint2((uint32_t)(pw + 256 * u + e), __float_as_uint(x[u][e]));
+          ++slot;
+        }
+      }
+    }
+    kept += all;
+  };
+  step(cbeg, 0, xa);
+  if (cbeg + kFtChunk < n) step(cbeg + kFtChunk, 1, xb);
+  if (tid == 0) cnt[slot0] = kept;
+}
+
+__global__ __launch_bounds__(kFtThreads) void topk_long_final(const float* __restrict__ scores, int64_t ld,
+                                                              const int32_t* __restrict__ q_pos, int n_k, int K,
+                                                              int nch, const uint2* __restrict__ list,
+                                                              const uint32_t* __restrict__ cnt,
+                                                              int32_t* __restrict__ idx) {
+  __shared__ TopkShared<kFtThreads> sh;
+  __shared__ uint32_t ckey[kLgCap];   // kept score bits (the streaming fallback's scratch)
+  __shared__ int32_t cpos[kLgCap];    // kept positions, ascending
+  __shared__ uint32_t s_off[kFtThreads];
+  __shared__ uint32_t s_fail;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int n = lg_row_len(q_pos, row, n_k);
+  int32_t* out = idx + (int64_t)row * K;
+  const float* src = scores + (int64_t)row * ld;
+  if (n <= K) {
+    for (int e = tid; e < K; e += kFtThreads) out[e] = e < n ? e : -1;
+    return;
+  }
+  const int nc = (n + kLgChunk - 1) / kLgChunk;
+  const uint32_t* rc = cnt + (int64_t)row * nch;
+  const uint2* rl = list + (int64_t)row * nch * kLgChunkCap;
+  if (tid == 0) s_fail = 0u;
+  __syncthreads();
+  // Concatenate the chunks' lists, kFtThreads chunks at a time: their counts
+  // are scanned first, then entry g of the group lies in the last chunk whose
+  // offset is <= g (an empty chunk shares its offset with the next one).
+  uint32_t total = 0;
+  for (int g0 = 0; g0 < nc; g0 += kFtThreads) {
+    const int c = g0 + tid;
+    const uint32_t v = c < nc ? rc[c] : 0u;
+    if (v > (uint32_t)kLgChunkCap) s_fail = 1u;
+    uint32_t ex, e2, tv, t2;
+    block_excl_scan2<kFtThreads>(v, 0u, ex, e2, tv, t2, sh);
+    s_off[tid] = total + ex;
+    __syncthreads();
+    if (s_fail || total + tv > (uint32_t)kLgCap) {
+      total += tv;
+      break;
+    }
+    const int gn = min(kFtThreads, nc - g0);
+    for (uint32_t g = total + tid; g < total + tv; g += kFtThreads) {
+      int lo = 0, hi = gn - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= g) lo = mid;
+        else hi = mid - 1;
+      }
+      const uint2 e = rl[(int64_t)(g0 + lo) * kLgChunkCap + (g - s_off[lo])];
+      cpos[g] = (int32_t)e.x;
+      ckey[g] = e.y;
+    }
+    total += tv;
+    __syncthreads();
+  }
+  __syncthreads();
+  if (s_fail || total < (uint32_t)K || total > (uint32_t)kLgCap) {   // threshold too high, or too many kept
+    topk_stream_row<kFtThreads>(src, n, K, out, sh, ckey);
+    return;
+  }
+  ft_select_kept<int32_t, kLgKeep>(ckey, cpos, (int)total, K, out, sh);
+}
+
+bool topk_long_wanted(int64_t n_k) { return n_k > 65536; }
+
+size_t topk_long_bytes(int32_t n_q, int64_t n_k, int32_t top_k) {
+  (void)top_k;
+  if (n_q <= 0 || n_k <= 0) return 0;
+  const int64_t nch = (n_k + kLgChunk - 1) / kLgChunk;
+  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+  return al((size_t)n_q * 4) + al((size_t)n_q * nch * 4) + al((size_t)n_q * nch * kLgChunkCap * 8);
+}
+
+static hipError_t launch_topk_long(const TopkArgs& A, bool aligned, hipStream_t st) {
+  const int nch = (int)((A.n_k + kLgChunk - 1) / kLgChunk);
+  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+  uint8_t* p = static_cast<uint8_t*>(A.ws);
+  float* thr = reinterpret_cast<float*>(p);
+  p += al((size_t)A.n_q * 4);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(p);
+  p += al((size_t)A.n_q * nch * 4);
+  uint2* list = reinterpret_cast<uint2*>(p);
+  const dim3 rows((unsigned)A.n_q), chunks((unsigned)nch, (unsigned)A.n_q);
+  if (aligned) {
+    hipLaunchKernelGGL(topk_long_sample<true>, rows, dim3(kFtThreads), 0, st, A.scores, A.ld, A.q_pos, (int)A.n_k,
+                       A.top_k, thr);
+    hipLaunchKernelGGL(topk_long_filter<true>, chunks, dim3(kFtThreads), 0, st, A.scores, A.ld, A.q_pos,
+                       (int)A.n_k, A.top_k, thr, nch, list, cnt);
+  } else {
+    hipLaunchKernelGGL(topk_long_sample<false>, rows, dim3(kFtThreads), 0, st, A.scores, A.ld, A.q_pos,
+                       (int)A.n_k, A.top_k, thr);
+    hipLaunchKernelGGL(topk_long_filter<false>, chunks, dim3(kFtThreads), 0, st, A.scores, A.ld, A.q_pos,
+                       (int)A.n_k, A.top_k, thr, nch, list, cnt);
+  }
+  hipLaunchKernelGGL(topk_long_final, rows, dim3(kFtThreads), 0, st, A.scores, A.ld, A.q_pos, (int)A.n_k, A.top_k,
+                     nch, list, cnt, A.idx);
+  return hipGetLastError();
+}
+
+
 
 hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   if (A.n_q <= 0) return hipSuccess;
@@ -620,8 +879,8 @@ hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
                        A.q_pos, (int)A.n_k, A.top_k, A.idx);
     return hipGetLastError();
   }
-  if (topk_multi_wanted(A.n_k) && A.ws && A.ws_bytes >= topk_multi_bytes(A.n_q, A.n_k, A.top_k))
-    return launch_topk_multi(A, A.ws, st);
+  if (topk_long_wanted(A.n_k) && A.ws && A.ws_bytes >= topk_long_bytes(A.n_q, A.n_k, A.top_k))
+    return launch_topk_long(A, rows_aligned, st);
   // 16-byte aligned rows of up to 65,536 scores take the filtered kernel
   // (one pass over the row); longer or unaligned rows are streamed from
   // memory in every pass.

@@ -50,11 +50,12 @@ def test_workspace_sizes():
     # prefill: idx list + one 64-row score block (256-byte aligned pieces)
     assert sma.workspace_bytes(_lib.SMA_OP_PREFILL, 65536, 65536, 2048) == 65536 * 2048 * 4 + 64 * 65536 * 4
     # rows longer than 65,536 scores: the 64-row block also holds the split
-    # top-k's buffers (per row: 32-B state, 2,048-bin histogram, and per
-    # 16,384-score chunk two counts, top_k positions and top_k (position, key))
+    # top-k's buffers (per row a threshold, and per 16,384-score chunk a count
+    # and a list of up to 4,096 (position, score) pairs), each 256-aligned
     def split_topk(n_q, n_k, k):
         nch = -(-n_k // 16384)
-        return n_q * 32 + n_q * 2048 * 4 + n_q * nch * 8 + n_q * nch * k * 4 + n_q * nch * k * 8
+        al = lambda b: -(-b // 256) * 256
+        return al(n_q * 4) + al(n_q * nch * 4) + al(n_q * nch * 4096 * 8)
     assert sma.workspace_bytes(_lib.SMA_OP_PCP_SHARE, 16384, 131072, 2048) == \
         16384 * 4 + 16384 * 2048 * 4 + 64 * 131072 * 4 + split_topk(64, 131072, 2048)
     assert sma.workspace_bytes(_lib.SMA_OP_TOPK, 10, 10, 5) == 0

@@ -101,3 +101,50 @@ def test_topk_misleading_sample():
     got = host(sma.topk_select(dev(sc), dev(pos), top_k))
     for r in range(4):
         assert np.array_equal(got[r], oracle.topk_row(sc[r, : pos[r] + 1], top_k)), r
+
+
+def _long_sampled_positions(n, n_clusters=1024, cluster=16):
+    """Positions the split top-k samples in a row of n > 8,192 scores: 1,024
+    clusters of 16 consecutive scores whose starts are spread evenly over the
+    row (rounded down to a multiple of 4)."""
+    starts = [((c * (n - cluster)) // (n_clusters - 1)) & ~3 for c in range(n_clusters)]
+    return np.unique(np.concatenate([np.arange(s, s + cluster) for s in starts]))
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "nan_heavy"])
+def test_topk_few_very_long_rows(kind):
+    """A decode-shaped batch: 16 rows of up to 1,048,576 scores, too few to
+    fill the device one per workgroup (the split path: one sampled threshold
+    per row, one filtering pass by 16,384-score chunks, the exact selection
+    over what was kept).  Ties and NaN-heavy rows keep too many or too few
+    and are redone by the streaming selection."""
+    n_rows, n_k, top_k = 16, 1 << 20, 2048
+    sc = synth.random_scores(31 + len(kind), n_rows, n_k, kind)
+    rng = np.random.default_rng(9)
+    pos = rng.integers(900_000, n_k, size=n_rows).astype(np.int32)
+    pos[:6] = [n_k - 1, 8191, 8192, 2047, 16383, 16384]
+    got = host(sma.topk_select(dev(sc), dev(pos), top_k))
+    for r in range(n_rows):
+        assert np.array_equal(got[r], oracle.topk_row(sc[r, : pos[r] + 1], top_k)), (kind, r, pos[r])
+
+
+def test_topk_long_misleading_sample():
+    """Long rows whose sample misleads the split path's threshold: every
+    unsampled score above all sampled ones (far more than 8,192 kept), the
+    samples holding the largest scores (fewer than K kept), 4,500 unsampled
+    scores of one chunk raised (that chunk keeps more than its 4,096-entry
+    list while the row keeps fewer than 8,192), beside an ordinary row.  Each
+    is redone by the streaming selection or selected exactly."""
+    n_k, top_k = 200000, 2048
+    rng = np.random.default_rng(23)
+    sc = rng.random((4, n_k)).astype(np.float32)
+    samp = _long_sampled_positions(n_k)
+    rest = np.setdiff1d(np.arange(n_k), samp)
+    sc[0, rest] += 10.0
+    sc[1, samp] += 10.0
+    chunk3 = rest[(rest >= 3 * 16384) & (rest < 4 * 16384)]
+    sc[2, chunk3[:4500]] += 10.0
+    pos = np.array([n_k - 1, n_k - 1, n_k - 1, 150001], dtype=np.int32)
+    got = host(sma.topk_select(dev(sc), dev(pos), top_k))
+    for r in range(4):
+        assert np.array_equal(got[r], oracle.topk_row(sc[r, : pos[r] + 1], top_k)), r
