@@ -286,8 +286,10 @@ __global__ __launch_bounds__(THREADS, 1) void topk_stream_kernel(const float* __
 //  1. a row longer than kFtCap takes a threshold from a sample of itself:
 //     S/16 clusters of 16 consecutive scores spread evenly over the row (S =
 //     2,048 or 4,096 samples).  One 2,048-bin histogram over the samples' key
-//     range finds the bin holding the r0-th largest sample; its lower edge is
-//     the threshold, r0 chosen so that about 1.3 mu + 3 sqrt(mu) samples lie at
+//     range finds the bin holding the r0-th largest sample (a second one
+//     within that bin when it holds more than kFtRefineBin samples, as with
+//     scores of both signs, whose keys lie far apart); its lower edge is the
+//     threshold, r0 chosen so that about 1.3 mu + 3 sqrt(mu) samples lie at
 //     or above it (mu = K * S / n, the samples expected among the row's K
 //     largest).  A shorter row keeps every key;
 //  2. one coalesced pass keeps every position whose score is at or above the
@@ -312,6 +314,7 @@ constexpr int kFtChunk = kFtThreads * 4 * kFtU;   // 8,192 positions
 constexpr int kFtWaveSpan = 256 * kFtU;           // a wave's contiguous share of a chunk
 constexpr int kFtKeep = kFtCap / kFtThreads;      // kept keys per thread in the final select
 constexpr int64_t kFtLongMax = 1 << 18;           // longest rows the filtered kernel takes
+constexpr uint32_t kFtRefineBin = 32;             // samples in the threshold's bin that call for a second round
 
 // The score whose key is k (the inverse of score_key for finite scores).
 __device__ __forceinline__ float key_score(uint32_t k) {
@@ -545,7 +548,12 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
     const uint32_t r0 = (uint32_t)fminf(ceilf(1.3f * mu + 3.f * sqrtf(mu) + 4.f), (float)kSamples);
     uint32_t lo, hi, rem = r0;
     ft_range<SPT>(sk, lo, hi, sh);
-    if (hi != lo) ft_round<SPT>(sk, lo, hi, rem, sh);
+    if (hi != lo) {
+      // a key range spanning both signs leaves coarse bins near the top:
+      // one more round when the kept bin holds many samples
+      const uint32_t in_bin = ft_round<SPT>(sk, lo, hi, rem, sh);
+      if (hi != lo && in_bin > kFtRefineBin) ft_round<SPT>(sk, lo, hi, rem, sh);
+    }
     thr = key_score(lo);   // at least r0 samples lie at or above it
   }
 
@@ -679,7 +687,10 @@ __global__ __launch_bounds__(kFtThreads) void topk_long_sample(const float* __re
   const uint32_t r0 = (uint32_t)fminf(ceilf(1.3f * mu + 3.f * sqrtf(mu) + 4.f), (float)kLgSamples);
   uint32_t lo, hi, rem = r0;
   ft_range<kLgSPT>(sk, lo, hi, sh);
-  if (hi != lo) ft_round<kLgSPT>(sk, lo, hi, rem, sh);
+  if (hi != lo) {
+    const uint32_t in_bin = ft_round<kLgSPT>(sk, lo, hi, rem, sh);
+    if (hi != lo && in_bin > kFtRefineBin) ft_round<kLgSPT>(sk, lo, hi, rem, sh);
+  }
   if (tid == 0) thr[row] = key_score(lo);   // at least r0 samples lie at or above it
 }
 
