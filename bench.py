@@ -386,6 +386,23 @@ def run_workload(name, args, headline):
               "project_out_frac_hbm": round(b_po / (t_po * 1e-3) / 1e9 / acc.PEAK_HBM_GBS, 4)}
         _log(f"absorption: absorb_q {t_aq:.3f} ms, project_out {t_po:.3f} ms")
 
+    # context, not part of the path: the bf16 rate the vendor GEMM library
+    # (hipBLASLt, through torch.matmul) reaches on a large square-ish product
+    # on this GPU, the practical ceiling the MFMA-bound kernels above are
+    # held against beside the published peak
+    lib_gemm = None
+    if name == "prefill64k":
+        m_, n_, k_ = 16384, 16384, 8192
+        ga = torch.randn((m_, k_), device=dev).to(torch.bfloat16)
+        gb = torch.randn((k_, n_), device=dev).to(torch.bfloat16)
+        gc = torch.empty((m_, n_), dtype=torch.bfloat16, device=dev)
+        t_g = timed(lambda: torch.matmul(ga, gb, out=gc), reps)
+        tf = 2 * m_ * n_ * k_ / (t_g * 1e-3) / 1e12
+        lib_gemm = {"shape_mnk": [m_, n_, k_], "ms": round(t_g, 4), "tflops": round(tf, 1),
+                    "frac_bf16_peak": round(tf / acc.PEAK_BF16_TFLOPS, 4), "library": "hipBLASLt via torch.matmul"}
+        del ga, gb, gc
+        _log(f"context: bf16 library GEMM {m_}x{n_}x{k_}: {tf:.1f} TFLOP/s")
+
     # dense MHA vs forced MQA on a prompt that fits inside top-k (the first
     # 2,048 tokens of the 16K prompt): the dense path expands the latent per
     # head and runs causal MHA; the MQA path absorbs W_UK into the query, runs
@@ -659,6 +676,8 @@ def run_workload(name, args, headline):
         rec["fp8_kv"] = fp8kv
     if ab:
         rec["absorption"] = ab
+    if lib_gemm:
+        rec["context_library_gemm"] = lib_gemm
     if dmha:
         rec["dense_mha_vs_forced_mqa"] = dmha
     return rec
