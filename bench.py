@@ -249,6 +249,32 @@ def run_workload(name, args, headline):
     ms_step = (time.perf_counter() - t_start) * 1e3 / max(args.steps, 1)
     _log(f"{name}: step {ms_step:.3f} ms over {args.steps} steps")
 
+    # the decode step replayed from a HIP graph (the library's calls launch
+    # kernels on the caller's stream and nothing else, so a serving loop can
+    # capture them): the same K steps, host launch work taken out
+    graph = None
+    if name == "decode":
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t_g0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms_graph = (time.perf_counter() - t_g0) * 1e3 / max(args.steps, 1)
+        graph = {"step_ms": round(ms_graph, 4), "eager_step_ms": round(ms_step, 4)}
+        del g
+        _log(f"{name}: step replayed from a HIP graph {ms_graph:.3f} ms")
+
     # ------------------------------------------- per-kernel breakdown --
     scores = ws[: blk * n_k * 4].view(torch.float32).view(blk, n_k)
     reps = max(2, min(args.steps, 5))
@@ -670,6 +696,8 @@ def run_workload(name, args, headline):
         rec["pcp_load_balance"] = pcp
     if dcp:
         rec["dcp_share"] = dcp
+    if graph:
+        rec["graph_step"] = graph
     if f8:
         rec["fp8_indexer"] = f8
     if fp8kv:
