@@ -27,11 +27,13 @@ __global__ __launch_bounds__(kDcpThreads) void dcp_local_idx_kernel(const int32_
   const int32_t* in = idx + (int64_t)blockIdx.x * K;
   int32_t* out = local + (int64_t)blockIdx.x * K;
   int32_t v[kDcpPer];
+#pragma unroll
+  for (int j = 0; j < kDcpPer; ++j) v[j] = in[min(kDcpPer * tid + j, K - 1)];   // all in flight together
   uint32_t keep = 0, cnt = 0;
 #pragma unroll
   for (int j = 0; j < kDcpPer; ++j) {
     const int e = kDcpPer * tid + j;
-    const int32_t x = e < K ? in[e] : -1;
+    const int32_t x = e < K ? v[j] : -1;
     const bool mine = x >= 0 && x % P == rank && (int64_t)(x / P) < n_k_local;
     v[j] = mine ? x / P : -1;
     keep |= (uint32_t)mine << j;
@@ -72,13 +74,20 @@ __global__ __launch_bounds__(kDcpThreads) void lse_merge_kernel(const float* __r
   const int tid = threadIdx.x;
   const int qi = blockIdx.x / (kHeads / kMergeHeads), h0 = kMergeHeads * (blockIdx.x % (kHeads / kMergeHeads));
   const int64_t part_stride = (int64_t)n_q * kHeads * kDv;
+  // the (rank, head) lse values, one per thread (head t & 7, rank t >> 3 and
+  // t >> 3 + 32), so that they arrive in one or two round trips
+  for (int i = tid; i < n_part * kMergeHeads; i += kDcpThreads) {
+    const int r = i / kMergeHeads, hh = i % kMergeHeads;
+    s_w[r][hh] = lses[((int64_t)r * n_q + qi) * kHeads + h0 + hh];
+  }
+  __syncthreads();
   if (tid < kMergeHeads) {
     const int h = h0 + tid;
     float m = -INFINITY;
-    for (int r = 0; r < n_part; ++r) m = fmaxf(m, lses[((int64_t)r * n_q + qi) * kHeads + h]);
+    for (int r = 0; r < n_part; ++r) m = fmaxf(m, s_w[r][tid]);
     float s = 0.f;
     for (int r = 0; r < n_part; ++r) {
-      const float l = lses[((int64_t)r * n_q + qi) * kHeads + h];
+      const float l = s_w[r][tid];
       const float a = m == -INFINITY || l == -INFINITY ? 0.f : __expf(l - m);
       s_w[r][tid] = a;
       s += a;
@@ -88,19 +97,39 @@ __global__ __launch_bounds__(kDcpThreads) void lse_merge_kernel(const float* __r
     if (lse_out) lse_out[(int64_t)qi * kHeads + h] = s > 0.f ? m + __logf(s) : -INFINITY;
   }
   __syncthreads();
+  // Each thread merges four 16-byte pieces (f = tid + 256i, head 2i + (tid
+  // >> 7) of the group); the ranks' pieces are loaded four ranks at a time
+  // (clamped rank index, all in flight together), and a rank of zero weight
+  // adds nothing.
+  constexpr int kPieces = kMergeHeads * kDv / 4 / kDcpThreads, kGroup = 4;
   const int64_t base = ((int64_t)qi * kHeads + h0) * kDv;   // first float of the group
-  for (int f = tid; f < kMergeHeads * kDv / 4; f += kDcpThreads) {
-    const int hh = f / (kDv / 4);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < n_part; ++r) {
-      const float wr = s_w[r][hh];
-      if (wr != 0.f) acc += wr * reinterpret_cast<const f32x4*>(parts + r * part_stride + base)[f];
+  f32x4 acc[kPieces];
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < n_part; r0 += kGroup) {
+    f32x4 v[kGroup][kPieces];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(parts + min(r0 + j, n_part - 1) * part_stride + base);
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) v[j][i] = src[tid + kDcpThreads * i];
     }
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j)
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) {
+        const float wr = r0 + j < n_part ? s_w[r0 + j][(tid + kDcpThreads * i) / (kDv / 4)] : 0.f;
+        if (wr != 0.f) acc[i] += wr * v[j][i];
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int f = tid + kDcpThreads * i;
     if constexpr (OUT_F32) {
-      reinterpret_cast<f32x4*>(static_cast<float*>(out) + base)[f] = acc;
+      reinterpret_cast<f32x4*>(static_cast<float*>(out) + base)[f] = acc[i];
     } else {
       reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + base)[f] =
-          u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+          u32x2{pack_bf16x2(acc[i][0], acc[i][1]), pack_bf16x2(acc[i][2], acc[i][3])};
     }
   }
 }

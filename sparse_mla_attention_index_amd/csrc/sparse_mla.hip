@@ -50,26 +50,46 @@ constexpr int kMergeHeads = 4;
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void mla_merge_kernel(const float* __restrict__ part, int n_split,
                                                         void* __restrict__ out, float* __restrict__ lse) {
-  constexpr int kMaxSplit = 16;
+  constexpr int kMaxSplit = 16, kGroup = 4;
   const int qi = blockIdx.x, h = kMergeHeads * blockIdx.y + (threadIdx.x >> 6), c8 = threadIdx.x & 63;
   const float* base = part + (int64_t)qi * n_split * kMlaPartFloats;
-  float m[kMaxSplit], wgt[kMaxSplit];
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) {
-    m[s] = base[s * kMlaPartFloats + kHeads * kDv + h];
-    M = fmaxf(M, m[s]);
+  // Every load below takes a clamped split index and is issued before any
+  // result is used, so the references and sums arrive in one round trip and
+  // the outputs in one per group of four slices.
+  float m[kMaxSplit], ls[kMaxSplit];
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    const float* ps = base + min(s, n_split - 1) * kMlaPartFloats + kHeads * kDv;
+    m[s] = ps[h];
+    ls[s] = ps[kHeads + h];
   }
-  float L = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    wgt[s] = m[s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[s] - M);
-    L += wgt[s] * base[s * kMlaPartFloats + kHeads * kDv + kHeads + h];
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) M = s < n_split ? fmaxf(M, m[s]) : M;
+  float wgt[kMaxSplit], L = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    wgt[s] = s >= n_split || m[s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[s] - M);
+    L += wgt[s] * ls[s];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  for (int s = 0; s < n_split; ++s) {
-    const float* src = base + s * kMlaPartFloats + h * kDv + 8 * c8;
-    acc0 += wgt[s] * *reinterpret_cast<const f32x4*>(src);
-    acc1 += wgt[s] * *reinterpret_cast<const f32x4*>(src + 4);
+  for (int s0 = 0; s0 < n_split; s0 += kGroup) {
+    f32x4 v[kGroup][2];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const float* src = base + min(s0 + j, n_split - 1) * kMlaPartFloats + h * kDv + 8 * c8;
+      v[j][0] = *reinterpret_cast<const f32x4*>(src);
+      v[j][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      float wj = 0.f;
+#pragma unroll
+      for (int s = 0; s < kMaxSplit; ++s) wj = s == s0 + j ? wgt[s] : wj;   // 0 past n_split
+      acc0 += wj * v[j][0];
+      acc1 += wj * v[j][1];
+    }
   }
   acc0 *= inv;
   acc1 *= inv;
@@ -332,15 +352,29 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
   const int h = lane >> 5, c32 = lane & 31;
   const int32_t* irow = idx + (int64_t)qi * K;
 
+  // ---- Q: block 0 = own heads 32d+c32, block 1 = partner heads; dims 288d +
+  // 16ks + 8h .. +7.  Issued first: it does not depend on the extent, so its
+  // loads and the extent loads below share one round trip ----
+  bf16x8 qf[2][kPairKs];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const uint16_t* src = q + ((int64_t)qi * kHeads + 32 * (d ^ hb) + c32) * kDqk + 16 * kPairKs * d + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < kPairKs; ++ks) qf[hb][ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
+  }
+
   // ---- extent of the selection: entries [0, n_ext) hold every valid index ----
+  // The loads take clamped positions and are all issued before any is
+  // tested, so they are in flight together.
+  constexpr int kExtLoads = SMA_MAX_TOPK_DEV / kPairThreads;
+  int ext[kExtLoads];
+#pragma unroll
+  for (int e = 0; e < kExtLoads; ++e) ext[e] = irow[min(e * kPairThreads + tid, K - 1)];
   int last = -1;
 #pragma unroll
-  for (int e = 0; e < SMA_MAX_TOPK_DEV / kPairThreads; ++e) {
+  for (int e = 0; e < kExtLoads; ++e) {
     const int j = e * kPairThreads + tid;
-    if (j < K) {
-      const int x = irow[j];
-      if (x >= 0 && x < n_k) last = j;
-    }
+    if (j < K && ext[e] >= 0 && ext[e] < n_k) last = j;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
@@ -352,6 +386,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
   const int tps = (n_tiles_all + n_split - 1) / n_split;
   const int t_beg = min(n_tiles_all, split * tps), t_end = min(n_tiles_all, t_beg + tps);
   if (mypart && t_beg == t_end) {   // empty slice: zero partial, reference -inf
+    wait_vmcnt<0>();                 // the Q loads retire before the wave ends
     for (int i = tid; i < kHeads * kDv / 4; i += kPairThreads)
       reinterpret_cast<f32x4*>(mypart)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (tid < kHeads) {
@@ -361,6 +396,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
     return;
   }
   if (n_ext == 0) {
+    wait_vmcnt<0>();
     for (int i = tid; i < kHeads * kDv / 4; i += kPairThreads) {
       if constexpr (OUT_F32) {
         reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)qi * kHeads * kDv)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -370,15 +406,6 @@ __global__ __launch_bounds__(kPairThreads, 1) void sparse_mla_kernel(
     }
     if (lse && tid < kHeads) lse[(int64_t)qi * kHeads + tid] = -INFINITY;
     return;
-  }
-
-  // ---- Q: block 0 = own heads 32d+c32, block 1 = partner heads; dims 288d + 16ks + 8h .. +7 ----
-  bf16x8 qf[2][kPairKs];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const uint16_t* src = q + ((int64_t)qi * kHeads + 32 * (d ^ hb) + c32) * kDqk + 16 * kPairKs * d + 8 * h;
-#pragma unroll
-    for (int ks = 0; ks < kPairKs; ++ks) qf[hb][ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
   }
 
   // ---- gather: wave d fills blocks (rg, cg) for rg = 2d, 2d+1 and all 9

@@ -35,6 +35,16 @@ namespace sma {
 constexpr int kBins = 2048;
 constexpr int kStreamV = 16;   // elements per thread per streamed chunk
 
+// The score read for a position past a row's end: NaN.  score_or_nan (and
+// the filter passes' quad_or_nan) select the address, never the load, so that
+// the loads of a row's last, partial chunk are all in flight together
+// instead of one round trip per guarded load.
+__device__ __attribute__((aligned(16))) float g_past_row4[4] = {__builtin_nanf(""), __builtin_nanf(""),
+                                                                 __builtin_nanf(""), __builtin_nanf("")};
+__device__ __forceinline__ float score_or_nan(const float* src, int pos, int n) {
+  return *(pos < n ? src + pos : g_past_row4);
+}
+
 template <int THREADS>
 struct TopkShared {
   static constexpr int WAVES = THREADS / 64;
@@ -101,8 +111,11 @@ __device__ void topk_stream_row(const float* __restrict__ src, int n, int K, int
   auto for_each = [&](auto&& fn) {
     for (int c0 = 0; c0 < n; c0 += kTopkThreads * kStreamV) {
       const int base = c0 + tid * kStreamV;
+      float x[kStreamV];
 #pragma unroll
-      for (int v = 0; v < kStreamV; ++v) fn(base + v, base + v < n ? score_key(src[base + v]) : 0u);
+      for (int v = 0; v < kStreamV; ++v) x[v] = score_or_nan(src, base + v, n);
+#pragma unroll
+      for (int v = 0; v < kStreamV; ++v) fn(base + v, base + v < n ? score_key(x[v]) : 0u);
     }
   };
 
@@ -230,11 +243,14 @@ __device__ void topk_stream_row(const float* __restrict__ src, int n, int K, int
   uint32_t g_run = 0, e_run = 0;   // totals of earlier chunks
   for (int c0 = 0; c0 < n; c0 += kTopkThreads * kStreamV) {
     const int base = c0 + tid * kStreamV;
+    float x[kStreamV];
+#pragma unroll
+    for (int v = 0; v < kStreamV; ++v) x[v] = score_or_nan(src, base + v, n);
     uint32_t kk[kStreamV];
     uint32_t cg = 0, ce = 0;
 #pragma unroll
     for (int v = 0; v < kStreamV; ++v) {
-      kk[v] = base + v < n ? score_key(src[base + v]) : 0u;
+      kk[v] = base + v < n ? score_key(x[v]) : 0u;
       cg += kk[v] > T;
       ce += kk[v] == T;
     }
@@ -315,6 +331,42 @@ constexpr int kFtWaveSpan = 256 * kFtU;           // a wave's contiguous share o
 constexpr int kFtKeep = kFtCap / kFtThreads;      // kept keys per thread in the final select
 constexpr int64_t kFtLongMax = 1 << 18;           // longest rows the filtered kernel takes
 constexpr uint32_t kFtRefineBin = 32;             // samples in the threshold's bin that call for a second round
+
+// Loads of a row's last, partial chunk.  On 16-byte aligned rows a lane
+// whose four positions all lie inside the row loads them as one vector and
+// a lane past the row's end loads four NaNs (which no threshold keeps) from
+// g_past_row4: the address is selected, never the load, so the chunk's loads
+// go out together instead of one round trip per guarded load.  The one lane
+// that straddles the end (n not a multiple of 4) gets NaNs too; its n & 3
+// in-row scores are read once per row (row_tail) and put back by fix_tail
+// before the chunk is used.  Unaligned rows read each position through
+// score_or_nan.
+__device__ __forceinline__ f32x4 quad_or_nan(const float* src, int p0, int n) {   // p0 % 4 == 0
+  return *reinterpret_cast<const f32x4*>(p0 + 3 < n ? src + p0 : g_past_row4);
+}
+struct RowTail {
+  int n4;      // n & ~3: the straddling lane's first position
+  float v[3];  // scores n4 .. n4 + 2 (those below n are used)
+};
+__device__ __forceinline__ RowTail row_tail(const float* src, int n) {   // n >= 1
+  RowTail t;
+  t.n4 = n & ~3;
+#pragma unroll
+  for (int e = 0; e < 3; ++e) t.v[e] = src[min(t.n4 + e, n - 1)];
+  return t;
+}
+// pw: the lane's first position in the chunk; step u covers pw + 256u + 0..3.
+__device__ __forceinline__ void fix_tail(f32x4 (&x)[kFtU], int pw, int n, const RowTail& t) {
+#pragma unroll
+  for (int u = 0; u < kFtU; ++u) {
+    const int p0 = pw + 256 * u;
+    if (p0 == t.n4 && p0 < n) {
+#pragma unroll
+      for (int e = 0; e < 3; ++e)
+        if (p0 + e < n) x[u][e] = t.v[e];
+    }
+  }
+}
 
 // The score whose key is k (the inverse of score_key for finite scores).
 __device__ __forceinline__ float key_score(uint32_t k) {
@@ -515,17 +567,10 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
       for (int u = 0; u < kFtU; ++u) x[u] = *reinterpret_cast<const f32x4*>(src + pw + 256 * u);
     } else {
 #pragma unroll
-      for (int u = 0; u < kFtU; ++u) {
-        const int p0 = pw + 256 * u;
-        if (p0 + 3 < n) {
-          x[u] = *reinterpret_cast<const f32x4*>(src + p0);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[u][e] = p0 + e < n ? src[p0 + e] : __builtin_nanf("");
-        }
-      }
+      for (int u = 0; u < kFtU; ++u) x[u] = quad_or_nan(src, pw + 256 * u, n);
     }
   };
+  const RowTail tail = row_tail(src, n);
 
   // ---- 1. threshold (the sample loads go out with the first chunk's) ----
   f32x4 sv[SPT / 4] = {};
@@ -562,6 +607,7 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
   // Keep the chunk at c0 (held in x), then load the chunk two ahead into x.
   // The kept list holds raw score bits; keys are formed for kept entries only.
   auto step = [&](int c0, int ci, f32x4 (&x)[kFtU]) {
+    if (c0 + kFtChunk > n) fix_tail(x, c0 + kFtWaveSpan * wave + 4 * lane, n, tail);
     // off[u]: this lane's first slot for step u within the wave's kept
     // entries of the chunk (ballot prefix counts, accumulated by mbcnt)
     uint32_t off[kFtU];
@@ -717,22 +763,27 @@ __global__ __launch_bounds__(kFtThreads) void topk_long_filter(const float* __re
   // NaN, which no threshold keeps.
   auto load = [&](int c0, f32x4 (&x)[kFtU]) {
     const int pw = c0 + kFtWaveSpan * wave + 4 * lane;
+    if (!ALIGNED) {
 #pragma unroll
-    for (int u = 0; u < kFtU; ++u) {
-      const int p0 = pw + 256 * u;
-      if (ALIGNED && p0 + 3 < n) {
-        x[u] = *reinterpret_cast<const f32x4*>(src + p0);
-      } else {
+      for (int u = 0; u < kFtU; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[u][e] = p0 + e < n ? src[p0 + e] : __builtin_nanf("");
-      }
+        for (int e = 0; e < 4; ++e) x[u][e] = score_or_nan(src, pw + 256 * u + e, n);
+    } else if (c0 + kFtChunk <= n) {
+#pragma unroll
+      for (int u = 0; u < kFtU; ++u) x[u] = *reinterpret_cast<const f32x4*>(src + pw + 256 * u);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kFtU; ++u) x[u] = quad_or_nan(src, pw + 256 * u, n);
     }
   };
   f32x4 xa[kFtU], xb[kFtU];
   load(cbeg, xa);
   if (cbeg + kFtChunk < n) load(cbeg + kFtChunk, xb);
+  RowTail tail{};
+  if (ALIGNED && cbeg + 2 * kFtChunk > n) tail = row_tail(src, n);   // this workgroup holds the row's end
   uint32_t kept = 0;
   auto step = [&](int c0, int ci, f32x4 (&x)[kFtU]) {
+    if (ALIGNED && c0 + kFtChunk > n) fix_tail(x, c0 + kFtWaveSpan * wave + 4 * lane, n, tail);
     uint32_t off[kFtU];
     uint32_t wcnt = 0;
 #pragma unroll
