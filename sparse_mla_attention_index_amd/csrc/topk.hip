@@ -27,13 +27,15 @@
 // those (topk_filter_kernel below); rows longer than 65,536 scores, too few
 // to fill the device one per workgroup, are split across workgroups when a
 // workspace is given (topk_long_* below).
+#include <type_traits>
+
 #include "sma_device.h"
 #include "sma_launch.h"
 
 namespace sma {
 
 constexpr int kBins = 2048;
-constexpr int kStreamV = 16;   // elements per thread per streamed chunk
+constexpr int kStreamV = 8;    // elements per thread per streamed chunk
 
 // The score read for a position past a row's end: NaN.  score_or_nan (and
 // the filter passes' quad_or_nan) select the address, never the load, so that
@@ -426,9 +428,10 @@ __device__ uint32_t ft_round(const uint32_t (&key)[M], uint32_t& lo, uint32_t& h
   constexpr int BPT = kBins / kFtThreads;
   uint32_t hb[BPT], hsum = 0;
 #pragma unroll
+  for (int e = 0; e < BPT; ++e) hb[e] = sh.hist[BPT * tid + e];   // all kBins words exist
+#pragma unroll
   for (int e = 0; e < BPT; ++e) {
-    const int b = BPT * tid + e;
-    hb[e] = b < nbins ? sh.hist[b] : 0u;
+    hb[e] = BPT * tid + e < nbins ? hb[e] : 0u;
     hsum += hb[e];
   }
   uint32_t ex, dummy_e, tot, dummy_t;
@@ -464,25 +467,30 @@ __device__ void ft_select_kept(const uint32_t* ckey, const PosT* cpos, int C, in
                                TopkShared<kFtThreads>& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // ---- 3. exact threshold key T among the kept keys ----
+  // (reads at clamped indices, all issued before any is used)
   uint32_t kk[KEEP];
 #pragma unroll
-  for (int j = 0; j < KEEP; ++j) {
-    const int i = tid + kFtThreads * j;
-    kk[j] = i < C ? score_key(__uint_as_float(ckey[i])) : 0u;
-  }
+  for (int j = 0; j < KEEP; ++j) kk[j] = ckey[min(tid + kFtThreads * j, C - 1)];
+#pragma unroll
+  for (int j = 0; j < KEEP; ++j) kk[j] = tid + kFtThreads * j < C ? score_key(__uint_as_float(kk[j])) : 0u;
   uint32_t lo, hi, need_ties = (uint32_t)K;
   ft_range<KEEP>(kk, lo, hi, sh);
   for (int round = 0; round < 3 && hi != lo; ++round) {
     const uint32_t in_bin = ft_round<KEEP>(kk, lo, hi, need_ties, sh);
     if (hi != lo && in_bin <= 64) {
       // one wave ranks the bin's keys: T has fewer than need_ties of them
-      // above it and at least need_ties at or above it
+      // above it and at least need_ties at or above it.  Each thread claims
+      // room for all of its bin keys with one atomic.
       uint32_t* list = sh.hist;
       if (tid == 0) sh.bcast[3] = 0u;
       __syncthreads();
+      uint32_t mine = 0;
+#pragma unroll
+      for (int j = 0; j < KEEP; ++j) mine += kk[j] >= lo && kk[j] <= hi;
+      uint32_t at = mine ? atomicAdd(&sh.bcast[3], mine) : 0u;
 #pragma unroll
       for (int j = 0; j < KEEP; ++j)
-        if (kk[j] >= lo && kk[j] <= hi) list[atomicAdd(&sh.bcast[3], 1u)] = kk[j];
+        if (kk[j] >= lo && kk[j] <= hi) list[at++] = kk[j];
       __syncthreads();
       if (wave == 0) {
         const int nb = (int)in_bin;
@@ -506,31 +514,63 @@ __device__ void ft_select_kept(const uint32_t* ckey, const PosT* cpos, int C, in
   }
   const uint32_t T = lo;
 
-  // ---- 4. ordered compaction: thread t owns kept entries [t*M, t*M + M) ----
-  // (kept scores are never NaN, so comparing them as floats with T's score
-  // orders them as their keys do, -0.0 == +0.0 included)
+  // ---- 4. ordered compaction: every kept entry above T and the first
+  // need_ties equal to T, in list (= position) order.  Wave w takes a
+  // contiguous quarter of the list, 64 consecutive entries per step; ballots
+  // rank an entry among those above / equal to T, so the reads and the
+  // writes of a step are coalesced.  (Kept scores are never NaN, so
+  // comparing them as floats with T's score orders them as their keys do,
+  // -0.0 == +0.0 included.) ----
   const float Tf = key_score(T);
-  const int M = (C + kFtThreads - 1) / kFtThreads;
-  const int i0 = min(C, tid * M), i1 = min(C, i0 + M);
-  uint32_t cg = 0, ce = 0;
-  for (int i = i0; i < i1; ++i) {
-    const float v = __uint_as_float(ckey[i]);
-    cg += v > Tf;
-    ce += v == Tf;
-  }
-  uint32_t g_before, e_before, tg, te;
-  block_excl_scan2<kFtThreads>(cg, ce, g_before, e_before, tg, te, sh);
-  for (int i = i0; i < i1; ++i) {
-    const float v = __uint_as_float(ckey[i]);
-    if (v > Tf) {
-      const uint32_t slot = g_before + min(e_before, need_ties);
-      if (slot < (uint32_t)K) out[slot] = cpos[i];
-      ++g_before;
-    } else if (v == Tf) {
-      if (e_before < need_ties && g_before + e_before < (uint32_t)K) out[g_before + e_before] = cpos[i];
-      ++e_before;
+  const int span = (((C + kFtWaves - 1) / kFtWaves) + 63) & ~63;   // entries per wave, whole steps
+  const int w0 = min(C, wave * span), w1 = min(C, w0 + span);
+  constexpr int kU = 4;   // steps whose reads are in flight together
+  auto visit = [&](auto with_pos, auto&& fn) {
+    for (int b = w0; b < w1; b += 64 * kU) {
+      float v[kU];
+      int32_t ps[kU] = {};
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int ic = min(b + 64 * u + lane, C - 1);
+        v[u] = __uint_as_float(ckey[ic]);
+        if constexpr (decltype(with_pos)::value) ps[u] = (int32_t)cpos[ic];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const bool in = b + 64 * u + lane < w1;
+        fn(ps[u], __ballot(in && v[u] > Tf), __ballot(in && v[u] == Tf));
+      }
     }
+  };
+  uint32_t cg = 0, ce = 0;   // this wave's counts
+  visit(std::false_type{}, [&](int32_t, uint64_t mg, uint64_t me) {
+    cg += (uint32_t)__popcll(mg);
+    ce += (uint32_t)__popcll(me);
+  });
+  if (lane == 0) {
+    sh.red[wave] = cg;
+    sh.red[kFtWaves + wave] = ce;
   }
+  __syncthreads();
+  uint32_t g_run = 0, e_run = 0;   // entries above / equal to T before this wave's quarter
+#pragma unroll
+  for (int w = 0; w < kFtWaves; ++w) {
+    g_run += w < wave ? sh.red[w] : 0u;
+    e_run += w < wave ? sh.red[kFtWaves + w] : 0u;
+  }
+  visit(std::true_type{}, [&](int32_t pos, uint64_t mg, uint64_t me) {
+    const uint32_t g_before = g_run + __builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
+    const uint32_t e_before = e_run + __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+    const bool is_g = (mg >> lane) & 1u, is_e = (me >> lane) & 1u;
+    uint32_t slot = 0xFFFFFFFFu;
+    if (is_g) slot = g_before + min(e_before, need_ties);
+    if (is_e && e_before < need_ties) slot = g_before + e_before;
+    if (slot < (uint32_t)K) out[slot] = pos;
+    g_run += (uint32_t)__popcll(mg);
+    e_run += (uint32_t)__popcll(me);
+  });
 }
 
 // PosT holds a position (uint16_t for rows of at most 65,536 scores); SPT
