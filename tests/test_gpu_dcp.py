@@ -93,13 +93,14 @@ def test_dcp_fp8_shards_merge_to_unsharded():
     _close(out_f64(out), out_f64(full), 1e-2)
 
 
+@pytest.mark.parametrize("P", [5, 1, 4, 9, 64])   # the merge loads ranks four at a time; 64 is the maximum
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_lse_merge_random_partials(out_dtype):
-    rng = np.random.default_rng(3)
-    P, n_q = 5, 7
+def test_lse_merge_random_partials(out_dtype, P):
+    rng = np.random.default_rng(3 + P)
+    n_q = 7
     parts = rng.standard_normal((P, n_q, 64, 512)).astype(np.float32)
     lses = (rng.standard_normal((P, n_q, 64)) * 4).astype(np.float32)
-    lses[1, 2, :] = -np.inf              # one empty partial
+    lses[min(1, P - 1), 2, :] = -np.inf  # one empty partial
     lses[:, 3, 10] = -np.inf             # an all-empty (query, head)
     out, lse = sma.lse_merge(dev(parts), dev(lses), out_dtype=out_dtype, want_lse=True)
     ref, ref_lse = oracle.lse_merge(parts.astype(np.float64), lses.astype(np.float64))

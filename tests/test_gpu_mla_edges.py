@@ -1,6 +1,7 @@
 """Edge cases of sma_sparse_mla_prefill for every KV row format (bf16,
 per-token FP8, 656-byte fp8_ds_mla), with and without the workspace that
-lets a small batch split its rows: top_k of 1 and around the 32-row tile,
+lets a small batch split its rows (up to the sixteen slices the merge
+takes): top_k of 1 and around the 32-row tile,
 contexts of one and two rows, a query whose only valid entry is the last
 slot, a fully padded query, repeated entries (each counts, as the oracle
 takes the list as given), and a single query.  Against the oracle, 1e-2 of
@@ -54,7 +55,7 @@ def _check(q, kv_args, kv64, idx, fmt, split):
 
 @pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp8_ds_mla"])
-@pytest.mark.parametrize("top_k", [1, 31, 32, 33, 64, 2047])
+@pytest.mark.parametrize("top_k", [1, 31, 32, 33, 64, 2047, 2048])   # 2048: sixteen row slices
 def test_top_k_around_the_tile(fmt, split, top_k):
     n_q, n_k = 6, 3000
     rng = np.random.default_rng(top_k)
