@@ -3,7 +3,9 @@
     python -m sparse_mla_attention_index_amd.build
 
 Each .hip file under csrc/ is compiled to an object under _build/ (in
-parallel), then linked into sparse_mla_attention_index_amd/libsma.so.
+parallel), then linked into sparse_mla_attention_index_amd/libsma.so (and
+libsma_debug.so); the C client of the ABI under tests/c_client/ is built
+against it.
 """
 from __future__ import annotations
 
@@ -24,6 +26,9 @@ LIB = os.path.join(PKG, "libsma.so")
 DEBUG_LIB = os.path.join(PKG, "libsma_debug.so")
 DEBUG_SRC = "sma_api.hip"
 ARCH = "gfx950"
+# A plain C client of the C ABI (test infrastructure: tests/test_gpu_c_client.py).
+CLIENT_SRC = os.path.join(ROOT, "tests", "c_client", "prefill_client.c")
+CLIENT = os.path.join(ROOT, "tests", "c_client", "prefill_client")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -71,7 +76,22 @@ def build(verbose: bool = False) -> str:
         tmp = lib + ".tmp"
         _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs])
         os.replace(tmp, lib)
+    build_c_client(cc)
     return LIB
+
+
+def build_c_client(cc: str) -> str:
+    """Compile the C client with the host C compiler against include/sma.h,
+    the HIP runtime's C API and libsma.so (found next to the package at run
+    time through a relative rpath)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(cc)))
+    tmp = CLIENT + ".tmp"
+    _run(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"), CLIENT_SRC, "-o", tmp,
+          "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-L", PKG, "-lsma",
+          f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-Wl,-rpath,$ORIGIN/../../sparse_mla_attention_index_amd"])
+    os.replace(tmp, CLIENT)
+    return CLIENT
 
 
 if __name__ == "__main__":

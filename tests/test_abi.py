@@ -119,6 +119,23 @@ def test_pcp_validation(rank, P_, L, msg):
     assert r == -1 and msg in sma.last_error()
 
 
+def test_c_client_built_and_rejects_bad_usage(tmp_path):
+    """The plain C client of the ABI (tests/c_client) links against
+    libsma.so and the HIP runtime, and reports usage and file errors with
+    exit status 2 before any GPU call (its GPU run is test_gpu_c_client)."""
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "tests", "c_client",
+                       "prefill_client")
+    assert os.path.exists(exe)
+    assert subprocess.run([exe], capture_output=True, timeout=60).returncode == 2
+    r = subprocess.run([exe, str(tmp_path)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "meta.txt" in r.stderr
+    (tmp_path / "meta.txt").write_text("4 8 8 64 2 0.1\n")
+    r = subprocess.run([exe, str(tmp_path)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "q_idx.bin" in r.stderr
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libsma.so"))
