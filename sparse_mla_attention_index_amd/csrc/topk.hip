@@ -35,7 +35,11 @@
 namespace sma {
 
 constexpr int kBins = 2048;
-constexpr int kStreamV = 8;    // elements per thread per streamed chunk
+// Elements per thread per streamed chunk.  The filtered kernel inlines the
+// streaming selection as its fallback, so these arrays count towards its
+// registers: at 8 the 16-bit-position kernel stays within four workgroups
+// per CU (at 16 it needed three).
+constexpr int kStreamV = 8;
 
 // The score read for a position past a row's end: NaN.  score_or_nan (and
 // the filter passes' quad_or_nan) select the address, never the load, so that
