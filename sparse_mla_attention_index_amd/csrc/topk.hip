@@ -51,10 +51,15 @@ __device__ __forceinline__ float score_or_nan(const float* src, int pos, int n) 
   return *(pos < n ? src + pos : g_past_row4);
 }
 
-template <int THREADS>
+// LDS scratch of a top-k workgroup: a BINS-bin histogram (BINS a power of
+// two; a refinement round narrows a key range by log2(BINS) bits) and the
+// block reductions' slots.
+template <int THREADS, int BINS = kBins>
 struct TopkShared {
   static constexpr int WAVES = THREADS / 64;
-  uint32_t hist[kBins];
+  static constexpr int kBinsN = BINS, kBinBits = __builtin_ctz(BINS);
+  static_assert((BINS & (BINS - 1)) == 0, "a power-of-two bin count");
+  uint32_t hist[BINS];
   uint32_t red[WAVES * 2];
   uint32_t bcast[4];
 };
@@ -71,9 +76,9 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 // Exclusive block-wide prefix of two counters at once (packed as 2 x 32 bit
 // in a 64-bit lane value would overflow for long rows, so they are scanned
 // separately through the same LDS slots).
-template <int THREADS>
+template <int THREADS, int BINS>
 __device__ __forceinline__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_t& ea, uint32_t& eb,
-                                                 uint32_t& ta, uint32_t& tb, TopkShared<THREADS>& sh) {
+                                                 uint32_t& ta, uint32_t& tb, TopkShared<THREADS, BINS>& sh) {
   constexpr int kTopkWaves = THREADS / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t ia = wave_incl_scan(a, lane), ib = wave_incl_scan(b, lane);
@@ -100,12 +105,12 @@ __device__ __forceinline__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_
 // Exact top-k of one row streamed from memory in every pass (rows of any
 // length, any alignment): key range, radix refinement to the threshold key
 // T, ordered compaction.  Called by a whole THREADS-thread workgroup; `sh`
-// and `cand` (kBins words) are its LDS scratch.
-template <int THREADS>
+// and `cand` (BINS words) are its LDS scratch.
+template <int THREADS, int BINS>
 __device__ void topk_stream_row(const float* __restrict__ src, int n, int K, int32_t* __restrict__ out,
-                                TopkShared<THREADS>& sh, uint32_t* cand) {
-  constexpr int kTopkThreads = THREADS, kTopkWaves = THREADS / 64;
-  static_assert(kBins % THREADS == 0, "whole histogram bins per thread");
+                                TopkShared<THREADS, BINS>& sh, uint32_t* cand) {
+  constexpr int kTopkThreads = THREADS, kTopkWaves = THREADS / 64, kBits = TopkShared<THREADS, BINS>::kBinBits;
+  static_assert(BINS % THREADS == 0, "whole histogram bins per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   auto note = [&](uint32_t k) {
@@ -151,7 +156,7 @@ __device__ void topk_stream_row(const float* __restrict__ src, int n, int K, int
   auto refine = [&](auto&& visit) {
     const uint32_t width = hi - lo;
     const int bits = 32 - __clz(width);
-    const int shift = bits > 11 ? bits - 11 : 0;
+    const int shift = bits > kBits ? bits - kBits : 0;
     const int nbins = (int)(width >> shift) + 1;
     for (int b = tid; b < nbins; b += kTopkThreads) sh.hist[b] = 0u;
     if (tid == 0) {
@@ -166,7 +171,7 @@ __device__ void topk_stream_row(const float* __restrict__ src, int n, int K, int
     __syncthreads();
     // thread t owns bins [BPT*t, BPT*t + BPT); keys above a bin = total minus
     // the inclusive prefix up to and including it
-    constexpr int BPT = kBins / THREADS;
+    constexpr int BPT = BINS / THREADS;
     uint32_t hb[BPT], hsum = 0;
 #pragma unroll
     for (int e = 0; e < BPT; ++e) {
@@ -197,11 +202,12 @@ __device__ void topk_stream_row(const float* __restrict__ src, int n, int K, int
     lo = (uint32_t)nlo;
     hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
   };
-  // Each round shrinks the range by 11 bits: three rounds reach a single key;
-  // the bound keeps the loops finite whatever the data.
+  // Each round shrinks the range by log2(BINS) >= 8 bits, so four rounds
+  // reach a single key; the bound keeps the loops finite whatever the data.
+  static_assert(4 * kBits >= 32, "four rounds narrow a 32-bit key range to one key");
   if (hi != lo) refine(for_each);
   if (hi != lo) {
-    if (in_range <= (uint32_t)kBins) {
+    if (in_range <= (uint32_t)BINS) {
       if (tid == 0) sh.bcast[3] = 0u;
       __syncthreads();
       for_each([&](int, uint32_t k) {
@@ -329,12 +335,18 @@ __global__ __launch_bounds__(THREADS, 1) void topk_stream_kernel(const float* __
 // ---------------------------------------------------------------------------
 constexpr int kFtThreads = 256;
 constexpr int kFtWaves = kFtThreads / 64;
-constexpr int kFtCap = 5120;                      // kept positions held in LDS
+constexpr int kFtCap = 5120;                      // kept positions held in LDS (32-bit positions)
+// For rows of at most 32,768 scores the 16-bit-position kernel holds fewer
+// (4,608) with a 1,024-bin histogram: 31 KiB of LDS, five workgroups per CU
+// instead of four (such rows keep about 3,240 +- 300 with the 2,048-sample
+// threshold).  Measured: the 16K top-k 0.29-0.36 -> 0.24-0.25 ms; with rows
+// of up to 65,536 scores the fifth workgroup made it ~2.5% slower, so those
+// keep four.
+constexpr int kFtCap16 = 4608, kFtBins16 = 1024, kFtShortMax = 32768;
 constexpr int kFtClusterLen = 16;                 // consecutive scores per sample cluster
 constexpr int kFtU = 8;                           // 16-byte loads per thread per chunk
 constexpr int kFtChunk = kFtThreads * 4 * kFtU;   // 8,192 positions
 constexpr int kFtWaveSpan = 256 * kFtU;           // a wave's contiguous share of a chunk
-constexpr int kFtKeep = kFtCap / kFtThreads;      // kept keys per thread in the final select
 constexpr int64_t kFtLongMax = 1 << 18;           // longest rows the filtered kernel takes
 constexpr uint32_t kFtRefineBin = 32;             // samples in the threshold's bin that call for a second round
 
@@ -381,9 +393,9 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 
 // Range [lo, hi] of the nonzero keys the workgroup holds (M per thread, 0 =
 // none).
-template <int M>
+template <int M, int BINS>
 __device__ __forceinline__ void ft_range(const uint32_t (&key)[M], uint32_t& lo, uint32_t& hi,
-                                         TopkShared<kFtThreads>& sh) {
+                                         TopkShared<kFtThreads, BINS>& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
@@ -415,13 +427,14 @@ __device__ __forceinline__ void ft_range(const uint32_t (&key)[M], uint32_t& lo,
 // into <= 2,048 bins of equal width and keep the bin holding the
 // remaining-th largest key inside [lo, hi].  Narrows lo, hi and remaining;
 // returns how many keys the kept bin holds.
-template <int M>
+template <int M, int BINS>
 __device__ uint32_t ft_round(const uint32_t (&key)[M], uint32_t& lo, uint32_t& hi, uint32_t& remaining,
-                             TopkShared<kFtThreads>& sh) {
+                             TopkShared<kFtThreads, BINS>& sh) {
+  constexpr int kBits = TopkShared<kFtThreads, BINS>::kBinBits;
   const int tid = threadIdx.x;
   const uint32_t width = hi - lo;
   const int bits = 32 - __clz(width);
-  const int shift = bits > 11 ? bits - 11 : 0;
+  const int shift = bits > kBits ? bits - kBits : 0;
   const int nbins = (int)(width >> shift) + 1;
   for (int b = tid; b < nbins; b += kFtThreads) sh.hist[b] = 0u;
   __syncthreads();
@@ -429,10 +442,10 @@ __device__ uint32_t ft_round(const uint32_t (&key)[M], uint32_t& lo, uint32_t& h
   for (int j = 0; j < M; ++j)
     if (key[j] >= lo && key[j] <= hi) atomicAdd(&sh.hist[(key[j] - lo) >> shift], 1u);
   __syncthreads();
-  constexpr int BPT = kBins / kFtThreads;
+  constexpr int BPT = BINS / kFtThreads;
   uint32_t hb[BPT], hsum = 0;
 #pragma unroll
-  for (int e = 0; e < BPT; ++e) hb[e] = sh.hist[BPT * tid + e];   // all kBins words exist
+  for (int e = 0; e < BPT; ++e) hb[e] = sh.hist[BPT * tid + e];   // all BINS words exist
 #pragma unroll
   for (int e = 0; e < BPT; ++e) {
     hb[e] = BPT * tid + e < nbins ? hb[e] : 0u;
@@ -466,9 +479,10 @@ __device__ uint32_t ft_round(const uint32_t (&key)[M], uint32_t& lo, uint32_t& h
 // <= KEEP * kFtThreads; raw score bits ckey[i] of ascending positions
 // cpos[i], no NaN among them), written to out in ascending position order.
 // Called by the whole kFtThreads-thread workgroup.
-template <typename PosT, int KEEP>
+template <typename PosT, int KEEP, int BINS>
 __device__ void ft_select_kept(const uint32_t* ckey, const PosT* cpos, int C, int K, int32_t* __restrict__ out,
-                               TopkShared<kFtThreads>& sh) {
+                               TopkShared<kFtThreads, BINS>& sh) {
+  constexpr int kBits = TopkShared<kFtThreads, BINS>::kBinBits;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // ---- 3. exact threshold key T among the kept keys ----
   // (reads at clamped indices, all issued before any is used)
@@ -479,7 +493,7 @@ __device__ void ft_select_kept(const uint32_t* ckey, const PosT* cpos, int C, in
   for (int j = 0; j < KEEP; ++j) kk[j] = tid + kFtThreads * j < C ? score_key(__uint_as_float(kk[j])) : 0u;
   uint32_t lo, hi, need_ties = (uint32_t)K;
   ft_range<KEEP>(kk, lo, hi, sh);
-  for (int round = 0; round < 3 && hi != lo; ++round) {
+  for (int round = 0; round < (32 + kBits - 1) / kBits && hi != lo; ++round) {
     const uint32_t in_bin = ft_round<KEEP>(kk, lo, hi, need_ties, sh);
     if (hi != lo && in_bin <= 64) {
       // one wave ranks the bin's keys: T has fewer than need_ties of them
@@ -578,16 +592,18 @@ __device__ void ft_select_kept(const uint32_t* ckey, const PosT* cpos, int C, in
 }
 
 // PosT holds a position (uint16_t for rows of at most 65,536 scores); SPT
-// samples per thread (SPT * 256 in all).
-template <typename PosT, int SPT, int OCC>
+// samples per thread (SPT * 256 in all); CAP kept positions in LDS; BINS
+// histogram bins.
+template <typename PosT, int SPT, int OCC, int CAP, int BINS>
 __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const float* __restrict__ scores, int64_t ld,
                                                                       const int32_t* __restrict__ q_pos, int n_k,
                                                                       int K, int32_t* __restrict__ idx) {
   constexpr int kSamples = kFtThreads * SPT, kClusters = kSamples / kFtClusterLen;
   static_assert(SPT % 4 == 0 && kFtClusterLen % SPT == 0, "whole 16-byte loads within one cluster");
-  __shared__ TopkShared<kFtThreads> sh;
-  __shared__ uint32_t ckey[kFtCap + 4];   // score bits of the kept positions (the streaming fallback's scratch)
-  __shared__ PosT cpos[kFtCap + 4];       // kept positions, ascending
+  static_assert(CAP % kFtThreads == 0 && CAP + 4 >= BINS, "whole kept keys per thread; room for the fallback");
+  __shared__ TopkShared<kFtThreads, BINS> sh;
+  __shared__ uint32_t ckey[CAP + 4];   // score bits of the kept positions (the streaming fallback's scratch)
+  __shared__ PosT cpos[CAP + 4];       // kept positions, ascending
   __shared__ uint32_t tab[2][kFtWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;
@@ -618,7 +634,7 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
 
   // ---- 1. threshold (the sample loads go out with the first chunk's) ----
   f32x4 sv[SPT / 4] = {};
-  const bool sampled = n > kFtCap;
+  const bool sampled = n > CAP;
   if (sampled) {   // thread t loads SPT consecutive scores of cluster t*SPT/16
     const int c = tid * SPT / kFtClusterLen;
     const int start = (int)(((int64_t)c * (n - kFtClusterLen)) / (kClusters - 1)) & ~3;
@@ -682,7 +698,7 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
     // histogram, idle during this pass, so that no lane branches
 #pragma unroll
     for (int u = 0; u < kFtU; ++u) {
-      uint32_t slot = min(base + off[u], (uint32_t)kFtCap);   // slots kFtCap.. absorb an overflow
+      uint32_t slot = min(base + off[u], (uint32_t)CAP);   // slots CAP.. absorb an overflow
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool f = x[u][e] >= thr;
@@ -703,12 +719,12 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
   }
   __syncthreads();   // kept positions and keys are visible
 
-  if (kept < (uint32_t)K || kept > (uint32_t)kFtCap) {   // threshold too high, or too many kept
+  if (kept < (uint32_t)K || kept > (uint32_t)CAP) {   // threshold too high, or too many kept
     topk_stream_row<kFtThreads>(src, n, K, out, sh, ckey);
     return;
   }
 
-  ft_select_kept<PosT, kFtKeep>(ckey, cpos, (int)kept, K, out, sh);
+  ft_select_kept<PosT, CAP / kFtThreads>(ckey, cpos, (int)kept, K, out, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -981,8 +997,8 @@ hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   // 4,710 +- 780 at 2^19, against kFtCap = 5,120 slots); a row that
   // overflows is redone by the streaming selection, several passes over it.
   if (rows_aligned && A.n_k > 65536 && A.n_k <= kFtLongMax && A.n_q >= 4 * device_cu_count()) {
-    hipLaunchKernelGGL((topk_filter_kernel<uint32_t, 16, 3>), grid, dim3(kFtThreads), 0, st, A.scores, A.ld,
-                       A.q_pos, (int)A.n_k, A.top_k, A.idx);
+    hipLaunchKernelGGL((topk_filter_kernel<uint32_t, 16, 3, kFtCap, kBins>), grid, dim3(kFtThreads), 0, st,
+                       A.scores, A.ld, A.q_pos, (int)A.n_k, A.top_k, A.idx);
     return hipGetLastError();
   }
   if (topk_long_wanted(A.n_k) && A.ws && A.ws_bytes >= topk_long_bytes(A.n_q, A.n_k, A.top_k))
@@ -990,9 +1006,12 @@ hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   // 16-byte aligned rows of up to 65,536 scores take the filtered kernel
   // (one pass over the row); longer or unaligned rows are streamed from
   // memory in every pass.
-  if (rows_aligned && A.n_k <= 65536) {
-    hipLaunchKernelGGL((topk_filter_kernel<uint16_t, 8, 4>), grid, dim3(kFtThreads), 0, st, A.scores, A.ld,
-                       A.q_pos, (int)A.n_k, A.top_k, A.idx);
+  if (rows_aligned && A.n_k <= kFtShortMax) {
+    hipLaunchKernelGGL((topk_filter_kernel<uint16_t, 8, 5, kFtCap16, kFtBins16>), grid, dim3(kFtThreads), 0, st,
+                       A.scores, A.ld, A.q_pos, (int)A.n_k, A.top_k, A.idx);
+  } else if (rows_aligned && A.n_k <= 65536) {
+    hipLaunchKernelGGL((topk_filter_kernel<uint16_t, 8, 4, kFtCap, kBins>), grid, dim3(kFtThreads), 0, st,
+                       A.scores, A.ld, A.q_pos, (int)A.n_k, A.top_k, A.idx);
   } else {
     hipLaunchKernelGGL((topk_stream_kernel<1024>), grid, dim3(1024), 0, st, A.scores, A.ld, A.q_pos,
                        (int)A.n_k, A.top_k, A.idx);

@@ -21,8 +21,9 @@ def _positions(n_rows, n_k, top_k, seed):
 
 
 @pytest.mark.parametrize("kind", ["normal", "ints", "ties", "signed_zero", "nan", "nan_heavy"])
-@pytest.mark.parametrize("n_k,top_k", [(300, 128), (5000, 2048), (20000, 2048), (40000, 1), (70000, 2048),
-                                       (140000, 2048)])
+# rows of <= 32,768 scores, <= 65,536 and longer take three different filtered kernels
+@pytest.mark.parametrize("n_k,top_k", [(300, 128), (5000, 2048), (20000, 2048), (32768, 2048), (40000, 1),
+                                       (50000, 2048), (70000, 2048), (140000, 2048)])
 def test_topk_exact(kind, n_k, top_k):
     n_rows = 24
     sc = synth.random_scores(n_k % 1000 + len(kind), n_rows, n_k, kind)
