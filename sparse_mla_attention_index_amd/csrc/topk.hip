@@ -335,7 +335,7 @@ __global__ __launch_bounds__(THREADS, 1) void topk_stream_kernel(const float* __
 // ---------------------------------------------------------------------------
 constexpr int kFtThreads = 256;
 constexpr int kFtWaves = kFtThreads / 64;
-constexpr int kFtCap = 5120;                      // kept positions held in LDS (32-bit positions)
+constexpr int kFtCap = 5120;                      // kept positions held in LDS (rows of > 32,768 scores)
 // For rows of at most 32,768 scores the 16-bit-position kernel holds fewer
 // (4,608) with a 1,024-bin histogram: 31 KiB of LDS, five workgroups per CU
 // instead of four (such rows keep about 3,240 +- 300 with the 2,048-sample
