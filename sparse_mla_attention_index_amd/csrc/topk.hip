@@ -59,7 +59,7 @@ struct TopkShared {
   static constexpr int WAVES = THREADS / 64;
   static constexpr int kBinsN = BINS, kBinBits = __builtin_ctz(BINS);
   static_assert((BINS & (BINS - 1)) == 0, "a power-of-two bin count");
-  uint32_t hist[BINS];
+  alignas(16) uint32_t hist[BINS];
   uint32_t red[WAVES * 2];
   uint32_t bcast[4];
 };
@@ -576,6 +576,11 @@ __device__ void ft_select_kept(const uint32_t* ckey, const PosT* cpos, int C, in
     g_run += w < wave ? sh.red[w] : 0u;
     e_run += w < wave ? sh.red[kFtWaves + w] : 0u;
   }
+  // With a histogram of at least K words, the K selected positions are
+  // assembled there (idle by now) and written out in whole 16-byte pieces,
+  // so the index writes reach memory as full lines rather than as each wave
+  // step's run of 4-byte stores (at 64K these cost ~0.2 ms).
+  constexpr bool kStage = BINS >= SMA_MAX_TOPK_DEV;
   visit(std::true_type{}, [&](int32_t pos, uint64_t mg, uint64_t me) {
     const uint32_t g_before = g_run + __builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
@@ -585,10 +590,22 @@ __device__ void ft_select_kept(const uint32_t* ckey, const PosT* cpos, int C, in
     uint32_t slot = 0xFFFFFFFFu;
     if (is_g) slot = g_before + min(e_before, need_ties);
     if (is_e && e_before < need_ties) slot = g_before + e_before;
-    if (slot < (uint32_t)K) out[slot] = pos;
+    if (slot < (uint32_t)K) {
+      if constexpr (kStage) sh.hist[slot] = (uint32_t)pos;
+      else out[slot] = pos;
+    }
     g_run += (uint32_t)__popcll(mg);
     e_run += (uint32_t)__popcll(me);
   });
+  if constexpr (kStage) {
+    __syncthreads();
+    if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+      for (int i = 4 * tid; i < K; i += 4 * kFtThreads)
+        *reinterpret_cast<u32x4*>(out + i) = *reinterpret_cast<const u32x4*>(&sh.hist[i]);
+    } else {
+      for (int i = tid; i < K; i += kFtThreads) out[i] = (int32_t)sh.hist[i];
+    }
+  }
 }
 
 // PosT holds a position (uint16_t for rows of at most 65,536 scores); SPT
