@@ -216,6 +216,46 @@ static hipError_t launch_idx(const IdxArgs& A, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The queries of the workgroup whose block starts at q0 (one per wave, W
+// waves): for a batch of at most 64 W queries, those of ranks q0 .. q0 + W -
+// 1 in position order (ties by index), so that a block's causal extent, its
+// largest position, wastes little on the block's other queries (a decode
+// batch's positions come in any order); for larger batches, queries q0 ..
+// q0 + W - 1.  Fills s_qid (-1: no query) and s_pos (clamped to [-1, n_k -
+// 1]) for the W slots, using s_allpos (64 W ints) as scratch, and ends with
+// a barrier.
+template <int W>
+__device__ __forceinline__ void idx_block_queries(const int32_t* __restrict__ q_pos, int n_q, int n_k, int q0,
+                                                  int* s_qid, int* s_pos, int* s_allpos) {
+  const int tid = threadIdx.x;
+  auto clamp_pos = [&](int p) { return p < -1 ? -1 : (p > n_k - 1 ? n_k - 1 : p); };
+  if (n_q <= 64 * W) {
+    int p = -1;
+    if (tid < n_q) s_allpos[tid] = p = clamp_pos(q_pos[tid]);
+    if (tid < W) {
+      s_qid[tid] = -1;
+      s_pos[tid] = -1;
+    }
+    __syncthreads();
+    if (tid < n_q) {
+      int rank = 0;
+      for (int j = 0; j < n_q; ++j) {
+        const int pj = s_allpos[j];
+        rank += (pj < p) || (pj == p && j < tid);
+      }
+      if (rank >= q0 && rank < q0 + W) {
+        s_qid[rank - q0] = tid;
+        s_pos[rank - q0] = p;
+      }
+    }
+  } else if (tid < W) {
+    const int qi = q0 + tid;
+    s_qid[tid] = qi < n_q ? qi : -1;
+    s_pos[tid] = qi < n_q ? clamp_pos(q_pos[qi]) : -1;
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // bf16 keys, 64 heads x d_I = 128 (the prefill shape): eight waves, one query
 // each, share a ring of key tiles filled by direct global->LDS loads, so a
@@ -263,7 +303,7 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_kernel(
     float* __restrict__ scores, int64_t ld, int n_qblocks, int n_chunks, int chunk_keys) {
   constexpr int H = 64, DI = 128, KS = DI / 16;
   __shared__ __attribute__((aligned(1024))) uint8_t s_k[kIdxStages][kIdxTileB];
-  __shared__ int s_pos[kIdxWaves];
+  __shared__ int s_pos[kIdxWaves], s_qid[kIdxWaves], s_allpos[64 * kIdxWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -271,13 +311,7 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_kernel(
   const int qb = n_qblocks - 1 - (int)(blockIdx.x / n_chunks);
   const int chunk = (int)(blockIdx.x % n_chunks);
   const int q0 = qb * kIdxWaves;
-
-  if (tid < kIdxWaves) {
-    const int qi = q0 + tid;
-    const int p = qi < n_q ? q_pos[qi] : -1;
-    s_pos[tid] = p < -1 ? -1 : (p > n_k - 1 ? n_k - 1 : p);
-  }
-  __syncthreads();
+  idx_block_queries<kIdxWaves>(q_pos, n_q, n_k, q0, s_qid, s_pos, s_allpos);
   int pmax = -1;
 #pragma unroll
   for (int t = 0; t < kIdxWaves; ++t) pmax = max(pmax, s_pos[t]);
@@ -286,7 +320,8 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_kernel(
   if (k_begin >= k_end) return;   // uniform across the workgroup
   const int ntiles = (k_end - k_begin + kIdxKT - 1) / kIdxKT;
   const int mypos = s_pos[wave];
-  const int qi = min(q0 + wave, n_q - 1);
+  const int myq = s_qid[wave];          // -1: no query in this slot
+  const int qi = myq < 0 ? 0 : myq;
 
   // ---- A operands: the wave's query, head rows 32t + lrow, dims 16j + 8khalf .. +7 ----
   const int lrow = lane & 31, khalf = lane >> 5;
@@ -344,8 +379,8 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_kernel(
     part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
                                                              false)[1]);
     const int key = key0 + lrow;
-    if (khalf == 0 && key0 >= 0 && q0 + wave < n_q && key <= mypos && key < k_end)
-      scores[(int64_t)(q0 + wave) * ld + key] = part;
+    if (khalf == 0 && key0 >= 0 && myq >= 0 && key <= mypos && key < k_end)
+      scores[(int64_t)myq * ld + key] = part;
   };
   // B operands are read one N-tile ahead of their MFMAs (bn), so the last
   // N-tile of tile i reads tile i + 1: the wait below therefore covers tiles
@@ -417,20 +452,14 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_f8k_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t s_c8[kIdxStages][kF8kTileB];   // codes, as stored
   __shared__ __attribute__((aligned(16))) float s_sc[kIdxStages][kIdxKT];
   __shared__ __attribute__((aligned(1024))) uint8_t s_k[2][kIdxTileB];             // widened, swizzled
-  __shared__ int s_pos[kIdxWaves];
+  __shared__ int s_pos[kIdxWaves], s_qid[kIdxWaves], s_allpos[64 * kIdxWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qb = n_qblocks - 1 - (int)(blockIdx.x / n_chunks);
   const int chunk = (int)(blockIdx.x % n_chunks);
   const int q0 = qb * kIdxWaves;
-
-  if (tid < kIdxWaves) {
-    const int qi = q0 + tid;
-    const int p = qi < n_q ? q_pos[qi] : -1;
-    s_pos[tid] = p < -1 ? -1 : (p > n_k - 1 ? n_k - 1 : p);
-  }
-  __syncthreads();
+  idx_block_queries<kIdxWaves>(q_pos, n_q, n_k, q0, s_qid, s_pos, s_allpos);
   int pmax = -1;
 #pragma unroll
   for (int t = 0; t < kIdxWaves; ++t) pmax = max(pmax, s_pos[t]);
@@ -439,7 +468,8 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_f8k_kernel(
   if (k_begin >= k_end) return;   // uniform across the workgroup
   const int ntiles = (k_end - k_begin + kIdxKT - 1) / kIdxKT;
   const int mypos = s_pos[wave];
-  const int qi = min(q0 + wave, n_q - 1);
+  const int myq = s_qid[wave];          // -1: no query in this slot
+  const int qi = myq < 0 ? 0 : myq;
 
   const int lrow = lane & 31, khalf = lane >> 5;
   bf16x8 a[2][KS];
@@ -501,8 +531,8 @@ __global__ __launch_bounds__(64 * kIdxWaves, 1) void idx_score_h64_f8k_kernel(
     part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
                                                              false)[1]);
     const int key = key0 + lrow;
-    if (khalf == 0 && key0 >= 0 && q0 + wave < n_q && key <= mypos && key < k_end)
-      scores[(int64_t)(q0 + wave) * ld + key] = part * sc;
+    if (khalf == 0 && key0 >= 0 && myq >= 0 && key <= mypos && key < k_end)
+      scores[(int64_t)myq * ld + key] = part * sc;
   };
   // tile 0 widened before the loop; iteration i widens tile i + 1 (whose B
   // operands the last N-tile of tile i reads), so the waits cover tiles i
@@ -670,20 +700,14 @@ __global__ __launch_bounds__(64 * kF8Waves, 1) void idx_score_h64_fp8_kernel(
   constexpr int kF8KT = G::KT, kF8NT = G::NT, kF8Stages = S, kF8Loads = G::Loads;
   __shared__ __attribute__((aligned(1024))) uint8_t s_k[S][G::TileB];
   __shared__ __attribute__((aligned(16))) float s_sc[S][G::KT];
-  __shared__ int s_pos[kF8Waves];
+  __shared__ int s_pos[kF8Waves], s_qid[kF8Waves], s_allpos[64 * kF8Waves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qb = n_qblocks - 1 - (int)(blockIdx.x / n_chunks);
   const int chunk = (int)(blockIdx.x % n_chunks);
   const int q0 = qb * kF8Waves;
-
-  if (tid < kF8Waves) {
-    const int qi = q0 + tid;
-    const int p = qi < n_q ? q_pos[qi] : -1;
-    s_pos[tid] = p < -1 ? -1 : (p > n_k - 1 ? n_k - 1 : p);
-  }
-  __syncthreads();
+  idx_block_queries<kF8Waves>(q_pos, n_q, n_k, q0, s_qid, s_pos, s_allpos);
   int pmax = -1;
 #pragma unroll
   for (int t = 0; t < kF8Waves; ++t) pmax = max(pmax, s_pos[t]);
@@ -693,8 +717,9 @@ __global__ __launch_bounds__(64 * kF8Waves, 1) void idx_score_h64_fp8_kernel(
   const int ntiles = (k_end - k_begin + kF8KT - 1) / kF8KT;
   // the wave's query: position (scalar), row (clamped for the operand reads)
   const int mypos = __builtin_amdgcn_readfirstlane(s_pos[wave]);
-  const bool q_ok = q0 + wave < n_q;
-  const int qi = min(q0 + wave, n_q - 1);
+  const int myq = __builtin_amdgcn_readfirstlane(s_qid[wave]);   // -1: no query in this slot
+  const bool q_ok = myq >= 0;
+  const int qi = q_ok ? myq : 0;
 
   // ---- A operands: head row 32t + lrow, bytes 64j + 32 khalf .. +31 ----
   const int lrow = lane & 31, khalf = lane >> 5;
