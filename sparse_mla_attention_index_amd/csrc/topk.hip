@@ -64,13 +64,68 @@ struct TopkShared {
   uint32_t bcast[4];
 };
 
+// Cross-lane steps by DPP (a VALU operand modifier) rather than by
+// ds_bpermute, whose round trip through the LDS unit each step of a chain
+// waits for.  dpp(v, CTRL, ROWS) reads v from the lane CTRL names; lanes with
+// no such source, or outside the rows of the mask ROWS, read 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;   // lane 15 / 31 of a row into the next row(s)
+constexpr int kDppQuadSwap1 = 0xB1, kDppQuadSwap2 = 0x4E;        // quad_perm [1,0,3,2] / [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141, kDppRowMirror = 0x140;     // mirror within 8 / 16 lanes
+
+// Inclusive prefix sum over a wave: shifts by 1, 2, 4, 8 within each row of
+// 16 lanes, then each row adds the total of the rows before it.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
+  (void)lane;
+  v += dpp<kDppRowShr1>(v);
+  v += dpp<kDppRowShr2>(v);
+  v += dpp<kDppRowShr4>(v);
+  v += dpp<kDppRowShr8>(v);
+  v += dpp<kDppRowBcast15, 0xa>(v);   // rows 1 and 3: + rows 0 and 2
+  v += dpp<kDppRowBcast31, 0xc>(v);   // rows 2 and 3: + rows 0-1
   return v;
+}
+
+// Minimum and maximum over a wave, returned to every lane: butterflies
+// within each row of 16 lanes, then the four rows' results read back.
+__device__ __forceinline__ void wave_min_max(uint32_t& mn, uint32_t& mx) {
+  mn = min(mn, dpp<kDppQuadSwap1>(mn));
+  mx = max(mx, dpp<kDppQuadSwap1>(mx));
+  mn = min(mn, dpp<kDppQuadSwap2>(mn));
+  mx = max(mx, dpp<kDppQuadSwap2>(mx));
+  mn = min(mn, dpp<kDppHalfMirror>(mn));
+  mx = max(mx, dpp<kDppHalfMirror>(mx));
+  mn = min(mn, dpp<kDppRowMirror>(mn));
+  mx = max(mx, dpp<kDppRowMirror>(mx));
+  mn = min(min((uint32_t)__builtin_amdgcn_readlane((int)mn, 0), (uint32_t)__builtin_amdgcn_readlane((int)mn, 16)),
+           min((uint32_t)__builtin_amdgcn_readlane((int)mn, 32), (uint32_t)__builtin_amdgcn_readlane((int)mn, 48)));
+  mx = max(max((uint32_t)__builtin_amdgcn_readlane((int)mx, 0), (uint32_t)__builtin_amdgcn_readlane((int)mx, 16)),
+           max((uint32_t)__builtin_amdgcn_readlane((int)mx, 32), (uint32_t)__builtin_amdgcn_readlane((int)mx, 48)));
+}
+
+// Exclusive block-wide prefix of one counter, and its block total.
+template <int THREADS, int BINS>
+__device__ __forceinline__ void block_excl_scan(uint32_t a, uint32_t& ea, uint32_t& ta,
+                                                TopkShared<THREADS, BINS>& sh) {
+  constexpr int kTopkWaves = THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t ia = wave_incl_scan(a, lane);
+  if (lane == 63) sh.red[wave] = ia;
+  __syncthreads();
+  uint32_t pa = 0, sa = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t xa = sh.red[w];
+    if (w < wave) pa += xa;
+    sa += xa;
+  }
+  ea = pa + ia - a;
+  ta = sa;
+  __syncthreads();
 }
 
 // Exclusive block-wide prefix of two counters at once (packed as 2 x 32 bit
@@ -132,11 +187,7 @@ __device__ void topk_stream_row(const float* __restrict__ src, int n, int K, int
 
   // ---- 1. key range ----
   for_each([&](int, uint32_t k) { note(k); });
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  wave_min_max(kmin, kmax);
   if (lane == 0) {
     sh.red[wave] = kmin;
     sh.red[kTopkWaves + wave] = kmax;
@@ -179,8 +230,8 @@ __device__ void topk_stream_row(const float* __restrict__ src, int n, int K, int
       hb[e] = b < nbins ? sh.hist[b] : 0u;
       hsum += hb[e];
     }
-    uint32_t ex, dummy_e, tot, dummy_t;
-    block_excl_scan2<THREADS>(hsum, 0u, ex, dummy_e, tot, dummy_t, sh);
+    uint32_t ex, tot;
+    block_excl_scan<THREADS>(hsum, ex, tot, sh);
     uint32_t above = tot - (ex + hsum);   // keys in bins past this thread's last bin
 #pragma unroll
     for (int e = BPT - 1; e >= 0; --e) {
@@ -223,7 +274,7 @@ __device__ void topk_stream_row(const float* __restrict__ src, int n, int K, int
           const uint32_t x = lane < n_cand ? cand[lane] : 0u;
           uint32_t gt = 0, ge = 0;
           for (int j = 0; j < n_cand; ++j) {
-            const uint32_t y = (uint32_t)__shfl((int)x, j, 64);
+            const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
             gt += y > x;
             ge += y >= x;
           }
@@ -403,11 +454,7 @@ __device__ __forceinline__ void ft_range(const uint32_t (&key)[M], uint32_t& lo,
     kmin = min(kmin, key[j] ? key[j] : 0xFFFFFFFFu);
     kmax = max(kmax, key[j]);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  wave_min_max(kmin, kmax);
   if (lane == 0) {
     sh.red[wave] = kmin;
     sh.red[kFtWaves + wave] = kmax;
@@ -451,8 +498,8 @@ __device__ uint32_t ft_round(const uint32_t (&key)[M], uint32_t& lo, uint32_t& h
     hb[e] = BPT * tid + e < nbins ? hb[e] : 0u;
     hsum += hb[e];
   }
-  uint32_t ex, dummy_e, tot, dummy_t;
-  block_excl_scan2<kFtThreads>(hsum, 0u, ex, dummy_e, tot, dummy_t, sh);
+  uint32_t ex, tot;
+  block_excl_scan<kFtThreads>(hsum, ex, tot, sh);
   uint32_t above = tot - (ex + hsum);   // keys in bins past this thread's last bin
 #pragma unroll
   for (int e = BPT - 1; e >= 0; --e) {
@@ -478,19 +525,29 @@ __device__ uint32_t ft_round(const uint32_t (&key)[M], uint32_t& lo, uint32_t& h
 // Steps 3-4 of the filtered top-k: the K largest of C kept entries (K <= C
 // <= KEEP * kFtThreads; raw score bits ckey[i] of ascending positions
 // cpos[i], no NaN among them), written to out in ascending position order.
-// Called by the whole kFtThreads-thread workgroup.
+// Thread t holds entries M t .. M t + M - 1 (M = ceil(C / kFtThreads),
+// made odd where that fits, so that the strided LDS reads fall on distinct
+// banks) in registers from the start: the threshold rounds count them in
+// any order, and the compaction takes each thread's run in list order after
+// one block-wide scan of the runs' counts.  The K selected positions are
+// assembled in ckey (free once the keys are in registers) and written out in
+// whole 16-byte pieces.  Called by the whole kFtThreads-thread workgroup.
 template <typename PosT, int KEEP, int BINS>
-__device__ void ft_select_kept(const uint32_t* ckey, const PosT* cpos, int C, int K, int32_t* __restrict__ out,
+__device__ void ft_select_kept(uint32_t* ckey, const PosT* cpos, int C, int K, int32_t* __restrict__ out,
                                TopkShared<kFtThreads, BINS>& sh) {
   constexpr int kBits = TopkShared<kFtThreads, BINS>::kBinBits;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int M = (C + kFtThreads - 1) / kFtThreads;
+  if ((M & 1) == 0 && M < KEEP) ++M;
+  const int e0 = M * tid;
   // ---- 3. exact threshold key T among the kept keys ----
-  // (reads at clamped indices, all issued before any is used)
+  // (reads at clamped indices, all issued before any is used; entries past
+  // the thread's run or the list get key 0, below every kept key)
   uint32_t kk[KEEP];
 #pragma unroll
-  for (int j = 0; j < KEEP; ++j) kk[j] = ckey[min(tid + kFtThreads * j, C - 1)];
+  for (int j = 0; j < KEEP; ++j) kk[j] = ckey[min(e0 + j, C - 1)];
 #pragma unroll
-  for (int j = 0; j < KEEP; ++j) kk[j] = tid + kFtThreads * j < C ? score_key(__uint_as_float(kk[j])) : 0u;
+  for (int j = 0; j < KEEP; ++j) kk[j] = j < M && e0 + j < C ? score_key(__uint_as_float(kk[j])) : 0u;
   uint32_t lo, hi, need_ties = (uint32_t)K;
   ft_range<KEEP>(kk, lo, hi, sh);
   for (int round = 0; round < (32 + kBits - 1) / kBits && hi != lo; ++round) {
@@ -533,78 +590,35 @@ __device__ void ft_select_kept(const uint32_t* ckey, const PosT* cpos, int C, in
   const uint32_t T = lo;
 
   // ---- 4. ordered compaction: every kept entry above T and the first
-  // need_ties equal to T, in list (= position) order.  Wave w takes a
-  // contiguous quarter of the list, 64 consecutive entries per step; ballots
-  // rank an entry among those above / equal to T, so the reads and the
-  // writes of a step are coalesced.  (Kept scores are never NaN, so
-  // comparing them as floats with T's score orders them as their keys do,
-  // -0.0 == +0.0 included.) ----
-  const float Tf = key_score(T);
-  const int span = (((C + kFtWaves - 1) / kFtWaves) + 63) & ~63;   // entries per wave, whole steps
-  const int w0 = min(C, wave * span), w1 = min(C, w0 + span);
-  constexpr int kU = 4;   // steps whose reads are in flight together
-  auto visit = [&](auto with_pos, auto&& fn) {
-    for (int b = w0; b < w1; b += 64 * kU) {
-      float v[kU];
-      int32_t ps[kU] = {};
+  // need_ties equal to T, in list (= position) order ----
+  PosT pp[KEEP];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int ic = min(b + 64 * u + lane, C - 1);
-        v[u] = __uint_as_float(ckey[ic]);
-        if constexpr (decltype(with_pos)::value) ps[u] = (int32_t)cpos[ic];
-      }
+  for (int j = 0; j < KEEP; ++j) pp[j] = cpos[min(e0 + j, C - 1)];
+  uint32_t cg = 0, ce = 0;
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const bool in = b + 64 * u + lane < w1;
-        fn(ps[u], __ballot(in && v[u] > Tf), __ballot(in && v[u] == Tf));
-      }
-    }
-  };
-  uint32_t cg = 0, ce = 0;   // this wave's counts
-  visit(std::false_type{}, [&](int32_t, uint64_t mg, uint64_t me) {
-    cg += (uint32_t)__popcll(mg);
-    ce += (uint32_t)__popcll(me);
-  });
-  if (lane == 0) {
-    sh.red[wave] = cg;
-    sh.red[kFtWaves + wave] = ce;
+  for (int j = 0; j < KEEP; ++j) {
+    cg += kk[j] > T;
+    ce += kk[j] == T;
+  }
+  uint32_t g_run, e_run, tg, te;   // entries above / equal to T in earlier threads' runs
+  block_excl_scan2<kFtThreads>(cg, ce, g_run, e_run, tg, te, sh);
+  uint32_t* stage = ckey;
+#pragma unroll
+  for (int j = 0; j < KEEP; ++j) {
+    const uint32_t k = kk[j];
+    uint32_t slot = 0xFFFFFFFFu;
+    if (k > T) slot = g_run + min(e_run, need_ties);
+    if (k == T && e_run < need_ties) slot = g_run + e_run;
+    g_run += k > T;
+    e_run += k == T;
+    if (slot < (uint32_t)K) stage[slot] = (uint32_t)pp[j];
   }
   __syncthreads();
-  uint32_t g_run = 0, e_run = 0;   // entries above / equal to T before this wave's quarter
-#pragma unroll
-  for (int w = 0; w < kFtWaves; ++w) {
-    g_run += w < wave ? sh.red[w] : 0u;
-    e_run += w < wave ? sh.red[kFtWaves + w] : 0u;
-  }
-  // With a histogram of at least K words, the K selected positions are
-  // assembled there (idle by now) and written out in whole 16-byte pieces,
-  // so the index writes reach memory as full lines rather than as each wave
-  // step's run of 4-byte stores (at 64K these cost ~0.2 ms).
-  constexpr bool kStage = BINS >= SMA_MAX_TOPK_DEV;
-  visit(std::true_type{}, [&](int32_t pos, uint64_t mg, uint64_t me) {
-    const uint32_t g_before = g_run + __builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
-    const uint32_t e_before = e_run + __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
-    const bool is_g = (mg >> lane) & 1u, is_e = (me >> lane) & 1u;
-    uint32_t slot = 0xFFFFFFFFu;
-    if (is_g) slot = g_before + min(e_before, need_ties);
-    if (is_e && e_before < need_ties) slot = g_before + e_before;
-    if (slot < (uint32_t)K) {
-      if constexpr (kStage) sh.hist[slot] = (uint32_t)pos;
-      else out[slot] = pos;
-    }
-    g_run += (uint32_t)__popcll(mg);
-    e_run += (uint32_t)__popcll(me);
-  });
-  if constexpr (kStage) {
-    __syncthreads();
-    if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
-      for (int i = 4 * tid; i < K; i += 4 * kFtThreads)
-        *reinterpret_cast<u32x4*>(out + i) = *reinterpret_cast<const u32x4*>(&sh.hist[i]);
-    } else {
-      for (int i = tid; i < K; i += kFtThreads) out[i] = (int32_t)sh.hist[i];
-    }
+  if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+    for (int i = 4 * tid; i < K; i += 4 * kFtThreads)
+      *reinterpret_cast<u32x4*>(out + i) = *reinterpret_cast<const u32x4*>(&stage[i]);
+  } else {
+    for (int i = tid; i < K; i += kFtThreads) out[i] = (int32_t)stage[i];
   }
 }
 
@@ -619,7 +633,7 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
   static_assert(SPT % 4 == 0 && kFtClusterLen % SPT == 0, "whole 16-byte loads within one cluster");
   static_assert(CAP % kFtThreads == 0 && CAP + 4 >= BINS, "whole kept keys per thread; room for the fallback");
   __shared__ TopkShared<kFtThreads, BINS> sh;
-  __shared__ uint32_t ckey[CAP + 4];   // score bits of the kept positions (the streaming fallback's scratch)
+  __shared__ alignas(16) uint32_t ckey[CAP + 4];   // score bits of the kept positions (the streaming fallback's scratch)
   __shared__ PosT cpos[CAP + 4];       // kept positions, ascending
   __shared__ uint32_t tab[2][kFtWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -912,7 +926,7 @@ __global__ __launch_bounds__(kFtThreads) void topk_long_final(const float* __res
                                                               const uint32_t* __restrict__ cnt,
                                                               int32_t* __restrict__ idx) {
   __shared__ TopkShared<kFtThreads> sh;
-  __shared__ uint32_t ckey[kLgCap];   // kept score bits (the streaming fallback's scratch)
+  __shared__ alignas(16) uint32_t ckey[kLgCap];   // kept score bits (the streaming fallback's scratch)
   __shared__ int32_t cpos[kLgCap];    // kept positions, ascending
   __shared__ uint32_t s_off[kFtThreads];
   __shared__ uint32_t s_fail;
@@ -937,8 +951,8 @@ __global__ __launch_bounds__(kFtThreads) void topk_long_final(const float* __res
     const int c = g0 + tid;
     const uint32_t v = c < nc ? rc[c] : 0u;
     if (v > (uint32_t)kLgChunkCap) s_fail = 1u;
-    uint32_t ex, e2, tv, t2;
-    block_excl_scan2<kFtThreads>(v, 0u, ex, e2, tv, t2, sh);
+    uint32_t ex, tv;
+    block_excl_scan<kFtThreads>(v, ex, tv, sh);
     s_off[tid] = total + ex;
     __syncthreads();
     if (s_fail || total + tv > (uint32_t)kLgCap) {
