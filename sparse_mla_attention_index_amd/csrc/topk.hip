@@ -442,17 +442,19 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Range [lo, hi] of the nonzero keys the workgroup holds (M per thread, 0 =
-// none).
+// Range [lo, hi] of the nonzero keys the workgroup holds (the first m <= M
+// registers per thread, m uniform; 0 = none).
 template <int M, int BINS>
 __device__ __forceinline__ void ft_range(const uint32_t (&key)[M], uint32_t& lo, uint32_t& hi,
-                                         TopkShared<kFtThreads, BINS>& sh) {
+                                         TopkShared<kFtThreads, BINS>& sh, int m = M) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
-    kmin = min(kmin, key[j] ? key[j] : 0xFFFFFFFFu);
-    kmax = max(kmax, key[j]);
+    if (j < m) {
+      kmin = min(kmin, key[j] ? key[j] : 0xFFFFFFFFu);
+      kmax = max(kmax, key[j]);
+    }
   }
   wave_min_max(kmin, kmax);
   if (lane == 0) {
@@ -470,13 +472,16 @@ __device__ __forceinline__ void ft_range(const uint32_t (&key)[M], uint32_t& lo,
   __syncthreads();
 }
 
-// One refinement round over the workgroup's keys (M per thread): cut [lo, hi]
-// into <= 2,048 bins of equal width and keep the bin holding the
-// remaining-th largest key inside [lo, hi].  Narrows lo, hi and remaining;
-// returns how many keys the kept bin holds.
+// One refinement round over the workgroup's keys (the first m <= M
+// registers per thread, m uniform): cut [lo, hi] into <= BINS bins of equal
+// width and keep the bin holding the remaining-th largest key at or above
+// lo.  Keys above hi are counted in the last bin when open_top is set (its
+// upper edge then becomes the largest key), and ignored otherwise.  Narrows
+// lo, hi and remaining; returns how many keys the kept bin holds.  Thread 0
+// also zeroes bcast[3] for a caller that gathers the bin's keys next.
 template <int M, int BINS>
 __device__ uint32_t ft_round(const uint32_t (&key)[M], uint32_t& lo, uint32_t& hi, uint32_t& remaining,
-                             TopkShared<kFtThreads, BINS>& sh) {
+                             TopkShared<kFtThreads, BINS>& sh, int m = M, bool open_top = false) {
   constexpr int kBits = TopkShared<kFtThreads, BINS>::kBinBits;
   const int tid = threadIdx.x;
   const uint32_t width = hi - lo;
@@ -484,10 +489,12 @@ __device__ uint32_t ft_round(const uint32_t (&key)[M], uint32_t& lo, uint32_t& h
   const int shift = bits > kBits ? bits - kBits : 0;
   const int nbins = (int)(width >> shift) + 1;
   for (int b = tid; b < nbins; b += kFtThreads) sh.hist[b] = 0u;
+  if (tid == 0) sh.bcast[3] = 0u;
   __syncthreads();
+  const uint32_t top = open_top ? 0xFFFFFFFFu : hi;
 #pragma unroll
   for (int j = 0; j < M; ++j)
-    if (key[j] >= lo && key[j] <= hi) atomicAdd(&sh.hist[(key[j] - lo) >> shift], 1u);
+    if (j < m && key[j] >= lo && key[j] <= top) atomicAdd(&sh.hist[min((key[j] - lo) >> shift, (uint32_t)nbins - 1)], 1u);
   __syncthreads();
   constexpr int BPT = BINS / kFtThreads;
   uint32_t hb[BPT], hsum = 0;
@@ -512,13 +519,14 @@ __device__ uint32_t ft_round(const uint32_t (&key)[M], uint32_t& lo, uint32_t& h
     above += hb[e];
   }
   __syncthreads();
+  // (no barrier after these reads: the next writer of bcast[0..2] is a later
+  // round's, two barriers on, and the histogram's reads are all done)
   const uint32_t bsel = sh.bcast[0], above_sel = sh.bcast[1], in_bin = sh.bcast[2];
-  __syncthreads();
   remaining -= above_sel;
   const uint64_t nlo = (uint64_t)lo + ((uint64_t)bsel << shift);
   const uint64_t nhi = nlo + ((uint64_t)1 << shift) - 1;
   lo = (uint32_t)nlo;
-  hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+  hi = open_top && (int)bsel == nbins - 1 ? 0xFFFFFFFFu : (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
   return in_bin;
 }
 
@@ -529,16 +537,21 @@ __device__ uint32_t ft_round(const uint32_t (&key)[M], uint32_t& lo, uint32_t& h
 // made odd where that fits, so that the strided LDS reads fall on distinct
 // banks) in registers from the start: the threshold rounds count them in
 // any order, and the compaction takes each thread's run in list order after
-// one block-wide scan of the runs' counts.  The K selected positions are
-// assembled in ckey (free once the keys are in registers) and written out in
-// whole 16-byte pieces.  Called by the whole kFtThreads-thread workgroup.
+// one block-wide scan of the runs' counts; loops over the registers stop at
+// M.  The K selected positions are assembled in ckey (free once the keys are
+// in registers) and written out in whole 16-byte pieces.  With klo > 0 every
+// kept key is at least klo (the filter's threshold) and khi is an estimate of
+// the largest (the sample's largest): the first round bins [klo, khi] with an
+// open top instead of first reducing the keys' range.  Called by the whole
+// kFtThreads-thread workgroup.
 template <typename PosT, int KEEP, int BINS>
 __device__ void ft_select_kept(uint32_t* ckey, const PosT* cpos, int C, int K, int32_t* __restrict__ out,
-                               TopkShared<kFtThreads, BINS>& sh) {
+                               TopkShared<kFtThreads, BINS>& sh, uint32_t klo = 0u, uint32_t khi = 0u) {
   constexpr int kBits = TopkShared<kFtThreads, BINS>::kBinBits;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   int M = (C + kFtThreads - 1) / kFtThreads;
   if ((M & 1) == 0 && M < KEEP) ++M;
+  M = __builtin_amdgcn_readfirstlane(M);
   const int e0 = M * tid;
   // ---- 3. exact threshold key T among the kept keys ----
   // (reads at clamped indices, all issued before any is used; entries past
@@ -549,16 +562,23 @@ __device__ void ft_select_kept(uint32_t* ckey, const PosT* cpos, int C, int K, i
 #pragma unroll
   for (int j = 0; j < KEEP; ++j) kk[j] = j < M && e0 + j < C ? score_key(__uint_as_float(kk[j])) : 0u;
   uint32_t lo, hi, need_ties = (uint32_t)K;
-  ft_range<KEEP>(kk, lo, hi, sh);
-  for (int round = 0; round < (32 + kBits - 1) / kBits && hi != lo; ++round) {
-    const uint32_t in_bin = ft_round<KEEP>(kk, lo, hi, need_ties, sh);
+  const bool bounded = klo != 0u && khi > klo;
+  if (bounded) {
+    lo = klo;
+    hi = khi;
+  } else {
+    ft_range<KEEP>(kk, lo, hi, sh);
+  }
+  // A round narrows the range by kBits bits; the open-topped first round
+  // may leave a range of up to 32 bits, hence one more round.
+  for (int round = 0; round < (32 + kBits - 1) / kBits + 1 && hi != lo; ++round) {
+    const uint32_t in_bin = ft_round<KEEP>(kk, lo, hi, need_ties, sh, KEEP, bounded && round == 0);
     if (hi != lo && in_bin <= 64) {
-      // one wave ranks the bin's keys: T has fewer than need_ties of them
-      // above it and at least need_ties at or above it.  Each thread claims
-      // room for all of its bin keys with one atomic.
+      // every wave ranks the bin's keys (gathered once): T has fewer than
+      // need_ties of them above it and at least need_ties at or above it.
+      // Each thread claims room for all of its bin keys with one atomic
+      // (bcast[3] was zeroed by the round).
       uint32_t* list = sh.hist;
-      if (tid == 0) sh.bcast[3] = 0u;
-      __syncthreads();
       uint32_t mine = 0;
 #pragma unroll
       for (int j = 0; j < KEEP; ++j) mine += kk[j] >= lo && kk[j] <= hi;
@@ -567,24 +587,20 @@ __device__ void ft_select_kept(uint32_t* ckey, const PosT* cpos, int C, int K, i
       for (int j = 0; j < KEEP; ++j)
         if (kk[j] >= lo && kk[j] <= hi) list[at++] = kk[j];
       __syncthreads();
-      if (wave == 0) {
-        const int nb = (int)in_bin;
-        const uint32_t x = lane < nb ? list[lane] : 0u;
-        uint32_t gt = 0, ge = 0;
-        for (int j = 0; j < nb; ++j) {
-          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
-          gt += y > x;
-          ge += y >= x;
-        }
-        if (lane < nb && gt < need_ties && need_ties <= ge) {   // every such lane holds T
-          sh.bcast[0] = x;
-          sh.bcast[1] = need_ties - gt;
-        }
+      const int nb = (int)in_bin;
+      const uint32_t x = lane < nb ? list[lane] : 0u;
+      uint32_t gt = 0, ge = 0;
+      for (int j = 0; j < nb; ++j) {
+        const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
+        gt += y > x;
+        ge += y >= x;
       }
-      __syncthreads();
-      lo = hi = sh.bcast[0];
-      need_ties = sh.bcast[1];
-      __syncthreads();
+      // every lane that qualifies holds T; take the first
+      const uint64_t q = __ballot(lane < nb && gt < need_ties && need_ties <= ge);
+      const int src = (int)__builtin_ctzll(q);
+      const uint32_t Tk = (uint32_t)__builtin_amdgcn_readlane((int)x, src);
+      need_ties -= (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
+      lo = hi = Tk;
     }
   }
   const uint32_t T = lo;
@@ -680,6 +696,7 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
   f32x4 xa[kFtU], xb[kFtU];
   load(0, xa);
   float thr = -INFINITY;
+  uint32_t klo = 0u, khi = 0u;   // the threshold's key and the largest sample's (0: no sample)
   if (sampled) {
     uint32_t sk[SPT];
 #pragma unroll
@@ -688,6 +705,7 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
     const uint32_t r0 = (uint32_t)fminf(ceilf(1.3f * mu + 3.f * sqrtf(mu) + 4.f), (float)kSamples);
     uint32_t lo, hi, rem = r0;
     ft_range<SPT>(sk, lo, hi, sh);
+    khi = __builtin_amdgcn_readfirstlane(hi);   // uniform: kept in a scalar register across the pass
     if (hi != lo) {
       // a key range spanning both signs leaves coarse bins near the top:
       // one more round when the kept bin holds many samples
@@ -695,6 +713,7 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
       if (hi != lo && in_bin > kFtRefineBin) ft_round<SPT>(sk, lo, hi, rem, sh);
     }
     thr = key_score(lo);   // at least r0 samples lie at or above it
+    klo = __builtin_amdgcn_readfirstlane(lo);
   }
 
   // ---- 2. one pass: positions with score >= thr, in ascending order ----
@@ -759,7 +778,7 @@ __global__ __launch_bounds__(kFtThreads, OCC) void topk_filter_kernel(const floa
     return;
   }
 
-  ft_select_kept<PosT, CAP / kFtThreads>(ckey, cpos, (int)kept, K, out, sh);
+  ft_select_kept<PosT, CAP / kFtThreads>(ckey, cpos, (int)kept, K, out, sh, klo, khi);
 }
 
 // ---------------------------------------------------------------------------
