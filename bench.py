@@ -412,6 +412,37 @@ def run_workload(name, args, headline):
               "project_out_frac_hbm": round(b_po / (t_po * 1e-3) / 1e9 / acc.PEAK_HBM_GBS, 4)}
         _log(f"absorption: absorb_q {t_aq:.3f} ms, project_out {t_po:.3f} ms")
 
+    # Where the indexer overtakes sparse MLA on this GPU (the pages place
+    # that point per GPU for their deployments): the same prompt cut to its
+    # first L tokens, L = 8K .. 64K, indexer and attention timed apart; the
+    # crossover is interpolated between the two sizes that bracket it.
+    xover = None
+    if name == "prefill64k":
+        pts = []
+        for L in range(8192, n_q + 1, 8192):
+            sc_L = ws[: L * L * 4].view(torch.float32).view(L, L)
+            idx_L = idx[:L]
+            t_i = timed(lambda: sma.index_scores(q_idx[:L], wts[:L], k_idx[:L], q_pos[:L], k_scale=k_scale,
+                                                 scores=sc_L), reps)
+            sma.topk_select(sc_L, q_pos[:L], w.top_k, idx=idx_L)
+            t_m = timed(lambda: sma.sparse_mla_prefill(q[:L], kv[:L], idx_L, w.sm_scale, kv_scale=kv_scale,
+                                                       out=out[:L], workspace=ws[L * L * 4:]), reps)
+            pos_L = pos_np[:L]
+            pts.append({"L": L, "index_scores_ms": round(t_i, 4), "sparse_mla_ms": round(t_m, 4),
+                        "index_over_mla_flops": round(acc.causal_pairs(pos_L) * acc.indexer_flops_per_pair(
+                            w.h_idx, w.d_idx) / acc.mla_flops(pos_L, w.top_k), 4)})
+        step()   # leave the full prompt's results in out/idx for the parity sample
+        cross = None
+        for a, b in zip(pts, pts[1:]):
+            da = a["index_scores_ms"] - a["sparse_mla_ms"]
+            db = b["index_scores_ms"] - b["sparse_mla_ms"]
+            if da < 0 <= db:
+                cross = round(a["L"] + (b["L"] - a["L"]) * (-da) / (db - da))
+                break
+        xover = {"points": pts, "crossover_tokens": cross,
+                 "flop_crossover_tokens": round(acc.flop_crossover_tokens(w.h_idx, w.d_idx, w.top_k))}
+        _log(f"{name}: indexer overtakes sparse MLA at L ~ {cross} (FLOP crossover {xover['flop_crossover_tokens']})")
+
     # context, not part of the path: the bf16 rate the vendor GEMM library
     # (hipBLASLt, through torch.matmul) reaches on a large square-ish product
     # on this GPU, the practical ceiling the MFMA-bound kernels above are
@@ -708,6 +739,8 @@ def run_workload(name, args, headline):
         rec["context_library_gemm"] = lib_gemm
     if dmha:
         rec["dense_mha_vs_forced_mqa"] = dmha
+    if xover:
+        rec["indexer_mla_crossover"] = xover
     return rec
 
 

@@ -108,3 +108,26 @@ def mla_bytes(q_pos, top_k: int, row_bytes: int, out_bytes: int, heads: int = N_
     n_q = q_pos.size
     return (selected_rows(q_pos, top_k) * row_bytes + n_q * top_k * 4
             + n_q * heads * (D_QK * 2 + D_V * out_bytes))
+
+
+def flop_crossover_tokens(h_idx: int, d_idx: int, top_k: int, heads: int = N_HEADS) -> int:
+    """Smallest prompt length L whose indexer FLOPs (every causal pair of
+    positions 0 .. L-1) reach its sparse-MLA FLOPs (min(p + 1, top_k)
+    selected rows per position).  Past top_k the indexer grows as L^2 and
+    the attention as L, which is why the GLM-5.3 part 2 article ("Pourquoi
+    pas TP ou DP ?") has the indexer overtake sparse MLA at some per-GPU
+    prompt length."""
+    def diff(L: int) -> int:
+        pos = np.arange(L, dtype=np.int64)
+        return causal_pairs(pos) * indexer_flops_per_pair(h_idx, d_idx) - mla_flops(pos, top_k, heads)
+
+    lo, hi = 1, 1
+    while diff(hi) < 0:
+        lo, hi = hi, hi * 2
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if diff(mid) < 0:
+            lo = mid + 1
+        else:
+            hi = mid
+    return lo

@@ -81,3 +81,22 @@ def test_query_positions():
     assert p4[0] == 7 * 8192 and p4[8192] == 8 * 8192 and p4.size == 16384
     p5 = synth.query_positions(synth.workload(5))
     assert p5.size == 64 and p5.min() >= 900_000 and p5.max() <= 1_048_575
+
+
+def test_flop_crossover_against_closed_form():
+    # Past top_k the causal sums have closed forms: indexer L(L+1)/2 pairs of
+    # 2 H_I d_I FLOPs, attention K(K+1)/2 + (L - K) K rows of 64 (2*576 +
+    # 2*512) FLOPs.  The helper's answer is the first L where the first
+    # reaches the second; without the first K queries' ramp the crossover
+    # would be 2 * 139,264 * K / (2 H_I d_I) = 34,816 for the 64 x 128
+    # indexer and K = 2,048.
+    def gap(L, h, d, k):
+        return L * (L + 1) // 2 * 2 * h * d - (k * (k + 1) // 2 + (L - k) * k) * 64 * (2 * 576 + 2 * 512)
+
+    for h, d, k in ((64, 128, 2048), (8, 64, 128), (64, 128, 512)):
+        L = accounting.flop_crossover_tokens(h, d, k)
+        assert L > k
+        assert gap(L, h, d, k) >= 0 > gap(L - 1, h, d, k)
+    approx = 2 * 64 * (2 * 576 + 2 * 512) * 2048 // (2 * 64 * 128)
+    assert approx == 34816
+    assert abs(accounting.flop_crossover_tokens(64, 128, 2048) - approx) < 0.04 * approx
