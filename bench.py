@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="query rows in the headline's CPU-oracle sample (0: the per-workload default)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--power", action="store_true",
+                    help="after the headline's timing, run each of its kernels alone for a few seconds while "
+                         "amd-smi samples the board's power and shader clocks")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps (a known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -121,6 +124,61 @@ def host(t, view=None):
     if view is np.uint8:
         return a.view(torch.uint8).numpy()
     return a.numpy()
+
+
+def _smi_sample():
+    """(socket power W, mean shader clock MHz over the XCDs) from one amd-smi
+    reading of GPU 0, or None when the tool or a field is missing."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True, text=True,
+                           timeout=10)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    g = d[0] if isinstance(d, list) and d else d
+    if isinstance(g, dict) and "gpu_data" in g:
+        g = g["gpu_data"][0]
+    try:
+        watts = float(g["power"]["socket_power"]["value"])
+        clocks = [float(v["clk"]["value"]) for k, v in g["clock"].items() if k.startswith("gfx_")]
+        return watts, sum(clocks) / len(clocks)
+    except (KeyError, TypeError, ValueError, ZeroDivisionError):
+        return None
+
+
+def power_under(fn, seconds=4.0, settle=1.0):
+    """Run fn back to back for `seconds` while a thread samples amd-smi every
+    0.2 s; returns the median power and clock over the samples taken after
+    the first `settle` seconds (the board's power management needs about a
+    second to reach its steady state)."""
+    import threading
+
+    import torch
+    rows, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            rows.append((time.time(), _smi_sample()))
+            time.sleep(0.2)
+
+    th = threading.Thread(target=sampler)
+    t0 = time.time()
+    th.start()
+    n = 0
+    while time.time() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    ok = [v for t, v in rows if v is not None and t - t0 >= settle]
+    if not ok:
+        return None
+    return {"launches": n, "samples": len(ok), "socket_power_w": float(np.median([v[0] for v in ok])),
+            "gfx_clock_mhz": round(float(np.median([v[1] for v in ok])), 1)}
 
 
 def _threshold_rule_ok(oracle, got, ref_scores, top_k, rel=1e-3):
@@ -411,6 +469,26 @@ def run_workload(name, args, headline):
               "absorb_q_frac_hbm": round(b_aq / (t_aq * 1e-3) / 1e9 / acc.PEAK_HBM_GBS, 4),
               "project_out_frac_hbm": round(b_po / (t_po * 1e-3) / 1e9 / acc.PEAK_HBM_GBS, 4)}
         _log(f"absorption: absorb_q {t_aq:.3f} ms, project_out {t_po:.3f} ms")
+
+    # Board power and shader clock under each kernel of the step run alone
+    # (the headline only, on request): whether a kernel's clock is held down
+    # by the board's power limit.
+    power = None
+    if headline and args.power:
+        power = {"idle": None}
+        time.sleep(1.5)
+        base = [v for v in (_smi_sample() for _ in range(3)) if v is not None]
+        if base:
+            power["idle"] = {"socket_power_w": float(np.median([v[0] for v in base])),
+                             "gfx_clock_mhz": round(float(np.median([v[1] for v in base])), 1)}
+        power["index_scores"] = power_under(lambda: sma.index_scores(q_idx[:nb], wts[:nb], k_idx, q_pos[:nb],
+                                                                     k_scale=k_scale, scores=scores))
+        power["topk_select"] = power_under(lambda: sma.topk_select(scores, q_pos[:nb], w.top_k, idx=idx[:nb],
+                                                                   workspace=topk_ws))
+        step()
+        power["sparse_mla"] = power_under(lambda: sma.sparse_mla_prefill(q, kv, idx, w.sm_scale, kv_scale=kv_scale,
+                                                                         out=out, workspace=ws))
+        _log(f"{name}: power " + json.dumps(power))
 
     # Where the indexer overtakes sparse MLA on this GPU (the pages place
     # that point per GPU for their deployments): the same prompt cut to its
@@ -741,6 +819,8 @@ def run_workload(name, args, headline):
         rec["dense_mha_vs_forced_mqa"] = dmha
     if xover:
         rec["indexer_mla_crossover"] = xover
+    if power:
+        rec["power"] = power
     return rec
 
 
