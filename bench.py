@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="query rows in the headline's CPU-oracle sample (0: the per-workload default)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--crossover", action="store_true",
+                    help="also time the indexer and sparse MLA on the 64K prompt cut to 8K, 16K, .. 64K tokens "
+                         "(where the indexer overtakes the attention)")
     ap.add_argument("--power", action="store_true",
                     help="after the headline's timing, run each of its kernels alone for a few seconds while "
                          "amd-smi samples the board's power and shader clocks")
@@ -495,7 +498,7 @@ def run_workload(name, args, headline):
     # first L tokens, L = 8K .. 64K, indexer and attention timed apart; the
     # crossover is interpolated between the two sizes that bracket it.
     xover = None
-    if name == "prefill64k":
+    if name == "prefill64k" and args.crossover:
         pts = []
         for L in range(8192, n_q + 1, 8192):
             sc_L = ws[: L * L * 4].view(torch.float32).view(L, L)
