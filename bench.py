@@ -498,7 +498,9 @@ def run_workload(name, args, headline):
     # first L tokens, L = 8K .. 64K, indexer and attention timed apart; the
     # crossover is interpolated between the two sizes that bracket it.
     xover = None
-    if name == "prefill64k" and args.crossover:
+    if name == "prefill64k" and args.crossover and ws.numel() < n_q * n_q * 4 + mla_b:
+        _log(f"{name}: crossover skipped: the workspace holds a score block of {nb} rows, not every row")
+    elif name == "prefill64k" and args.crossover:
         pts = []
         for L in range(8192, n_q + 1, 8192):
             sc_L = ws[: L * L * 4].view(torch.float32).view(L, L)
