@@ -54,6 +54,11 @@ Pins: tests/test_oracle_*.py check each function against what the pages and
 the mathematics fix (integer brute force, library routines for the dense and
 non-absorbed special cases, invariants, the FP8 library cast, the pages'
 printed byte and FLOP figures).
+
+Parity unpinned: fp8_ds_mla_rows_to_f64 beyond the row's 656 bytes.  The
+pages give only the size; the order of codes, scales and rope inside the
+row is a reading of FlashMLA's description, and the test that checks the
+decoder builds its rows from that same reading.
 """
 from __future__ import annotations
 
@@ -106,7 +111,8 @@ def fp8_ds_mla_rows_to_f64(rows: np.ndarray) -> np.ndarray:
     FlashMLA's public description gives): bytes 0..511 are the e4m3fn codes
     of latent dims 0..511, bytes 512..527 four little-endian fp32 scales,
     scale b for dims 128b .. 128b+127, and bytes 528..655 the 64 rope dims
-    512..575 as bf16, unscaled.  rows uint8 [n, 656] -> float64 [n, 576]."""
+    512..575 as bf16, unscaled.  rows uint8 [n, 656] -> float64 [n, 576].
+    Parity unpinned beyond the 656 bytes (the pages do not give the layout)."""
     rows = np.ascontiguousarray(rows, dtype=np.uint8)
     if rows.ndim != 2 or rows.shape[1] != DS_ROW_BYTES:
         raise ValueError("fp8_ds_mla rows are uint8 [n, 656]")
