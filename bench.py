@@ -165,18 +165,20 @@ def power_under(fn, seconds=4.0, settle=1.0):
             rows.append((time.time(), _smi_sample()))
             time.sleep(0.2)
 
-    th = threading.Thread(target=sampler)
+    th = threading.Thread(target=sampler, daemon=True)
     t0 = time.time()
     th.start()
     n = 0
-    while time.time() - t0 < seconds:
-        fn()
-        n += 1
-        if n % 4 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    stop.set()
-    th.join()
+    try:
+        while time.time() - t0 < seconds:
+            fn()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    finally:
+        stop.set()
+        th.join()
     ok = [v for t, v in rows if v is not None and t - t0 >= settle]
     if not ok:
         return None
