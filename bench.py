@@ -13,7 +13,11 @@ top-level fields of the JSON line.  Unless --only is given, every other
 workload is then run the same way (W warm-up steps, K timed steps) and
 reported under "configs": `tiny` (L = 512, top_k = 128, integer indexer),
 `prefill16k`, `pcp` (one PCP8 rank's share of a 131,072-token prompt, ranks
-7 and 0) and `decode` (64 queries over a 1,048,576-token FP8 context).
+7 and 0) and `decode` (64 queries over a 1,048,576-token FP8 context), and
+the 64K headline also gets two legs after its timing (`--crossover` and
+`--power` ask for them with --only): the indexer and the attention timed on
+the prompt cut to 8K .. 64K tokens, and the board's power and shader clock
+(amd-smi) under each kernel of its step run alone.
 
 For each workload every kernel is also timed on its own (HIP events on the
 stream it runs on), the dominant kernel is placed against its roofline, the
@@ -57,10 +61,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--crossover", action="store_true",
                     help="also time the indexer and sparse MLA on the 64K prompt cut to 8K, 16K, .. 64K tokens "
-                         "(where the indexer overtakes the attention)")
+                         "(where the indexer overtakes the attention; on by default without --only)")
     ap.add_argument("--power", action="store_true",
                     help="after the headline's timing, run each of its kernels alone for a few seconds while "
-                         "amd-smi samples the board's power and shader clocks")
+                         "amd-smi samples the board's power and shader clocks (on by default without --only)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps (a known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -479,7 +483,7 @@ def run_workload(name, args, headline):
     # (the headline only, on request): whether a kernel's clock is held down
     # by the board's power limit.
     power = None
-    if headline and args.power:
+    if headline and (args.power or not args.only):
         power = {"idle": None}
         time.sleep(1.5)
         base = [v for v in (_smi_sample() for _ in range(3)) if v is not None]
@@ -500,9 +504,10 @@ def run_workload(name, args, headline):
     # first L tokens, L = 8K .. 64K, indexer and attention timed apart; the
     # crossover is interpolated between the two sizes that bracket it.
     xover = None
-    if name == "prefill64k" and args.crossover and ws.numel() < n_q * n_q * 4 + mla_b:
+    want_xover = name == "prefill64k" and headline and (args.crossover or not args.only)
+    if want_xover and ws.numel() < n_q * n_q * 4 + mla_b:
         _log(f"{name}: crossover skipped: the workspace holds a score block of {nb} rows, not every row")
-    elif name == "prefill64k" and args.crossover:
+    elif want_xover:
         pts = []
         for L in range(8192, n_q + 1, 8192):
             sc_L = ws[: L * L * 4].view(torch.float32).view(L, L)
